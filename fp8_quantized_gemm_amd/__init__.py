@@ -1,0 +1,21 @@
+"""fp8_quantized_gemm_amd: FP8 E4M3 per-tensor-scaled linear layers and the
+NestedFP dual-precision GEMM for AMD MI355X (gfx950).
+
+The compute lives in ``libfp8q.so`` (hand-written HIP kernels behind a C ABI,
+declared in ``include/fp8q.h``).  ``fp8_quantized_gemm_amd.fp8q`` is the thin
+ctypes binding with the same entry-point names; importing any of those names
+from this package loads the library and raises if it has not been built.
+"""
+_API = (
+    "fp8_quantize_act", "fp8_gemm", "nested_split", "nested_rebuild_fp16",
+    "nested_gemm_fp16", "nested_gemm_fp8", "abi_version", "Fp8qError",
+)
+
+__all__ = list(_API)
+
+
+def __getattr__(name):
+    if name in _API:
+        from . import fp8q  # loads libfp8q.so; raises loudly if it is missing
+        return getattr(fp8q, name)
+    raise AttributeError(name)

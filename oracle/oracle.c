@@ -1,0 +1,454 @@
+/*
+ * fp8q oracle: a plain, slow, obviously-correct CPU model of the FP8 linear
+ * layer and of the NestedFP dual-precision GEMM.
+ *
+ * TEST INFRASTRUCTURE ONLY.  Nothing on the product path may call, link or
+ * load this file: only the tests, the package smoke check and the CPU-baseline
+ * leg of the benchmark use it.  It shares no code, header or table with the
+ * HIP library; the two meet only through the seeded input generator, which
+ * holds none of the method's arithmetic.
+ *
+ * Pages cited (full titles and addresses are listed in the design notes):
+ *   [RTX4060]  intelliparadigm.com/article/weixin_29051149/2151670
+ *              (7B model on an RTX 4060 with FP8 E4M3)
+ *   [C++FP8]   "C++与FP8量化：大模型推理部署的系统级优化实践" (tqpw.cn/news/201730)
+ *   [NestedFP] "NestedFP双精度推理框架：LLM部署中的内存与计算优化"
+ *              (intelliparadigm.com/article/weixin_42537919/2229392)
+ *
+ * Every floating-point format below is written from its published bit-level
+ * definition: value = (-1)^s * 2^(e-bias) * (1 + m/2^p) for normals and
+ * (-1)^s * 2^(1-bias) * (m/2^p) for subnormals.  Rounding to a format is done
+ * in double precision by scaling with an exact power of two and calling
+ * nearbyint() under the default round-to-nearest-even mode, so the only
+ * rounding is the one the definition asks for.
+ *
+ * Parity status: every function here is pinned by a CPU test against a library
+ * routine, a closed form, brute force in exact rational arithmetic or an
+ * invariant; none is "parity unpinned".
+ */
+#include <fenv.h>
+#include <math.h>
+#include <pthread.h>
+#include <stdint.h>
+#include <stdlib.h>
+#include <string.h>
+
+#define ORC_BF16 0
+#define ORC_FP16 1
+
+/* ------------------------------------------------------------------------ */
+/* Generic helpers                                                           */
+/* ------------------------------------------------------------------------ */
+
+static float u32_as_f32(uint32_t u) { float f; memcpy(&f, &u, 4); return f; }
+static uint32_t f32_as_u32(float f) { uint32_t u; memcpy(&u, &f, 4); return u; }
+
+/*
+ * Round a finite, non-negative magnitude `a` to the nearest value of a binary
+ * format with `p` stored mantissa bits and minimum normal exponent `emin`
+ * (subnormals included, exponent unbounded above), ties to even.
+ * The quantum (spacing of representable values) around `a` is
+ * 2^(max(exponent(a), emin) - p); a/quantum is exact in double because the
+ * division is by a power of two.
+ */
+static double round_to_format(double a, int p, int emin)
+{
+    if (a == 0.0) return 0.0;
+    int e2;
+    (void)frexp(a, &e2);          /* a = f * 2^e2 with f in [0.5,1): exponent(a) = e2-1 */
+    int e = e2 - 1;
+    if (e < emin) e = emin;
+    double quantum = ldexp(1.0, e - p);
+    return nearbyint(a / quantum) * quantum;   /* FE_TONEAREST: ties to even */
+}
+
+/* ------------------------------------------------------------------------ */
+/* bfloat16: 1 sign, 8 exponent (bias 127), 7 mantissa bits.                 */
+/* The activation dtype of the FP8 GEMM's output and of its input            */
+/* ([C++FP8] §3.3, kernel name ..._e4m3bf16_e4m3f32_f32_tn).                 */
+/* ------------------------------------------------------------------------ */
+
+float orc_bf16_decode(uint16_t b)
+{
+    /* bf16 is the upper half of an IEEE binary32. */
+    return u32_as_f32((uint32_t)b << 16);
+}
+
+uint16_t orc_bf16_encode(float f)
+{
+    uint32_t u = f32_as_u32(f);
+    uint16_t sign = (uint16_t)((u >> 16) & 0x8000u);
+    if (isnan(f)) return (uint16_t)(sign | 0x7FC0u);
+    double a = fabs((double)f);
+    if (isinf(f)) return (uint16_t)(sign | 0x7F80u);
+    double r = round_to_format(a, 7, -126);
+    if (r > 0x1.FEp127) return (uint16_t)(sign | 0x7F80u);  /* above max finite -> inf */
+    if (r == 0.0) return sign;
+    /* r is exactly representable in bf16 and therefore in binary32. */
+    return (uint16_t)(sign | (f32_as_u32((float)r) >> 16));
+}
+
+/* ------------------------------------------------------------------------ */
+/* IEEE binary16: 1 sign, 5 exponent (bias 15), 10 mantissa bits.            */
+/* The dtype of the NestedFP weights and activations ([NestedFP] §2.1).      */
+/* ------------------------------------------------------------------------ */
+
+double orc_f16_decode(uint16_t h)
+{
+    int s = (h >> 15) & 1, e = (h >> 10) & 31, m = h & 1023;
+    double v;
+    if (e == 31) v = (m == 0) ? INFINITY : NAN;
+    else if (e == 0) v = ldexp((double)m, -24);                 /* m/2^10 * 2^-14 */
+    else v = ldexp(1.0 + (double)m / 1024.0, e - 15);
+    return s ? -v : v;
+}
+
+uint16_t orc_f16_encode(float f)
+{
+    uint16_t sign = (f32_as_u32(f) >> 31) ? 0x8000u : 0;
+    if (isnan(f)) return (uint16_t)(sign | 0x7E00u);
+    if (isinf(f)) return (uint16_t)(sign | 0x7C00u);
+    double r = round_to_format(fabs((double)f), 10, -14);
+    if (r > 65504.0) return (uint16_t)(sign | 0x7C00u);       /* overflow -> inf */
+    if (r < ldexp(1.0, -14)) {                                  /* subnormal or zero */
+        return (uint16_t)(sign | (uint16_t)ldexp(r, 24));
+    }
+    int e2; double fr = frexp(r, &e2);                          /* r = fr*2^e2, fr in [0.5,1) */
+    int e = e2 - 1;                                             /* r = (2fr) * 2^e */
+    int m = (int)((2.0 * fr - 1.0) * 1024.0);
+    return (uint16_t)(sign | ((e + 15) << 10) | m);
+}
+
+/* ------------------------------------------------------------------------ */
+/* FP8 E4M3 (OCP "FN" variant): 1 sign, 4 exponent (bias 7), 3 mantissa.    */
+/* No infinities; S.1111.111 is NaN; largest finite 448 = 1.75*2^8.          */
+/* E4M3 is the format named for both operands ([RTX4060] §2.1, [C++FP8]      */
+/* §3.1); its bound 448 appears in [RTX4060] §6.1, which only fits the OCP   */
+/* variant (the "FNUZ" variant tops out at 240).                             */
+/* ------------------------------------------------------------------------ */
+
+double orc_e4m3_decode(uint8_t c)
+{
+    int s = (c >> 7) & 1, e = (c >> 3) & 15, m = c & 7;
+    double v;
+    if (e == 15 && m == 7) v = NAN;
+    else if (e == 0) v = ldexp((double)m, -9);                  /* m/8 * 2^-6 */
+    else v = ldexp(1.0 + (double)m / 8.0, e - 7);
+    return s ? -v : v;
+}
+
+/*
+ * Encode one binary32 value to E4M3 with a single round-to-nearest-even step
+ * and saturation: magnitudes above 448 (and infinities) become 448, so the
+ * exponent field never reaches the NaN pattern ([RTX4060] §6.1 asks that the
+ * E4M3 exponent not saturate and that scaled values stay within 448).
+ * Values below the smallest normal 2^-6 round into the subnormals, without
+ * flushing to zero ([NestedFP] §4.1 asks that the E4M3 converter handle
+ * underflow).  NaN maps to the NaN code with its sign.
+ */
+uint8_t orc_e4m3_encode(float f)
+{
+    uint8_t sign = (f32_as_u32(f) >> 31) ? 0x80u : 0;
+    if (isnan(f)) return (uint8_t)(sign | 0x7Fu);
+    double a = fabs((double)f);                                  /* inf stays inf */
+    if (a >= 448.0) return (uint8_t)(sign | 0x7Eu);
+    double r = round_to_format(a, 3, -6);
+    if (r > 448.0) r = 448.0;                                    /* (unreachable: a < 448) */
+    uint8_t code;
+    if (r < ldexp(1.0, -6)) {
+        code = (uint8_t)ldexp(r, 9);                             /* subnormal: r = m * 2^-9 */
+    } else {
+        int e2; double fr = frexp(r, &e2);
+        int e = e2 - 1;                                          /* r = (2fr) * 2^e, e in [-6, 8] */
+        int m = (int)((2.0 * fr - 1.0) * 8.0);
+        code = (uint8_t)(((e + 7) << 3) | m);
+    }
+    return (uint8_t)(sign | code);
+}
+
+/* ------------------------------------------------------------------------ */
+/* FP8 E5M2: 1 sign, 5 exponent (bias 15), 2 mantissa, IEEE-style inf/NaN.   */
+/* Named next to E4M3 in [C++FP8] §3.1.  In the NestedFP byte split the      */
+/* upper byte of an fp16 word is, bit for bit, an E5M2 code ([NestedFP]      */
+/* §2.1: upper 8 bits carry sign, the exponent and the top mantissa bits).   */
+/* ------------------------------------------------------------------------ */
+
+double orc_e5m2_decode(uint8_t c)
+{
+    int s = (c >> 7) & 1, e = (c >> 2) & 31, m = c & 3;
+    double v;
+    if (e == 31) v = (m == 0) ? INFINITY : NAN;
+    else if (e == 0) v = ldexp((double)m, -16);                 /* m/4 * 2^-14 */
+    else v = ldexp(1.0 + (double)m / 4.0, e - 15);
+    return s ? -v : v;
+}
+
+/* ------------------------------------------------------------------------ */
+/* Dynamic per-tensor quantization ([RTX4060] §2.2: activations quantized at */
+/* run time from each layer's amax; weights quantized statically offline).   */
+/* Steps, in order:                                                          */
+/*   1. amax = max |x_i|                                                     */
+/*   2. s = fl32(amax / 448), or 1 when amax == 0                            */
+/*   3. q_i = E4M3(fl32(x_i / s))                                            */
+/* ------------------------------------------------------------------------ */
+
+static float load_elem(const uint16_t* x, int dtype, int64_t i)
+{
+    return dtype == ORC_BF16 ? orc_bf16_decode(x[i]) : (float)orc_f16_decode(x[i]);
+}
+
+/* Step 1.  NaN elements are skipped (non-finite inputs are outside the
+   parity contract; this is the documented behaviour). */
+float orc_amax(const uint16_t* x, int dtype, int64_t n)
+{
+    float amax = 0.0f;
+    for (int64_t i = 0; i < n; ++i) {
+        float a = fabsf(load_elem(x, dtype, i));
+        if (a > amax) amax = a;
+    }
+    return amax;
+}
+
+/* Step 2. */
+float orc_scale_from_amax(float amax)
+{
+    if (amax > 0.0f) return amax / 448.0f;      /* one IEEE binary32 division */
+    return 1.0f;
+}
+
+/* Step 3, for elements [0, n) with a given scale. */
+void orc_quantize_with_scale(const uint16_t* x, int dtype, int64_t n, float s, uint8_t* q)
+{
+    for (int64_t i = 0; i < n; ++i) {
+        float v = load_elem(x, dtype, i);
+        float t = v / s;                        /* one IEEE binary32 division */
+        q[i] = orc_e4m3_encode(t);
+    }
+}
+
+/* All three steps. */
+void orc_quantize(const uint16_t* x, int dtype, int64_t n, uint8_t* q, float* scale, float* amax)
+{
+    float a = orc_amax(x, dtype, n);
+    float s = orc_scale_from_amax(a);
+    orc_quantize_with_scale(x, dtype, n, s, q);
+    *scale = s;
+    *amax = a;
+}
+
+/* ------------------------------------------------------------------------ */
+/* NestedFP byte split and rebuild ([NestedFP] §2.1): an fp16 word is kept   */
+/* as its upper byte and its lower byte; FP16 mode rebuilds (upper<<8)|lower */
+/* and FP8 mode uses the upper byte alone as an 8-bit float.                 */
+/* ------------------------------------------------------------------------ */
+
+void orc_nested_split(const uint16_t* w, uint8_t* hi, uint8_t* lo, int64_t n)
+{
+    for (int64_t i = 0; i < n; ++i) {
+        hi[i] = (uint8_t)(w[i] >> 8);
+        lo[i] = (uint8_t)(w[i] & 0xFF);
+    }
+}
+
+void orc_nested_rebuild(const uint8_t* hi, const uint8_t* lo, uint16_t* w, int64_t n)
+{
+    for (int64_t i = 0; i < n; ++i) w[i] = (uint16_t)(((uint16_t)hi[i] << 8) | lo[i]);
+}
+
+/* ------------------------------------------------------------------------ */
+/* GEMM checkers (fp64).  All matrices are row-major: activations [M,K],     */
+/* weights [N,K] (K contiguous: the "tn" layout of the FP8 GEMM named in     */
+/* [C++FP8] §3.3), outputs [M,N].  Each checker returns, for a list of       */
+/* (m, n) pairs, ref = sum_k a[m,k]*w[n,k] times the dequantization scale,   */
+/* and absref = sum_k |a[m,k]*w[n,k]| times the same scale, both in double.  */
+/* ------------------------------------------------------------------------ */
+
+/* FP8 GEMM: operands are E4M3 codes; scale = s_a * s_w. */
+void orc_gemm_fp8_ref(const uint8_t* qa, float sa, const uint8_t* qw, float sw,
+                      int64_t M, int64_t N, int64_t K,
+                      const int64_t* ms, const int64_t* ns, int64_t count,
+                      double* ref, double* absref)
+{
+    (void)M; (void)N;
+    double scale = (double)sa * (double)sw;
+    for (int64_t t = 0; t < count; ++t) {
+        const uint8_t* a = qa + ms[t] * K;
+        const uint8_t* w = qw + ns[t] * K;
+        double sum = 0.0, sabs = 0.0;
+        for (int64_t k = 0; k < K; ++k) {
+            double p = orc_e4m3_decode(a[k]) * orc_e4m3_decode(w[k]);
+            sum += p;
+            sabs += fabs(p);
+        }
+        ref[t] = sum * scale;
+        absref[t] = sabs * scale;
+    }
+}
+
+/* NestedFP FP16 mode: a is fp16 [M,K]; weight = fp16 word (hi<<8)|lo. */
+void orc_nested_fp16_ref(const uint16_t* a16, const uint8_t* hi, const uint8_t* lo,
+                         int64_t M, int64_t N, int64_t K,
+                         const int64_t* ms, const int64_t* ns, int64_t count,
+                         double* ref, double* absref)
+{
+    (void)M; (void)N;
+    for (int64_t t = 0; t < count; ++t) {
+        const uint16_t* a = a16 + ms[t] * K;
+        const uint8_t* h = hi + ns[t] * K;
+        const uint8_t* l = lo + ns[t] * K;
+        double sum = 0.0, sabs = 0.0;
+        for (int64_t k = 0; k < K; ++k) {
+            uint16_t wbits = (uint16_t)(((uint16_t)h[k] << 8) | l[k]);
+            double p = orc_f16_decode(a[k]) * orc_f16_decode(wbits);
+            sum += p;
+            sabs += fabs(p);
+        }
+        ref[t] = sum;
+        absref[t] = sabs;
+    }
+}
+
+/* NestedFP FP8 mode: a is E4M3 codes with scale s_a; weight = E5M2(hi). */
+void orc_nested_fp8_ref(const uint8_t* qa, float sa, const uint8_t* hi,
+                        int64_t M, int64_t N, int64_t K,
+                        const int64_t* ms, const int64_t* ns, int64_t count,
+                        double* ref, double* absref)
+{
+    (void)M; (void)N;
+    for (int64_t t = 0; t < count; ++t) {
+        const uint8_t* a = qa + ms[t] * K;
+        const uint8_t* h = hi + ns[t] * K;
+        double sum = 0.0, sabs = 0.0;
+        for (int64_t k = 0; k < K; ++k) {
+            double p = orc_e4m3_decode(a[k]) * orc_e5m2_decode(h[k]);
+            sum += p;
+            sabs += fabs(p);
+        }
+        ref[t] = sum * (double)sa;
+        absref[t] = sabs * (double)sa;
+    }
+}
+
+/* ------------------------------------------------------------------------ */
+/* Plain fp32-accumulating GEMMs: the same triple loop the method states     */
+/* (fp32 accumulate in k order, then dequantize and round the output once).  */
+/* These are what the CPU baseline times.  Threads only split the N range.   */
+/* ------------------------------------------------------------------------ */
+
+enum { KIND_FP8 = 0, KIND_NESTED_FP16 = 1, KIND_NESTED_FP8 = 2 };
+
+typedef struct {
+    int kind;
+    const void* a; const uint8_t* w; const uint8_t* w2;
+    float sa, sw;
+    int64_t M, N, K, n0, n1;
+    uint16_t* y;
+} gemm_job;
+
+static void* gemm_worker(void* arg)
+{
+    gemm_job* j = (gemm_job*)arg;
+    for (int64_t m = 0; m < j->M; ++m) {
+        for (int64_t n = j->n0; n < j->n1; ++n) {
+            float acc = 0.0f;
+            if (j->kind == KIND_FP8) {
+                const uint8_t* a = (const uint8_t*)j->a + m * j->K;
+                const uint8_t* w = j->w + n * j->K;
+                for (int64_t k = 0; k < j->K; ++k)
+                    acc += (float)orc_e4m3_decode(a[k]) * (float)orc_e4m3_decode(w[k]);
+                float s = j->sa * j->sw;                    /* fl32(s_a * s_w) */
+                j->y[m * j->N + n] = orc_bf16_encode(acc * s);
+            } else if (j->kind == KIND_NESTED_FP16) {
+                const uint16_t* a = (const uint16_t*)j->a + m * j->K;
+                const uint8_t* h = j->w + n * j->K;
+                const uint8_t* l = j->w2 + n * j->K;
+                for (int64_t k = 0; k < j->K; ++k) {
+                    uint16_t wbits = (uint16_t)(((uint16_t)h[k] << 8) | l[k]);
+                    acc += (float)orc_f16_decode(a[k]) * (float)orc_f16_decode(wbits);
+                }
+                j->y[m * j->N + n] = orc_f16_encode(acc);
+            } else {
+                const uint8_t* a = (const uint8_t*)j->a + m * j->K;
+                const uint8_t* h = j->w + n * j->K;
+                for (int64_t k = 0; k < j->K; ++k)
+                    acc += (float)orc_e4m3_decode(a[k]) * (float)orc_e5m2_decode(h[k]);
+                j->y[m * j->N + n] = orc_f16_encode(acc * j->sa);
+            }
+        }
+    }
+    return NULL;
+}
+
+static void run_gemm(int kind, const void* a, const uint8_t* w, const uint8_t* w2,
+                     float sa, float sw, int64_t M, int64_t N, int64_t K,
+                     uint16_t* y, int nthreads)
+{
+    if (nthreads < 1) nthreads = 1;
+    if (nthreads > 256) nthreads = 256;
+    if (nthreads > N) nthreads = (int)N;
+    pthread_t th[256];
+    gemm_job jobs[256];
+    int64_t chunk = (N + nthreads - 1) / nthreads;
+    int started = 0;
+    for (int t = 0; t < nthreads; ++t) {
+        int64_t n0 = t * chunk, n1 = n0 + chunk < N ? n0 + chunk : N;
+        if (n0 >= n1) break;
+        jobs[t] = (gemm_job){kind, a, w, w2, sa, sw, M, N, K, n0, n1, y};
+        if (pthread_create(&th[t], NULL, gemm_worker, &jobs[t]) != 0) {
+            gemm_worker(&jobs[t]);                           /* run inline if no thread */
+            th[t] = 0;
+        }
+        started = t + 1;
+    }
+    for (int t = 0; t < started; ++t)
+        if (th[t]) pthread_join(th[t], NULL);
+}
+
+/* y[M,N] bf16 = bf16(fl32(acc) * fl32(s_a*s_w)), acc = fp32 sum over k. */
+void orc_gemm_fp8_f32(const uint8_t* qa, float sa, const uint8_t* qw, float sw,
+                      int64_t M, int64_t N, int64_t K, uint16_t* y, int nthreads)
+{
+    run_gemm(KIND_FP8, qa, qw, NULL, sa, sw, M, N, K, y, nthreads);
+}
+
+/* y[M,N] fp16 = fp16(acc), acc = fp32 sum of a16 * fp16((hi<<8)|lo). */
+void orc_nested_fp16_f32(const uint16_t* a16, const uint8_t* hi, const uint8_t* lo,
+                         int64_t M, int64_t N, int64_t K, uint16_t* y, int nthreads)
+{
+    run_gemm(KIND_NESTED_FP16, a16, hi, lo, 1.0f, 1.0f, M, N, K, y, nthreads);
+}
+
+/* y[M,N] fp16 = fp16(acc * s_a), acc = fp32 sum of E4M3(qa) * E5M2(hi). */
+void orc_nested_fp8_f32(const uint8_t* qa, float sa, const uint8_t* hi,
+                        int64_t M, int64_t N, int64_t K, uint16_t* y, int nthreads)
+{
+    run_gemm(KIND_NESTED_FP8, qa, hi, NULL, sa, 1.0f, M, N, K, y, nthreads);
+}
+
+/* Reports the rounding mode the oracle runs under (must be FE_TONEAREST). */
+int orc_rounding_is_nearest(void) { return fegetround() == FE_TONEAREST; }
+
+/* ------------------------------------------------------------------------ */
+/* Array forms of the scalar codecs above (plain loops, for the tests).      */
+/* ------------------------------------------------------------------------ */
+
+void orc_e4m3_encode_array(const float* v, uint8_t* out, int64_t n)
+{ for (int64_t i = 0; i < n; ++i) out[i] = orc_e4m3_encode(v[i]); }
+
+void orc_e4m3_decode_array(const uint8_t* c, double* out, int64_t n)
+{ for (int64_t i = 0; i < n; ++i) out[i] = orc_e4m3_decode(c[i]); }
+
+void orc_e5m2_decode_array(const uint8_t* c, double* out, int64_t n)
+{ for (int64_t i = 0; i < n; ++i) out[i] = orc_e5m2_decode(c[i]); }
+
+void orc_f16_decode_array(const uint16_t* h, double* out, int64_t n)
+{ for (int64_t i = 0; i < n; ++i) out[i] = orc_f16_decode(h[i]); }
+
+void orc_f16_encode_array(const float* v, uint16_t* out, int64_t n)
+{ for (int64_t i = 0; i < n; ++i) out[i] = orc_f16_encode(v[i]); }
+
+void orc_bf16_decode_array(const uint16_t* b, float* out, int64_t n)
+{ for (int64_t i = 0; i < n; ++i) out[i] = orc_bf16_decode(b[i]); }
+
+void orc_bf16_encode_array(const float* v, uint16_t* out, int64_t n)
+{ for (int64_t i = 0; i < n; ++i) out[i] = orc_bf16_encode(v[i]); }
