@@ -8,7 +8,7 @@ from this package loads the library and raises if it has not been built.
 """
 _API = (
     "fp8_quantize_act", "fp8_gemm", "nested_split", "nested_rebuild_fp16",
-    "nested_gemm_fp16", "nested_gemm_fp8", "abi_version", "Fp8qError",
+    "nested_gemm_fp16", "nested_gemm_fp8", "e4m3_encode_f32", "abi_version", "Fp8qError",
 )
 
 __all__ = list(_API)

@@ -1,0 +1,134 @@
+// Internal header of libfp8q: device-side number-format helpers, wave
+// reductions and the launcher declarations shared by the kernel files and the
+// C ABI in api.hip.  gfx950 (CDNA4) only.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace fp8q {
+
+typedef int v2i __attribute__((ext_vector_type(2)));
+typedef int v4i __attribute__((ext_vector_type(4)));
+typedef int v8i __attribute__((ext_vector_type(8)));
+typedef float v4f __attribute__((ext_vector_type(4)));
+typedef _Float16 v8h __attribute__((ext_vector_type(8)));
+
+// Input dtype tags (same numbering as fp8q_dtype in the public header).
+enum : int { DT_BF16 = 0, DT_FP16 = 1 };
+// Weight-operand format of the FP8 MFMA (the cbsz/blgp format selector of
+// v_mfma_*_f8f6f4): 0 = FP8 E4M3, 1 = BF8 E5M2.
+enum : int { WF_E4M3 = 0, WF_E5M2 = 1 };
+// Output format of the GEMM epilogues.
+enum : int { OUT_BF16 = 0, OUT_FP16 = 1 };
+
+// ---------------------------------------------------------------- 16-bit floats
+__device__ __forceinline__ float bf16_bits_to_f32(uint32_t b) { return __uint_as_float(b << 16); }
+
+__device__ __forceinline__ float f16_bits_to_f32(uint32_t h)
+{
+    return (float)__builtin_bit_cast(_Float16, (uint16_t)h);
+}
+
+template <int DT>
+__device__ __forceinline__ float half_bits_to_f32(uint32_t h)
+{
+    if constexpr (DT == DT_BF16) return bf16_bits_to_f32(h);
+    else return f16_bits_to_f32(h);
+}
+
+// binary32 -> bfloat16, round to nearest even on the bit pattern (carry into
+// the exponent gives the next binade or infinity); NaN stays a quiet NaN.
+__device__ __forceinline__ uint32_t f32_to_bf16_bits(float f)
+{
+    uint32_t u = __float_as_uint(f);
+    if ((u & 0x7fffffffu) > 0x7f800000u) return ((u >> 16) | 0x40u) & 0xffffu;
+    u += 0x7fffu + ((u >> 16) & 1u);
+    return u >> 16;
+}
+
+// binary32 -> binary16 with the hardware conversion (round to nearest even,
+// subnormal results kept, overflow to infinity).
+__device__ __forceinline__ uint32_t f32_to_f16_bits(float f)
+{
+    return __builtin_bit_cast(uint16_t, (_Float16)f);
+}
+
+template <int OUTF>
+__device__ __forceinline__ uint32_t f32_to_out_bits(float f)
+{
+    if constexpr (OUTF == OUT_BF16) return f32_to_bf16_bits(f);
+    else return f32_to_f16_bits(f);
+}
+
+// ---------------------------------------------------------------- FP8 E4M3
+// Saturate to the E4M3 range first (|v| > 448 and +-inf -> +-448; NaN passes
+// through), then let the gfx950 packed converter round to nearest even into
+// the OCP E4M3 encoding (subnormals kept).
+__device__ __forceinline__ float e4m3_saturate(float v)
+{
+    return fabsf(v) > 448.0f ? copysignf(448.0f, v) : v;
+}
+
+// Four binary32 values -> four E4M3 codes, value i in byte i.
+__device__ __forceinline__ uint32_t e4m3_pack4(float a, float b, float c, float d)
+{
+    int r = __builtin_amdgcn_cvt_pk_fp8_f32(e4m3_saturate(a), e4m3_saturate(b), 0, false);
+    r = __builtin_amdgcn_cvt_pk_fp8_f32(e4m3_saturate(c), e4m3_saturate(d), r, true);
+    return (uint32_t)r;
+}
+
+// ---------------------------------------------------------------- NestedFP rebuild
+// Interleave four upper bytes (h) and four lower bytes (l) into two dwords
+// holding the fp16 words (h_i << 8) | l_i, i = 0..3, little-endian.
+// v_perm_b32 selects bytes from {src0 (bytes 4..7), src1 (bytes 0..3)}.
+__device__ __forceinline__ void nested_rebuild4(uint32_t h, uint32_t l, uint32_t& w01, uint32_t& w23)
+{
+    w01 = __builtin_amdgcn_perm(h, l, 0x05010400u);  // [l0, h0, l1, h1]
+    w23 = __builtin_amdgcn_perm(h, l, 0x07030602u);  // [l2, h2, l3, h3]
+}
+
+// ---------------------------------------------------------------- reductions
+// Max over a wave64 with DPP row operations; the result is valid in every lane.
+#define FP8Q_DPP_MAX(v, ctrl, rowmask)                                                    \
+    v = fmaxf(v, __int_as_float(__builtin_amdgcn_update_dpp(__float_as_int(v),            \
+                                                            __float_as_int(v), ctrl,      \
+                                                            rowmask, 0xf, false)))
+
+__device__ __forceinline__ float wave_max(float v)
+{
+    FP8Q_DPP_MAX(v, 0xB1, 0xf);   // quad_perm [1,0,3,2]
+    FP8Q_DPP_MAX(v, 0x4E, 0xf);   // quad_perm [2,3,0,1]
+    FP8Q_DPP_MAX(v, 0x141, 0xf);  // row_half_mirror
+    FP8Q_DPP_MAX(v, 0x140, 0xf);  // row_mirror: lanes of each row of 16 hold its max
+    FP8Q_DPP_MAX(v, 0x142, 0xa);  // row_bcast15 -> rows 1, 3
+    FP8Q_DPP_MAX(v, 0x143, 0xc);  // row_bcast31 -> rows 2, 3: lane 63 holds the max
+    return __int_as_float(__builtin_amdgcn_readlane(__float_as_int(v), 63));
+}
+
+// ---------------------------------------------------------------- launchers
+// Each returns the hipError_t of hipGetLastError() after its launches.
+hipError_t launch_quantize(const void* x, int dtype, int64_t n, uint8_t* q, float* scale,
+                           float* amax, hipStream_t stream);
+hipError_t launch_e4m3_encode_f32(const float* v, uint8_t* q, int64_t n, hipStream_t stream);
+
+// Decode path (M <= 16) and tile path (M > 16) of the FP8 GEMM; wfmt selects
+// the weight format (E4M3 / E5M2), outf the output format (bf16 / fp16), and
+// sw == nullptr means the scale is *sa alone.
+hipError_t launch_gemv_fp8(const uint8_t* qa, const float* sa, const uint8_t* qw,
+                           const float* sw, uint16_t* y, int M, int N, int K, int wfmt,
+                           int outf, hipStream_t stream);
+hipError_t launch_tile_fp8(const uint8_t* qa, const float* sa, const uint8_t* qw,
+                           const float* sw, uint16_t* y, int M, int N, int K, int wfmt,
+                           int outf, hipStream_t stream);
+
+hipError_t launch_nested_split(const uint16_t* w, uint8_t* hi, uint8_t* lo, int64_t n,
+                               hipStream_t stream);
+hipError_t launch_nested_rebuild(const uint8_t* hi, const uint8_t* lo, uint16_t* w, int64_t n,
+                                 hipStream_t stream);
+hipError_t launch_gemv_nested16(const uint16_t* a, const uint8_t* hi, const uint8_t* lo,
+                                uint16_t* y, int M, int N, int K, hipStream_t stream);
+hipError_t launch_tile_nested16(const uint16_t* a, const uint8_t* hi, const uint8_t* lo,
+                                uint16_t* y, int M, int N, int K, hipStream_t stream);
+
+}  // namespace fp8q

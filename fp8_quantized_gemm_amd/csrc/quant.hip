@@ -1,0 +1,228 @@
+// Dynamic per-tensor E4M3 quantization: amax reduction, scale = amax/448,
+// round-to-nearest-even with saturation (page on a 7B model on an RTX 4060,
+// §2.2 and §6.1; the E4M3 converter keeps underflow as subnormals, page
+// "NestedFP双精度推理框架" §4.1).
+//
+// Two paths:
+//  - n <= kSmallN: one workgroup loads the whole tensor into registers,
+//    reduces amax (DPP within waves, LDS across waves), then quantizes from
+//    the same registers.  One launch, no atomics: the decode case.
+//  - larger n: a one-thread init kernel zeroes *amax, a grid-stride kernel
+//    reduces per workgroup and folds into *amax with an integer atomicMax on
+//    the float bit pattern (monotone for non-negative floats), and a
+//    grid-stride kernel quantizes.  Every element is read twice (HBM-bound).
+//
+// x / s is the IEEE correctly rounded binary32 division (no reciprocal), so
+// codes are a function of (x, s) alone and independent of the launch shape.
+#include "common.hpp"
+
+namespace fp8q {
+namespace {
+
+constexpr int kSmallThreads = 1024;
+constexpr int kSmallVecPerThread = 4;                                   // 8 elements each
+constexpr int64_t kSmallN = (int64_t)kSmallThreads * kSmallVecPerThread * 8;  // 32768
+
+constexpr int kBigThreads = 256;
+constexpr int kBigUnroll = 4;
+
+template <int DT>
+__device__ __forceinline__ float vec_absmax(const v4i& v)
+{
+    float m = 0.0f;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+        uint32_t u = (uint32_t)v[i];
+        m = fmaxf(m, fabsf(half_bits_to_f32<DT>(u & 0xffffu)));
+        m = fmaxf(m, fabsf(half_bits_to_f32<DT>(u >> 16)));
+    }
+    return m;
+}
+
+// 8 input halves -> 8 E4M3 codes (two dwords)
+template <int DT>
+__device__ __forceinline__ v2i vec_quantize(const v4i& v, float s)
+{
+    float f[8];
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+        uint32_t u = (uint32_t)v[i];
+        f[2 * i] = half_bits_to_f32<DT>(u & 0xffffu) / s;
+        f[2 * i + 1] = half_bits_to_f32<DT>(u >> 16) / s;
+    }
+    v2i r;
+    r[0] = (int)e4m3_pack4(f[0], f[1], f[2], f[3]);
+    r[1] = (int)e4m3_pack4(f[4], f[5], f[6], f[7]);
+    return r;
+}
+
+template <int DT>
+__device__ __forceinline__ uint8_t scalar_quantize(uint16_t h, float s)
+{
+    return (uint8_t)(e4m3_pack4(half_bits_to_f32<DT>(h) / s, 0.f, 0.f, 0.f) & 0xffu);
+}
+
+__device__ __forceinline__ float scale_from_amax(float amax)
+{
+    return amax > 0.0f ? amax / 448.0f : 1.0f;
+}
+
+// Block-wide max for blockDim.x = NT threads; result valid in every thread.
+template <int NT>
+__device__ __forceinline__ float block_max(float v, float* lds)
+{
+    constexpr int W = NT / 64;
+    v = wave_max(v);
+    const int wave = threadIdx.x >> 6;
+    if ((threadIdx.x & 63) == 0) lds[wave] = v;
+    __syncthreads();
+    float m = lds[0];
+#pragma unroll
+    for (int i = 1; i < W; ++i) m = fmaxf(m, lds[i]);
+    return m;
+}
+
+// ---------------------------------------------------------------- small path
+template <int DT>
+__global__ __launch_bounds__(kSmallThreads) void quant_small_kernel(
+    const uint16_t* __restrict__ x, int64_t n, uint8_t* __restrict__ q,
+    float* __restrict__ scale, float* __restrict__ amax_out)
+{
+    __shared__ float lds[kSmallThreads / 64];
+    const int tid = threadIdx.x;
+    const int64_t nvec = n >> 3;
+    const int tail = (int)(n & 7);
+    const v4i* xv = reinterpret_cast<const v4i*>(x);
+
+    v4i v[kSmallVecPerThread];
+    float m = 0.0f;
+#pragma unroll
+    for (int j = 0; j < kSmallVecPerThread; ++j) {
+        const int64_t i = tid + (int64_t)j * kSmallThreads;
+        v[j] = (i < nvec) ? xv[i] : v4i{0, 0, 0, 0};
+        m = fmaxf(m, vec_absmax<DT>(v[j]));
+    }
+    uint16_t th = 0;
+    if (tid < tail) {
+        th = x[nvec * 8 + tid];
+        m = fmaxf(m, fabsf(half_bits_to_f32<DT>(th)));
+    }
+    const float a = block_max<kSmallThreads>(m, lds);
+    const float s = scale_from_amax(a);
+
+    v2i* qv = reinterpret_cast<v2i*>(q);
+#pragma unroll
+    for (int j = 0; j < kSmallVecPerThread; ++j) {
+        const int64_t i = tid + (int64_t)j * kSmallThreads;
+        if (i < nvec) qv[i] = vec_quantize<DT>(v[j], s);
+    }
+    if (tid < tail) q[nvec * 8 + tid] = scalar_quantize<DT>(th, s);
+    if (tid == 0) {
+        *scale = s;
+        *amax_out = a;
+    }
+}
+
+// ---------------------------------------------------------------- large path
+__global__ void amax_init_kernel(float* amax) { *amax = 0.0f; }
+
+template <int DT>
+__global__ __launch_bounds__(kBigThreads) void amax_kernel(const uint16_t* __restrict__ x,
+                                                           int64_t n, float* amax)
+{
+    __shared__ float lds[kBigThreads / 64];
+    const int64_t nvec = n >> 3;
+    const v4i* xv = reinterpret_cast<const v4i*>(x);
+    const int64_t stride = (int64_t)gridDim.x * kBigThreads;
+    float m = 0.0f;
+    int64_t i = (int64_t)blockIdx.x * kBigThreads + threadIdx.x;
+    for (; i + (kBigUnroll - 1) * stride < nvec; i += kBigUnroll * stride) {
+        v4i v[kBigUnroll];
+#pragma unroll
+        for (int u = 0; u < kBigUnroll; ++u) v[u] = xv[i + u * stride];
+#pragma unroll
+        for (int u = 0; u < kBigUnroll; ++u) m = fmaxf(m, vec_absmax<DT>(v[u]));
+    }
+    for (; i < nvec; i += stride) m = fmaxf(m, vec_absmax<DT>(xv[i]));
+    if (blockIdx.x == 0 && threadIdx.x < (int)(n & 7))
+        m = fmaxf(m, fabsf(half_bits_to_f32<DT>(x[nvec * 8 + threadIdx.x])));
+    m = block_max<kBigThreads>(m, lds);
+    if (threadIdx.x == 0) atomicMax(reinterpret_cast<unsigned int*>(amax), __float_as_uint(m));
+}
+
+template <int DT>
+__global__ __launch_bounds__(kBigThreads) void quant_kernel(const uint16_t* __restrict__ x,
+                                                            int64_t n, uint8_t* __restrict__ q,
+                                                            float* __restrict__ scale,
+                                                            const float* __restrict__ amax)
+{
+    const float s = scale_from_amax(*amax);
+    const int64_t nvec = n >> 3;
+    const v4i* xv = reinterpret_cast<const v4i*>(x);
+    v2i* qv = reinterpret_cast<v2i*>(q);
+    const int64_t stride = (int64_t)gridDim.x * kBigThreads;
+    int64_t i = (int64_t)blockIdx.x * kBigThreads + threadIdx.x;
+    for (; i + (kBigUnroll - 1) * stride < nvec; i += kBigUnroll * stride) {
+        v4i v[kBigUnroll];
+#pragma unroll
+        for (int u = 0; u < kBigUnroll; ++u) v[u] = xv[i + u * stride];
+#pragma unroll
+        for (int u = 0; u < kBigUnroll; ++u) qv[i + u * stride] = vec_quantize<DT>(v[u], s);
+    }
+    for (; i < nvec; i += stride) qv[i] = vec_quantize<DT>(xv[i], s);
+    if (blockIdx.x == 0) {
+        if (threadIdx.x < (int)(n & 7))
+            q[nvec * 8 + threadIdx.x] = scalar_quantize<DT>(x[nvec * 8 + threadIdx.x], s);
+        if (threadIdx.x == 0) *scale = s;
+    }
+}
+
+// ---------------------------------------------------------------- encoder export
+__global__ __launch_bounds__(256) void e4m3_encode_kernel(const float* __restrict__ v,
+                                                          uint8_t* __restrict__ q, int64_t n)
+{
+    const int64_t stride = (int64_t)gridDim.x * 256;
+    for (int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x; i < n; i += stride)
+        q[i] = (uint8_t)(e4m3_pack4(v[i], 0.f, 0.f, 0.f) & 0xffu);
+}
+
+int grid_for(int64_t nvec, int per_block)
+{
+    int64_t g = (nvec + per_block - 1) / per_block;
+    if (g < 1) g = 1;
+    if (g > 2048) g = 2048;   // 8 workgroups per CU, grid-stride beyond
+    return (int)g;
+}
+
+}  // namespace
+
+hipError_t launch_quantize(const void* x, int dtype, int64_t n, uint8_t* q, float* scale,
+                           float* amax, hipStream_t stream)
+{
+    const uint16_t* xs = static_cast<const uint16_t*>(x);
+    if (n <= kSmallN) {
+        if (dtype == DT_BF16)
+            quant_small_kernel<DT_BF16><<<1, kSmallThreads, 0, stream>>>(xs, n, q, scale, amax);
+        else
+            quant_small_kernel<DT_FP16><<<1, kSmallThreads, 0, stream>>>(xs, n, q, scale, amax);
+        return hipGetLastError();
+    }
+    const int g = grid_for(n >> 3, kBigThreads * kBigUnroll);
+    amax_init_kernel<<<1, 1, 0, stream>>>(amax);
+    if (dtype == DT_BF16) {
+        amax_kernel<DT_BF16><<<g, kBigThreads, 0, stream>>>(xs, n, amax);
+        quant_kernel<DT_BF16><<<g, kBigThreads, 0, stream>>>(xs, n, q, scale, amax);
+    } else {
+        amax_kernel<DT_FP16><<<g, kBigThreads, 0, stream>>>(xs, n, amax);
+        quant_kernel<DT_FP16><<<g, kBigThreads, 0, stream>>>(xs, n, q, scale, amax);
+    }
+    return hipGetLastError();
+}
+
+hipError_t launch_e4m3_encode_f32(const float* v, uint8_t* q, int64_t n, hipStream_t stream)
+{
+    e4m3_encode_kernel<<<grid_for(n, 256 * 4), 256, 0, stream>>>(v, q, n);
+    return hipGetLastError();
+}
+
+}  // namespace fp8q

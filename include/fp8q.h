@@ -1,0 +1,161 @@
+/*
+ * fp8q.h - C ABI of libfp8q: FP8 E4M3 per-tensor-scaled linear layers and the
+ * NestedFP dual-precision GEMM on AMD MI355X (gfx950).
+ *
+ * Pages whose statement of the problem these calls follow:
+ *   [RTX4060]  the page on a 7B model on an RTX 4060 with FP8
+ *              (intelliparadigm.com/article/weixin_29051149/2151670)
+ *   [C++FP8]   "C++与FP8量化：大模型推理部署的系统级优化实践" (tqpw.cn/news/201730)
+ *   [NestedFP] "NestedFP双精度推理框架：LLM部署中的内存与计算优化"
+ *              (intelliparadigm.com/article/weixin_42537919/2229392)
+ *
+ * Conventions shared by every entry point
+ * ---------------------------------------
+ *  - Pointers named x, q, qa, qw, y, w, hi, lo, a, scale, amax, sa, sw are
+ *    DEVICE pointers on the current HIP device.  The caller owns every buffer;
+ *    the library allocates no device memory on any call.
+ *  - Matrices are dense, row-major, without strides: activations [M,K],
+ *    weights and NestedFP planes [N,K] (K contiguous: the "tn" layout of the
+ *    FP8 GEMM named in [C++FP8] §3.3), outputs [M,N].
+ *  - 16-bit floating-point tensors (bf16, fp16) are passed as their uint16
+ *    bit patterns; FP8 tensors as uint8 codes (OCP E4M3 "FN": bias 7, max 448,
+ *    0x7F/0xFF NaN; E5M2: bias 15).
+ *  - Every call is asynchronous on `stream` (a hipStream_t passed as void*;
+ *    NULL is the null stream) and never synchronizes the host.  Scales and
+ *    amax stay on the device.
+ *  - Arguments are validated on the host before any HIP call; on a validation
+ *    error nothing is launched.  Base pointers must be 16-byte aligned.
+ *    A failed launch returns FP8Q_ERR_LAUNCH; faults inside a kernel surface
+ *    at the caller's next synchronization, as for any HIP work.
+ *  - Calls on different streams are independent (no shared mutable state).
+ */
+#ifndef FP8Q_H
+#define FP8Q_H
+
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define FP8Q_ABI_VERSION 1
+
+typedef enum {
+    FP8Q_OK = 0,
+    FP8Q_ERR_NULL = 1,    /* a required pointer is NULL                        */
+    FP8Q_ERR_SHAPE = 2,   /* a size is out of range (see each call)            */
+    FP8Q_ERR_ALIGN = 3,   /* a base pointer is not 16-byte aligned             */
+    FP8Q_ERR_DTYPE = 4,   /* unknown input dtype                               */
+    FP8Q_ERR_LAUNCH = 5,  /* a HIP call or kernel launch failed                */
+    FP8Q_ERR_DEVICE = 6   /* the current device is not a gfx950 GPU            */
+} fp8q_status;
+
+typedef enum { FP8Q_BF16 = 0, FP8Q_FP16 = 1 } fp8q_dtype;
+
+typedef void* fp8q_stream; /* hipStream_t */
+
+/* Symbols of the shared library; everything else in it is hidden. */
+#if defined(FP8Q_BUILD)
+#define FP8Q_API __attribute__((visibility("default")))
+#else
+#define FP8Q_API
+#endif
+
+/* Returns FP8Q_ABI_VERSION of the built library. */
+FP8Q_API int fp8q_abi_version(void);
+
+/* Static, never-NULL description of a status code. */
+FP8Q_API const char* fp8q_status_str(int status);
+
+/* Text of the last HIP error seen by this thread's calls ("" if none). */
+FP8Q_API const char* fp8q_last_error(void);
+
+/*
+ * fp8_quantize_act - dynamic per-tensor E4M3 quantization.
+ *   [RTX4060] §2.2: activations are quantized at run time from the layer's
+ *   amax; §6.1: scaled values stay within 448 and the E4M3 exponent does not
+ *   saturate.  The same call quantizes weights offline (static quantization,
+ *   [RTX4060] §2.2) when given the fp16 weight tensor.
+ *
+ *   x[n]     in : bf16 (dtype FP8Q_BF16) or fp16 (FP8Q_FP16) bit patterns
+ *   q[n]     out: E4M3 codes, q_i = E4M3_rne_sat(fl32(x_i / s))
+ *   *scale   out: s = fl32(amax / 448), or 1.0 when amax == 0
+ *   *amax    out: max_i |x_i| (also used as the reduction accumulator; its
+ *                 previous contents are ignored)
+ *   n >= 1.  E4M3 rounding: nearest, ties to even, subnormals kept,
+ *   |v| > 448 (and +-inf) saturate to +-448.  NaN inputs are outside the
+ *   contract.
+ */
+FP8Q_API fp8q_status fp8_quantize_act(const void* x, int dtype, int64_t n, uint8_t* q,
+                             float* scale, float* amax, fp8q_stream stream);
+
+/*
+ * fp8_gemm - y = bf16( (qa . qw^T) * fl32(*sa * *sw) ), fp32 accumulation.
+ *   The FP8 GEMM of [C++FP8] §3.3 (E4M3 operands, fp32 accumulate, bf16
+ *   output, "tn" layout), on statically quantized weights ([RTX4060] §2.2).
+ *
+ *   qa[M,K]  in : E4M3 activation codes        *sa in: activation scale
+ *   qw[N,K]  in : E4M3 weight codes            *sw in: weight scale
+ *   y[M,N]   out: bf16 bit patterns, round to nearest even
+ *   1 <= M, N <= 2^31-1;  16 <= K <= 2^31-1 and K % 16 == 0.
+ *   M <= 16 runs the weight-streaming decode path, larger M the MFMA tile path.
+ */
+FP8Q_API fp8q_status fp8_gemm(const uint8_t* qa, const float* sa, const uint8_t* qw,
+                     const float* sw, uint16_t* y, int64_t M, int64_t N, int64_t K,
+                     fp8q_stream stream);
+
+/*
+ * nested_split - NestedFP byte split of fp16 weights ([NestedFP] §2.1):
+ *   hi[i] = w[i] >> 8, lo[i] = w[i] & 0xFF.   n >= 1.
+ */
+FP8Q_API fp8q_status nested_split(const uint16_t* w, uint8_t* hi, uint8_t* lo, int64_t n,
+                         fp8q_stream stream);
+
+/*
+ * nested_rebuild_fp16 - the FP16-mode rebuild of [NestedFP] §2.1 on its own:
+ *   w[i] = (hi[i] << 8) | lo[i].   n >= 1.  Uses the same device routine as
+ *   nested_gemm_fp16; exported so the rebuild can be checked exhaustively.
+ */
+FP8Q_API fp8q_status nested_rebuild_fp16(const uint8_t* hi, const uint8_t* lo, uint16_t* w,
+                                int64_t n, fp8q_stream stream);
+
+/*
+ * nested_gemm_fp16 - NestedFP FP16 mode ([NestedFP] §2.1, §2.2): weights are
+ *   rebuilt in-kernel as fp16 (hi<<8)|lo, bit-exactly, then
+ *   y = fp16( a . w^T ), fp32 accumulation, round to nearest even.
+ *
+ *   a[M,K]   in : fp16 activations;  hi[N,K], lo[N,K] in: byte planes
+ *   y[M,N]   out: fp16 bit patterns
+ *   Same size rules as fp8_gemm.
+ */
+FP8Q_API fp8q_status nested_gemm_fp16(const uint16_t* a, const uint8_t* hi, const uint8_t* lo,
+                             uint16_t* y, int64_t M, int64_t N, int64_t K,
+                             fp8q_stream stream);
+
+/*
+ * nested_gemm_fp8 - NestedFP FP8 mode ([NestedFP] §2.1): only the hi plane is
+ *   read, as an 8-bit float; the upper byte of an fp16 word is exactly an E5M2
+ *   code, so its value is fp16(hi << 8).  Activations are E4M3 codes from
+ *   fp8_quantize_act (on the fp16 activation) with scale *sa:
+ *   y = fp16( (qa . E5M2(hi)^T) * *sa ), fp32 accumulation.
+ *
+ *   qa[M,K] in, *sa in, hi[N,K] in, y[M,N] out (fp16 bits).
+ *   Same size rules as fp8_gemm.
+ */
+FP8Q_API fp8q_status nested_gemm_fp8(const uint8_t* qa, const float* sa, const uint8_t* hi,
+                            uint16_t* y, int64_t M, int64_t N, int64_t K,
+                            fp8q_stream stream);
+
+/*
+ * fp8q_e4m3_encode_f32 - the device E4M3 encoder used by fp8_quantize_act,
+ *   applied to binary32 values directly: q[i] = E4M3_rne_sat(v[i]).  n >= 1.
+ *   Exported so the encoder can be checked exhaustively; not on the hot path.
+ */
+FP8Q_API fp8q_status fp8q_e4m3_encode_f32(const float* v, uint8_t* q, int64_t n,
+                                 fp8q_stream stream);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* FP8Q_H */

@@ -263,6 +263,93 @@ void orc_nested_rebuild(const uint8_t* hi, const uint8_t* lo, uint16_t* w, int64
 /* and absref = sum_k |a[m,k]*w[n,k]| times the same scale, both in double.  */
 /* ------------------------------------------------------------------------ */
 
+/* The checkers evaluate each requested (m, n) pair independently; threads
+   only split the list of pairs (no change to any sum). */
+typedef struct {
+    int kind;                       /* 0: FP8, 1: NestedFP FP16, 2: NestedFP FP8 */
+    const void* a; const uint8_t* w; const uint8_t* w2;
+    float sa, sw;
+    int64_t K;
+    const int64_t* ms; const int64_t* ns;
+    int64_t t0, t1;
+    double* ref; double* absref;
+} ref_job;
+
+static void ref_pair(const ref_job* j, int64_t t)
+{
+    const int64_t K = j->K, m = j->ms[t], n = j->ns[t];
+    double sum = 0.0, sabs = 0.0, scale = 1.0;
+    if (j->kind == 0) {
+        /* FP8 GEMM: E4M3 x E4M3, scale = s_a * s_w */
+        const uint8_t* a = (const uint8_t*)j->a + m * K;
+        const uint8_t* w = j->w + n * K;
+        for (int64_t k = 0; k < K; ++k) {
+            double p = orc_e4m3_decode(a[k]) * orc_e4m3_decode(w[k]);
+            sum += p;
+            sabs += fabs(p);
+        }
+        scale = (double)j->sa * (double)j->sw;
+    } else if (j->kind == 1) {
+        /* NestedFP FP16 mode: fp16 activation x fp16 word (hi<<8)|lo, no scale */
+        const uint16_t* a = (const uint16_t*)j->a + m * K;
+        const uint8_t* h = j->w + n * K;
+        const uint8_t* l = j->w2 + n * K;
+        for (int64_t k = 0; k < K; ++k) {
+            uint16_t wbits = (uint16_t)(((uint16_t)h[k] << 8) | l[k]);
+            double p = orc_f16_decode(a[k]) * orc_f16_decode(wbits);
+            sum += p;
+            sabs += fabs(p);
+        }
+    } else {
+        /* NestedFP FP8 mode: E4M3 activation x E5M2(hi), scale = s_a */
+        const uint8_t* a = (const uint8_t*)j->a + m * K;
+        const uint8_t* h = j->w + n * K;
+        for (int64_t k = 0; k < K; ++k) {
+            double p = orc_e4m3_decode(a[k]) * orc_e5m2_decode(h[k]);
+            sum += p;
+            sabs += fabs(p);
+        }
+        scale = (double)j->sa;
+    }
+    j->ref[t] = sum * scale;
+    j->absref[t] = sabs * scale;
+}
+
+static void* ref_worker(void* arg)
+{
+    const ref_job* j = (const ref_job*)arg;
+    for (int64_t t = j->t0; t < j->t1; ++t) ref_pair(j, t);
+    return NULL;
+}
+
+static int g_ref_threads = 1;
+
+/* Number of host threads the checkers below may use (default 1). */
+void orc_set_ref_threads(int n) { g_ref_threads = n < 1 ? 1 : (n > 256 ? 256 : n); }
+
+static void run_ref(ref_job proto, int64_t count)
+{
+    int nt = g_ref_threads;
+    if (nt > count) nt = count > 0 ? (int)count : 1;
+    pthread_t th[256];
+    ref_job jobs[256];
+    int64_t chunk = (count + nt - 1) / nt;
+    int started = 0;
+    for (int t = 0; t < nt; ++t) {
+        jobs[t] = proto;
+        jobs[t].t0 = t * chunk;
+        jobs[t].t1 = jobs[t].t0 + chunk < count ? jobs[t].t0 + chunk : count;
+        if (jobs[t].t0 >= jobs[t].t1) break;
+        if (pthread_create(&th[t], NULL, ref_worker, &jobs[t]) != 0) {
+            ref_worker(&jobs[t]);
+            th[t] = 0;
+        }
+        started = t + 1;
+    }
+    for (int t = 0; t < started; ++t)
+        if (th[t]) pthread_join(th[t], NULL);
+}
+
 /* FP8 GEMM: operands are E4M3 codes; scale = s_a * s_w. */
 void orc_gemm_fp8_ref(const uint8_t* qa, float sa, const uint8_t* qw, float sw,
                       int64_t M, int64_t N, int64_t K,
@@ -270,19 +357,8 @@ void orc_gemm_fp8_ref(const uint8_t* qa, float sa, const uint8_t* qw, float sw,
                       double* ref, double* absref)
 {
     (void)M; (void)N;
-    double scale = (double)sa * (double)sw;
-    for (int64_t t = 0; t < count; ++t) {
-        const uint8_t* a = qa + ms[t] * K;
-        const uint8_t* w = qw + ns[t] * K;
-        double sum = 0.0, sabs = 0.0;
-        for (int64_t k = 0; k < K; ++k) {
-            double p = orc_e4m3_decode(a[k]) * orc_e4m3_decode(w[k]);
-            sum += p;
-            sabs += fabs(p);
-        }
-        ref[t] = sum * scale;
-        absref[t] = sabs * scale;
-    }
+    ref_job j = {0, qa, qw, NULL, sa, sw, K, ms, ns, 0, 0, ref, absref};
+    run_ref(j, count);
 }
 
 /* NestedFP FP16 mode: a is fp16 [M,K]; weight = fp16 word (hi<<8)|lo. */
@@ -292,20 +368,8 @@ void orc_nested_fp16_ref(const uint16_t* a16, const uint8_t* hi, const uint8_t* 
                          double* ref, double* absref)
 {
     (void)M; (void)N;
-    for (int64_t t = 0; t < count; ++t) {
-        const uint16_t* a = a16 + ms[t] * K;
-        const uint8_t* h = hi + ns[t] * K;
-        const uint8_t* l = lo + ns[t] * K;
-        double sum = 0.0, sabs = 0.0;
-        for (int64_t k = 0; k < K; ++k) {
-            uint16_t wbits = (uint16_t)(((uint16_t)h[k] << 8) | l[k]);
-            double p = orc_f16_decode(a[k]) * orc_f16_decode(wbits);
-            sum += p;
-            sabs += fabs(p);
-        }
-        ref[t] = sum;
-        absref[t] = sabs;
-    }
+    ref_job j = {1, a16, hi, lo, 1.0f, 1.0f, K, ms, ns, 0, 0, ref, absref};
+    run_ref(j, count);
 }
 
 /* NestedFP FP8 mode: a is E4M3 codes with scale s_a; weight = E5M2(hi). */
@@ -315,18 +379,8 @@ void orc_nested_fp8_ref(const uint8_t* qa, float sa, const uint8_t* hi,
                         double* ref, double* absref)
 {
     (void)M; (void)N;
-    for (int64_t t = 0; t < count; ++t) {
-        const uint8_t* a = qa + ms[t] * K;
-        const uint8_t* h = hi + ns[t] * K;
-        double sum = 0.0, sabs = 0.0;
-        for (int64_t k = 0; k < K; ++k) {
-            double p = orc_e4m3_decode(a[k]) * orc_e5m2_decode(h[k]);
-            sum += p;
-            sabs += fabs(p);
-        }
-        ref[t] = sum * (double)sa;
-        absref[t] = sabs * (double)sa;
-    }
+    ref_job j = {2, qa, hi, NULL, sa, 1.0f, K, ms, ns, 0, 0, ref, absref};
+    run_ref(j, count);
 }
 
 /* ------------------------------------------------------------------------ */

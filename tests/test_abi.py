@@ -1,0 +1,122 @@
+"""The C ABI library loads, exports every function include/fp8q.h declares, and
+rejects invalid arguments on the host before any HIP call (CPU only: none of
+these calls reaches the GPU)."""
+import ctypes
+import os
+import re
+
+import pytest
+
+from fp8_quantized_gemm_amd import fp8q
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "fp8q.h")
+
+OK, ERR_NULL, ERR_SHAPE, ERR_ALIGN, ERR_DTYPE = 0, 1, 2, 3, 4
+
+P16 = ctypes.c_void_p(0x1000)      # aligned, never dereferenced: validation fails first
+P17 = ctypes.c_void_p(0x1001)
+NULL = None
+
+
+def declared_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"^\s*[A-Za-z_][\w\s\*]*?\b(\w+)\s*\(", text, flags=re.M)))
+
+
+def test_header_declares_the_entry_points():
+    names = declared_functions()
+    for want in ["fp8_quantize_act", "fp8_gemm", "nested_split", "nested_rebuild_fp16",
+                 "nested_gemm_fp16", "nested_gemm_fp8", "fp8q_abi_version",
+                 "fp8q_status_str", "fp8q_last_error", "fp8q_e4m3_encode_f32"]:
+        assert want in names
+
+
+def test_library_exports_every_declared_symbol():
+    for name in declared_functions():
+        assert hasattr(fp8q.lib, name), name
+
+
+def test_no_internal_symbols_exported():
+    out = os.popen(f"nm -D --defined-only {fp8q.LIB_PATH}").read()
+    exported = {ln.split()[-1] for ln in out.splitlines() if " T " in ln}
+    assert exported == set(declared_functions())
+
+
+def test_version_and_status_strings():
+    assert fp8q.lib.fp8q_abi_version() == 1
+    for s in range(7):
+        assert fp8q.lib.fp8q_status_str(s)
+    assert fp8q.lib.fp8q_status_str(99) == b"unknown status"
+
+
+GEMM_SIG = [P16, P16, P16, P16, P16]
+
+
+@pytest.mark.parametrize("fn,args,status", [
+    # fp8_quantize_act(x, dtype, n, q, scale, amax, stream)
+    ("fp8_quantize_act", [NULL, 0, 8, P16, P16, P16, NULL], ERR_NULL),
+    ("fp8_quantize_act", [P16, 0, 8, NULL, P16, P16, NULL], ERR_NULL),
+    ("fp8_quantize_act", [P16, 0, 8, P16, NULL, P16, NULL], ERR_NULL),
+    ("fp8_quantize_act", [P16, 0, 8, P16, P16, NULL, NULL], ERR_NULL),
+    ("fp8_quantize_act", [P16, 2, 8, P16, P16, P16, NULL], ERR_DTYPE),
+    ("fp8_quantize_act", [P16, -1, 8, P16, P16, P16, NULL], ERR_DTYPE),
+    ("fp8_quantize_act", [P16, 0, 0, P16, P16, P16, NULL], ERR_SHAPE),
+    ("fp8_quantize_act", [P16, 1, -5, P16, P16, P16, NULL], ERR_SHAPE),
+    ("fp8_quantize_act", [P17, 0, 8, P16, P16, P16, NULL], ERR_ALIGN),
+    ("fp8_quantize_act", [P16, 0, 8, P17, P16, P16, NULL], ERR_ALIGN),
+    ("fp8_quantize_act", [P16, 0, 8, P16, ctypes.c_void_p(0x1002), P16, NULL], ERR_ALIGN),
+    # fp8_gemm(qa, sa, qw, sw, y, M, N, K, stream)
+    ("fp8_gemm", [NULL, P16, P16, P16, P16, 1, 1, 16, NULL], ERR_NULL),
+    ("fp8_gemm", [P16, NULL, P16, P16, P16, 1, 1, 16, NULL], ERR_NULL),
+    ("fp8_gemm", [P16, P16, NULL, P16, P16, 1, 1, 16, NULL], ERR_NULL),
+    ("fp8_gemm", [P16, P16, P16, NULL, P16, 1, 1, 16, NULL], ERR_NULL),
+    ("fp8_gemm", [P16, P16, P16, P16, NULL, 1, 1, 16, NULL], ERR_NULL),
+    ("fp8_gemm", [P16, P16, P16, P16, P16, 0, 1, 16, NULL], ERR_SHAPE),
+    ("fp8_gemm", [P16, P16, P16, P16, P16, 1, 0, 16, NULL], ERR_SHAPE),
+    ("fp8_gemm", [P16, P16, P16, P16, P16, 1, 1, 0, NULL], ERR_SHAPE),
+    ("fp8_gemm", [P16, P16, P16, P16, P16, 1, 1, 8, NULL], ERR_SHAPE),
+    ("fp8_gemm", [P16, P16, P16, P16, P16, 1, 1, 40, NULL], ERR_SHAPE),
+    ("fp8_gemm", [P16, P16, P16, P16, P16, 2**31, 1, 16, NULL], ERR_SHAPE),
+    ("fp8_gemm", [P16, P16, P16, P16, P16, 1, 2**31, 16, NULL], ERR_SHAPE),
+    ("fp8_gemm", [P16, P16, P16, P16, P16, 1, 1, 2**31 + 16, NULL], ERR_SHAPE),
+    ("fp8_gemm", [P17, P16, P16, P16, P16, 1, 1, 16, NULL], ERR_ALIGN),
+    ("fp8_gemm", [P16, P16, P17, P16, P16, 1, 1, 16, NULL], ERR_ALIGN),
+    ("fp8_gemm", [P16, P16, P16, P16, P17, 1, 1, 16, NULL], ERR_ALIGN),
+    ("fp8_gemm", [P16, P17, P16, P16, P16, 1, 1, 16, NULL], ERR_ALIGN),
+    # nested_split(w, hi, lo, n, stream) / nested_rebuild_fp16(hi, lo, w, n, stream)
+    ("nested_split", [NULL, P16, P16, 8, NULL], ERR_NULL),
+    ("nested_split", [P16, P16, P16, 0, NULL], ERR_SHAPE),
+    ("nested_split", [P16, P17, P16, 8, NULL], ERR_ALIGN),
+    ("nested_rebuild_fp16", [P16, NULL, P16, 8, NULL], ERR_NULL),
+    ("nested_rebuild_fp16", [P16, P16, P16, -1, NULL], ERR_SHAPE),
+    ("nested_rebuild_fp16", [P16, P16, P17, 8, NULL], ERR_ALIGN),
+    # nested_gemm_fp16(a, hi, lo, y, M, N, K, stream)
+    ("nested_gemm_fp16", [P16, P16, NULL, P16, 1, 1, 16, NULL], ERR_NULL),
+    ("nested_gemm_fp16", [P16, P16, P16, P16, 1, 1, 24, NULL], ERR_SHAPE),
+    ("nested_gemm_fp16", [P16, P16, P16, P17, 1, 1, 16, NULL], ERR_ALIGN),
+    # nested_gemm_fp8(qa, sa, hi, y, M, N, K, stream)
+    ("nested_gemm_fp8", [P16, NULL, P16, P16, 1, 1, 16, NULL], ERR_NULL),
+    ("nested_gemm_fp8", [P16, P16, P16, P16, -3, 1, 16, NULL], ERR_SHAPE),
+    ("nested_gemm_fp8", [P16, P16, P17, P16, 1, 1, 16, NULL], ERR_ALIGN),
+    # fp8q_e4m3_encode_f32(v, q, n, stream)
+    ("fp8q_e4m3_encode_f32", [NULL, P16, 4, NULL], ERR_NULL),
+    ("fp8q_e4m3_encode_f32", [P16, P16, 0, NULL], ERR_SHAPE),
+    ("fp8q_e4m3_encode_f32", [P16, P17, 4, NULL], ERR_ALIGN),
+])
+def test_validation_before_any_hip_call(fn, args, status):
+    assert getattr(fp8q.lib, fn)(*args) == status
+
+
+def test_binding_raises_on_cpu_tensors():
+    import torch
+    with pytest.raises(TypeError):
+        fp8q.fp8_quantize_act(torch.zeros(8, dtype=torch.bfloat16))
+    with pytest.raises(TypeError):
+        fp8q.fp8_quantize_act(torch.zeros(8, dtype=torch.float32))
+
+
+def test_error_type_carries_status():
+    e = fp8q.Fp8qError("fp8_gemm", ERR_SHAPE)
+    assert e.status == ERR_SHAPE and "size out of range" in str(e)

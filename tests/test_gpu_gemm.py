@@ -1,0 +1,189 @@
+"""GPU parity of fp8_gemm (decode path M <= 16 and tile path M > 16) against
+the oracle: bit-exact on identity and small-integer operands, within
+|y - ref| <= 2e-3 * sum|a*b| + 1e-6 per element on random operands.
+
+Operands are quantized by the oracle on the host (so the GEMM is checked on
+its own); the end-to-end test quantizes on the GPU and compares the codes too.
+"""
+import numpy as np
+import pytest
+import torch
+
+import oracle
+from fp8_quantized_gemm_amd import fp8q, synth
+from gpu_helpers import DEV, assert_within, host, say, scalar_dev, to_dev_u8
+
+pytestmark = pytest.mark.gpu
+
+
+def _run_gemm(qa, sa, qw, sw, guard=32):
+    M, N = qa.shape[0], qw.shape[0]
+    ybuf = torch.full((M * N + guard,), 7.0, dtype=torch.bfloat16, device=DEV)
+    y = ybuf[:M * N].view(M, N)
+    fp8q.fp8_gemm(to_dev_u8(qa), scalar_dev(sa), to_dev_u8(qw), scalar_dev(sw), y)
+    out = host(ybuf)
+    assert np.all(out[M * N:] == synth.bits(torch.tensor([7.0], dtype=torch.bfloat16))[0]), \
+        "wrote past the end of y"
+    return out[:M * N].reshape(M, N)
+
+
+def _random_codes(rng, shape):
+    c = rng.integers(0, 256, size=shape, dtype=np.uint8)
+    c[(c & 0x7F) == 0x7F] = 0x7E       # no NaN codes; keeps +-448 in play
+    return c
+
+
+def _ident_act(M, K, cols):
+    qa = np.zeros((M, K), np.uint8)
+    qa[np.arange(M), cols] = 0x38      # E4M3 1.0
+    return qa
+
+
+# ------------------------------------------------------------------ bit-exact
+@pytest.mark.parametrize("N,K", [(272, 512), (33, 144), (16, 16)])
+def test_decode_identity_returns_every_weight(N, K):
+    """One-hot activation rows (M = 16 per launch) read every weight back
+    through the decode path: y[m, n] = E4M3(qw[n, c_m]) exactly in bf16."""
+    rng = np.random.Generator(np.random.PCG64(N * K))
+    qw = _random_codes(rng, (N, K))
+    # a -0 weight times 1.0 plus the +0 products of the other columns sums to +0
+    want = oracle.bf16_encode((oracle.e4m3_decode(qw) + 0.0).astype(np.float32))
+    for c0 in range(0, K, 16):
+        M = min(16, K - c0)
+        say("decode identity", N, K, c0)
+        y = _run_gemm(_ident_act(M, K, np.arange(c0, c0 + M)), 1.0, qw, 1.0)
+        assert np.array_equal(y, want[:, c0:c0 + M].T), f"columns {c0}..{c0 + M}"
+
+
+@pytest.mark.parametrize("M,N,K", [(256, 300, 256), (17, 40, 32), (144, 129, 144)])
+def test_tile_identity_returns_every_weight(M, N, K):
+    """qa = the first M rows of I (M <= K): the tile path must return the first
+    M columns of W, transposed, bit-exactly."""
+    rng = np.random.Generator(np.random.PCG64(M + N + K))
+    qw = _random_codes(rng, (N, K))
+    say("tile identity", M, N, K)
+    y = _run_gemm(_ident_act(M, K, np.arange(M)), 1.0, qw, 1.0)
+    want = oracle.bf16_encode((oracle.e4m3_decode(qw) + 0.0).astype(np.float32))
+    assert np.array_equal(y, want[:, :M].T)
+
+
+def _small_int(rng, M, N, K):
+    a = rng.integers(-16, 17, size=(M, K)).astype(np.float32)
+    w = rng.integers(-16, 17, size=(N, K)).astype(np.float32)
+    a.flat[rng.integers(a.size)] = 448.0
+    w.flat[rng.integers(w.size)] = -448.0
+    qa, sa, _ = oracle.quantize(synth.bits(torch.from_numpy(a).to(torch.bfloat16)), oracle.BF16)
+    qw, sw, _ = oracle.quantize(synth.bits(torch.from_numpy(w).to(torch.float16)), oracle.FP16)
+    assert sa == 1.0 and sw == 1.0
+    return qa.reshape(M, K), qw.reshape(N, K)
+
+
+@pytest.mark.parametrize("M,N,K", [(1, 64, 160), (5, 1000, 4096), (16, 48, 11008),
+                                   (17, 64, 160), (100, 300, 4096), (300, 129, 1040)])
+def test_small_integers_bit_exact(M, N, K):
+    rng = np.random.Generator(np.random.PCG64(M * 7 + N * 3 + K))
+    qa, qw = _small_int(rng, M, N, K)
+    say("small int", M, N, K)
+    y = _run_gemm(qa, 1.0, qw, 1.0)
+    want = oracle.gemm_fp8_f32(qa, 1.0, qw, 1.0)        # exact integer sums, then bf16
+    assert np.array_equal(y, want)
+
+
+# ------------------------------------------------------------------ tolerance
+def _quantized_operands(M, N, K, seed, outliers=False, sigma=0.02):
+    x = synth.activation(M, K, seed=seed, outliers=outliers)
+    w = synth.normal((N, K), sigma, "fp16", seed=seed + 1)
+    qa, sa, _ = oracle.quantize(synth.bits(x), oracle.BF16)
+    qw, sw, _ = oracle.quantize(synth.bits(w), oracle.FP16)
+    return qa.reshape(M, K), sa, qw.reshape(N, K), sw
+
+
+SHAPES = [(1, 1, 16), (1, 15, 48), (2, 16, 144), (3, 17, 4096), (8, 100, 11008), (15, 31, 4112),
+          (16, 4096, 4096), (17, 33, 272), (31, 129, 1024), (129, 257, 4096), (257, 100, 11008),
+          (512, 64, 176)]
+
+
+@pytest.mark.parametrize("M,N,K", SHAPES)
+def test_random_within_tolerance(M, N, K):
+    qa, sa, qw, sw = _quantized_operands(M, N, K, seed=M * 1000 + N + K, outliers=M > 16)
+    say("random", M, N, K)
+    y = _run_gemm(qa, sa, qw, sw)
+    ref, ab = oracle.gemm_fp8_ref(qa, sa, qw, sw)
+    assert_within(oracle.bf16_decode(y).astype(np.float64).ravel(), ref, ab, f"{M}x{N}x{K}", "bf16")
+
+
+def test_cfg_single_linear_all_outputs():
+    """M=1, K=N=4096 (weights ~N(0,0.02), activation ~N(0,1)): every output."""
+    qa, sa, qw, sw = _quantized_operands(1, 4096, 4096, seed=synth.seed_for("cfg1"))
+    say("single 4096x4096")
+    y = _run_gemm(qa, sa, qw, sw)
+    ref, ab = oracle.gemm_fp8_ref(qa, sa, qw, sw)
+    assert_within(oracle.bf16_decode(y).astype(np.float64).ravel(), ref, ab, "4096x4096 M=1", "bf16")
+
+
+def _gpu_pipeline(M, N, K, seed, outliers, sigma):
+    """GPU quantize of x and W, then GPU GEMM; returns device tensors and the
+    host bits of x and W (for the oracle)."""
+    x = synth.activation(M, K, seed=seed, outliers=outliers, device=DEV)
+    w = synth.normal((N, K), sigma, "fp16", seed=seed + 1, device=DEV)
+    say("pipeline", M, N, K)
+    qw, sw, _ = fp8q.fp8_quantize_act(w)
+    qa, sa, _ = fp8q.fp8_quantize_act(x)
+    y = fp8q.fp8_gemm(qa, sa, qw, sw)
+    torch.cuda.synchronize()
+    return x, w, qa, sa, qw, sw, y
+
+
+LAYER_SHAPES = [(K, N) for _, K, N in synth.LLAMA7B_LINEARS] + \
+               [(K, N) for _, K, N in synth.QWEN32B_LINEARS]
+
+
+@pytest.mark.parametrize("M", [1, 8, 16, 512])
+@pytest.mark.parametrize("K,N", LAYER_SHAPES)
+def test_full_size_layers_sampled(M, K, N):
+    """Full Llama-7B / Qwen-32B linear shapes, GPU quantization + GEMM: codes of
+    the sampled rows bit-exact, outputs within tolerance on a seeded sample
+    (whole rows for M <= 16, 2 rows + 2 columns + 256 pairs otherwise)."""
+    sigma = 0.015 if (K, N) in [(k, n) for _, k, n in synth.QWEN32B_LINEARS] else 0.02
+    seed = synth.seed_for("layer", M, K, N)
+    x, w, qa, sa, qw, sw, y = _gpu_pipeline(M, N, K, seed, outliers=M > 16, sigma=sigma)
+    rng = np.random.Generator(np.random.PCG64(seed))
+    # oracle quantization of W: full amax, codes of the sampled rows only
+    wb = synth.bits(w)
+    s_w = oracle.scale_from_amax(oracle.amax(wb.ravel(), oracle.FP16))
+    xb = synth.bits(x)
+    oqa, osa, _ = oracle.quantize(xb.ravel(), oracle.BF16)
+    assert np.float32(host(sa)[0]) == np.float32(osa)
+    assert np.float32(host(sw)[0]) == np.float32(s_w)
+    assert np.array_equal(host(qa).ravel(), oqa)
+    if M <= 16:
+        ns = np.sort(rng.choice(N, size=min(N, 512), replace=False))
+        ms_all = np.repeat(np.arange(M), ns.size)
+        ns_all = np.tile(np.arange(ns.size), M)
+    else:
+        rows = rng.choice(M, 2, replace=False)
+        cols = rng.choice(N, 2, replace=False)
+        ns = np.unique(np.concatenate([cols, rng.choice(N, 254, replace=False)]))
+        pm = np.concatenate([np.repeat(rows, ns.size), np.arange(M), np.arange(M)])
+        pn_glob = np.concatenate([np.tile(ns, rows.size), np.full(M, cols[0]), np.full(M, cols[1])])
+        pos = {n: i for i, n in enumerate(ns)}
+        ms_all = pm
+        ns_all = np.array([pos[n] for n in pn_glob])
+    wq_rows = oracle.quantize_with_scale(wb[ns].ravel(), oracle.FP16, s_w).reshape(ns.size, K)
+    assert np.array_equal(host(qw)[ns], wq_rows), "weight codes differ"
+    ref, ab = oracle.gemm_fp8_ref(oqa.reshape(M, K), osa, wq_rows, s_w, ms_all, ns_all)
+    yb = host(y)
+    out = oracle.bf16_decode(yb[ms_all, ns[ns_all]]).astype(np.float64)
+    assert_within(out, ref, ab, f"M={M} {K}->{N}", "bf16")
+
+
+def test_deterministic_and_stream_order():
+    qa, sa, qw, sw = _quantized_operands(300, 1000, 4096, seed=99)
+    say("determinism")
+    y1 = _run_gemm(qa, sa, qw, sw)
+    y2 = _run_gemm(qa, sa, qw, sw)
+    assert np.array_equal(y1, y2)
+    s = torch.cuda.Stream()
+    with torch.cuda.stream(s):
+        y3 = _run_gemm(qa, sa, qw, sw)
+    assert np.array_equal(y1, y3)

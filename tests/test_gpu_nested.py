@@ -1,0 +1,153 @@
+"""GPU parity of the NestedFP path against the oracle: the byte split and the
+fp16 rebuild bit-exact over all 65,536 words, the FP16- and FP8-mode GEMMs
+bit-exact on identity activations and within the GEMM tolerance on random
+operands (decode and tile paths)."""
+import numpy as np
+import pytest
+import torch
+
+import oracle
+from fp8_quantized_gemm_amd import fp8q, synth
+from gpu_helpers import DEV, assert_within, host, say, scalar_dev, to_dev_bits, to_dev_u8
+
+pytestmark = pytest.mark.gpu
+
+ALL16 = np.arange(65536, dtype=np.uint32).astype(np.uint16)
+
+
+@pytest.mark.parametrize("reps,extra", [(1, 0), (3, 7), (1, 5)])
+def test_split_and_rebuild_exhaustive(reps, extra):
+    w = np.concatenate([np.tile(ALL16, reps), ALL16[:extra]]) if extra else np.tile(ALL16, reps)
+    if extra == 5:
+        w = w[:13]                                   # tiny: tail-only path
+    say("split/rebuild", w.size)
+    wd = to_dev_bits(w, "fp16")
+    hi, lo = fp8q.nested_split(wd)
+    ohi, olo = oracle.nested_split(w)
+    assert np.array_equal(host(hi), ohi)
+    assert np.array_equal(host(lo), olo)
+    back = fp8q.nested_rebuild_fp16(hi, lo)
+    assert np.array_equal(host(back), w)
+    assert np.array_equal(host(back), oracle.nested_rebuild(ohi, olo))
+
+
+def _finite_weights(rng, N, K):
+    """fp16 words over the whole finite range (normals, subnormals, zeros)."""
+    w = rng.integers(0, 65536, size=(N, K), dtype=np.uint32).astype(np.uint16)
+    bad = (w & 0x7C00) == 0x7C00                       # inf / NaN
+    w[bad] &= 0x83FF
+    return w
+
+
+def _run(fn, *args, M, N, guard=32):
+    ybuf = torch.full((M * N + guard,), 3.0, dtype=torch.float16, device=DEV)
+    y = ybuf[:M * N].view(M, N)
+    fn(*args, y)
+    out = host(ybuf)
+    assert np.all(out[M * N:] == 0x4200), "wrote past the end of y"
+    return out[:M * N].reshape(M, N)
+
+
+def _one_hot_f16(M, K, cols):
+    a = np.zeros((M, K), np.uint16)
+    a[np.arange(M), cols] = 0x3C00                    # fp16 1.0
+    return a
+
+
+@pytest.mark.parametrize("M,N,K", [(16, 40, 64), (256, 130, 256), (48, 33, 48)])
+def test_fp16_mode_identity_bit_exact(M, N, K):
+    """a = one-hot rows: y = rebuilt weight bit-exactly (subnormals included)."""
+    rng = np.random.Generator(np.random.PCG64(M * N * K))
+    w = _finite_weights(rng, N, K)
+    hi, lo = oracle.nested_split(w)
+    dhi, dlo = to_dev_u8(hi), to_dev_u8(lo)
+    want = np.where(w == 0x8000, 0, w).astype(np.uint16)   # -0 * 1 + (+0) = +0
+    for c0 in range(0, K, M):
+        m = min(M, K - c0)
+        say("fp16 identity", m, N, K, c0)
+        a = to_dev_bits(_one_hot_f16(m, K, np.arange(c0, c0 + m)), "fp16")
+        y = _run(fp8q.nested_gemm_fp16, a, dhi, dlo, M=m, N=N)
+        assert np.array_equal(y, want[:, c0:c0 + m].T), f"columns {c0}.."
+
+
+@pytest.mark.parametrize("M,N,K", [(16, 40, 128), (200, 70, 208)])
+def test_fp8_mode_identity_bit_exact(M, N, K):
+    """qa = one-hot E4M3 1.0, sa = 1: y = fp16(hi << 8) bit-exactly."""
+    rng = np.random.Generator(np.random.PCG64(M + N + K))
+    w = _finite_weights(rng, N, K)
+    hi, _ = oracle.nested_split(w)
+    want = (hi.astype(np.uint16) << 8)
+    want[want == 0x8000] = 0                            # -0 * 1 + (+0) = +0
+    dhi = to_dev_u8(hi)
+    for c0 in range(0, K, M):
+        m = min(M, K - c0)
+        qa = np.zeros((m, K), np.uint8)
+        qa[np.arange(m), np.arange(c0, c0 + m)] = 0x38
+        say("fp8 identity", m, N, K, c0)
+        y = _run(fp8q.nested_gemm_fp8, to_dev_u8(qa), scalar_dev(1.0), dhi, M=m, N=N)
+        assert np.array_equal(y, want[:, c0:c0 + m].T), f"columns {c0}.."
+
+
+SHAPES = [(1, 1, 16), (1, 40, 4096), (3, 17, 48), (8, 100, 11008), (16, 64, 4112),
+          (17, 33, 272), (64, 129, 1024), (256, 300, 4096), (300, 77, 160)]
+
+
+def _operands(M, N, K, seed):
+    a16 = synth.bits(synth.activation(M, K, seed=seed, dtype="fp16"))
+    w16 = synth.bits(synth.normal((N, K), 0.02, "fp16", seed=seed + 1))
+    hi, lo = oracle.nested_split(w16)
+    return a16, hi, lo
+
+
+@pytest.mark.parametrize("M,N,K", SHAPES)
+def test_fp16_mode_random(M, N, K):
+    a16, hi, lo = _operands(M, N, K, seed=M * 100 + N + K)
+    say("fp16 mode", M, N, K)
+    y = _run(fp8q.nested_gemm_fp16, to_dev_bits(a16, "fp16"), to_dev_u8(hi), to_dev_u8(lo),
+             M=M, N=N)
+    ref, ab = oracle.nested_fp16_ref(a16, hi, lo)
+    assert_within(oracle.f16_decode(y).ravel(), ref, ab, f"fp16 mode {M}x{N}x{K}", "fp16")
+
+
+@pytest.mark.parametrize("M,N,K", SHAPES)
+def test_fp8_mode_random(M, N, K):
+    a16, hi, _ = _operands(M, N, K, seed=M * 100 + N + K + 5)
+    qa, sa, _ = oracle.quantize(a16.ravel(), oracle.FP16)
+    qa = qa.reshape(M, K)
+    say("fp8 mode", M, N, K)
+    y = _run(fp8q.nested_gemm_fp8, to_dev_u8(qa), scalar_dev(sa), to_dev_u8(hi), M=M, N=N)
+    ref, ab = oracle.nested_fp8_ref(qa, sa, hi)
+    assert_within(oracle.f16_decode(y).ravel(), ref, ab, f"fp8 mode {M}x{N}x{K}", "fp16")
+
+
+@pytest.mark.parametrize("M", [1, 256])
+@pytest.mark.parametrize("K,N", [(K, N) for _, K, N in synth.LLAMA7B_LINEARS])
+def test_full_size_llama_shapes_sampled(M, K, N):
+    """NestedFP on the Llama-7B linear shapes (GPU split, GPU fp16-activation
+    quantization for FP8 mode); sampled outputs within tolerance."""
+    seed = synth.seed_for("nested", M, K, N)
+    a = synth.activation(M, K, seed=seed, dtype="fp16", device=DEV)
+    w = synth.normal((N, K), 0.02, "fp16", seed=seed + 1, device=DEV)
+    say("nested full", M, K, N)
+    hi, lo = fp8q.nested_split(w)
+    y16 = fp8q.nested_gemm_fp16(a, hi, lo)
+    qa, sa, _ = fp8q.fp8_quantize_act(a)
+    y8 = fp8q.nested_gemm_fp8(qa, sa, hi)
+    torch.cuda.synchronize()
+    rng = np.random.Generator(np.random.PCG64(seed))
+    ns = np.sort(rng.choice(N, 256, replace=False))
+    rows = np.arange(M) if M <= 16 else np.sort(rng.choice(M, 4, replace=False))
+    wb = synth.bits(w)[ns]
+    ohi, olo = oracle.nested_split(wb)
+    assert np.array_equal(host(hi)[ns], ohi) and np.array_equal(host(lo)[ns], olo)
+    ab16 = synth.bits(a)
+    ms = np.repeat(np.arange(rows.size), ns.size)
+    nn = np.tile(np.arange(ns.size), rows.size)
+    ref, ab = oracle.nested_fp16_ref(ab16[rows], ohi, olo, ms, nn)
+    out = oracle.f16_decode(host(y16)[rows][:, ns]).ravel()
+    assert_within(out, ref, ab, f"fp16 mode M={M} {K}->{N}", "fp16")
+    oqa, osa, _ = oracle.quantize(ab16.ravel(), oracle.FP16)
+    assert np.array_equal(host(qa).ravel(), oqa)
+    ref8, ab8 = oracle.nested_fp8_ref(oqa.reshape(M, K)[rows], osa, ohi, ms, nn)
+    out8 = oracle.f16_decode(host(y8)[rows][:, ns]).ravel()
+    assert_within(out8, ref8, ab8, f"fp8 mode M={M} {K}->{N}", "fp16")

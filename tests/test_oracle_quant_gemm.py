@@ -218,7 +218,7 @@ def test_fp8_f32_within_tolerance_of_ref(threads):
     y = oracle.gemm_fp8_f32(qa.reshape(M, K), sa, qw.reshape(N, K), sw, nthreads=threads)
     ref, ab = oracle.gemm_fp8_ref(qa.reshape(M, K), sa, qw.reshape(N, K), sw)
     out = oracle.bf16_decode(y).astype(np.float64).ravel()
-    assert np.all(oracle.within_tolerance(out, ref, ab))
+    assert np.all(oracle.within_tolerance(out, ref, ab, "bf16"))
 
 
 def test_nested_f32_within_tolerance_of_ref():
@@ -228,11 +228,11 @@ def test_nested_f32_within_tolerance_of_ref():
     hi, lo = oracle.nested_split(w16)
     y = oracle.nested_fp16_f32(a16, hi, lo)
     ref, ab = oracle.nested_fp16_ref(a16, hi, lo)
-    assert np.all(oracle.within_tolerance(oracle.f16_decode(y).ravel(), ref, ab))
+    assert np.all(oracle.within_tolerance(oracle.f16_decode(y).ravel(), ref, ab, "fp16"))
     qa, sa, _ = oracle.quantize(a16, oracle.FP16)
     y8 = oracle.nested_fp8_f32(qa.reshape(M, K), sa, hi)
     ref8, ab8 = oracle.nested_fp8_ref(qa.reshape(M, K), sa, hi)
-    assert np.all(oracle.within_tolerance(oracle.f16_decode(y8).ravel(), ref8, ab8))
+    assert np.all(oracle.within_tolerance(oracle.f16_decode(y8).ravel(), ref8, ab8, "fp16"))
 
 
 def test_nested_fp16_identity_returns_weights():
@@ -259,3 +259,31 @@ def test_tolerance_catches_a_dropped_k_block():
     qa2[:, 128:256] = 0
     bad, _ = oracle.gemm_fp8_ref(qa2, sa, qw, sw)
     assert not np.all(oracle.within_tolerance(bad, ref, ab))
+
+
+def test_half_ulp_against_numpy_spacing():
+    """half_ulp(v) is half of numpy's spacing of float16 at v, and half of the
+    bf16 spacing (2^(e-7)) computed from torch's own rounding."""
+    v = np.array([1.0, 1.5, 4.015, 60000.0, 2.0**-14, 2.0**-20, 3e-5, 0.0, 7.9e4 / 2])
+    assert np.array_equal(oracle.half_ulp(v, "fp16"),
+                          np.spacing(v.astype(np.float16)).astype(np.float64) / 2)
+    b = torch.tensor(v, dtype=torch.float32).to(torch.bfloat16)
+    nxt = (b.view(torch.int16) + 1).view(torch.bfloat16).to(torch.float64).numpy()
+    spacing = nxt - b.to(torch.float64).numpy()
+    assert np.array_equal(oracle.half_ulp(v, "bf16"), spacing / 2)
+
+
+def test_tolerance_admits_correct_rounding_of_the_exact_result():
+    """Outlier channels on a short K make single products dominate; the exact
+    result rounded to bf16 must still pass (it is the best answer a bf16
+    output can give), while the bound stays tight enough to reject a result
+    missing one K block (test above)."""
+    M, N, K = 512, 64, 176
+    x = synth.activation(M, K, seed=M * 1000 + N + K, outliers=True)
+    w = synth.normal((N, K), 0.02, "fp16", seed=M * 1000 + N + K + 1)
+    qa, sa, _ = oracle.quantize(synth.bits(x), oracle.BF16)
+    qw, sw, _ = oracle.quantize(synth.bits(w), oracle.FP16)
+    ref, ab = oracle.gemm_fp8_ref(qa.reshape(M, K), sa, qw.reshape(N, K), sw)
+    rounded = oracle.bf16_decode(oracle.bf16_encode(ref.astype(np.float32))).astype(np.float64)
+    assert not np.all(oracle.within_tolerance(rounded, ref, ab, "exact"))
+    assert np.all(oracle.within_tolerance(rounded, ref, ab, "bf16"))
