@@ -1,0 +1,339 @@
+"""Benchmark of the FP8 linear-layer hot path on one MI355X.
+
+    python bench.py [--gpus 1] [--steps K] [--warmup W] [--no-cpu-baseline]
+                    [--no-secondary] [--graph]
+
+Workload (one "step"): the 32 layers of Llama-7B-shaped decode linears at
+M = 1 token (fused QKV 4096->12288, O 4096->4096, gate+up 4096->22016,
+down 11008->4096), each one a dynamic per-tensor E4M3 quantization of its bf16
+activation followed by the FP8 GEMM against statically quantized E4M3 weights
+(fp32 accumulation, bf16 output).  The 128 weight matrices are distinct
+(6.48 GB of FP8 codes), so every step streams them from HBM.
+
+`value` is whole-step algorithmic HBM traffic divided by the step time
+(GB/s): per linear N*K weight bytes + M*K code bytes + 2*M*N output bytes for
+the GEMM and 3*M*K bytes for the quantizer.  Inputs are resident in HBM
+before timing.  `roofline` reports the decode GEMV kernel alone (its
+algorithmic bytes over its average duration, measured with HIP events around
+every GEMV launch on the launch stream inside the timed region).
+`secondary` adds the prefill (M = 512, 2048: TFLOP/s of the tile GEMM) and
+NestedFP figures; `cpu_baseline` times the oracle on a bounded sample.
+Rank 0 prints one JSON line.
+"""
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+HBM_PEAK_GBS = 8000.0         # MI355X HBM3E, GB/s
+FP8_PEAK_TFLOPS = 5000.0      # dense FP8 MFMA
+FP16_PEAK_TFLOPS = 2500.0     # dense FP16 MFMA
+LAYERS = 32
+METRIC = "FP8 linear: HBM GB/s @M=1 and TFLOP/s @M=512, % of MI355X peak"
+
+
+def parse():
+    p = argparse.ArgumentParser(description=__doc__.split("\n")[0])
+    p.add_argument("--gpus", type=int, default=1)
+    p.add_argument("--steps", type=int, default=20)
+    p.add_argument("--warmup", type=int, default=5)
+    p.add_argument("--no-cpu-baseline", action="store_true")
+    p.add_argument("--no-secondary", action="store_true")
+    p.add_argument("--graph", action="store_true",
+                   help="replay each step as one captured HIP graph")
+    p.add_argument("--cpu-seconds", type=float, default=10.0,
+                   help="lower bound on the oracle's timed CPU work")
+    return p.parse_args()
+
+
+def kernel_source_hash() -> str:
+    h = hashlib.sha256()
+    for f in ("gemv.hip", "common.hpp"):
+        with open(os.path.join(ROOT, "fp8_quantized_gemm_amd", "csrc", f), "rb") as fh:
+            h.update(fh.read())
+    return h.hexdigest()[:16]
+
+
+def load_traffic(src_hash: str):
+    """HBM traffic per GEMV launch from the committed counter summary, if it
+    was taken on the current kernel source."""
+    path = os.path.join(ROOT, "profiles", "gemv_fp8_llama7b_decode_m1_traffic.json")
+    try:
+        with open(path) as f:
+            d = json.load(f)
+    except (OSError, ValueError):
+        return None
+    if d.get("kernel_source_hash") != src_hash:
+        return None
+    return d.get("traffic_bytes_per_launch")
+
+
+class Model:
+    """Device-resident weights and per-linear buffers of one decode workload."""
+
+    def __init__(self, torch, fp8q, synth, M: int, dev: str):
+        self.M = M
+        self.linears = []
+        for layer in range(LAYERS):
+            for name, K, N in synth.LLAMA7B_LINEARS:
+                w = synth.normal((N, K), 0.02, "fp16", seed=synth.seed_for("w", layer, name),
+                                 device=dev)
+                qw, sw, _ = fp8q.fp8_quantize_act(w)      # offline static quantization
+                del w
+                self.linears.append(dict(layer=layer, name=name, K=K, N=N, qw=qw, sw=sw))
+        for L in self.linears:
+            K, N = L["K"], L["N"]
+            L["x"] = synth.activation(M, K, seed=synth.seed_for("x", M, L["layer"], L["name"]),
+                                      device=dev)
+            L["q"] = torch.empty((M, K), dtype=torch.uint8, device=dev)
+            L["sa"] = torch.empty(1, dtype=torch.float32, device=dev)
+            L["amax"] = torch.empty(1, dtype=torch.float32, device=dev)
+            L["y"] = torch.empty((M, N), dtype=torch.bfloat16, device=dev)
+        torch.cuda.synchronize()
+
+    def gemm_bytes(self, L):
+        M, K, N = self.M, L["K"], L["N"]
+        return N * K + M * K + 2 * M * N
+
+    def quant_bytes(self, L):
+        return 3 * self.M * L["K"]
+
+    def flops(self, L):
+        return 2 * self.M * L["N"] * L["K"]
+
+
+def run_step(fp8q, model, events=None):
+    for i, L in enumerate(model.linears):
+        fp8q.fp8_quantize_act(L["x"], L["q"], L["sa"], L["amax"])
+        if events is not None:
+            events[i][0].record()
+        fp8q.fp8_gemm(L["q"], L["sa"], L["qw"], L["sw"], L["y"])
+        if events is not None:
+            events[i][1].record()
+
+
+def time_steps(torch, fp8q, model, steps, warmup, graph=False, with_events=False):
+    """Returns (seconds per step, average GEMV launch seconds or None)."""
+    for _ in range(warmup):
+        run_step(fp8q, model)
+    torch.cuda.synchronize()
+    g = None
+    if graph:
+        s = torch.cuda.Stream()
+        s.wait_stream(torch.cuda.current_stream())
+        with torch.cuda.stream(s):
+            run_step(fp8q, model)            # warm on the capture stream
+            torch.cuda.synchronize()
+            g = torch.cuda.CUDAGraph()
+            with torch.cuda.graph(g, stream=s):
+                run_step(fp8q, model)
+        torch.cuda.synchronize()
+        for _ in range(warmup):
+            g.replay()
+        torch.cuda.synchronize()
+    ev = None
+    if with_events and not graph:
+        ev = [[(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+               for _ in model.linears] for _ in range(steps)]
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for k in range(steps):
+        if g is not None:
+            g.replay()
+        else:
+            run_step(fp8q, model, ev[k] if ev else None)
+    torch.cuda.synchronize()
+    dt = (time.perf_counter() - t0) / steps
+    kern = None
+    if ev:
+        tot = sum(a.elapsed_time(b) for step in ev for (a, b) in step) * 1e-3
+        kern = tot / (steps * len(model.linears))
+    return dt, kern
+
+
+def cpu_baseline(torch, synth, dev, seconds):
+    """The oracle (quantize + fp32-accumulating GEMM) on a bounded sample of
+    the same decode workload: layers 0..L-1, repeated until `seconds` pass."""
+    import numpy as np
+    import oracle
+
+    threads = oracle.default_threads()
+    work = []
+    for layer in range(2):
+        for name, K, N in synth.LLAMA7B_LINEARS:
+            w = synth.normal((N, K), 0.02, "fp16", seed=synth.seed_for("w", layer, name), device=dev)
+            wb = synth.bits(w).ravel()
+            del w
+            qw, sw, _ = oracle.quantize(wb, oracle.FP16)            # offline, untimed
+            x = synth.activation(1, K, seed=synth.seed_for("x", 1, layer, name), device=dev)
+            work.append((synth.bits(x).ravel(), qw.reshape(N, K), sw, K, N))
+    done_bytes = 0
+    passes = 0
+    t0 = time.perf_counter()
+    while True:
+        for xb, qw, sw, K, N in work:
+            qa, sa, _ = oracle.quantize(xb, oracle.BF16)
+            oracle.gemm_fp8_f32(qa.reshape(1, K), sa, qw, sw, nthreads=threads)
+            done_bytes += N * K + K + 2 * N + 3 * K
+        passes += 1
+        el = time.perf_counter() - t0
+        if el >= seconds:
+            break
+    return {"value": round(done_bytes / el / 1e9, 3), "unit": "GB/s", "cores": threads,
+            "kind": "oracle",
+            "sample": f"layers 0-1 of the 32 (8 linears, M=1), {passes} pass(es), "
+                      f"{el:.1f} s of CPU work; same algorithmic bytes as the GPU metric"}
+
+
+def secondary(torch, fp8q, synth, model1, dev):
+    """Prefill, M = 4/8 decode and NestedFP figures (a few steps each)."""
+    out = {}
+    # decode at M = 4, 8 on the same weights (activations re-drawn)
+    for M in (4, 8):
+        mm = Model.__new__(Model)
+        mm.M = M
+        mm.linears = []
+        for L in model1.linears:
+            K, N = L["K"], L["N"]
+            d = dict(L)
+            d["x"] = synth.activation(M, K, seed=synth.seed_for("x", M, L["layer"], L["name"]),
+                                      device=dev)
+            d["q"] = torch.empty((M, K), dtype=torch.uint8, device=dev)
+            d["y"] = torch.empty((M, N), dtype=torch.bfloat16, device=dev)
+            mm.linears.append(d)
+        dt, _ = time_steps(torch, fp8q, mm, steps=5, warmup=2)
+        byts = sum(mm.gemm_bytes(L) + mm.quant_bytes(L) for L in mm.linears)
+        out[f"decode_m{M}"] = {"GB_per_s": round(byts / dt / 1e9, 1),
+                               "frac_hbm": round(byts / dt / 1e9 / HBM_PEAK_GBS, 4),
+                               "ms_per_step": round(dt * 1e3, 3)}
+    # prefill M = 512, 2048 (activations with 0.1% outlier channels x50)
+    for M in (512, 2048):
+        mm = Model.__new__(Model)
+        mm.M = M
+        mm.linears = []
+        for L in model1.linears:
+            K, N = L["K"], L["N"]
+            d = dict(L)
+            d["x"] = synth.activation(M, K, seed=synth.seed_for("xp", M, L["layer"], L["name"]),
+                                      outliers=True, device=dev)
+            d["q"] = torch.empty((M, K), dtype=torch.uint8, device=dev)
+            d["y"] = torch.empty((M, N), dtype=torch.bfloat16, device=dev)
+            mm.linears.append(d)
+        dt, kern = time_steps(torch, fp8q, mm, steps=3, warmup=1, with_events=True)
+        fl = sum(mm.flops(L) for L in mm.linears)
+        out[f"prefill_m{M}"] = {"TFLOP_per_s": round(fl / dt / 1e12, 1),
+                                "frac_fp8_mfma": round(fl / dt / 1e12 / FP8_PEAK_TFLOPS, 4),
+                                "gemm_only_TFLOP_per_s": round(fl / (kern * len(mm.linears)) / 1e12, 1),
+                                "ms_per_step": round(dt * 1e3, 3)}
+        del mm
+    # NestedFP at M = 1 and 256 on 8 layers of fp16 weights (hi/lo planes)
+    nested = []
+    for layer in range(8):
+        for name, K, N in synth.LLAMA7B_LINEARS:
+            w = synth.normal((N, K), 0.02, "fp16", seed=synth.seed_for("w", layer, name), device=dev)
+            hi, lo = fp8q.nested_split(w)
+            del w
+            nested.append((K, N, hi, lo))
+    for M in (1, 256):
+        bufs = []
+        for K, N, hi, lo in nested:
+            a = synth.activation(M, K, seed=synth.seed_for("a16", M, K, N), dtype="fp16", device=dev)
+            bufs.append((a, torch.empty((M, K), dtype=torch.uint8, device=dev),
+                         torch.empty(1, dtype=torch.float32, device=dev),
+                         torch.empty(1, dtype=torch.float32, device=dev),
+                         torch.empty((M, N), dtype=torch.float16, device=dev)))
+
+        def step16():
+            for (K, N, hi, lo), (a, q, s, am, y) in zip(nested, bufs):
+                fp8q.nested_gemm_fp16(a, hi, lo, y)
+
+        def step8():
+            for (K, N, hi, lo), (a, q, s, am, y) in zip(nested, bufs):
+                fp8q.fp8_quantize_act(a, q, s, am)
+                fp8q.nested_gemm_fp8(q, s, hi, y)
+
+        for mode, fn, wbytes in (("fp16", step16, 2), ("fp8", step8, 1)):
+            for _ in range(2):
+                fn()
+            torch.cuda.synchronize()
+            t0 = time.perf_counter()
+            for _ in range(5):
+                fn()
+            torch.cuda.synchronize()
+            dt = (time.perf_counter() - t0) / 5
+            byts = sum(wbytes * N * K + 2 * M * K + 2 * M * N for K, N, _, _ in nested)
+            if mode == "fp8":
+                byts = sum(N * K + M * K + 2 * M * N + 3 * M * K for K, N, _, _ in nested)
+            fl = sum(2 * M * N * K for K, N, _, _ in nested)
+            out[f"nested_{mode}_m{M}"] = {"GB_per_s": round(byts / dt / 1e9, 1),
+                                          "frac_hbm": round(byts / dt / 1e9 / HBM_PEAK_GBS, 4),
+                                          "TFLOP_per_s": round(fl / dt / 1e12, 2),
+                                          "layers": 8}
+    return out
+
+
+def main():
+    args = parse()
+    if args.gpus != 1:
+        print(f"bench.py runs on exactly one GPU; --gpus {args.gpus} is not supported "
+              "(this build has no multi-GPU path)", file=sys.stderr)
+        sys.exit(2)
+    import torch
+
+    from fp8_quantized_gemm_amd import fp8q, synth
+
+    dev = "cuda:0"
+    torch.cuda.set_device(0)
+    model = Model(torch, fp8q, synth, M=1, dev=dev)
+    dt, kern = time_steps(torch, fp8q, model, args.steps, args.warmup, graph=args.graph,
+                          with_events=not args.graph)
+    step_bytes = sum(model.gemm_bytes(L) + model.quant_bytes(L) for L in model.linears)
+    value = step_bytes / dt / 1e9
+    if kern is None:        # graph mode: time the GEMV launches in an eager pass
+        _, kern = time_steps(torch, fp8q, model, max(3, args.steps // 4), 1, with_events=True)
+    gemv_bytes = sum(model.gemm_bytes(L) for L in model.linears) / len(model.linears)
+    achieved = gemv_bytes / kern / 1e9
+    src_hash = kernel_source_hash()
+    traffic = load_traffic(src_hash)
+    result = {
+        "metric": METRIC,
+        "value": round(value, 2),
+        "unit": "GB/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(dt * 1e3, 4),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "fp8_e4m3 (fp32 accumulate, bf16 out)",
+        "data": "synthetic",
+        "config": {"workload": "llama7b_decode_m1_32layers", "M": 1, "layers": LAYERS,
+                   "linears_K_N": [[K, N] for _, K, N in synth.LLAMA7B_LINEARS],
+                   "weights": "fp16 N(0,0.02) -> E4M3 per-tensor", "activations": "bf16 N(0,1)",
+                   "frac_hbm_step": round(value / HBM_PEAK_GBS, 4),
+                   "graph": bool(args.graph)},
+        "roofline": {"bound": "hbm", "kernel": "gemv_f8_kernel (fp8_gemm, M<=16)",
+                     "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                     "frac": round(achieved / HBM_PEAK_GBS, 4),
+                     "avg_launch_us": round(kern * 1e6, 3),
+                     "algorithmic_bytes_per_launch": int(gemv_bytes),
+                     "traffic": traffic, "kernel_source_hash": src_hash},
+    }
+    if not args.no_secondary:
+        result["secondary"] = secondary(torch, fp8q, synth, model, dev)
+    if not args.no_cpu_baseline:
+        result["cpu_baseline"] = cpu_baseline(torch, synth, dev, args.cpu_seconds)
+    print(json.dumps(result), flush=True)
+
+
+if __name__ == "__main__":
+    main()
