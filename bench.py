@@ -1,21 +1,25 @@
 """Benchmark of the FP8 linear-layer hot path on one MI355X.
 
     python bench.py [--gpus 1] [--steps K] [--warmup W] [--no-cpu-baseline]
-                    [--no-secondary] [--graph]
+                    [--no-secondary] [--eager]
 
 Workload (one "step"): the 32 layers of Llama-7B-shaped decode linears at
 M = 1 token (fused QKV 4096->12288, O 4096->4096, gate+up 4096->22016,
 down 11008->4096), each one a dynamic per-tensor E4M3 quantization of its bf16
 activation followed by the FP8 GEMM against statically quantized E4M3 weights
-(fp32 accumulation, bf16 output).  The 128 weight matrices are distinct
+(fp32 accumulation, bf16 output), issued as one fp8_linear call per linear
+(a single fused kernel at M = 1).  The 128 weight matrices are distinct
 (6.48 GB of FP8 codes), so every step streams them from HBM.
 
 `value` is whole-step algorithmic HBM traffic divided by the step time
 (GB/s): per linear N*K weight bytes + M*K code bytes + 2*M*N output bytes for
 the GEMM and 3*M*K bytes for the quantizer.  Inputs are resident in HBM
-before timing.  `roofline` reports the decode GEMV kernel alone (its
-algorithmic bytes over its average duration, measured with HIP events around
-every GEMV launch on the launch stream inside the timed region).
+before timing.  By default the 128 launches of a step are captured once into
+a HIP graph and the timed steps are graph replays.  `roofline` reports the
+decode kernel alone: its algorithmic bytes over its average duration,
+measured with HIP events around every fp8_linear launch on the launch stream
+over a timed region of eager steps (events cannot bracket single kernels
+inside a graph replay).
 `secondary` adds the prefill (M = 512, 2048: TFLOP/s of the tile GEMM) and
 NestedFP figures; `cpu_baseline` times the oracle on a bounded sample.
 Rank 0 prints one JSON line.
@@ -47,8 +51,9 @@ def parse():
     p.add_argument("--warmup", type=int, default=5)
     p.add_argument("--no-cpu-baseline", action="store_true")
     p.add_argument("--no-secondary", action="store_true")
-    p.add_argument("--graph", action="store_true",
-                   help="replay each step as one captured HIP graph")
+    p.add_argument("--eager", action="store_true",
+                   help="launch every kernel from Python instead of replaying the step as "
+                        "one captured HIP graph")
     p.add_argument("--cpu-seconds", type=float, default=10.0,
                    help="lower bound on the oracle's timed CPU work")
     return p.parse_args()
@@ -56,7 +61,7 @@ def parse():
 
 def kernel_source_hash() -> str:
     h = hashlib.sha256()
-    for f in ("gemv.hip", "common.hpp"):
+    for f in ("linear.hip", "common.hpp"):
         with open(os.path.join(ROOT, "fp8_quantized_gemm_amd", "csrc", f), "rb") as fh:
             h.update(fh.read())
     return h.hexdigest()[:16]
@@ -65,7 +70,7 @@ def kernel_source_hash() -> str:
 def load_traffic(src_hash: str):
     """HBM traffic per GEMV launch from the committed counter summary, if it
     was taken on the current kernel source."""
-    path = os.path.join(ROOT, "profiles", "gemv_fp8_llama7b_decode_m1_traffic.json")
+    path = os.path.join(ROOT, "profiles", "linear_fused_llama7b_decode_m1_traffic.json")
     try:
         with open(path) as f:
             d = json.load(f)
@@ -111,17 +116,18 @@ class Model:
 
 
 def run_step(fp8q, model, events=None):
+    """One pass over every linear: dynamic quantization + FP8 GEMM (fp8_linear).
+    With `events`, a HIP event pair brackets each call on its stream."""
     for i, L in enumerate(model.linears):
-        fp8q.fp8_quantize_act(L["x"], L["q"], L["sa"], L["amax"])
         if events is not None:
             events[i][0].record()
-        fp8q.fp8_gemm(L["q"], L["sa"], L["qw"], L["sw"], L["y"])
+        fp8q.fp8_linear(L["x"], L["qw"], L["sw"], L["y"], L["q"], L["sa"], L["amax"])
         if events is not None:
             events[i][1].record()
 
 
 def time_steps(torch, fp8q, model, steps, warmup, graph=False, with_events=False):
-    """Returns (seconds per step, average GEMV launch seconds or None)."""
+    """Returns (seconds per step, average seconds of one fp8_linear call or None)."""
     for _ in range(warmup):
         run_step(fp8q, model)
     torch.cuda.synchronize()
@@ -293,14 +299,15 @@ def main():
     dev = "cuda:0"
     torch.cuda.set_device(0)
     model = Model(torch, fp8q, synth, M=1, dev=dev)
-    dt, kern = time_steps(torch, fp8q, model, args.steps, args.warmup, graph=args.graph,
-                          with_events=not args.graph)
+    graph = not args.eager
+    dt, kern = time_steps(torch, fp8q, model, args.steps, args.warmup, graph=graph,
+                          with_events=not graph)
     step_bytes = sum(model.gemm_bytes(L) + model.quant_bytes(L) for L in model.linears)
     value = step_bytes / dt / 1e9
-    if kern is None:        # graph mode: time the GEMV launches in an eager pass
+    if kern is None:        # graph mode: time the launches in an eager pass
         _, kern = time_steps(torch, fp8q, model, max(3, args.steps // 4), 1, with_events=True)
-    gemv_bytes = sum(model.gemm_bytes(L) for L in model.linears) / len(model.linears)
-    achieved = gemv_bytes / kern / 1e9
+    launch_bytes = step_bytes / len(model.linears)
+    achieved = launch_bytes / kern / 1e9
     src_hash = kernel_source_hash()
     traffic = load_traffic(src_hash)
     result = {
@@ -320,12 +327,13 @@ def main():
                    "linears_K_N": [[K, N] for _, K, N in synth.LLAMA7B_LINEARS],
                    "weights": "fp16 N(0,0.02) -> E4M3 per-tensor", "activations": "bf16 N(0,1)",
                    "frac_hbm_step": round(value / HBM_PEAK_GBS, 4),
-                   "graph": bool(args.graph)},
-        "roofline": {"bound": "hbm", "kernel": "gemv_f8_kernel (fp8_gemm, M<=16)",
+                   "launch": "hip_graph_replay" if graph else "eager"},
+        "roofline": {"bound": "hbm",
+                     "kernel": "rowk_f8_kernel, fused quantize + FP8 GEMM (fp8_linear, M=1)",
                      "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
                      "frac": round(achieved / HBM_PEAK_GBS, 4),
                      "avg_launch_us": round(kern * 1e6, 3),
-                     "algorithmic_bytes_per_launch": int(gemv_bytes),
+                     "algorithmic_bytes_per_launch": int(launch_bytes),
                      "traffic": traffic, "kernel_source_hash": src_hash},
     }
     if not args.no_secondary:

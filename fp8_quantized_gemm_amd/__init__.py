@@ -7,7 +7,7 @@ ctypes binding with the same entry-point names; importing any of those names
 from this package loads the library and raises if it has not been built.
 """
 _API = (
-    "fp8_quantize_act", "fp8_gemm", "nested_split", "nested_rebuild_fp16",
+    "fp8_quantize_act", "fp8_gemm", "fp8_linear", "nested_split", "nested_rebuild_fp16",
     "nested_gemm_fp16", "nested_gemm_fp8", "e4m3_encode_f32", "abi_version", "Fp8qError",
 )
 

@@ -17,7 +17,7 @@ BUILD = os.path.join(HERE, "_build")
 OUT = os.path.join(HERE, "libfp8q.so")
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 
-SOURCES = ["quant.hip", "gemv.hip", "gemm.hip", "nested.hip", "api.hip"]
+SOURCES = ["quant.hip", "gemv.hip", "linear.hip", "gemm.hip", "nested.hip", "api.hip"]
 
 FLAGS = [
     "--offload-arch=gfx950",

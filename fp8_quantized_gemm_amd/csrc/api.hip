@@ -1,6 +1,6 @@
 // libfp8q C ABI (declared in include/fp8q.h): host-side validation, M-based
-// dispatch between the decode (M <= 16) and tile (M > 16) kernels, and launch
-// on the caller's stream.  No device memory is allocated and no host
+// dispatch between the decode kernels (M <= 2 row-contiguous, M <= 16 MFMA
+// GEMV) and the MFMA tile kernels (M > 16), and launch on the caller's stream.  No device memory is allocated and no host
 // synchronization happens in any call.
 #include <atomic>
 #include <cstdio>
@@ -14,6 +14,9 @@ using namespace fp8q;
 namespace {
 
 constexpr int64_t kMaxDim = 0x7fffffff;
+// K bound: a 128-row tile of fp16 activations (128 * K * 2 bytes) must stay
+// addressable by the kernels' 31-bit buffer offsets.
+constexpr int64_t kMaxK = (int64_t)1 << 22;
 constexpr int kDecodeMaxM = 16;
 
 thread_local char g_last_error[256] = "";
@@ -70,8 +73,18 @@ fp8q_status finish(const char* where, hipError_t e)
 fp8q_status check_gemm_sizes(int64_t M, int64_t N, int64_t K)
 {
     if (M < 1 || N < 1 || K < 16 || (K % 16) != 0) return FP8Q_ERR_SHAPE;
-    if (M > kMaxDim || N > kMaxDim || K > kMaxDim) return FP8Q_ERR_SHAPE;
+    if (M > kMaxDim || N > kMaxDim || K > kMaxK) return FP8Q_ERR_SHAPE;
     return FP8Q_OK;
+}
+
+// FP8-operand GEMM dispatch on M: row-contiguous VALU path (M <= 2),
+// MFMA GEMV (M <= 16), MFMA tile GEMM (larger M).
+hipError_t dispatch_fp8(const uint8_t* qa, const float* sa, const uint8_t* qw, const float* sw,
+                        uint16_t* y, int M, int N, int K, int wfmt, int outf, hipStream_t st)
+{
+    if (M <= kRowkMaxM) return launch_rowk_fp8(qa, sa, qw, sw, y, M, N, K, wfmt, outf, st);
+    if (M <= kDecodeMaxM) return launch_gemv_fp8(qa, sa, qw, sw, y, M, N, K, wfmt, outf, st);
+    return launch_tile_fp8(qa, sa, qw, sw, y, M, N, K, wfmt, outf, st);
 }
 
 #define FP8Q_TRY(expr)                     \
@@ -122,13 +135,29 @@ fp8q_status fp8_gemm(const uint8_t* qa, const float* sa, const uint8_t* qw, cons
     if (!aligned16(qa) || !aligned16(qw) || !aligned16(y) || !aligned4(sa) || !aligned4(sw))
         return FP8Q_ERR_ALIGN;
     FP8Q_TRY(check_device());
+    return finish("fp8_gemm", dispatch_fp8(qa, sa, qw, sw, y, (int)M, (int)N, (int)K, WF_E4M3,
+                                           OUT_BF16, (hipStream_t)stream));
+}
+
+fp8q_status fp8_linear(const void* x, int dtype, const uint8_t* qw, const float* sw, uint16_t* y,
+                       uint8_t* q, float* scale, float* amax, int64_t M, int64_t N, int64_t K,
+                       fp8q_stream stream)
+{
+    if (!x || !qw || !sw || !y || !q || !scale || !amax) return FP8Q_ERR_NULL;
+    if (dtype != FP8Q_BF16 && dtype != FP8Q_FP16) return FP8Q_ERR_DTYPE;
+    FP8Q_TRY(check_gemm_sizes(M, N, K));
+    if (!aligned16(x) || !aligned16(qw) || !aligned16(y) || !aligned16(q) || !aligned4(sw) ||
+        !aligned4(scale) || !aligned4(amax))
+        return FP8Q_ERR_ALIGN;
+    FP8Q_TRY(check_device());
     hipStream_t st = (hipStream_t)stream;
-    hipError_t e = M <= kDecodeMaxM
-                       ? launch_gemv_fp8(qa, sa, qw, sw, y, (int)M, (int)N, (int)K, WF_E4M3,
-                                         OUT_BF16, st)
-                       : launch_tile_fp8(qa, sa, qw, sw, y, (int)M, (int)N, (int)K, WF_E4M3,
-                                         OUT_BF16, st);
-    return finish("fp8_gemm", e);
+    if (M <= kRowkMaxM && M * K <= kFusedMaxMK)
+        return finish("fp8_linear", launch_linear_fused(x, dtype, qw, sw, y, q, scale, amax,
+                                                        (int)M, (int)N, (int)K, st));
+    hipError_t e = launch_quantize(x, dtype, M * K, q, scale, amax, st);
+    if (e == hipSuccess)
+        e = dispatch_fp8(q, scale, qw, sw, y, (int)M, (int)N, (int)K, WF_E4M3, OUT_BF16, st);
+    return finish("fp8_linear", e);
 }
 
 fp8q_status nested_split(const uint16_t* w, uint8_t* hi, uint8_t* lo, int64_t n,
@@ -159,9 +188,9 @@ fp8q_status nested_gemm_fp16(const uint16_t* a, const uint8_t* hi, const uint8_t
     if (!aligned16(a) || !aligned16(hi) || !aligned16(lo) || !aligned16(y)) return FP8Q_ERR_ALIGN;
     FP8Q_TRY(check_device());
     hipStream_t st = (hipStream_t)stream;
-    hipError_t e = M <= kDecodeMaxM
-                       ? launch_gemv_nested16(a, hi, lo, y, (int)M, (int)N, (int)K, st)
-                       : launch_tile_nested16(a, hi, lo, y, (int)M, (int)N, (int)K, st);
+    hipError_t e = M <= kRowkMaxM     ? launch_rowk_nested16(a, hi, lo, y, (int)M, (int)N, (int)K, st)
+                   : M <= kDecodeMaxM ? launch_gemv_nested16(a, hi, lo, y, (int)M, (int)N, (int)K, st)
+                                      : launch_tile_nested16(a, hi, lo, y, (int)M, (int)N, (int)K, st);
     return finish("nested_gemm_fp16", e);
 }
 
@@ -172,13 +201,8 @@ fp8q_status nested_gemm_fp8(const uint8_t* qa, const float* sa, const uint8_t* h
     FP8Q_TRY(check_gemm_sizes(M, N, K));
     if (!aligned16(qa) || !aligned16(hi) || !aligned16(y) || !aligned4(sa)) return FP8Q_ERR_ALIGN;
     FP8Q_TRY(check_device());
-    hipStream_t st = (hipStream_t)stream;
-    hipError_t e = M <= kDecodeMaxM
-                       ? launch_gemv_fp8(qa, sa, hi, nullptr, y, (int)M, (int)N, (int)K, WF_E5M2,
-                                         OUT_FP16, st)
-                       : launch_tile_fp8(qa, sa, hi, nullptr, y, (int)M, (int)N, (int)K, WF_E5M2,
-                                         OUT_FP16, st);
-    return finish("nested_gemm_fp8", e);
+    return finish("nested_gemm_fp8", dispatch_fp8(qa, sa, hi, nullptr, y, (int)M, (int)N, (int)K,
+                                                  WF_E5M2, OUT_FP16, (hipStream_t)stream));
 }
 
 fp8q_status fp8q_e4m3_encode_f32(const float* v, uint8_t* q, int64_t n, fp8q_stream stream)

@@ -78,6 +78,51 @@ __device__ __forceinline__ uint32_t e4m3_pack4(float a, float b, float c, float 
     return (uint32_t)r;
 }
 
+// ---------------------------------------------------------------- quantizer elements
+// Shared by the stand-alone quantizer and the fused decode linear, so both
+// produce the same codes: q = E4M3_rne_sat(fl32(x / s)), s = fl32(amax / 448)
+// (1 when amax == 0), with x / s the IEEE correctly rounded division.
+template <int DT>
+__device__ __forceinline__ float vec_absmax(const v4i& v)
+{
+    float m = 0.0f;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+        uint32_t u = (uint32_t)v[i];
+        m = fmaxf(m, fabsf(half_bits_to_f32<DT>(u & 0xffffu)));
+        m = fmaxf(m, fabsf(half_bits_to_f32<DT>(u >> 16)));
+    }
+    return m;
+}
+
+// 8 input halves -> 8 E4M3 codes (two dwords)
+template <int DT>
+__device__ __forceinline__ v2i vec_quantize(const v4i& v, float s)
+{
+    float f[8];
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+        uint32_t u = (uint32_t)v[i];
+        f[2 * i] = half_bits_to_f32<DT>(u & 0xffffu) / s;
+        f[2 * i + 1] = half_bits_to_f32<DT>(u >> 16) / s;
+    }
+    v2i r;
+    r[0] = (int)e4m3_pack4(f[0], f[1], f[2], f[3]);
+    r[1] = (int)e4m3_pack4(f[4], f[5], f[6], f[7]);
+    return r;
+}
+
+template <int DT>
+__device__ __forceinline__ uint8_t scalar_quantize(uint16_t h, float s)
+{
+    return (uint8_t)(e4m3_pack4(half_bits_to_f32<DT>(h) / s, 0.f, 0.f, 0.f) & 0xffu);
+}
+
+__device__ __forceinline__ float scale_from_amax(float amax)
+{
+    return amax > 0.0f ? amax / 448.0f : 1.0f;
+}
+
 // ---------------------------------------------------------------- NestedFP rebuild
 // Interleave four upper bytes (h) and four lower bytes (l) into two dwords
 // holding the fp16 words (h_i << 8) | l_i, i = 0..3, little-endian.
@@ -86,6 +131,38 @@ __device__ __forceinline__ void nested_rebuild4(uint32_t h, uint32_t l, uint32_t
 {
     w01 = __builtin_amdgcn_perm(h, l, 0x05010400u);  // [l0, h0, l1, h1]
     w23 = __builtin_amdgcn_perm(h, l, 0x07030602u);  // [l2, h2, l3, h3]
+}
+
+// ---------------------------------------------------------------- buffer loads
+// Raw buffer resources (gfx9 V#: base, stride 0, num_records bytes, word 3 =
+// 0x00020000).  A buffer load whose byte offset lies at or past num_records
+// returns zeros without touching memory, which gives free zero padding for
+// ragged rows and K tails without branches.
+typedef __amdgpu_buffer_rsrc_t rsrc_t;
+
+// Callers pass wave-uniform base and size; readfirstlane states that to the
+// compiler so the descriptor lives in SGPRs (no per-load waterfall loop).
+__device__ __forceinline__ rsrc_t make_rsrc(const void* base, uint32_t bytes)
+{
+    const uint64_t p = reinterpret_cast<uint64_t>(base);
+    const uint32_t lo = __builtin_amdgcn_readfirstlane((uint32_t)p);
+    const uint32_t hi = __builtin_amdgcn_readfirstlane((uint32_t)(p >> 32));
+    const uint32_t n = __builtin_amdgcn_readfirstlane(bytes);
+    void* b = reinterpret_cast<void*>(((uint64_t)hi << 32) | lo);
+    return __builtin_amdgcn_make_buffer_rsrc(b, (short)0, (int)n, 0x00020000);
+}
+
+// An offset that always lies out of range (num_records < 2^31).
+constexpr uint32_t kOOB = 0x80000000u;
+
+// Cache policy bits of the buffer instructions (aux operand): 0 = default,
+// 2 = non-temporal (streamed data that will not be reused).
+enum : int { CP_DEFAULT = 0, CP_NT = 2 };
+
+template <int CP = CP_DEFAULT>
+__device__ __forceinline__ v4i buf_load16(rsrc_t r, uint32_t off)
+{
+    return __builtin_amdgcn_raw_buffer_load_b128(r, off, 0, CP);
 }
 
 // ---------------------------------------------------------------- reductions
@@ -106,10 +183,46 @@ __device__ __forceinline__ float wave_max(float v)
     return __int_as_float(__builtin_amdgcn_readlane(__float_as_int(v), 63));
 }
 
+// Block-wide max for blockDim.x = NT threads; result valid in every thread.
+template <int NT>
+__device__ __forceinline__ float block_max(float v, float* lds)
+{
+    constexpr int W = NT / 64;
+    v = wave_max(v);
+    const int wave = threadIdx.x >> 6;
+    if ((threadIdx.x & 63) == 0) lds[wave] = v;
+    __syncthreads();
+    float m = lds[0];
+#pragma unroll
+    for (int i = 1; i < W; ++i) m = fmaxf(m, lds[i]);
+    return m;
+}
+
+// Sum over a wave64 (butterfly through the LDS crossbar); valid in every lane.
+__device__ __forceinline__ float wave_sum(float v)
+{
+#pragma unroll
+    for (int off = 32; off >= 1; off >>= 1) v += __shfl_xor(v, off);
+    return v;
+}
+
 // ---------------------------------------------------------------- launchers
 // Each returns the hipError_t of hipGetLastError() after its launches.
 hipError_t launch_quantize(const void* x, int dtype, int64_t n, uint8_t* q, float* scale,
                            float* amax, hipStream_t stream);
+
+// Row-contiguous decode path for M <= kRowkMaxM (see linear.hip).
+constexpr int kRowkMaxM = 2;
+// Largest M*K the fused decode linear quantizes in LDS.
+constexpr int64_t kFusedMaxMK = 32768;
+hipError_t launch_rowk_fp8(const uint8_t* qa, const float* sa, const uint8_t* qw, const float* sw,
+                           uint16_t* y, int M, int N, int K, int wfmt, int outf,
+                           hipStream_t stream);
+hipError_t launch_rowk_nested16(const uint16_t* a, const uint8_t* hi, const uint8_t* lo,
+                                uint16_t* y, int M, int N, int K, hipStream_t stream);
+hipError_t launch_linear_fused(const void* x, int dtype, const uint8_t* qw, const float* sw,
+                               uint16_t* y, uint8_t* q, float* scale, float* amax, int M, int N,
+                               int K, hipStream_t stream);
 hipError_t launch_e4m3_encode_f32(const float* v, uint8_t* q, int64_t n, hipStream_t stream);
 
 // Decode path (M <= 16) and tile path (M > 16) of the FP8 GEMM; wfmt selects

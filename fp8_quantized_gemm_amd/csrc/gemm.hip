@@ -84,28 +84,23 @@ __global__ __launch_bounds__(kThreads) void gemm_f8_tile_kernel(
     const int n0 = (bid / tiles_m) * kBN;
 
     // global -> register staging: thread owns unit (tid & 7) of rows
-    // (tid >> 3) + 32 j, j = 0..3, of both the A and the W tile
+    // (tid >> 3) + 32 j, j = 0..3, of both the A and the W tile.  Buffer
+    // resources span the valid rows of each tile, so rows past M or N and
+    // units past K (given an out-of-range offset) read as zero, unpredicated.
     const int su = tid & 7;
-    const uint8_t* aptr[4];
-    const uint8_t* wptr[4];
-    bool aok[4], wok[4];
+    const rsrc_t ra = make_rsrc(qa + (size_t)m0 * K, (uint32_t)(min(kBM, M - m0) * K));
+    const rsrc_t rw = make_rsrc(qw + (size_t)n0 * K, (uint32_t)(min(kBN, N - n0) * K));
+    uint32_t roff[4];
 #pragma unroll
-    for (int j = 0; j < 4; ++j) {
-        const int row = (tid >> 3) + 32 * j;
-        aok[j] = m0 + row < M;
-        wok[j] = n0 + row < N;
-        aptr[j] = qa + (size_t)(aok[j] ? m0 + row : 0) * K + su * 16;
-        wptr[j] = qw + (size_t)(wok[j] ? n0 + row : 0) * K + su * 16;
-    }
-    const v4i z = {0, 0, 0, 0};
-    v4i ra[4], rw[4];
+    for (int j = 0; j < 4; ++j) roff[j] = (uint32_t)(((tid >> 3) + 32 * j) * K + su * 16);
+    v4i ra_[4], rw_[4];
     auto gload = [&](int kt) {
-        const int k = kt * BK + su * 16;
-        const bool kin = k < K;
+        const bool kin = kt * BK + su * 16 < K;
 #pragma unroll
         for (int j = 0; j < 4; ++j) {
-            ra[j] = (aok[j] && kin) ? *reinterpret_cast<const v4i*>(aptr[j] + kt * BK) : z;
-            rw[j] = (wok[j] && kin) ? *reinterpret_cast<const v4i*>(wptr[j] + kt * BK) : z;
+            const uint32_t o = kin ? roff[j] + kt * BK : kOOB;
+            ra_[j] = buf_load16(ra, o);
+            rw_[j] = buf_load16(rw, o);
         }
     };
     auto lstore = [&](int buf) {
@@ -114,8 +109,8 @@ __global__ __launch_bounds__(kThreads) void gemm_f8_tile_kernel(
 #pragma unroll
         for (int j = 0; j < 4; ++j) {
             const int row = (tid >> 3) + 32 * j;
-            *reinterpret_cast<v4i*>(As + swz128(row, su)) = ra[j];
-            *reinterpret_cast<v4i*>(Ws + swz128(row, su)) = rw[j];
+            *reinterpret_cast<v4i*>(As + swz128(row, su)) = ra_[j];
+            *reinterpret_cast<v4i*>(Ws + swz128(row, su)) = rw_[j];
         }
     };
 
@@ -189,37 +184,25 @@ __global__ __launch_bounds__(kThreads) void gemm_nested16_tile_kernel(
     // A staging: unit (tid & 7) (8 elements) of rows (tid >> 3) + 32 j, j = 0..3
     // plane staging: unit (tid & 3) (16 bytes) of rows (tid >> 2) + 64 j, j = 0..1
     const int au = tid & 7, pu = tid & 3;
-    const uint16_t* aptr[4];
-    bool aok[4];
+    const int mrows = min(kBM, M - m0), nrows = min(kBN, N - n0);
+    const rsrc_t ra = make_rsrc(a + (size_t)m0 * K, (uint32_t)(mrows * K * 2));
+    const rsrc_t rh = make_rsrc(hi + (size_t)n0 * K, (uint32_t)(nrows * K));
+    const rsrc_t rl = make_rsrc(lo + (size_t)n0 * K, (uint32_t)(nrows * K));
+    uint32_t aoff[4], poff[2];
 #pragma unroll
-    for (int j = 0; j < 4; ++j) {
-        const int row = (tid >> 3) + 32 * j;
-        aok[j] = m0 + row < M;
-        aptr[j] = a + (size_t)(aok[j] ? m0 + row : 0) * K + au * 8;
-    }
-    const uint8_t* hptr[2];
-    const uint8_t* lptr[2];
-    bool pok[2];
+    for (int j = 0; j < 4; ++j) aoff[j] = (uint32_t)((((tid >> 3) + 32 * j) * K + au * 8) * 2);
 #pragma unroll
-    for (int j = 0; j < 2; ++j) {
-        const int row = (tid >> 2) + 64 * j;
-        pok[j] = n0 + row < N;
-        const size_t off = (size_t)(pok[j] ? n0 + row : 0) * K + pu * 16;
-        hptr[j] = hi + off;
-        lptr[j] = lo + off;
-    }
-    const v4i z = {0, 0, 0, 0};
-    v4i ra[4], rh[2], rl[2];
+    for (int j = 0; j < 2; ++j) poff[j] = (uint32_t)(((tid >> 2) + 64 * j) * K + pu * 16);
+    v4i ra_[4], rh_[2], rl_[2];
     auto gload = [&](int kt) {
         const bool ain = kt * BK + au * 8 < K;
         const bool pin = kt * BK + pu * 16 < K;
 #pragma unroll
-        for (int j = 0; j < 4; ++j)
-            ra[j] = (aok[j] && ain) ? *reinterpret_cast<const v4i*>(aptr[j] + kt * BK) : z;
+        for (int j = 0; j < 4; ++j) ra_[j] = buf_load16(ra, ain ? aoff[j] + kt * BK * 2 : kOOB);
 #pragma unroll
         for (int j = 0; j < 2; ++j) {
-            rh[j] = (pok[j] && pin) ? *reinterpret_cast<const v4i*>(hptr[j] + kt * BK) : z;
-            rl[j] = (pok[j] && pin) ? *reinterpret_cast<const v4i*>(lptr[j] + kt * BK) : z;
+            rh_[j] = buf_load16(rh, pin ? poff[j] + kt * BK : kOOB);
+            rl_[j] = buf_load16(rl, pin ? poff[j] + kt * BK : kOOB);
         }
     };
     auto lstore = [&](int buf) {
@@ -228,12 +211,12 @@ __global__ __launch_bounds__(kThreads) void gemm_nested16_tile_kernel(
         uint8_t* Ls = Hs + P_BYTES;
 #pragma unroll
         for (int j = 0; j < 4; ++j)
-            *reinterpret_cast<v4i*>(As + swz128((tid >> 3) + 32 * j, au)) = ra[j];
+            *reinterpret_cast<v4i*>(As + swz128((tid >> 3) + 32 * j, au)) = ra_[j];
 #pragma unroll
         for (int j = 0; j < 2; ++j) {
             const int row = (tid >> 2) + 64 * j;
-            *reinterpret_cast<v4i*>(Hs + swz64(row, pu)) = rh[j];
-            *reinterpret_cast<v4i*>(Ls + swz64(row, pu)) = rl[j];
+            *reinterpret_cast<v4i*>(Hs + swz64(row, pu)) = rh_[j];
+            *reinterpret_cast<v4i*>(Ls + swz64(row, pu)) = rl_[j];
         }
     };
 

@@ -37,15 +37,17 @@ __device__ __forceinline__ v8i cat(const v4i& lo, const v4i& hi)
     return v8i{lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
 }
 
-__device__ __forceinline__ v4i ld16(const uint8_t* p)
-{
-    return *reinterpret_cast<const v4i*>(p);
-}
-
 // ---------------------------------------------------------------- FP8 GEMV
 // y[m, n] = out( sum_k qa[m,k] * W[n,k] * scale ),  scale = *sa * *sw (or *sa
 // when sw == nullptr).
-template <int WFMT, int OUTF, int WAVES, int UNROLL>
+//
+// All loads are raw buffer loads: the weight resource spans only the valid
+// rows of this workgroup's 16-row tile and the activation resource only the
+// M valid rows, so padded rows read as zero, and a chunk past the end of K
+// gets an always-out-of-range offset.  No load is predicated, so each wave
+// issues its U blocks (2 x 16 bytes of weights per lane per block) back to
+// back before the first MFMA waits on them.
+template <int WFMT, int OUTF, int WAVES, int U, int CP>
 __global__ __launch_bounds__(WAVES * 64) void gemv_f8_kernel(
     const uint8_t* __restrict__ qa, const float* __restrict__ sa,
     const uint8_t* __restrict__ qw, const float* __restrict__ sw,
@@ -57,33 +59,33 @@ __global__ __launch_bounds__(WAVES * 64) void gemv_f8_kernel(
     const int r = lane & 15;
     const int g = lane >> 4;
     const int n0 = blockIdx.x * 16;
+    const int rows = min(16, N - n0);
 
-    const bool wrow_ok = (n0 + r) < N;
-    const bool arow_ok = r < M;
-    const uint8_t* wrow = qw + (size_t)(wrow_ok ? n0 + r : 0) * K;
-    const uint8_t* arow = qa + (size_t)(arow_ok ? r : 0) * K;
+    const rsrc_t rw = make_rsrc(qw + (size_t)n0 * K, (uint32_t)(rows * K));
+    const rsrc_t ra = make_rsrc(qa, (uint32_t)(M * K));
+    const uint32_t row_off = (uint32_t)(r * K);   // past the resource for padded rows
 
     const int nblk = (K + 127) >> 7;
     v4f acc = {0.f, 0.f, 0.f, 0.f};
-    const v4i z = {0, 0, 0, 0};
 
-    for (int kb0 = wave; kb0 < nblk; kb0 += WAVES * UNROLL) {
-        v4i wl[UNROLL], wh[UNROLL], al[UNROLL], ah[UNROLL];
+    for (int kb0 = wave; kb0 < nblk; kb0 += WAVES * U) {
+        v4i w0[U], w1[U], a0[U], a1[U];
 #pragma unroll
-        for (int u = 0; u < UNROLL; ++u) {
-            const int kb = kb0 + u * WAVES;
-            const int k0 = kb * 128 + g * 16;
+        for (int u = 0; u < U; ++u) {
+            const int k0 = (kb0 + u * WAVES) * 128 + g * 16;
             const int k1 = k0 + 64;
-            const bool in0 = kb < nblk && k0 < K;
-            const bool in1 = kb < nblk && k1 < K;
-            wl[u] = (wrow_ok && in0) ? ld16(wrow + k0) : z;
-            wh[u] = (wrow_ok && in1) ? ld16(wrow + k1) : z;
-            al[u] = (arow_ok && in0) ? ld16(arow + k0) : z;
-            ah[u] = (arow_ok && in1) ? ld16(arow + k1) : z;
+            const uint32_t o0 = k0 < K ? row_off + k0 : kOOB;
+            const uint32_t o1 = k1 < K ? row_off + k1 : kOOB;
+            w0[u] = buf_load16<CP>(rw, o0);
+            w1[u] = buf_load16<CP>(rw, o1);
+            a0[u] = buf_load16(ra, o0);
+            a1[u] = buf_load16(ra, o1);
         }
+        // keep every load of the batch ahead of the first MFMA
+        __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
-        for (int u = 0; u < UNROLL; ++u)
-            acc = mfma_f8<WFMT>(cat(al[u], ah[u]), cat(wl[u], wh[u]), acc);
+        for (int u = 0; u < U; ++u)
+            acc = mfma_f8<WFMT>(cat(a0[u], a1[u]), cat(w0[u], w1[u]), acc);
     }
 
 #pragma unroll
@@ -94,7 +96,7 @@ __global__ __launch_bounds__(WAVES * 64) void gemv_f8_kernel(
     if (sw != nullptr) s = s * *sw;
     for (int t = threadIdx.x; t < M * 16; t += WAVES * 64) {
         const int m = t >> 4, c = t & 15;
-        if (n0 + c >= N) continue;
+        if (c >= rows) continue;
         float v = red[0][m][c];
 #pragma unroll
         for (int w = 1; w < WAVES; ++w) v += red[w][m][c];
@@ -105,8 +107,9 @@ __global__ __launch_bounds__(WAVES * 64) void gemv_f8_kernel(
 // ---------------------------------------------------------------- NestedFP FP16 GEMV
 // y[m, n] = fp16( sum_k a[m,k] * fp16((hi[n,k] << 8) | lo[n,k]) ).
 // A K block is 64 elements: lane group g takes elements [16g, 16g+16) (16
-// bytes of hi, 16 of lo, 32 of a) and feeds two 16x16x32 MFMAs.
-template <int WAVES, int UNROLL>
+// bytes of hi, 16 of lo, 32 of a) and feeds two 16x16x32 MFMAs.  Same
+// buffer-load scheme as the FP8 GEMV.
+template <int WAVES, int U, int CP>
 __global__ __launch_bounds__(WAVES * 64) void gemv_nested16_kernel(
     const uint16_t* __restrict__ a, const uint8_t* __restrict__ hi,
     const uint8_t* __restrict__ lo, uint16_t* __restrict__ y, int M, int N, int K)
@@ -117,31 +120,32 @@ __global__ __launch_bounds__(WAVES * 64) void gemv_nested16_kernel(
     const int r = lane & 15;
     const int g = lane >> 4;
     const int n0 = blockIdx.x * 16;
+    const int rows = min(16, N - n0);
 
-    const bool wrow_ok = (n0 + r) < N;
-    const bool arow_ok = r < M;
-    const uint8_t* hrow = hi + (size_t)(wrow_ok ? n0 + r : 0) * K;
-    const uint8_t* lrow = lo + (size_t)(wrow_ok ? n0 + r : 0) * K;
-    const uint16_t* arow = a + (size_t)(arow_ok ? r : 0) * K;
+    const rsrc_t rh = make_rsrc(hi + (size_t)n0 * K, (uint32_t)(rows * K));
+    const rsrc_t rl = make_rsrc(lo + (size_t)n0 * K, (uint32_t)(rows * K));
+    const rsrc_t ra = make_rsrc(a, (uint32_t)(M * K * 2));
+    const uint32_t row_off = (uint32_t)(r * K);
 
     const int nblk = (K + 63) >> 6;
     v4f acc = {0.f, 0.f, 0.f, 0.f};
-    const v4i z = {0, 0, 0, 0};
 
-    for (int kb0 = wave; kb0 < nblk; kb0 += WAVES * UNROLL) {
-        v4i hv[UNROLL], lv[UNROLL], a0[UNROLL], a1[UNROLL];
+    for (int kb0 = wave; kb0 < nblk; kb0 += WAVES * U) {
+        v4i hv[U], lv[U], a0[U], a1[U];
 #pragma unroll
-        for (int u = 0; u < UNROLL; ++u) {
-            const int kb = kb0 + u * WAVES;
-            const int k0 = kb * 64 + g * 16;
-            const bool in = kb < nblk && k0 < K;
-            hv[u] = (wrow_ok && in) ? ld16(hrow + k0) : z;
-            lv[u] = (wrow_ok && in) ? ld16(lrow + k0) : z;
-            a0[u] = (arow_ok && in) ? *reinterpret_cast<const v4i*>(arow + k0) : z;
-            a1[u] = (arow_ok && in) ? *reinterpret_cast<const v4i*>(arow + k0 + 8) : z;
+        for (int u = 0; u < U; ++u) {
+            const int k0 = (kb0 + u * WAVES) * 64 + g * 16;
+            const bool in = k0 < K;
+            const uint32_t ow = in ? row_off + k0 : kOOB;
+            const uint32_t oa = in ? 2 * (row_off + k0) : kOOB;
+            hv[u] = buf_load16<CP>(rh, ow);
+            lv[u] = buf_load16<CP>(rl, ow);
+            a0[u] = buf_load16(ra, oa);
+            a1[u] = buf_load16(ra, in ? oa + 16 : kOOB);
         }
+        __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
-        for (int u = 0; u < UNROLL; ++u) {
+        for (int u = 0; u < U; ++u) {
             uint32_t w[8];
             nested_rebuild4((uint32_t)hv[u][0], (uint32_t)lv[u][0], w[0], w[1]);
             nested_rebuild4((uint32_t)hv[u][1], (uint32_t)lv[u][1], w[2], w[3]);
@@ -162,7 +166,7 @@ __global__ __launch_bounds__(WAVES * 64) void gemv_nested16_kernel(
 
     for (int t = threadIdx.x; t < M * 16; t += WAVES * 64) {
         const int m = t >> 4, c = t & 15;
-        if (n0 + c >= N) continue;
+        if (c >= rows) continue;
         float v = red[0][m][c];
 #pragma unroll
         for (int w = 1; w < WAVES; ++w) v += red[w][m][c];
@@ -171,7 +175,8 @@ __global__ __launch_bounds__(WAVES * 64) void gemv_nested16_kernel(
 }
 
 constexpr int kGemvWaves = 4;
-constexpr int kGemvUnroll = 4;
+constexpr int kGemvUnroll = 8;
+constexpr int kNestedUnroll = 4;
 
 }  // namespace
 
@@ -181,10 +186,10 @@ hipError_t launch_gemv_fp8(const uint8_t* qa, const float* sa, const uint8_t* qw
 {
     const dim3 grid((N + 15) / 16), block(kGemvWaves * 64);
     if (wfmt == WF_E4M3 && outf == OUT_BF16)
-        gemv_f8_kernel<WF_E4M3, OUT_BF16, kGemvWaves, kGemvUnroll>
+        gemv_f8_kernel<WF_E4M3, OUT_BF16, kGemvWaves, kGemvUnroll, CP_NT>
             <<<grid, block, 0, stream>>>(qa, sa, qw, sw, y, M, N, K);
     else if (wfmt == WF_E5M2 && outf == OUT_FP16)
-        gemv_f8_kernel<WF_E5M2, OUT_FP16, kGemvWaves, kGemvUnroll>
+        gemv_f8_kernel<WF_E5M2, OUT_FP16, kGemvWaves, kGemvUnroll, CP_NT>
             <<<grid, block, 0, stream>>>(qa, sa, qw, sw, y, M, N, K);
     else
         return hipErrorInvalidValue;
@@ -194,7 +199,7 @@ hipError_t launch_gemv_fp8(const uint8_t* qa, const float* sa, const uint8_t* qw
 hipError_t launch_gemv_nested16(const uint16_t* a, const uint8_t* hi, const uint8_t* lo,
                                 uint16_t* y, int M, int N, int K, hipStream_t stream)
 {
-    gemv_nested16_kernel<kGemvWaves, kGemvUnroll>
+    gemv_nested16_kernel<kGemvWaves, kNestedUnroll, CP_NT>
         <<<dim3((N + 15) / 16), dim3(kGemvWaves * 64), 0, stream>>>(a, hi, lo, y, M, N, K);
     return hipGetLastError();
 }

@@ -1,0 +1,371 @@
+// Decode path for M <= 2 activation rows: row-contiguous weight streaming on
+// the VALU, and the fused decode linear (dynamic activation quantization +
+// FP8 GEMM in one launch).
+//
+// The weight matrix is read once and dominates the bytes (page "7B参数模型在
+// 消费级GPU上的极限" §1: memory bandwidth is the first bottleneck of token
+// generation), so the access pattern is chosen for HBM: each wave streams
+// its weight rows with every lane reading 16 consecutive bytes, i.e. 1 KiB
+// of one row per load instruction, rather than the 16-rows-by-64-bytes
+// pattern the MFMA operand layout would impose.  With at most two activation
+// rows the arithmetic (two fp8 -> fp32 conversions per packed instruction and
+// one FMA per element and row) fits comfortably in the VALU budget at full
+// HBM rate, and each wave finishes its dot products with a 64-lane sum.
+//
+// The fused variant quantizes the bf16/fp16 activation itself: every
+// workgroup reduces amax over the whole activation (L2-resident), computes
+// s = amax/448 and the E4M3 codes with the same device routines as
+// fp8_quantize_act, keeps the codes in LDS, and workgroup 0 also writes the
+// codes, scale and amax to memory.  The first batch of weight loads is issued
+// before this prologue so HBM is busy while it runs.  The FP8 GEMM is the one
+// of page "C++与FP8量化" §3.3; the quantization follows the page on a 7B
+// model on an RTX 4060, §2.2 and §6.1.
+#include "common.hpp"
+
+namespace fp8q {
+namespace {
+
+constexpr int kThreads = 256;     // NestedFP kernel: 4 waves, each owning ROWS weight rows
+constexpr int kRows = 2;
+constexpr int kUnroll = 4;        // 1 KiB chunks per row in flight per wave
+constexpr int kWgThreads = 1024;  // FP8 kernel: 16 waves per workgroup
+constexpr int kCUs = 256;         // compute units of an MI355X
+// FP8 kernel configuration, measured on MI355X over the Llama-7B / Qwen-32B
+// decode shapes: one activation row runs one weight row per wave, 2 KiB
+// batches and two workgroups per CU (57 VGPRs, 32 waves per CU); two
+// activation rows need more registers and run one workgroup per CU.
+template <int MR> struct RowkCfg;
+template <> struct RowkCfg<1> { static constexpr int ROWS = 1, U = 2, WPC = 2; };
+template <> struct RowkCfg<2> { static constexpr int ROWS = 1, U = 2, WPC = 1; };
+
+typedef float v2f __attribute__((ext_vector_type(2)));
+typedef _Float16 h2 __attribute__((ext_vector_type(2)));
+
+// 16 FP8 codes (E4M3 or E5M2) -> 16 floats, element i from byte i.
+template <int FMT>
+__device__ __forceinline__ void decode16(const v4i& v, float (&f)[16])
+{
+#pragma unroll
+    for (int d = 0; d < 4; ++d) {
+        v2f lo, hi;
+        if constexpr (FMT == WF_E4M3) {
+            lo = __builtin_amdgcn_cvt_pk_f32_fp8(v[d], false);
+            hi = __builtin_amdgcn_cvt_pk_f32_fp8(v[d], true);
+        } else {
+            lo = __builtin_amdgcn_cvt_pk_f32_bf8(v[d], false);
+            hi = __builtin_amdgcn_cvt_pk_f32_bf8(v[d], true);
+        }
+        f[4 * d] = lo[0];
+        f[4 * d + 1] = lo[1];
+        f[4 * d + 2] = hi[0];
+        f[4 * d + 3] = hi[1];
+    }
+}
+
+// ---------------------------------------------------------------- FP8 / BF8 weights
+// Activation source of the FP8 kernel.
+enum : int {
+    AS_GLOBAL = 0,   // E4M3 codes read from memory (L2) in the main loop
+    AS_COPY = 1,     // E4M3 codes copied into LDS once per workgroup
+    AS_BF16 = 2,     // bf16 activation quantized into LDS once per workgroup (fused)
+    AS_FP16 = 3,     // fp16 activation quantized into LDS once per workgroup (fused)
+};
+
+// y[m, n] = out( sum_k dec(a[m,k]) * dec(W[n,k]) * s_a * (*sw or 1) ).
+//
+// At most WPC 1024-thread workgroups per CU: the activation prologue (copy or
+// quantization into LDS) is paid once per workgroup and spread over 16 waves.  The
+// weight rows are cut into groups of ROWS rows and each workgroup takes one
+// contiguous span of groups, its 16 waves taking consecutive groups of the
+// span in turn, so that at any moment a workgroup streams one compact window
+// of the weight matrix: measured on MI355X, block-contiguous streaming with
+// non-temporal loads sustains about 7.1 TB/s where grid-strided streaming
+// stays near 6 TB/s.  Per group a wave streams K in batches of U 1 KiB chunks
+// per row; the 4 waves per SIMD overlap each other's loads and arithmetic.
+// The first batch is issued before the prologue.
+template <int WFMT, int OUTF, int AS, int MR, int ROWS, int U, int CP, int WPC = 1>
+__global__ __launch_bounds__(kWgThreads) __attribute__((amdgpu_waves_per_eu(4 * WPC)))
+void rowk_f8_kernel(
+    const void* __restrict__ act, const float* __restrict__ sa_in,
+    const uint8_t* __restrict__ qw, const float* __restrict__ sw,
+    uint16_t* __restrict__ y, uint8_t* __restrict__ q_out, float* __restrict__ sa_out,
+    float* __restrict__ amax_out, int N, int K)
+{
+    constexpr bool FUSED = AS == AS_BF16 || AS == AS_FP16;
+    constexpr bool IN_LDS = AS != AS_GLOBAL;
+    constexpr int DT = AS == AS_BF16 ? DT_BF16 : DT_FP16;
+    constexpr int W = kWgThreads / 64;
+    extern __shared__ __attribute__((aligned(16))) uint8_t codes_lds[];   // IN_LDS: MR*K codes
+    __shared__ float red[W];
+
+    const int tid = threadIdx.x, lane = tid & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+    const int ngroups = (N + ROWS - 1) / ROWS;
+    const int gpw = (ngroups + gridDim.x - 1) / gridDim.x;      // groups per workgroup
+    const int gend = min(ngroups, (int)(blockIdx.x + 1) * gpw);
+    const int nkb = (K + 1024 * U - 1) / (1024 * U);
+
+    v4i w[ROWS][U];
+    // weights of rows [row0, row0 + ROWS) at K slice kb; the resource covers
+    // only the valid rows, so padded rows and the K tail read zero
+    auto load_w = [&](int row0, int kb) {
+        const int nrow = min(ROWS, N - row0);
+        const rsrc_t rw = make_rsrc(qw + (size_t)row0 * K, (uint32_t)(nrow * K));
+#pragma unroll
+        for (int u = 0; u < U; ++u) {
+            const int k = kb + u * 1024 + lane * 16;
+#pragma unroll
+            for (int j = 0; j < ROWS; ++j)
+                w[j][u] = buf_load16<CP>(rw, k < K ? (uint32_t)(j * K + k) : kOOB);
+        }
+    };
+
+    int grp = blockIdx.x * gpw + wave;
+    if (grp < gend) load_w(grp * ROWS, 0);
+
+    float s_a;
+    if constexpr (FUSED) {
+        // whole activation in registers: at most kFusedMaxMK / 8 / kWgThreads
+        // 16-byte vectors per thread
+        constexpr int VPT = (int)(kFusedMaxMK / 8 / kWgThreads);
+        const int nvec = MR * K / 8;                  // K % 16 == 0
+        const v4i* xv = reinterpret_cast<const v4i*>(act);
+        v4i xr[VPT];
+        float m = 0.0f;
+#pragma unroll
+        for (int i = 0; i < VPT; ++i) {
+            const int v = tid + i * kWgThreads;
+            xr[i] = v < nvec ? xv[v] : v4i{0, 0, 0, 0};
+            m = fmaxf(m, vec_absmax<DT>(xr[i]));
+        }
+        const float amax = block_max<kWgThreads>(m, red);
+        s_a = scale_from_amax(amax);
+        v2i* cl = reinterpret_cast<v2i*>(codes_lds);
+        v2i* qg = reinterpret_cast<v2i*>(q_out);
+#pragma unroll
+        for (int i = 0; i < VPT; ++i) {
+            const int v = tid + i * kWgThreads;
+            if (v < nvec) {
+                const v2i c = vec_quantize<DT>(xr[i], s_a);
+                cl[v] = c;
+                if (blockIdx.x == 0) qg[v] = c;
+            }
+        }
+        if (blockIdx.x == 0 && tid == 0) {
+            *sa_out = s_a;
+            *amax_out = amax;
+        }
+        __syncthreads();
+    } else {
+        s_a = *sa_in;
+        if constexpr (AS == AS_COPY) {
+            const v4i* src = reinterpret_cast<const v4i*>(act);
+            v4i* dst = reinterpret_cast<v4i*>(codes_lds);
+            for (int i = tid; i < MR * K / 16; i += kWgThreads) dst[i] = src[i];
+            __syncthreads();
+        }
+    }
+    const float s = (sw != nullptr) ? s_a * *sw : s_a;
+    const rsrc_t ra = make_rsrc(act, (uint32_t)(MR * K));
+
+    for (; grp < gend; grp += W) {
+        const int row0 = grp * ROWS;
+        float acc[MR][ROWS];
+#pragma unroll
+        for (int m = 0; m < MR; ++m)
+#pragma unroll
+            for (int j = 0; j < ROWS; ++j) acc[m][j] = 0.0f;
+        for (int kbi = 0; kbi < nkb; ++kbi) {
+            const int kb = kbi * 1024 * U;
+            if (kbi > 0) load_w(row0, kb);       // (the first batch is already in flight)
+            v4i a[MR][U];
+#pragma unroll
+            for (int u = 0; u < U; ++u) {
+                const int k = kb + u * 1024 + lane * 16;
+                const bool in = k < K;
+#pragma unroll
+                for (int m = 0; m < MR; ++m) {
+                    if constexpr (IN_LDS) {
+                        const v4i v = *reinterpret_cast<const v4i*>(codes_lds + m * K + (in ? k : 0));
+                        a[m][u] = in ? v : v4i{0, 0, 0, 0};
+                    } else {
+                        a[m][u] = buf_load16(ra, in ? (uint32_t)(m * K + k) : kOOB);
+                    }
+                }
+            }
+#pragma unroll
+            for (int u = 0; u < U; ++u) {
+                float af[MR][16];
+#pragma unroll
+                for (int m = 0; m < MR; ++m) decode16<WF_E4M3>(a[m][u], af[m]);
+#pragma unroll
+                for (int j = 0; j < ROWS; ++j) {
+                    float wf[16];
+                    decode16<WFMT>(w[j][u], wf);
+#pragma unroll
+                    for (int m = 0; m < MR; ++m)
+#pragma unroll
+                        for (int e = 0; e < 16; ++e) acc[m][j] += af[m][e] * wf[e];
+                }
+            }
+        }
+#pragma unroll
+        for (int m = 0; m < MR; ++m)
+#pragma unroll
+            for (int j = 0; j < ROWS; ++j) {
+                const float v = wave_sum(acc[m][j]);
+                if (lane == 0 && row0 + j < N)
+                    y[(size_t)m * N + row0 + j] = (uint16_t)f32_to_out_bits<OUTF>(v * s);
+            }
+        // next group's first batch
+        if (grp + W < gend) load_w((grp + W) * ROWS, 0);
+    }
+}
+
+// ---------------------------------------------------------------- NestedFP FP16 mode
+// y[m, n] = fp16( sum_k a[m,k] * fp16((hi[n,k] << 8) | lo[n,k]) ): each lane
+// reads 16 bytes of each plane (1 KiB of a plane row per instruction),
+// rebuilds 16 fp16 words with v_perm and accumulates fp16 pairs with
+// v_dot2_f32_f16 (fp32 accumulation).
+template <int MR, int ROWS, int U, int CP>
+__global__ __launch_bounds__(kThreads) void rowk_nested16_kernel(
+    const uint16_t* __restrict__ a, const uint8_t* __restrict__ hi,
+    const uint8_t* __restrict__ lo, uint16_t* __restrict__ y, int N, int K)
+{
+    const int lane = threadIdx.x & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+    const int row0 = (blockIdx.x * (kThreads / 64) + wave) * ROWS;   // one group per wave
+    const int nrow = max(0, min(ROWS, N - row0));
+    const size_t base = (size_t)min(row0, N - 1) * K;
+    const rsrc_t rh = make_rsrc(hi + base, (uint32_t)(nrow * K));
+    const rsrc_t rl = make_rsrc(lo + base, (uint32_t)(nrow * K));
+    const rsrc_t ra = make_rsrc(a, (uint32_t)(MR * K * 2));
+
+    float acc[MR][ROWS];
+#pragma unroll
+    for (int m = 0; m < MR; ++m)
+#pragma unroll
+        for (int j = 0; j < ROWS; ++j) acc[m][j] = 0.0f;
+
+    for (int kb = 0; kb < K; kb += 1024 * U) {
+        v4i hv[ROWS][U], lv[ROWS][U], av[MR][U][2];
+#pragma unroll
+        for (int u = 0; u < U; ++u) {
+            const int k = kb + u * 1024 + lane * 16;
+            const bool in = k < K;
+#pragma unroll
+            for (int j = 0; j < ROWS; ++j) {
+                hv[j][u] = buf_load16<CP>(rh, in ? (uint32_t)(j * K + k) : kOOB);
+                lv[j][u] = buf_load16<CP>(rl, in ? (uint32_t)(j * K + k) : kOOB);
+            }
+#pragma unroll
+            for (int m = 0; m < MR; ++m) {
+                av[m][u][0] = buf_load16(ra, in ? (uint32_t)(2 * (m * K + k)) : kOOB);
+                av[m][u][1] = buf_load16(ra, in ? (uint32_t)(2 * (m * K + k) + 16) : kOOB);
+            }
+        }
+        __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+        for (int u = 0; u < U; ++u) {
+#pragma unroll
+            for (int j = 0; j < ROWS; ++j) {
+                uint32_t wv[8];
+#pragma unroll
+                for (int d = 0; d < 4; ++d)
+                    nested_rebuild4((uint32_t)hv[j][u][d], (uint32_t)lv[j][u][d], wv[2 * d],
+                                    wv[2 * d + 1]);
+#pragma unroll
+                for (int m = 0; m < MR; ++m)
+#pragma unroll
+                    for (int d = 0; d < 8; ++d)
+                        acc[m][j] = __builtin_amdgcn_fdot2(
+                            __builtin_bit_cast(h2, (int)av[m][u][d >> 2][d & 3]),
+                            __builtin_bit_cast(h2, wv[d]), acc[m][j], false);
+            }
+        }
+    }
+
+#pragma unroll
+    for (int m = 0; m < MR; ++m)
+#pragma unroll
+        for (int j = 0; j < ROWS; ++j) {
+            const float v = wave_sum(acc[m][j]);
+            if (lane == 0 && j < nrow) y[(size_t)m * N + row0 + j] = (uint16_t)f32_to_f16_bits(v);
+        }
+}
+
+int rowk_grid(int N) { return (N + kRows * (kThreads / 64) - 1) / (kRows * (kThreads / 64)); }
+
+template <int WFMT, int OUTF, int AS, int MR>
+void launch_rowk(const void* act, const float* sa_in, const uint8_t* qw, const float* sw,
+                 uint16_t* y, uint8_t* q, float* sa_out, float* amax, int N, int K,
+                 hipStream_t st)
+{
+    using C = RowkCfg<MR>;
+    const size_t lds = AS != AS_GLOBAL ? (size_t)MR * K : 0;
+    const int ngroups = (N + C::ROWS - 1) / C::ROWS;
+    const int grid = min(ngroups, kCUs * C::WPC);
+    rowk_f8_kernel<WFMT, OUTF, AS, MR, C::ROWS, C::U, CP_NT, C::WPC>
+        <<<grid, kWgThreads, lds, st>>>(act, sa_in, qw, sw, y, q, sa_out, amax, N, K);
+}
+
+// Unfused FP8 weights: codes staged in LDS when they fit, else read from L2.
+template <int WFMT, int OUTF, int MR>
+void launch_rowk_codes(const uint8_t* qa, const float* sa, const uint8_t* qw, const float* sw,
+                       uint16_t* y, int N, int K, hipStream_t st)
+{
+    if ((int64_t)MR * K <= kFusedMaxMK)
+        launch_rowk<WFMT, OUTF, AS_COPY, MR>(qa, sa, qw, sw, y, nullptr, nullptr, nullptr, N, K, st);
+    else
+        launch_rowk<WFMT, OUTF, AS_GLOBAL, MR>(qa, sa, qw, sw, y, nullptr, nullptr, nullptr, N, K, st);
+}
+
+}  // namespace
+
+hipError_t launch_rowk_fp8(const uint8_t* qa, const float* sa, const uint8_t* qw, const float* sw,
+                           uint16_t* y, int M, int N, int K, int wfmt, int outf,
+                           hipStream_t stream)
+{
+    if (wfmt == WF_E4M3 && outf == OUT_BF16) {
+        if (M == 1) launch_rowk_codes<WF_E4M3, OUT_BF16, 1>(qa, sa, qw, sw, y, N, K, stream);
+        else launch_rowk_codes<WF_E4M3, OUT_BF16, 2>(qa, sa, qw, sw, y, N, K, stream);
+    } else if (wfmt == WF_E5M2 && outf == OUT_FP16) {
+        if (M == 1) launch_rowk_codes<WF_E5M2, OUT_FP16, 1>(qa, sa, qw, sw, y, N, K, stream);
+        else launch_rowk_codes<WF_E5M2, OUT_FP16, 2>(qa, sa, qw, sw, y, N, K, stream);
+    } else {
+        return hipErrorInvalidValue;
+    }
+    return hipGetLastError();
+}
+
+hipError_t launch_rowk_nested16(const uint16_t* a, const uint8_t* hi, const uint8_t* lo,
+                                uint16_t* y, int M, int N, int K, hipStream_t stream)
+{
+    if (M == 1)
+        rowk_nested16_kernel<1, kRows, kUnroll, CP_NT>
+            <<<rowk_grid(N), kThreads, 0, stream>>>(a, hi, lo, y, N, K);
+    else
+        rowk_nested16_kernel<2, kRows, kUnroll, CP_NT>
+            <<<rowk_grid(N), kThreads, 0, stream>>>(a, hi, lo, y, N, K);
+    return hipGetLastError();
+}
+
+hipError_t launch_linear_fused(const void* x, int dtype, const uint8_t* qw, const float* sw,
+                               uint16_t* y, uint8_t* q, float* scale, float* amax, int M, int N,
+                               int K, hipStream_t stream)
+{
+    if (dtype == DT_BF16) {
+        if (M == 1)
+            launch_rowk<WF_E4M3, OUT_BF16, AS_BF16, 1>(x, nullptr, qw, sw, y, q, scale, amax, N, K, stream);
+        else
+            launch_rowk<WF_E4M3, OUT_BF16, AS_BF16, 2>(x, nullptr, qw, sw, y, q, scale, amax, N, K, stream);
+    } else {
+        if (M == 1)
+            launch_rowk<WF_E4M3, OUT_BF16, AS_FP16, 1>(x, nullptr, qw, sw, y, q, scale, amax, N, K, stream);
+        else
+            launch_rowk<WF_E4M3, OUT_BF16, AS_FP16, 2>(x, nullptr, qw, sw, y, q, scale, amax, N, K, stream);
+    }
+    return hipGetLastError();
+}
+
+}  // namespace fp8q

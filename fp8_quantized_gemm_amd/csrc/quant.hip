@@ -26,62 +26,6 @@ constexpr int64_t kSmallN = (int64_t)kSmallThreads * kSmallVecPerThread * 8;  //
 constexpr int kBigThreads = 256;
 constexpr int kBigUnroll = 4;
 
-template <int DT>
-__device__ __forceinline__ float vec_absmax(const v4i& v)
-{
-    float m = 0.0f;
-#pragma unroll
-    for (int i = 0; i < 4; ++i) {
-        uint32_t u = (uint32_t)v[i];
-        m = fmaxf(m, fabsf(half_bits_to_f32<DT>(u & 0xffffu)));
-        m = fmaxf(m, fabsf(half_bits_to_f32<DT>(u >> 16)));
-    }
-    return m;
-}
-
-// 8 input halves -> 8 E4M3 codes (two dwords)
-template <int DT>
-__device__ __forceinline__ v2i vec_quantize(const v4i& v, float s)
-{
-    float f[8];
-#pragma unroll
-    for (int i = 0; i < 4; ++i) {
-        uint32_t u = (uint32_t)v[i];
-        f[2 * i] = half_bits_to_f32<DT>(u & 0xffffu) / s;
-        f[2 * i + 1] = half_bits_to_f32<DT>(u >> 16) / s;
-    }
-    v2i r;
-    r[0] = (int)e4m3_pack4(f[0], f[1], f[2], f[3]);
-    r[1] = (int)e4m3_pack4(f[4], f[5], f[6], f[7]);
-    return r;
-}
-
-template <int DT>
-__device__ __forceinline__ uint8_t scalar_quantize(uint16_t h, float s)
-{
-    return (uint8_t)(e4m3_pack4(half_bits_to_f32<DT>(h) / s, 0.f, 0.f, 0.f) & 0xffu);
-}
-
-__device__ __forceinline__ float scale_from_amax(float amax)
-{
-    return amax > 0.0f ? amax / 448.0f : 1.0f;
-}
-
-// Block-wide max for blockDim.x = NT threads; result valid in every thread.
-template <int NT>
-__device__ __forceinline__ float block_max(float v, float* lds)
-{
-    constexpr int W = NT / 64;
-    v = wave_max(v);
-    const int wave = threadIdx.x >> 6;
-    if ((threadIdx.x & 63) == 0) lds[wave] = v;
-    __syncthreads();
-    float m = lds[0];
-#pragma unroll
-    for (int i = 1; i < W; ++i) m = fmaxf(m, lds[i]);
-    return m;
-}
-
 // ---------------------------------------------------------------- small path
 template <int DT>
 __global__ __launch_bounds__(kSmallThreads) void quant_small_kernel(

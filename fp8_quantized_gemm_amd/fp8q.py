@@ -33,6 +33,7 @@ _SIGS = {
     "fp8q_last_error": (ctypes.c_char_p, []),
     "fp8_quantize_act": (_i, [_p, _i, _i64, _p, _p, _p, _p]),
     "fp8_gemm": (_i, [_p, _p, _p, _p, _p, _i64, _i64, _i64, _p]),
+    "fp8_linear": (_i, [_p, _i, _p, _p, _p, _p, _p, _p, _i64, _i64, _i64, _p]),
     "nested_split": (_i, [_p, _p, _p, _i64, _p]),
     "nested_rebuild_fp16": (_i, [_p, _p, _p, _i64, _p]),
     "nested_gemm_fp16": (_i, [_p, _p, _p, _p, _i64, _i64, _i64, _p]),
@@ -133,6 +134,34 @@ def fp8_gemm(qa: torch.Tensor, sa: torch.Tensor, qw: torch.Tensor, sw: torch.Ten
         _dev(qa, "qa", torch.uint8), _scalar(sa, "sa"), _dev(qw, "qw", torch.uint8),
         _scalar(sw, "sw"), _dev(y, "y", torch.bfloat16, (M, N)), M, N, K, _stream(qa)))
     return y
+
+
+def fp8_linear(x: torch.Tensor, qw: torch.Tensor, sw: torch.Tensor,
+               y: torch.Tensor | None = None, q: torch.Tensor | None = None,
+               scale: torch.Tensor | None = None, amax: torch.Tensor | None = None):
+    """One FP8 linear layer: quantize x[M,K] (bf16/fp16) per tensor, then
+    y[M,N] bf16 = (q . qw^T) * scale * sw.  Returns (y, q, scale, amax)."""
+    if x.dtype == torch.bfloat16:
+        code = BF16
+    elif x.dtype == torch.float16:
+        code = FP16
+    else:
+        raise TypeError(f"x must be bfloat16 or float16, got {x.dtype}")
+    M, N, K = _mnk(x, qw)
+    dev = x.device
+    if y is None:
+        y = torch.empty((M, N), dtype=torch.bfloat16, device=dev)
+    if q is None:
+        q = torch.empty((M, K), dtype=torch.uint8, device=dev)
+    if scale is None:
+        scale = torch.empty(1, dtype=torch.float32, device=dev)
+    if amax is None:
+        amax = torch.empty(1, dtype=torch.float32, device=dev)
+    _check("fp8_linear", lib.fp8_linear(
+        _dev(x, "x"), code, _dev(qw, "qw", torch.uint8), _scalar(sw, "sw"),
+        _dev(y, "y", torch.bfloat16, (M, N)), _dev(q, "q", torch.uint8, (M, K)),
+        _scalar(scale, "scale"), _scalar(amax, "amax"), M, N, K, _stream(x)))
+    return y, q, scale, amax
 
 
 def nested_split(w: torch.Tensor, hi: torch.Tensor | None = None,

@@ -97,12 +97,31 @@ FP8Q_API fp8q_status fp8_quantize_act(const void* x, int dtype, int64_t n, uint8
  *   qa[M,K]  in : E4M3 activation codes        *sa in: activation scale
  *   qw[N,K]  in : E4M3 weight codes            *sw in: weight scale
  *   y[M,N]   out: bf16 bit patterns, round to nearest even
- *   1 <= M, N <= 2^31-1;  16 <= K <= 2^31-1 and K % 16 == 0.
- *   M <= 16 runs the weight-streaming decode path, larger M the MFMA tile path.
+ *   1 <= M, N <= 2^31-1;  16 <= K <= 2^22 and K % 16 == 0.
+ *   M <= 16 runs the weight-streaming decode kernels, larger M the MFMA tile
+ *   GEMM.
  */
 FP8Q_API fp8q_status fp8_gemm(const uint8_t* qa, const float* sa, const uint8_t* qw,
                      const float* sw, uint16_t* y, int64_t M, int64_t N, int64_t K,
                      fp8q_stream stream);
+
+/*
+ * fp8_linear - one FP8 linear layer: fp8_quantize_act on the activation,
+ *   then fp8_gemm on its codes ([RTX4060] §2.2: dynamic activation
+ *   quantization against statically quantized weights; [C++FP8] §3.3: the
+ *   FP8 GEMM).  Results are bit-identical to the two calls made in sequence:
+ *
+ *   x[M,K]   in : bf16/fp16 activation (dtype as for fp8_quantize_act)
+ *   qw[N,K], *sw in: E4M3 weight codes and scale
+ *   y[M,N]   out: bf16 bit patterns
+ *   q[M,K], *scale, *amax out: the activation codes, scale and amax
+ *   Size rules as fp8_gemm.  For M <= 2 and M*K <= 32768 the whole layer is
+ *   one kernel (each workgroup quantizes the activation in LDS); otherwise it
+ *   launches the quantizer and then the GEMM.
+ */
+FP8Q_API fp8q_status fp8_linear(const void* x, int dtype, const uint8_t* qw, const float* sw,
+                       uint16_t* y, uint8_t* q, float* scale, float* amax, int64_t M,
+                       int64_t N, int64_t K, fp8q_stream stream);
 
 /*
  * nested_split - NestedFP byte split of fp16 weights ([NestedFP] §2.1):

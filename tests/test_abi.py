@@ -27,7 +27,7 @@ def declared_functions():
 
 def test_header_declares_the_entry_points():
     names = declared_functions()
-    for want in ["fp8_quantize_act", "fp8_gemm", "nested_split", "nested_rebuild_fp16",
+    for want in ["fp8_quantize_act", "fp8_gemm", "fp8_linear", "nested_split", "nested_rebuild_fp16",
                  "nested_gemm_fp16", "nested_gemm_fp8", "fp8q_abi_version",
                  "fp8q_status_str", "fp8q_last_error", "fp8q_e4m3_encode_f32"]:
         assert want in names
@@ -81,10 +81,20 @@ GEMM_SIG = [P16, P16, P16, P16, P16]
     ("fp8_gemm", [P16, P16, P16, P16, P16, 2**31, 1, 16, NULL], ERR_SHAPE),
     ("fp8_gemm", [P16, P16, P16, P16, P16, 1, 2**31, 16, NULL], ERR_SHAPE),
     ("fp8_gemm", [P16, P16, P16, P16, P16, 1, 1, 2**31 + 16, NULL], ERR_SHAPE),
+    ("fp8_gemm", [P16, P16, P16, P16, P16, 1, 1, 2**22 + 16, NULL], ERR_SHAPE),
     ("fp8_gemm", [P17, P16, P16, P16, P16, 1, 1, 16, NULL], ERR_ALIGN),
     ("fp8_gemm", [P16, P16, P17, P16, P16, 1, 1, 16, NULL], ERR_ALIGN),
     ("fp8_gemm", [P16, P16, P16, P16, P17, 1, 1, 16, NULL], ERR_ALIGN),
     ("fp8_gemm", [P16, P17, P16, P16, P16, 1, 1, 16, NULL], ERR_ALIGN),
+    # fp8_linear(x, dtype, qw, sw, y, q, scale, amax, M, N, K, stream)
+    ("fp8_linear", [NULL, 0, P16, P16, P16, P16, P16, P16, 1, 1, 16, NULL], ERR_NULL),
+    ("fp8_linear", [P16, 0, P16, P16, P16, NULL, P16, P16, 1, 1, 16, NULL], ERR_NULL),
+    ("fp8_linear", [P16, 0, P16, P16, P16, P16, P16, NULL, 1, 1, 16, NULL], ERR_NULL),
+    ("fp8_linear", [P16, 3, P16, P16, P16, P16, P16, P16, 1, 1, 16, NULL], ERR_DTYPE),
+    ("fp8_linear", [P16, 0, P16, P16, P16, P16, P16, P16, 1, 1, 24, NULL], ERR_SHAPE),
+    ("fp8_linear", [P16, 1, P16, P16, P16, P16, P16, P16, 0, 1, 16, NULL], ERR_SHAPE),
+    ("fp8_linear", [P16, 0, P16, P16, P16, P17, P16, P16, 1, 1, 16, NULL], ERR_ALIGN),
+    ("fp8_linear", [P17, 0, P16, P16, P16, P16, P16, P16, 1, 1, 16, NULL], ERR_ALIGN),
     # nested_split(w, hi, lo, n, stream) / nested_rebuild_fp16(hi, lo, w, n, stream)
     ("nested_split", [NULL, P16, P16, 8, NULL], ERR_NULL),
     ("nested_split", [P16, P16, P16, 0, NULL], ERR_SHAPE),

@@ -55,6 +55,22 @@ def test_decode_identity_returns_every_weight(N, K):
         assert np.array_equal(y, want[:, c0:c0 + M].T), f"columns {c0}..{c0 + M}"
 
 
+@pytest.mark.parametrize("M", [1, 2])
+@pytest.mark.parametrize("N,K", [(37, 48), (9, 1040)])
+def test_row_path_identity_returns_every_weight(M, N, K):
+    """The M <= 2 decode path (row-contiguous, VALU decode) reads every weight
+    back bit-exactly through one-hot activation rows."""
+    rng = np.random.Generator(np.random.PCG64(N * K + M))
+    qw = _random_codes(rng, (N, K))
+    want = oracle.bf16_encode((oracle.e4m3_decode(qw) + 0.0).astype(np.float32))
+    cols = list(range(K)) if K <= 64 else list(range(0, 40)) + list(range(K - 40, K))
+    for c0 in range(0, len(cols), M):
+        cc = cols[c0:c0 + M]
+        say("row identity", M, N, K, cc[0])
+        y = _run_gemm(_ident_act(len(cc), K, np.array(cc)), 1.0, qw, 1.0)
+        assert np.array_equal(y, want[:, cc].T), f"columns {cc}"
+
+
 @pytest.mark.parametrize("M,N,K", [(256, 300, 256), (17, 40, 32), (144, 129, 144)])
 def test_tile_identity_returns_every_weight(M, N, K):
     """qa = the first M rows of I (M <= K): the tile path must return the first
@@ -187,3 +203,37 @@ def test_deterministic_and_stream_order():
     with torch.cuda.stream(s):
         y3 = _run_gemm(qa, sa, qw, sw)
     assert np.array_equal(y1, y3)
+
+
+# ------------------------------------------------------------------ fp8_linear
+@pytest.mark.parametrize("dtype", ["bf16", "fp16"])
+@pytest.mark.parametrize("M,N,K", [(1, 4096, 4096), (2, 300, 11008), (1, 37, 16), (1, 64, 32768),
+                                   (2, 64, 16384), (2, 64, 32768),
+                                   (1, 100, 65536), (2, 50, 33792), (3, 200, 1024), (16, 64, 4096),
+                                   (40, 96, 512)])
+def test_linear_matches_quantize_then_gemm(M, N, K, dtype):
+    """fp8_linear (fused for M <= 2, M*K <= 32768) returns the codes, scale and
+    amax of fp8_quantize_act bit-exactly and the same y as fp8_gemm on them;
+    both agree with the oracle."""
+    seed = synth.seed_for("linear", M, N, K, dtype)
+    x = synth.activation(M, K, seed=seed, dtype=dtype, outliers=M > 2)
+    w = synth.normal((N, K), 0.02, "fp16", seed=seed + 1)
+    oqw, osw, _ = oracle.quantize(synth.bits(w).ravel(), oracle.FP16)
+    qw, sw = to_dev_u8(oqw.reshape(N, K)), scalar_dev(osw)
+    xd = x.to(DEV)
+    say("linear", M, N, K, dtype)
+    y, q, s, a = fp8q.fp8_linear(xd, qw, sw)
+    q2, s2, a2 = fp8q.fp8_quantize_act(xd)
+    y2 = fp8q.fp8_gemm(q2, s2, qw, sw)
+    torch.cuda.synchronize()
+    assert torch.equal(q, q2) and torch.equal(s, s2) and torch.equal(a, a2)
+    assert torch.equal(y, y2)
+    code = oracle.BF16 if dtype == "bf16" else oracle.FP16
+    oq, os_, oa = oracle.quantize(synth.bits(x).ravel(), code)
+    assert np.array_equal(host(q).ravel(), oq)
+    assert float(host(s)[0]) == os_ and float(host(a)[0]) == oa
+    ms = np.repeat(np.arange(M), min(N, 64))
+    ns = np.tile(np.arange(min(N, 64)), M)
+    ref, ab = oracle.gemm_fp8_ref(oq.reshape(M, K), os_, oqw.reshape(N, K), osw, ms, ns)
+    out = oracle.bf16_decode(host(y)[ms, ns]).astype(np.float64)
+    assert_within(out, ref, ab, f"linear {M}x{N}x{K}", "bf16")

@@ -54,7 +54,8 @@ def _one_hot_f16(M, K, cols):
     return a
 
 
-@pytest.mark.parametrize("M,N,K", [(16, 40, 64), (256, 130, 256), (48, 33, 48)])
+@pytest.mark.parametrize("M,N,K", [(1, 24, 32), (2, 40, 48), (16, 40, 64), (256, 130, 256),
+                                   (48, 33, 48)])
 def test_fp16_mode_identity_bit_exact(M, N, K):
     """a = one-hot rows: y = rebuilt weight bit-exactly (subnormals included)."""
     rng = np.random.Generator(np.random.PCG64(M * N * K))
@@ -70,7 +71,7 @@ def test_fp16_mode_identity_bit_exact(M, N, K):
         assert np.array_equal(y, want[:, c0:c0 + m].T), f"columns {c0}.."
 
 
-@pytest.mark.parametrize("M,N,K", [(16, 40, 128), (200, 70, 208)])
+@pytest.mark.parametrize("M,N,K", [(1, 21, 32), (2, 30, 64), (16, 40, 128), (200, 70, 208)])
 def test_fp8_mode_identity_bit_exact(M, N, K):
     """qa = one-hot E4M3 1.0, sa = 1: y = fp16(hi << 8) bit-exactly."""
     rng = np.random.Generator(np.random.PCG64(M + N + K))
@@ -88,7 +89,8 @@ def test_fp8_mode_identity_bit_exact(M, N, K):
         assert np.array_equal(y, want[:, c0:c0 + m].T), f"columns {c0}.."
 
 
-SHAPES = [(1, 1, 16), (1, 40, 4096), (3, 17, 48), (8, 100, 11008), (16, 64, 4112),
+SHAPES = [(1, 1, 16), (1, 40, 4096), (2, 33, 1040), (2, 9, 11008), (3, 17, 48), (8, 100, 11008),
+          (16, 64, 4112),
           (17, 33, 272), (64, 129, 1024), (256, 300, 4096), (300, 77, 160)]
 
 
