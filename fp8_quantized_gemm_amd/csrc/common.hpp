@@ -165,6 +165,16 @@ __device__ __forceinline__ v4i buf_load16(rsrc_t r, uint32_t off)
     return __builtin_amdgcn_raw_buffer_load_b128(r, off, 0, CP);
 }
 
+// Direct global -> LDS load of 16 bytes per lane: lane l's bytes land at
+// lds_block + 16 l (the block is wave-uniform).  The compiler does not order
+// later LDS reads after these asynchronous writes; callers wait (vmcnt) and
+// synchronize explicitly.
+__device__ __forceinline__ void dma_load16(rsrc_t r, void* lds_block, uint32_t off)
+{
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(
+        r, (__attribute__((address_space(3))) void*)lds_block, 16, off, 0, 0, 0);
+}
+
 // ---------------------------------------------------------------- reductions
 // Max over a wave64 with DPP row operations; the result is valid in every lane.
 #define FP8Q_DPP_MAX(v, ctrl, rowmask)                                                    \

@@ -1,20 +1,26 @@
-// Prefill-path GEMMs (M > 16): LDS-staged, double-buffered MFMA tile GEMMs.
+// Prefill-path GEMMs (M > 16): LDS-staged MFMA tile GEMMs.
 //
 //  - FP8: y = out( (qa . W^T) * scale ) with E4M3 activations and E4M3 (FP8
 //    GEMM, page "C++与FP8量化" §3.3) or E5M2 (NestedFP FP8 mode, page
-//    "NestedFP双精度推理框架" §2.1) weights, v_mfma_f32_16x16x128_f8f6f4.
+//    "NestedFP双精度推理框架" §2.1) weights.  Two kernels:
+//      gemm_f8_tile_kernel  128x128 tiles, v_mfma_f32_16x16x128_f8f6f4,
+//                           register-staged double buffer (grids below 512
+//                           256x256 tiles);
+//      gemm_f8_pipe_kernel  256x256 tiles, v_mfma_f32_32x32x64_f8f6f4, a
+//                           4-stage LDS ring filled by direct global->LDS
+//                           loads plus register double-buffered operands.
 //  - NestedFP FP16 mode (same page, §2.1-§2.2): the weight tile is staged in
 //    LDS as its two byte planes and rebuilt as fp16 (hi<<8)|lo with v_perm
 //    while it is moved from LDS to registers, then v_mfma_f32_16x16x32_f16.
 //
-// A 256-thread workgroup computes a 128x128 output tile; its 4 waves form a
-// 2x2 grid of 64x64 sub-tiles (4x4 MFMA tiles of 16x16 each).  Each K step
-// stages the next tiles in registers while the current LDS buffer feeds the
-// MFMAs, so one barrier per step suffices.  Rows of A and W are K-contiguous;
-// LDS rows hold 16-byte units XOR-swizzled by row so that 16 lanes reading the
-// same unit of 16 consecutive rows hit distinct banks.  Workgroup ids are
-// remapped so that consecutive tiles (which share the weight tile) land on
-// the same XCD and its L2.
+// 128x128 kernels: a 256-thread workgroup computes a 128x128 output tile; its
+// 4 waves form a 2x2 grid of 64x64 sub-tiles (4x4 MFMA tiles of 16x16 each).
+// Each K step stages the next tiles in registers while the current LDS buffer
+// feeds the MFMAs, so one barrier per step suffices.  Rows of A and W are
+// K-contiguous; LDS rows hold 16-byte units XOR-swizzled by row so that 16
+// lanes reading the same unit of 16 consecutive rows hit distinct banks.
+// Workgroup ids are remapped so that consecutive tiles (which share the
+// weight tile) land on the same XCD and its L2.
 #include "common.hpp"
 
 namespace fp8q {
@@ -23,6 +29,7 @@ namespace {
 constexpr int kBM = 128;
 constexpr int kBN = 128;
 constexpr int kThreads = 256;
+constexpr int kBigTileMinGrid = 512;     // 256 x 256 tiles: two per CU
 
 __device__ __forceinline__ v8i cat(const v4i& lo, const v4i& hi)
 {
@@ -157,6 +164,190 @@ __global__ __launch_bounds__(kThreads) void gemm_f8_tile_kernel(
     store_tile<OUTF>(y, acc, s, M, N, m0 + wm * 64, n0 + wn * 64, r, g);
 }
 
+// ---------------------------------------------------------------- FP8 pipelined big-tile GEMM
+// BM x BN output tile per workgroup of WM x WN waves, each wave a
+// (BM/WM) x (BN/WN) sub-tile of v_mfma_f32_32x32x64_f8f6f4 tiles (the 32x32
+// shape reads half the LDS operand bytes per flop of the 16x16 one).
+// Operand layout of the 32x32x64 MFMA: lane l supplies row (l % 32) of A (and
+// of W) and 32 bytes of K; lane half h = l / 32 takes 16-byte units 2h, 2h+1
+// of the 64-byte K step (the same units for A and W).  The result lane l
+// holds D[8 (r/4) + 4 h + r % 4][l % 32], r = 0..15.
+//
+// K steps of 64 bytes flow through a STAGES-deep LDS ring filled by direct
+// global->LDS loads (buffer_load ... lds): no register staging and no LDS
+// store instructions; the loads of step kt + STAGES - 1 are in flight while
+// step kt is multiplied.  LDS rows are 64 bytes (four 16-byte units), unit u
+// of row r stored at position u ^ ((r >> 2) & 3), so 16 consecutive rows read
+// at one unit touch 16 distinct 16-byte bank groups.  A DMA load writes lane
+// l's 16 bytes to slot l of a 1 KiB block (16 rows), so each lane fetches the
+// global unit that belongs in its slot.  The compiler does not order LDS
+// reads after these asynchronous LDS writes, so every step waits explicitly
+// (s_waitcnt vmcnt) for its own loads and then synchronizes the workgroup.
+//
+// On top of the ring, the MFMA operands are double-buffered in registers:
+// after the barrier that publishes stage kt+1, the wave multiplies step kt
+// from registers while it reads step kt+1's operands from LDS, the reads
+// interleaved between the MFMAs (sched_group_barrier) so that they overlap
+// the matrix unit instead of leaving it idle between steps.
+constexpr int kDmaBK = 64;
+
+template <int N_OUTSTANDING>
+__device__ __forceinline__ void wait_vm()
+{
+    // s_waitcnt vmcnt(N) with expcnt and lgkmcnt left at their maxima (gfx9 encoding)
+    static_assert(N_OUTSTANDING >= 0 && N_OUTSTANDING < 64, "vmcnt range");
+    __builtin_amdgcn_s_waitcnt((N_OUTSTANDING & 15) | ((N_OUTSTANDING >> 4) << 14) | (7 << 4) | (15 << 8));
+}
+
+template <int WFMT, int OUTF, int BM, int BN, int WM, int WN, int STAGES>
+__global__ __launch_bounds__(WM * WN * 64) void gemm_f8_pipe_kernel(
+    const uint8_t* __restrict__ qa, const float* __restrict__ sa,
+    const uint8_t* __restrict__ qw, const float* __restrict__ sw,
+    uint16_t* __restrict__ y, int M, int N, int K)
+{
+    constexpr int NT = WM * WN * 64;
+    constexpr int BK = kDmaBK;
+    constexpr int TM = BM / WM, TN = BN / WN;
+    constexpr int FM = TM / 32, FN = TN / 32;
+    constexpr int STAGE = (BM + BN) * BK;
+    constexpr int BLOCKS = STAGE / 1024;
+    constexpr int BPW = BLOCKS / (NT / 64);
+    static_assert(BPW * (NT / 64) == BLOCKS, "stage must split evenly over waves");
+    static_assert(STAGES >= 3, "the ring needs a stage in use, one published and one loading");
+    extern __shared__ __attribute__((aligned(16))) uint8_t lds[];
+
+    const int tid = threadIdx.x;
+    const int lane = tid & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+    const int wm = wave / WN, wn = wave % WN;
+    const int r32 = lane & 31, h = lane >> 5;
+
+    const int tiles_m = (M + BM - 1) / BM;
+    const int bid = xcd_remap(blockIdx.x, gridDim.x);
+    const int m0 = (bid % tiles_m) * BM;
+    const int n0 = (bid / tiles_m) * BN;
+
+    const rsrc_t ra = make_rsrc(qa + (size_t)m0 * K, (uint32_t)(min(BM, M - m0) * K));
+    const rsrc_t rw = make_rsrc(qw + (size_t)n0 * K, (uint32_t)(min(BN, N - n0) * K));
+    uint32_t goff[BPW];
+    int gunit[BPW];
+    bool is_a[BPW];
+#pragma unroll
+    for (int j = 0; j < BPW; ++j) {
+        const int b = wave * BPW + j;
+        const int row = b * 16 + (lane >> 2);
+        gunit[j] = (lane & 3) ^ ((row >> 2) & 3);
+        is_a[j] = row < BM;
+        const int trow = is_a[j] ? row : row - BM;
+        goff[j] = (uint32_t)(trow * K + gunit[j] * 16);
+    }
+    const int nk = (K + BK - 1) / BK;
+    auto dma = [&](int kt) {
+        uint8_t* st = lds + (kt % STAGES) * STAGE;
+#pragma unroll
+        for (int j = 0; j < BPW; ++j) {
+            const bool kin = kt * BK + gunit[j] * 16 < K;
+            dma_load16(is_a[j] ? ra : rw, st + (wave * BPW + j) * 1024,
+                       kin ? goff[j] + kt * BK : kOOB);
+        }
+    };
+    // LDS byte offsets (within a stage) of this lane's two units of operand
+    // tile 0; tile i adds i * 32 rows.  Tile bases are multiples of 16 rows, so
+    // the swizzle term ((row >> 2) & 3) depends on the lane alone.
+    const int sw4 = (r32 >> 2) & 3;
+    const int a_off0 = (wm * TM + r32) * BK + (((2 * h) ^ sw4) << 4);
+    const int a_off1 = (wm * TM + r32) * BK + (((2 * h + 1) ^ sw4) << 4);
+    const int w_off0 = (BM + wn * TN + r32) * BK + (((2 * h) ^ sw4) << 4);
+    const int w_off1 = (BM + wn * TN + r32) * BK + (((2 * h + 1) ^ sw4) << 4);
+    auto read_frags = [&](int kt, v8i (&af)[FM], v8i (&wf)[FN]) {
+        const uint8_t* st = lds + (kt % STAGES) * STAGE;
+#pragma unroll
+        for (int i = 0; i < FM; ++i)
+            af[i] = cat(*reinterpret_cast<const v4i*>(st + a_off0 + i * 32 * BK),
+                        *reinterpret_cast<const v4i*>(st + a_off1 + i * 32 * BK));
+#pragma unroll
+        for (int j = 0; j < FN; ++j)
+            wf[j] = cat(*reinterpret_cast<const v4i*>(st + w_off0 + j * 32 * BK),
+                        *reinterpret_cast<const v4i*>(st + w_off1 + j * 32 * BK));
+    };
+
+    typedef float v16f __attribute__((ext_vector_type(16)));
+    v16f acc[FM][FN];
+#pragma unroll
+    for (int i = 0; i < FM; ++i)
+#pragma unroll
+        for (int j = 0; j < FN; ++j)
+#pragma unroll
+            for (int e = 0; e < 16; ++e) acc[i][j][e] = 0.0f;
+    auto mfmas = [&](const v8i (&af)[FM], const v8i (&wf)[FN]) {
+#pragma unroll
+        for (int i = 0; i < FM; ++i)
+#pragma unroll
+            for (int j = 0; j < FN; ++j)
+                acc[i][j] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(
+                    af[i], wf[j], acc[i][j], WF_E4M3, WFMT, 0, 0, 0, 0);
+    };
+    // wait until at most `later` steps' loads are still in flight
+    auto wait_steps = [&](int later) {
+        if (later >= 2) wait_vm<2 * BPW>();
+        else if (later == 1) wait_vm<BPW>();
+        else wait_vm<0>();
+    };
+
+#pragma unroll
+    for (int p = 0; p < STAGES - 1; ++p)
+        if (p < nk) dma(p);
+
+    v8i af0[FM], wf0[FN], af1[FM], wf1[FN];
+    wait_steps(min(STAGES - 2, nk - 1));
+    __syncthreads();
+    read_frags(0, af0, wf0);
+
+    auto interleave = [&]() {
+#pragma unroll
+        for (int q = 0; q < FM * FN; ++q) {
+            __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);     // one MFMA
+            __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);     // two LDS reads
+        }
+    };
+    // one iteration = two K steps, so the two register sets swap roles by name
+    int kt = 0;
+    for (; kt + 1 < nk; kt += 2) {
+        // step kt: read step kt+1 into set 1 while multiplying set 0
+        wait_steps(min(STAGES - 3, nk - 2 - kt));
+        __syncthreads();                       // stage kt+1 published; stage kt-1 free
+        if (kt + STAGES - 1 < nk) dma(kt + STAGES - 1);
+        read_frags(kt + 1, af1, wf1);
+        mfmas(af0, wf0);
+        interleave();
+        // step kt+1: read step kt+2 into set 0 while multiplying set 1
+        if (kt + 2 < nk) {
+            wait_steps(min(STAGES - 3, nk - 3 - kt));
+            __syncthreads();
+            if (kt + STAGES < nk) dma(kt + STAGES);
+            read_frags(kt + 2, af0, wf0);
+        }
+        mfmas(af1, wf1);
+        interleave();
+    }
+    if (kt < nk) mfmas(af0, wf0);              // odd number of steps: the last one
+
+    float sc = *sa;
+    if (sw != nullptr) sc = sc * *sw;
+#pragma unroll
+    for (int i = 0; i < FM; ++i)
+#pragma unroll
+        for (int j = 0; j < FN; ++j) {
+            const int n = n0 + wn * TN + j * 32 + r32;
+            if (n >= N) continue;
+#pragma unroll
+            for (int e = 0; e < 16; ++e) {
+                const int m = m0 + wm * TM + i * 32 + 8 * (e >> 2) + 4 * h + (e & 3);
+                if (m < M) y[(size_t)m * N + n] = (uint16_t)f32_to_out_bits<OUTF>(acc[i][j][e] * sc);
+            }
+        }
+}
+
 // ---------------------------------------------------------------- NestedFP FP16 tile GEMM
 // K step = 64 elements: A tile 128 rows x 128 bytes, hi and lo tiles 128 rows
 // x 64 bytes each.  MFMA s (s = 0, 1) of a step covers elements
@@ -277,17 +468,42 @@ int tile_grid(int M, int N)
 
 }  // namespace
 
+template <int WFMT, int OUTF, int BM, int BN, int WM, int WN, int STAGES>
+hipError_t launch_pipe(const uint8_t* qa, const float* sa, const uint8_t* qw, const float* sw,
+                       uint16_t* y, int M, int N, int K, hipStream_t stream)
+{
+    auto kern = gemm_f8_pipe_kernel<WFMT, OUTF, BM, BN, WM, WN, STAGES>;
+    constexpr size_t lds = (size_t)STAGES * (BM + BN) * kDmaBK;
+    static bool attr_set = false;        // idempotent host attribute, set on first use
+    if (!attr_set) {
+        const hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(kern),
+                                                 hipFuncAttributeMaxDynamicSharedMemorySize,
+                                                 (int)lds);
+        if (e != hipSuccess) return e;
+        attr_set = true;
+    }
+    const int grid = ((M + BM - 1) / BM) * ((N + BN - 1) / BN);
+    kern<<<grid, WM * WN * 64, lds, stream>>>(qa, sa, qw, sw, y, M, N, K);
+    return hipGetLastError();
+}
+
 hipError_t launch_tile_fp8(const uint8_t* qa, const float* sa, const uint8_t* qw, const float* sw,
                            uint16_t* y, int M, int N, int K, int wfmt, int outf,
                            hipStream_t stream)
 {
-    const dim3 grid(tile_grid(M, N)), block(kThreads);
-    if (wfmt == WF_E4M3 && outf == OUT_BF16)
-        gemm_f8_tile_kernel<WF_E4M3, OUT_BF16><<<grid, block, 0, stream>>>(qa, sa, qw, sw, y, M, N, K);
-    else if (wfmt == WF_E5M2 && outf == OUT_FP16)
-        gemm_f8_tile_kernel<WF_E5M2, OUT_FP16><<<grid, block, 0, stream>>>(qa, sa, qw, sw, y, M, N, K);
-    else
+    // 256 x 256 pipelined tiles once there are at least two per CU (measured
+    // faster there); below that the 128 x 128 kernel, whose 4x larger grid
+    // fills the 256 CUs better.
+    const bool big = (int64_t)((M + 255) / 256) * ((N + 255) / 256) >= kBigTileMinGrid;
+    if (wfmt == WF_E4M3 && outf == OUT_BF16) {
+        if (big) return launch_pipe<WF_E4M3, OUT_BF16, 256, 256, 4, 2, 4>(qa, sa, qw, sw, y, M, N, K, stream);
+        gemm_f8_tile_kernel<WF_E4M3, OUT_BF16><<<tile_grid(M, N), kThreads, 0, stream>>>(qa, sa, qw, sw, y, M, N, K);
+    } else if (wfmt == WF_E5M2 && outf == OUT_FP16) {
+        if (big) return launch_pipe<WF_E5M2, OUT_FP16, 256, 256, 4, 2, 4>(qa, sa, qw, sw, y, M, N, K, stream);
+        gemm_f8_tile_kernel<WF_E5M2, OUT_FP16><<<tile_grid(M, N), kThreads, 0, stream>>>(qa, sa, qw, sw, y, M, N, K);
+    } else {
         return hipErrorInvalidValue;
+    }
     return hipGetLastError();
 }
 

@@ -154,7 +154,7 @@ LAYER_SHAPES = [(K, N) for _, K, N in synth.LLAMA7B_LINEARS] + \
                [(K, N) for _, K, N in synth.QWEN32B_LINEARS]
 
 
-@pytest.mark.parametrize("M", [1, 8, 16, 512])
+@pytest.mark.parametrize("M", [1, 8, 16, 512, 2048])
 @pytest.mark.parametrize("K,N", LAYER_SHAPES)
 def test_full_size_layers_sampled(M, K, N):
     """Full Llama-7B / Qwen-32B linear shapes, GPU quantization + GEMM: codes of
@@ -237,3 +237,58 @@ def test_linear_matches_quantize_then_gemm(M, N, K, dtype):
     ref, ab = oracle.gemm_fp8_ref(oq.reshape(M, K), os_, oqw.reshape(N, K), osw, ms, ns)
     out = oracle.bf16_decode(host(y)[ms, ns]).astype(np.float64)
     assert_within(out, ref, ab, f"linear {M}x{N}x{K}", "bf16")
+
+
+# ------------------------------------------------------------------ big-tile path
+# The tile path switches from 128 x 128 tiles to the pipelined 256 x 256
+# kernel once the grid holds at least 512 tiles of 256 x 256; the cases below
+# sit on both sides of that switch.
+def _big_tiles(M, N):
+    return -(-M // 256) * -(-N // 256)
+
+
+@pytest.mark.parametrize("N", [4096, 8192])
+def test_big_tile_identity_returns_every_weight(N):
+    """qa = I with M = K = 4096: y = W^T bit-exactly for every weight, with
+    N = 4096 (256 tiles of 256 x 256: 128 x 128 kernel) and N = 8192 (512:
+    pipelined kernel)."""
+    M = K = 4096
+    rng = np.random.Generator(np.random.PCG64(4096 + N))
+    qw = _random_codes(rng, (N, K))
+    say("big identity", M, N, K, "tiles256", _big_tiles(M, N))
+    y = _run_gemm(_ident_act(M, K, np.arange(M)), 1.0, qw, 1.0)
+    want = oracle.bf16_encode((oracle.e4m3_decode(qw) + 0.0).astype(np.float32))
+    assert np.array_equal(y, want.T)
+
+
+@pytest.mark.parametrize("M,N,K", [(4096, 4096, 80), (4096, 8192, 80), (4100, 8200, 48)])
+def test_big_tile_small_integers_bit_exact(M, N, K):
+    """Small integers through both tile kernels; K = 80 and 48 leave a
+    partial K step (out-of-range units read as zero)."""
+    rng = np.random.Generator(np.random.PCG64(K + N))
+    qa, qw = _small_int(rng, M, N, K)
+    say("big small int", M, N, K, "tiles256", _big_tiles(M, N))
+    y = _run_gemm(qa, 1.0, qw, 1.0)
+    want = oracle.gemm_fp8_f32(qa, 1.0, qw, 1.0)
+    assert np.array_equal(y, want)
+
+
+@pytest.mark.parametrize("M,N,K", [(2065, 8292, 4112), (4096, 4100, 272),
+                                   (2065, 14436, 4112), (4100, 8200, 272)])
+def test_big_tile_random_ragged_sampled(M, N, K):
+    """Ragged M, N and K on both tile kernels; every output of 3 rows and 3
+    columns plus 512 random pairs against the fp64 checker."""
+    seed = synth.seed_for("big", M, N, K)
+    qa, sa, qw, sw = _quantized_operands(M, N, K, seed=seed, outliers=True)
+    say("big random", M, N, K, "tiles256", _big_tiles(M, N))
+    y = _run_gemm(qa, sa, qw, sw)
+    rng = np.random.Generator(np.random.PCG64(seed))
+    rows = np.concatenate([[0, M - 1], rng.integers(0, M, 1)])
+    cols = np.concatenate([[0, N - 1], rng.integers(0, N, 1)])
+    ms = np.concatenate([np.repeat(rows, N), np.tile(np.arange(M), cols.size),
+                         rng.integers(0, M, 512)])
+    ns = np.concatenate([np.tile(np.arange(N), rows.size), np.repeat(cols, M),
+                         rng.integers(0, N, 512)])
+    ref, ab = oracle.gemm_fp8_ref(qa, sa, qw, sw, ms, ns)
+    out = oracle.bf16_decode(y[ms, ns]).astype(np.float64)
+    assert_within(out, ref, ab, f"big {M}x{N}x{K}", "bf16")
