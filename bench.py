@@ -17,9 +17,11 @@ the GEMM and 3*M*K bytes for the quantizer.  Inputs are resident in HBM
 before timing.  By default the 128 launches of a step are captured once into
 a HIP graph and the timed steps are graph replays.  `roofline` reports the
 decode kernel alone: its algorithmic bytes over its average duration,
-measured with HIP events around every fp8_linear launch on the launch stream
-over a timed region of eager steps (events cannot bracket single kernels
-inside a graph replay).
+measured with a HIP event pair around the timed region on the replay stream (the step
+is the 128 launches of that one kernel, so device time over launch count is
+its average launch duration, inter-launch gaps included).  `traffic` is
+the HBM bytes per launch from hardware counters, read from the committed
+counter summary when it was taken on the current kernel source.
 `secondary` adds the prefill (M = 512, 2048: TFLOP/s of the tile GEMM) and
 NestedFP figures; `cpu_baseline` times the oracle on a bounded sample.
 Rank 0 prints one JSON line.
@@ -56,6 +58,10 @@ def parse():
                         "one captured HIP graph")
     p.add_argument("--cpu-seconds", type=float, default=10.0,
                    help="lower bound on the oracle's timed CPU work")
+    p.add_argument("--copy-calibration-mib", type=int, default=0, metavar="MIB",
+                   help="instead of the benchmark, run 5 launches of a plain elementwise "
+                        "copy (read MIB MiB, write MIB MiB) so that HBM byte counters "
+                        "can be calibrated against a kernel of known traffic")
     return p.parse_args()
 
 
@@ -70,7 +76,7 @@ def kernel_source_hash() -> str:
 def load_traffic(src_hash: str):
     """HBM traffic per GEMV launch from the committed counter summary, if it
     was taken on the current kernel source."""
-    path = os.path.join(ROOT, "profiles", "linear_fused_llama7b_decode_m1_traffic.json")
+    path = os.path.join(ROOT, "profiles", "rowk_f8_llama7b_decode_m1_traffic.json")
     try:
         with open(path) as f:
             d = json.load(f)
@@ -115,54 +121,66 @@ class Model:
         return 2 * self.M * L["N"] * L["K"]
 
 
-def run_step(fp8q, model, events=None):
-    """One pass over every linear: dynamic quantization + FP8 GEMM (fp8_linear).
-    With `events`, a HIP event pair brackets each call on its stream."""
+def linear_call(fp8q, L):
+    fp8q.fp8_linear(L["x"], L["qw"], L["sw"], L["y"], L["q"], L["sa"], L["amax"])
+
+
+def gemm_call(fp8q, L):
+    fp8q.fp8_gemm(L["q"], L["sa"], L["qw"], L["sw"], L["y"])
+
+
+def run_step(fp8q, model, events=None, call=linear_call):
+    """One pass over every linear (by default dynamic quantization + FP8 GEMM,
+    fp8_linear).  With `events`, a HIP event pair brackets each call on its
+    stream."""
     for i, L in enumerate(model.linears):
         if events is not None:
             events[i][0].record()
-        fp8q.fp8_linear(L["x"], L["qw"], L["sw"], L["y"], L["q"], L["sa"], L["amax"])
+        call(fp8q, L)
         if events is not None:
             events[i][1].record()
 
 
-def time_steps(torch, fp8q, model, steps, warmup, graph=False, with_events=False):
-    """Returns (seconds per step, average seconds of one fp8_linear call or None)."""
+def time_fn(torch, fn, steps, warmup, graph=True):
+    """Time `steps` calls of fn() (one step each).  With `graph`, fn's launches
+    are captured once into a HIP graph and the timed steps are replays.
+    Returns (wall seconds per step, device seconds per step): the second from
+    a HIP event pair recorded on the stream the work runs on (torch's current
+    stream) around the whole timed region."""
     for _ in range(warmup):
-        run_step(fp8q, model)
+        fn()
     torch.cuda.synchronize()
     g = None
     if graph:
         s = torch.cuda.Stream()
         s.wait_stream(torch.cuda.current_stream())
         with torch.cuda.stream(s):
-            run_step(fp8q, model)            # warm on the capture stream
+            fn()                             # warm on the capture stream
             torch.cuda.synchronize()
             g = torch.cuda.CUDAGraph()
             with torch.cuda.graph(g, stream=s):
-                run_step(fp8q, model)
+                fn()
         torch.cuda.synchronize()
         for _ in range(warmup):
             g.replay()
         torch.cuda.synchronize()
-    ev = None
-    if with_events and not graph:
-        ev = [[(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
-               for _ in model.linears] for _ in range(steps)]
-    torch.cuda.synchronize()
+    e0 = torch.cuda.Event(enable_timing=True)
+    e1 = torch.cuda.Event(enable_timing=True)
     t0 = time.perf_counter()
-    for k in range(steps):
+    e0.record()
+    for _ in range(steps):
         if g is not None:
             g.replay()
         else:
-            run_step(fp8q, model, ev[k] if ev else None)
+            fn()
+    e1.record()
     torch.cuda.synchronize()
-    dt = (time.perf_counter() - t0) / steps
-    kern = None
-    if ev:
-        tot = sum(a.elapsed_time(b) for step in ev for (a, b) in step) * 1e-3
-        kern = tot / (steps * len(model.linears))
-    return dt, kern
+    wall = (time.perf_counter() - t0) / steps
+    return wall, e0.elapsed_time(e1) * 1e-3 / steps
+
+
+def time_steps(torch, fp8q, model, steps, warmup, graph=True, call=linear_call):
+    return time_fn(torch, lambda: run_step(fp8q, model, call=call), steps, warmup, graph)
 
 
 def cpu_baseline(torch, synth, dev, seconds):
@@ -220,6 +238,7 @@ def secondary(torch, fp8q, synth, model1, dev):
         out[f"decode_m{M}"] = {"GB_per_s": round(byts / dt / 1e9, 1),
                                "frac_hbm": round(byts / dt / 1e9 / HBM_PEAK_GBS, 4),
                                "ms_per_step": round(dt * 1e3, 3)}
+        progress(f"decode M={M} done")
     # prefill M = 512, 2048 (activations with 0.1% outlier channels x50)
     for M in (512, 2048):
         mm = Model.__new__(Model)
@@ -233,12 +252,16 @@ def secondary(torch, fp8q, synth, model1, dev):
             d["q"] = torch.empty((M, K), dtype=torch.uint8, device=dev)
             d["y"] = torch.empty((M, N), dtype=torch.bfloat16, device=dev)
             mm.linears.append(d)
-        dt, kern = time_steps(torch, fp8q, mm, steps=3, warmup=1, with_events=True)
+        dt, _ = time_steps(torch, fp8q, mm, steps=3, warmup=1)
+        # the GEMM alone, on the codes and scales the timed steps left behind
+        _, gdev = time_steps(torch, fp8q, mm, steps=3, warmup=1, call=gemm_call)
+        kern = gdev / len(mm.linears)
         fl = sum(mm.flops(L) for L in mm.linears)
         out[f"prefill_m{M}"] = {"TFLOP_per_s": round(fl / dt / 1e12, 1),
                                 "frac_fp8_mfma": round(fl / dt / 1e12 / FP8_PEAK_TFLOPS, 4),
                                 "gemm_only_TFLOP_per_s": round(fl / (kern * len(mm.linears)) / 1e12, 1),
                                 "ms_per_step": round(dt * 1e3, 3)}
+        progress(f"prefill M={M} done")
         del mm
     # NestedFP at M = 1 and 256 on 8 layers of fp16 weights (hi/lo planes)
     nested = []
@@ -267,14 +290,7 @@ def secondary(torch, fp8q, synth, model1, dev):
                 fp8q.nested_gemm_fp8(q, s, hi, y)
 
         for mode, fn, wbytes in (("fp16", step16, 2), ("fp8", step8, 1)):
-            for _ in range(2):
-                fn()
-            torch.cuda.synchronize()
-            t0 = time.perf_counter()
-            for _ in range(5):
-                fn()
-            torch.cuda.synchronize()
-            dt = (time.perf_counter() - t0) / 5
+            dt, _ = time_fn(torch, fn, steps=5, warmup=2)
             byts = sum(wbytes * N * K + 2 * M * K + 2 * M * N for K, N, _, _ in nested)
             if mode == "fp8":
                 byts = sum(N * K + M * K + 2 * M * N + 3 * M * K for K, N, _, _ in nested)
@@ -283,7 +299,27 @@ def secondary(torch, fp8q, synth, model1, dev):
                                           "frac_hbm": round(byts / dt / 1e9 / HBM_PEAK_GBS, 4),
                                           "TFLOP_per_s": round(fl / dt / 1e12, 2),
                                           "layers": 8}
+            progress(f"nested {mode} M={M} done")
     return out
+
+
+def progress(msg):
+    """Phase marker on stderr (stdout carries only the JSON result line)."""
+    print(f"[bench] {msg}", file=sys.stderr, flush=True)
+
+
+def copy_calibration(torch, mib):
+    """A plain copy kernel of known traffic (torch's elementwise bitwise_not on
+    int32: reads and writes mib MiB per launch) for scaling byte counters."""
+    n = mib * (1 << 20) // 4
+    x = torch.arange(n, dtype=torch.int32, device="cuda:0")
+    y = torch.empty_like(x)
+    for _ in range(5):
+        torch.bitwise_not(x, out=y)
+    torch.cuda.synchronize()
+    print(json.dumps({"copy_calibration": {"bytes_read_per_launch": n * 4,
+                                           "bytes_written_per_launch": n * 4,
+                                           "launches": 5}}), flush=True)
 
 
 def main():
@@ -294,18 +330,25 @@ def main():
         sys.exit(2)
     import torch
 
+    if args.copy_calibration_mib > 0:
+        copy_calibration(torch, args.copy_calibration_mib)
+        return
+
     from fp8_quantized_gemm_amd import fp8q, synth
 
     dev = "cuda:0"
     torch.cuda.set_device(0)
     model = Model(torch, fp8q, synth, M=1, dev=dev)
+    progress("decode model built (128 E4M3 weight matrices)")
     graph = not args.eager
-    dt, kern = time_steps(torch, fp8q, model, args.steps, args.warmup, graph=graph,
-                          with_events=not graph)
+    dt, dev_step = time_steps(torch, fp8q, model, args.steps, args.warmup, graph=graph)
     step_bytes = sum(model.gemm_bytes(L) + model.quant_bytes(L) for L in model.linears)
     value = step_bytes / dt / 1e9
-    if kern is None:        # graph mode: time the launches in an eager pass
-        _, kern = time_steps(torch, fp8q, model, max(3, args.steps // 4), 1, with_events=True)
+    # The step is the 128 launches of the decode kernel and nothing else, so
+    # the event-timed device time of the timed region over its launch count is
+    # that kernel's average launch duration (inter-launch gaps included).
+    kern = dev_step / len(model.linears)
+    progress(f"timed {args.steps} steps: {dt * 1e3:.3f} ms/step, {kern * 1e6:.2f} us/launch")
     launch_bytes = step_bytes / len(model.linears)
     achieved = launch_bytes / kern / 1e9
     src_hash = kernel_source_hash()
@@ -338,8 +381,10 @@ def main():
     }
     if not args.no_secondary:
         result["secondary"] = secondary(torch, fp8q, synth, model, dev)
+        progress("secondary figures done")
     if not args.no_cpu_baseline:
         result["cpu_baseline"] = cpu_baseline(torch, synth, dev, args.cpu_seconds)
+        progress("cpu baseline done")
     print(json.dumps(result), flush=True)
 
 
