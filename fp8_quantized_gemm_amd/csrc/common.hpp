@@ -81,7 +81,33 @@ __device__ __forceinline__ uint32_t e4m3_pack4(float a, float b, float c, float 
 // ---------------------------------------------------------------- quantizer elements
 // Shared by the stand-alone quantizer and the fused decode linear, so both
 // produce the same codes: q = E4M3_rne_sat(fl32(x / s)), s = fl32(amax / 448)
-// (1 when amax == 0), with x / s the IEEE correctly rounded division.
+// (1 when amax == 0), with fl32(x / s) the correctly rounded quotient.
+//
+// The quotient is computed with one reciprocal per scale and two FMAs per
+// element (Markstein's correction step): r = RN(1/s), q0 = RN(x r),
+// e = x - q0 s (exact through the FMA), q = RN(q0 + e r).  q equals the
+// correctly rounded x / s for every bf16 and fp16 input significand and every
+// fp32 divisor significand (checked exhaustively against IEEE division); the
+// argument needs a finite r and an exact residual, which hold for
+// 2^-80 <= s <= 2^120 and every quotient large enough to give a nonzero code.
+// Scales outside that range use the IEEE division.  An exact quotient
+// (e == 0, which includes x = -0) returns q0, keeping the sign of zero.
+struct Quotient {
+    float s, r;
+    bool fast;
+    __device__ __forceinline__ explicit Quotient(float s_) : s(s_)
+    {
+        r = 1.0f / s_;
+        fast = s_ >= 0x1p-80f && s_ <= 0x1p120f;
+    }
+    __device__ __forceinline__ float fast_div(float x) const
+    {
+        const float q0 = x * r;
+        const float e = __builtin_fmaf(-q0, s, x);
+        return e == 0.0f ? q0 : __builtin_fmaf(e, r, q0);
+    }
+};
+
 template <int DT>
 __device__ __forceinline__ float vec_absmax(const v4i& v)
 {
@@ -95,27 +121,66 @@ __device__ __forceinline__ float vec_absmax(const v4i& v)
     return m;
 }
 
+template <int DT>
+__device__ __forceinline__ float vec_absmax(const v2i& v)
+{
+    float m = 0.0f;
+#pragma unroll
+    for (int i = 0; i < 2; ++i) {
+        uint32_t u = (uint32_t)v[i];
+        m = fmaxf(m, fabsf(half_bits_to_f32<DT>(u & 0xffffu)));
+        m = fmaxf(m, fabsf(half_bits_to_f32<DT>(u >> 16)));
+    }
+    return m;
+}
+
+// 2*NW input halves (NW dwords) -> 2*NW quotients x / s
+template <int DT, int NW>
+__device__ __forceinline__ void vec_divide(const int (&w)[NW], const Quotient& d, float (&f)[2 * NW])
+{
+    if (d.fast) {
+#pragma unroll
+        for (int i = 0; i < NW; ++i) {
+            f[2 * i] = d.fast_div(half_bits_to_f32<DT>((uint32_t)w[i] & 0xffffu));
+            f[2 * i + 1] = d.fast_div(half_bits_to_f32<DT>((uint32_t)w[i] >> 16));
+        }
+    } else {
+#pragma unroll
+        for (int i = 0; i < NW; ++i) {
+            f[2 * i] = half_bits_to_f32<DT>((uint32_t)w[i] & 0xffffu) / d.s;
+            f[2 * i + 1] = half_bits_to_f32<DT>((uint32_t)w[i] >> 16) / d.s;
+        }
+    }
+}
+
 // 8 input halves -> 8 E4M3 codes (two dwords)
 template <int DT>
-__device__ __forceinline__ v2i vec_quantize(const v4i& v, float s)
+__device__ __forceinline__ v2i vec_quantize(const v4i& v, const Quotient& d)
 {
+    const int w[4] = {v[0], v[1], v[2], v[3]};
     float f[8];
-#pragma unroll
-    for (int i = 0; i < 4; ++i) {
-        uint32_t u = (uint32_t)v[i];
-        f[2 * i] = half_bits_to_f32<DT>(u & 0xffffu) / s;
-        f[2 * i + 1] = half_bits_to_f32<DT>(u >> 16) / s;
-    }
+    vec_divide<DT, 4>(w, d, f);
     v2i r;
     r[0] = (int)e4m3_pack4(f[0], f[1], f[2], f[3]);
     r[1] = (int)e4m3_pack4(f[4], f[5], f[6], f[7]);
     return r;
 }
 
+// 4 input halves -> 4 E4M3 codes (one dword)
 template <int DT>
-__device__ __forceinline__ uint8_t scalar_quantize(uint16_t h, float s)
+__device__ __forceinline__ uint32_t vec_quantize(const v2i& v, const Quotient& d)
 {
-    return (uint8_t)(e4m3_pack4(half_bits_to_f32<DT>(h) / s, 0.f, 0.f, 0.f) & 0xffu);
+    const int w[2] = {v[0], v[1]};
+    float f[4];
+    vec_divide<DT, 2>(w, d, f);
+    return e4m3_pack4(f[0], f[1], f[2], f[3]);
+}
+
+template <int DT>
+__device__ __forceinline__ uint8_t scalar_quantize(uint16_t h, const Quotient& d)
+{
+    const float x = half_bits_to_f32<DT>(h);
+    return (uint8_t)(e4m3_pack4(d.fast ? d.fast_div(x) : x / d.s, 0.f, 0.f, 0.f) & 0xffu);
 }
 
 __device__ __forceinline__ float scale_from_amax(float amax)
@@ -163,6 +228,11 @@ template <int CP = CP_DEFAULT>
 __device__ __forceinline__ v4i buf_load16(rsrc_t r, uint32_t off)
 {
     return __builtin_amdgcn_raw_buffer_load_b128(r, off, 0, CP);
+}
+template <int CP = CP_DEFAULT>
+__device__ __forceinline__ v2i buf_load8(rsrc_t r, uint32_t off)
+{
+    return __builtin_amdgcn_raw_buffer_load_b64(r, off, 0, CP);
 }
 
 // Direct global -> LDS load of 16 bytes per lane: lane l's bytes land at

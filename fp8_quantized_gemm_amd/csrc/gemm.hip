@@ -30,6 +30,7 @@ constexpr int kBM = 128;
 constexpr int kBN = 128;
 constexpr int kThreads = 256;
 constexpr int kBigTileMinGrid = 512;     // 256 x 256 tiles: two per CU
+constexpr int kCUs = 256;                // compute units of an MI355X
 
 __device__ __forceinline__ v8i cat(const v4i& lo, const v4i& hi)
 {
@@ -50,14 +51,14 @@ __device__ __forceinline__ int swz128(int row, int u) { return row * 128 + ((u ^
 // ... with 64-byte rows (4 units).
 __device__ __forceinline__ int swz64(int row, int u) { return row * 64 + ((u ^ ((row >> 1) & 3)) << 4); }
 
-template <int OUTF>
-__device__ __forceinline__ void store_tile(uint16_t* __restrict__ y, const v4f (&acc)[4][4], float s,
+template <int OUTF, int FM = 4, int FN = 4>
+__device__ __forceinline__ void store_tile(uint16_t* __restrict__ y, const v4f (&acc)[FM][FN], float s,
                                            int M, int N, int mb, int nb, int r, int g)
 {
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
+    for (int i = 0; i < FM; ++i) {
 #pragma unroll
-        for (int j = 0; j < 4; ++j) {
+        for (int j = 0; j < FN; ++j) {
             const int n = nb + j * 16 + r;
             if (n >= N) continue;
 #pragma unroll
@@ -70,14 +71,20 @@ __device__ __forceinline__ void store_tile(uint16_t* __restrict__ y, const v4f (
 }
 
 // ---------------------------------------------------------------- FP8 tile GEMM
-template <int WFMT, int OUTF>
+// BM x BN output tile (BM, BN in {64, 128}) per 256-thread workgroup; the 4
+// waves form a 2x2 grid of (BM/2) x (BN/2) sub-tiles of 16x16x128 MFMAs.
+// The smaller tiles exist for grids that would otherwise leave CUs idle
+// (M = 512 against N = 4096 is 128 tiles of 128x128 for 256 CUs).
+template <int WFMT, int OUTF, int BM, int BN>
 __global__ __launch_bounds__(kThreads) void gemm_f8_tile_kernel(
     const uint8_t* __restrict__ qa, const float* __restrict__ sa,
     const uint8_t* __restrict__ qw, const float* __restrict__ sw,
     uint16_t* __restrict__ y, int M, int N, int K)
 {
     constexpr int BK = 128;                       // bytes = elements
-    constexpr int STAGE = (kBM + kBN) * BK;       // 32 KiB
+    constexpr int STAGE = (BM + BN) * BK;
+    constexpr int FM = BM / 32, FN = BN / 32;     // 16x16 MFMA tiles per wave
+    constexpr int JA = BM / 32, JW = BN / 32;     // 16-byte units per thread per step
     __shared__ __attribute__((aligned(16))) uint8_t lds[2 * STAGE];
 
     const int tid = threadIdx.x;
@@ -85,47 +92,45 @@ __global__ __launch_bounds__(kThreads) void gemm_f8_tile_kernel(
     const int wm = wave >> 1, wn = wave & 1;
     const int r = lane & 15, g = lane >> 4;
 
-    const int tiles_m = (M + kBM - 1) / kBM;
+    const int tiles_m = (M + BM - 1) / BM;
     const int bid = xcd_remap(blockIdx.x, gridDim.x);
-    const int m0 = (bid % tiles_m) * kBM;
-    const int n0 = (bid / tiles_m) * kBN;
+    const int m0 = (bid % tiles_m) * BM;
+    const int n0 = (bid / tiles_m) * BN;
 
     // global -> register staging: thread owns unit (tid & 7) of rows
-    // (tid >> 3) + 32 j, j = 0..3, of both the A and the W tile.  Buffer
-    // resources span the valid rows of each tile, so rows past M or N and
-    // units past K (given an out-of-range offset) read as zero, unpredicated.
+    // (tid >> 3) + 32 j of the A and the W tile.  Buffer resources span the
+    // valid rows of each tile, so rows past M or N and units past K (given an
+    // out-of-range offset) read as zero, unpredicated.
     const int su = tid & 7;
-    const rsrc_t ra = make_rsrc(qa + (size_t)m0 * K, (uint32_t)(min(kBM, M - m0) * K));
-    const rsrc_t rw = make_rsrc(qw + (size_t)n0 * K, (uint32_t)(min(kBN, N - n0) * K));
-    uint32_t roff[4];
+    const rsrc_t ra = make_rsrc(qa + (size_t)m0 * K, (uint32_t)(min(BM, M - m0) * K));
+    const rsrc_t rw = make_rsrc(qw + (size_t)n0 * K, (uint32_t)(min(BN, N - n0) * K));
+    uint32_t roff[JA > JW ? JA : JW];
 #pragma unroll
-    for (int j = 0; j < 4; ++j) roff[j] = (uint32_t)(((tid >> 3) + 32 * j) * K + su * 16);
-    v4i ra_[4], rw_[4];
+    for (int j = 0; j < (JA > JW ? JA : JW); ++j) roff[j] = (uint32_t)(((tid >> 3) + 32 * j) * K + su * 16);
+    v4i ra_[JA], rw_[JW];
     auto gload = [&](int kt) {
         const bool kin = kt * BK + su * 16 < K;
 #pragma unroll
-        for (int j = 0; j < 4; ++j) {
-            const uint32_t o = kin ? roff[j] + kt * BK : kOOB;
-            ra_[j] = buf_load16(ra, o);
-            rw_[j] = buf_load16(rw, o);
-        }
+        for (int j = 0; j < JA; ++j) ra_[j] = buf_load16(ra, kin ? roff[j] + kt * BK : kOOB);
+#pragma unroll
+        for (int j = 0; j < JW; ++j) rw_[j] = buf_load16(rw, kin ? roff[j] + kt * BK : kOOB);
     };
     auto lstore = [&](int buf) {
         uint8_t* As = lds + buf * STAGE;
-        uint8_t* Ws = As + kBM * BK;
+        uint8_t* Ws = As + BM * BK;
 #pragma unroll
-        for (int j = 0; j < 4; ++j) {
-            const int row = (tid >> 3) + 32 * j;
-            *reinterpret_cast<v4i*>(As + swz128(row, su)) = ra_[j];
-            *reinterpret_cast<v4i*>(Ws + swz128(row, su)) = rw_[j];
-        }
+        for (int j = 0; j < JA; ++j)
+            *reinterpret_cast<v4i*>(As + swz128((tid >> 3) + 32 * j, su)) = ra_[j];
+#pragma unroll
+        for (int j = 0; j < JW; ++j)
+            *reinterpret_cast<v4i*>(Ws + swz128((tid >> 3) + 32 * j, su)) = rw_[j];
     };
 
-    v4f acc[4][4];
+    v4f acc[FM][FN];
 #pragma unroll
-    for (int i = 0; i < 4; ++i)
+    for (int i = 0; i < FM; ++i)
 #pragma unroll
-        for (int j = 0; j < 4; ++j) acc[i][j] = v4f{0.f, 0.f, 0.f, 0.f};
+        for (int j = 0; j < FN; ++j) acc[i][j] = v4f{0.f, 0.f, 0.f, 0.f};
 
     const int nk = (K + BK - 1) / BK;
     gload(0);
@@ -133,26 +138,26 @@ __global__ __launch_bounds__(kThreads) void gemm_f8_tile_kernel(
     __syncthreads();
     for (int kt = 0; kt < nk; ++kt) {
         const int cur = kt & 1;
-        if (kt + 1 < nk) gload(kt + 1);
+        gload(kt + 1);                 // past the end: out-of-range offsets, zeros
         const uint8_t* As = lds + cur * STAGE;
-        const uint8_t* Ws = As + kBM * BK;
-        v8i af[4], wf[4];
+        const uint8_t* Ws = As + BM * BK;
+        v8i af[FM], wf[FN];
 #pragma unroll
-        for (int i = 0; i < 4; ++i) {
-            const int row = wm * 64 + i * 16 + r;
+        for (int i = 0; i < FM; ++i) {
+            const int row = wm * (BM / 2) + i * 16 + r;
             af[i] = cat(*reinterpret_cast<const v4i*>(As + swz128(row, g)),
                         *reinterpret_cast<const v4i*>(As + swz128(row, g + 4)));
         }
 #pragma unroll
-        for (int j = 0; j < 4; ++j) {
-            const int row = wn * 64 + j * 16 + r;
+        for (int j = 0; j < FN; ++j) {
+            const int row = wn * (BN / 2) + j * 16 + r;
             wf[j] = cat(*reinterpret_cast<const v4i*>(Ws + swz128(row, g)),
                         *reinterpret_cast<const v4i*>(Ws + swz128(row, g + 4)));
         }
 #pragma unroll
-        for (int i = 0; i < 4; ++i)
+        for (int i = 0; i < FM; ++i)
 #pragma unroll
-            for (int j = 0; j < 4; ++j)
+            for (int j = 0; j < FN; ++j)
                 acc[i][j] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(
                     af[i], wf[j], acc[i][j], WF_E4M3, WFMT, 0, 0, 0, 0);
         if (kt + 1 < nk) lstore(cur ^ 1);
@@ -161,7 +166,7 @@ __global__ __launch_bounds__(kThreads) void gemm_f8_tile_kernel(
 
     float s = *sa;
     if (sw != nullptr) s = s * *sw;
-    store_tile<OUTF>(y, acc, s, M, N, m0 + wm * 64, n0 + wn * 64, r, g);
+    store_tile<OUTF, FM, FN>(y, acc, s, M, N, m0 + wm * (BM / 2), n0 + wn * (BN / 2), r, g);
 }
 
 // ---------------------------------------------------------------- FP8 pipelined big-tile GEMM
@@ -487,24 +492,44 @@ hipError_t launch_pipe(const uint8_t* qa, const float* sa, const uint8_t* qw, co
     return hipGetLastError();
 }
 
+template <int WFMT, int OUTF, int BM, int BN>
+hipError_t launch_tile(const uint8_t* qa, const float* sa, const uint8_t* qw, const float* sw,
+                       uint16_t* y, int M, int N, int K, hipStream_t stream)
+{
+    const int grid = ((M + BM - 1) / BM) * ((N + BN - 1) / BN);
+    gemm_f8_tile_kernel<WFMT, OUTF, BM, BN><<<grid, kThreads, 0, stream>>>(qa, sa, qw, sw, y, M, N, K);
+    return hipGetLastError();
+}
+
+template <int WFMT, int OUTF>
+hipError_t launch_tile_fmt(const uint8_t* qa, const float* sa, const uint8_t* qw, const float* sw,
+                           uint16_t* y, int M, int N, int K, hipStream_t stream)
+{
+    auto tiles = [&](int bm, int bn) { return (int64_t)((M + bm - 1) / bm) * ((N + bn - 1) / bn); };
+    // Tile shape by grid fill, from measurements on MI355X over the Llama-7B
+    // and Qwen-32B prefill shapes: 256 x 256 pipelined tiles once there are
+    // at least two per CU; 128 x 128 when its tiles fill whole rounds of the
+    // 512 that fit at once (two per CU, 64 KiB of LDS each) to at least 90%;
+    // else 128 x 64 if that still gives two workgroups per CU; else 64 x 64.
+    const int64_t t128 = tiles(128, 128);
+    const int64_t rounds = (t128 + 2 * kCUs - 1) / (2 * kCUs);
+    if (tiles(256, 256) >= kBigTileMinGrid)
+        return launch_pipe<WFMT, OUTF, 256, 256, 4, 2, 4>(qa, sa, qw, sw, y, M, N, K, stream);
+    if (t128 >= 2 * kCUs && 10 * t128 >= 9 * rounds * 2 * kCUs)
+        return launch_tile<WFMT, OUTF, 128, 128>(qa, sa, qw, sw, y, M, N, K, stream);
+    if (tiles(128, 64) >= 2 * kCUs) return launch_tile<WFMT, OUTF, 128, 64>(qa, sa, qw, sw, y, M, N, K, stream);
+    return launch_tile<WFMT, OUTF, 64, 64>(qa, sa, qw, sw, y, M, N, K, stream);
+}
+
 hipError_t launch_tile_fp8(const uint8_t* qa, const float* sa, const uint8_t* qw, const float* sw,
                            uint16_t* y, int M, int N, int K, int wfmt, int outf,
                            hipStream_t stream)
 {
-    // 256 x 256 pipelined tiles once there are at least two per CU (measured
-    // faster there); below that the 128 x 128 kernel, whose 4x larger grid
-    // fills the 256 CUs better.
-    const bool big = (int64_t)((M + 255) / 256) * ((N + 255) / 256) >= kBigTileMinGrid;
-    if (wfmt == WF_E4M3 && outf == OUT_BF16) {
-        if (big) return launch_pipe<WF_E4M3, OUT_BF16, 256, 256, 4, 2, 4>(qa, sa, qw, sw, y, M, N, K, stream);
-        gemm_f8_tile_kernel<WF_E4M3, OUT_BF16><<<tile_grid(M, N), kThreads, 0, stream>>>(qa, sa, qw, sw, y, M, N, K);
-    } else if (wfmt == WF_E5M2 && outf == OUT_FP16) {
-        if (big) return launch_pipe<WF_E5M2, OUT_FP16, 256, 256, 4, 2, 4>(qa, sa, qw, sw, y, M, N, K, stream);
-        gemm_f8_tile_kernel<WF_E5M2, OUT_FP16><<<tile_grid(M, N), kThreads, 0, stream>>>(qa, sa, qw, sw, y, M, N, K);
-    } else {
-        return hipErrorInvalidValue;
-    }
-    return hipGetLastError();
+    if (wfmt == WF_E4M3 && outf == OUT_BF16)
+        return launch_tile_fmt<WF_E4M3, OUT_BF16>(qa, sa, qw, sw, y, M, N, K, stream);
+    if (wfmt == WF_E5M2 && outf == OUT_FP16)
+        return launch_tile_fmt<WF_E5M2, OUT_FP16>(qa, sa, qw, sw, y, M, N, K, stream);
+    return hipErrorInvalidValue;
 }
 
 hipError_t launch_tile_nested16(const uint16_t* a, const uint8_t* hi, const uint8_t* lo,

@@ -16,8 +16,9 @@
 // workgroup reduces amax over the whole activation (L2-resident), computes
 // s = amax/448 and the E4M3 codes with the same device routines as
 // fp8_quantize_act, keeps the codes in LDS, and workgroup 0 also writes the
-// codes, scale and amax to memory.  The first batch of weight loads is issued
-// before this prologue so HBM is busy while it runs.  The FP8 GEMM is the one
+// codes, scale and amax to memory.  The activation loads and then the first
+// batch of weight loads are issued before this prologue, so the prologue
+// waits only for the activation and HBM is busy while it runs.  The FP8 GEMM is the one
 // of page "C++与FP8量化" §3.3; the quantization follows the page on a 7B
 // model on an RTX 4060, §2.2 and §6.1.
 #include "common.hpp"
@@ -82,7 +83,8 @@ enum : int {
 // non-temporal loads sustains about 7.1 TB/s where grid-strided streaming
 // stays near 6 TB/s.  Per group a wave streams K in batches of U 1 KiB chunks
 // per row; the 4 waves per SIMD overlap each other's loads and arithmetic.
-// The first batch is issued before the prologue.
+// The activation and then the first weight batch are requested before the
+// prologue.
 template <int WFMT, int OUTF, int AS, int MR, int ROWS, int U, int CP, int WPC = 1>
 __global__ __launch_bounds__(kWgThreads) __attribute__((amdgpu_waves_per_eu(4 * WPC)))
 void rowk_f8_kernel(
@@ -107,9 +109,12 @@ void rowk_f8_kernel(
 
     v4i w[ROWS][U];
     // weights of rows [row0, row0 + ROWS) at K slice kb; the resource covers
-    // only the valid rows, so padded rows and the K tail read zero
-    auto load_w = [&](int row0, int kb) {
-        const int nrow = min(ROWS, N - row0);
+    // only the valid rows, so padded rows and the K tail read zero, and an
+    // empty resource (!valid) makes every load read zero: the loads are still
+    // issued without a branch, which keeps the compiler's wait counts exact
+    // for the activation loads issued before them
+    auto load_w = [&](int row0, int kb, bool valid) {
+        const int nrow = valid ? min(ROWS, N - row0) : 0;
         const rsrc_t rw = make_rsrc(qw + (size_t)row0 * K, (uint32_t)(nrow * K));
 #pragma unroll
         for (int u = 0; u < U; ++u) {
@@ -120,33 +125,52 @@ void rowk_f8_kernel(
         }
     };
 
-    int grp = blockIdx.x * gpw + wave;
-    if (grp < gend) load_w(grp * ROWS, 0);
-
-    float s_a;
+    // The activation (bf16/fp16 for the fused prologue, codes for AS_COPY) is
+    // requested before the first weight batch, so its (L2-resident) lines
+    // return first and the prologue waits for them alone while the weights
+    // are still in flight.
+    constexpr int VPT = (int)(kFusedMaxMK / 8 / kWgThreads);
+    constexpr int CPT = (int)(kFusedMaxMK / 16 / kWgThreads);
+    const int nunit = MR * K / 8;
+    const int ncopy = MR * K / 16;
+    v4i xr[VPT];
+    v4i cr[CPT];
     if constexpr (FUSED) {
-        // whole activation in registers: at most kFusedMaxMK / 8 / kWgThreads
-        // 16-byte vectors per thread
-        constexpr int VPT = (int)(kFusedMaxMK / 8 / kWgThreads);
-        const int nvec = MR * K / 8;                  // K % 16 == 0
-        const v4i* xv = reinterpret_cast<const v4i*>(act);
-        v4i xr[VPT];
-        float m = 0.0f;
+        const rsrc_t rx = make_rsrc(act, (uint32_t)(MR * K * 2));
 #pragma unroll
         for (int i = 0; i < VPT; ++i) {
             const int v = tid + i * kWgThreads;
-            xr[i] = v < nvec ? xv[v] : v4i{0, 0, 0, 0};
-            m = fmaxf(m, vec_absmax<DT>(xr[i]));
+            xr[i] = buf_load16(rx, v < nunit ? (uint32_t)(v * 16) : kOOB);
         }
+    } else if constexpr (AS == AS_COPY) {
+        const rsrc_t rc = make_rsrc(act, (uint32_t)(MR * K));
+#pragma unroll
+        for (int i = 0; i < CPT; ++i) {
+            const int v = tid + i * kWgThreads;
+            cr[i] = buf_load16(rc, v < ncopy ? (uint32_t)(v * 16) : kOOB);
+        }
+    }
+    __builtin_amdgcn_sched_barrier(0);
+
+    int grp = blockIdx.x * gpw + wave;
+    load_w(min(grp, ngroups - 1) * ROWS, 0, grp < gend);   // unconditional: see load_w
+    __builtin_amdgcn_sched_barrier(0);
+
+    float s_a;
+    if constexpr (FUSED) {
+        float m = 0.0f;
+#pragma unroll
+        for (int i = 0; i < VPT; ++i) m = fmaxf(m, vec_absmax<DT>(xr[i]));
         const float amax = block_max<kWgThreads>(m, red);
         s_a = scale_from_amax(amax);
+        const Quotient d(s_a);
         v2i* cl = reinterpret_cast<v2i*>(codes_lds);
         v2i* qg = reinterpret_cast<v2i*>(q_out);
 #pragma unroll
         for (int i = 0; i < VPT; ++i) {
             const int v = tid + i * kWgThreads;
-            if (v < nvec) {
-                const v2i c = vec_quantize<DT>(xr[i], s_a);
+            if (v < nunit) {
+                const v2i c = vec_quantize<DT>(xr[i], d);
                 cl[v] = c;
                 if (blockIdx.x == 0) qg[v] = c;
             }
@@ -159,9 +183,12 @@ void rowk_f8_kernel(
     } else {
         s_a = *sa_in;
         if constexpr (AS == AS_COPY) {
-            const v4i* src = reinterpret_cast<const v4i*>(act);
             v4i* dst = reinterpret_cast<v4i*>(codes_lds);
-            for (int i = tid; i < MR * K / 16; i += kWgThreads) dst[i] = src[i];
+#pragma unroll
+            for (int i = 0; i < CPT; ++i) {
+                const int v = tid + i * kWgThreads;
+                if (v < ncopy) dst[v] = cr[i];
+            }
             __syncthreads();
         }
     }
@@ -177,7 +204,7 @@ void rowk_f8_kernel(
             for (int j = 0; j < ROWS; ++j) acc[m][j] = 0.0f;
         for (int kbi = 0; kbi < nkb; ++kbi) {
             const int kb = kbi * 1024 * U;
-            if (kbi > 0) load_w(row0, kb);       // (the first batch is already in flight)
+            if (kbi > 0) load_w(row0, kb, true);   // (the first batch is already in flight)
             v4i a[MR][U];
 #pragma unroll
             for (int u = 0; u < U; ++u) {
@@ -218,7 +245,7 @@ void rowk_f8_kernel(
                     y[(size_t)m * N + row0 + j] = (uint16_t)f32_to_out_bits<OUTF>(v * s);
             }
         // next group's first batch
-        if (grp + W < gend) load_w((grp + W) * ROWS, 0);
+        if (grp + W < gend) load_w((grp + W) * ROWS, 0, true);
     }
 }
 

@@ -12,8 +12,9 @@
 //    the float bit pattern (monotone for non-negative floats), and a
 //    grid-stride kernel quantizes.  Every element is read twice (HBM-bound).
 //
-// x / s is the IEEE correctly rounded binary32 division (no reciprocal), so
-// codes are a function of (x, s) alone and independent of the launch shape.
+// fl32(x / s) is the correctly rounded binary32 quotient (see Quotient in
+// common.hpp), so codes are a function of (x, s) alone and independent of the
+// launch shape.
 #include "common.hpp"
 
 namespace fp8q {
@@ -53,14 +54,15 @@ __global__ __launch_bounds__(kSmallThreads) void quant_small_kernel(
     }
     const float a = block_max<kSmallThreads>(m, lds);
     const float s = scale_from_amax(a);
+    const Quotient d(s);
 
     v2i* qv = reinterpret_cast<v2i*>(q);
 #pragma unroll
     for (int j = 0; j < kSmallVecPerThread; ++j) {
         const int64_t i = tid + (int64_t)j * kSmallThreads;
-        if (i < nvec) qv[i] = vec_quantize<DT>(v[j], s);
+        if (i < nvec) qv[i] = vec_quantize<DT>(v[j], d);
     }
-    if (tid < tail) q[nvec * 8 + tid] = scalar_quantize<DT>(th, s);
+    if (tid < tail) q[nvec * 8 + tid] = scalar_quantize<DT>(th, d);
     if (tid == 0) {
         *scale = s;
         *amax_out = a;
@@ -101,6 +103,7 @@ __global__ __launch_bounds__(kBigThreads) void quant_kernel(const uint16_t* __re
                                                             const float* __restrict__ amax)
 {
     const float s = scale_from_amax(*amax);
+    const Quotient d(s);
     const int64_t nvec = n >> 3;
     const v4i* xv = reinterpret_cast<const v4i*>(x);
     v2i* qv = reinterpret_cast<v2i*>(q);
@@ -111,12 +114,12 @@ __global__ __launch_bounds__(kBigThreads) void quant_kernel(const uint16_t* __re
 #pragma unroll
         for (int u = 0; u < kBigUnroll; ++u) v[u] = xv[i + u * stride];
 #pragma unroll
-        for (int u = 0; u < kBigUnroll; ++u) qv[i + u * stride] = vec_quantize<DT>(v[u], s);
+        for (int u = 0; u < kBigUnroll; ++u) qv[i + u * stride] = vec_quantize<DT>(v[u], d);
     }
-    for (; i < nvec; i += stride) qv[i] = vec_quantize<DT>(xv[i], s);
+    for (; i < nvec; i += stride) qv[i] = vec_quantize<DT>(xv[i], d);
     if (blockIdx.x == 0) {
         if (threadIdx.x < (int)(n & 7))
-            q[nvec * 8 + threadIdx.x] = scalar_quantize<DT>(x[nvec * 8 + threadIdx.x], s);
+            q[nvec * 8 + threadIdx.x] = scalar_quantize<DT>(x[nvec * 8 + threadIdx.x], d);
         if (threadIdx.x == 0) *scale = s;
     }
 }

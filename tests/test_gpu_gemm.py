@@ -240,9 +240,10 @@ def test_linear_matches_quantize_then_gemm(M, N, K, dtype):
 
 
 # ------------------------------------------------------------------ big-tile path
-# The tile path switches from 128 x 128 tiles to the pipelined 256 x 256
-# kernel once the grid holds at least 512 tiles of 256 x 256; the cases below
-# sit on both sides of that switch.
+# The tile path picks 64x64, 128x64, 128x128 or pipelined 256x256 tiles by
+# grid size; the cases below cover every kernel (64x64: 500x4000;
+# 128x64: 2065x8292, 4096x4100; 128x128: 2040x4090 and the 4096^3 identity;
+# 256x256: N = 8192 and above).
 def _big_tiles(M, N):
     return -(-M // 256) * -(-N // 256)
 
@@ -273,8 +274,8 @@ def test_big_tile_small_integers_bit_exact(M, N, K):
     assert np.array_equal(y, want)
 
 
-@pytest.mark.parametrize("M,N,K", [(2065, 8292, 4112), (4096, 4100, 272),
-                                   (2065, 14436, 4112), (4100, 8200, 272)])
+@pytest.mark.parametrize("M,N,K", [(2065, 8292, 4112), (4096, 4100, 272), (2040, 4090, 4112),
+                                   (2065, 14436, 4112), (4100, 8200, 272), (500, 4000, 1040)])
 def test_big_tile_random_ragged_sampled(M, N, K):
     """Ragged M, N and K on both tile kernels; every output of 3 rows and 3
     columns plus 512 random pairs against the fp64 checker."""

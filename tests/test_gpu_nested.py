@@ -122,7 +122,7 @@ def test_fp8_mode_random(M, N, K):
     assert_within(oracle.f16_decode(y).ravel(), ref, ab, f"fp8 mode {M}x{N}x{K}", "fp16")
 
 
-@pytest.mark.parametrize("M", [1, 256, 2048])
+@pytest.mark.parametrize("M", [1, 256, 512, 2048])
 @pytest.mark.parametrize("K,N", [(K, N) for _, K, N in synth.LLAMA7B_LINEARS])
 def test_full_size_llama_shapes_sampled(M, K, N):
     """NestedFP on the Llama-7B linear shapes (GPU split, GPU fp16-activation

@@ -134,6 +134,25 @@ def test_quantize_zero_and_constant(n):
     _quant_case(tiny, f"tiny n={n}")
 
 
+@pytest.mark.parametrize("n", [600, 40_000])
+@pytest.mark.parametrize("below", [False, True])
+def test_quantize_scale_threshold(n, below):
+    """The device divides by s with a reciprocal and an FMA correction for
+    2^-80 <= s <= 2^120 and with IEEE division otherwise.  amax = 1.75 * 2^-72
+    gives s = 2^-80 exactly (first path); one bf16 step lower gives the
+    second.  The rest: random magnitudes over 40 binades below amax, both
+    signs, +-0 and bf16 subnormals (codes must match the oracle's division)."""
+    rng = np.random.Generator(np.random.PCG64(n + below))
+    top = torch.tensor([1.75 * 2.0 ** -72], dtype=torch.bfloat16)
+    tb = int(synth.bits(top)[0]) - (1 if below else 0)
+    mag = 2.0 ** rng.uniform(-112, -72.5, n)
+    vals = torch.from_numpy((mag * rng.choice([-1.0, 1.0], n)).astype(np.float32)).to(torch.bfloat16)
+    b = synth.bits(vals).copy()
+    b[:4] = [0x0000, 0x8000, 0x0001, 0x8003]           # +0, -0, subnormals
+    b[n // 2] = tb
+    _quant_case(synth.from_bits(b, "bf16"), f"threshold below={below} n={n}")
+
+
 def test_quantize_deterministic_large_path():
     x = synth.activation(512, 11008, seed=3, outliers=True).to(DEV)
     say("quantize determinism")
