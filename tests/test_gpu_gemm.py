@@ -240,20 +240,18 @@ def test_linear_matches_quantize_then_gemm(M, N, K, dtype):
 
 
 # ------------------------------------------------------------------ big-tile path
-# The tile path picks 64x64, 128x64, 128x128 or pipelined 256x256 tiles by
-# grid size; the cases below cover every kernel (64x64: 500x4000;
-# 128x64: 2065x8292, 4096x4100; 128x128: 2040x4090 and the 4096^3 identity;
-# 256x256: N = 8192 and above).
+# The tile path uses 128x128 tiles from 192 of them (4096x4096, 2065x8292,
+# 510x8190, ...) and 64x128 tiles below (1024x2048, 500x4000); ragged M, N and
+# K (K % 128 != 0: the last step is partial) on both.
 def _big_tiles(M, N):
     return -(-M // 256) * -(-N // 256)
 
 
-@pytest.mark.parametrize("N", [4096, 8192])
-def test_big_tile_identity_returns_every_weight(N):
-    """qa = I with M = K = 4096: y = W^T bit-exactly for every weight, with
-    N = 4096 (256 tiles of 256 x 256: 128 x 128 kernel) and N = 8192 (512:
-    pipelined kernel)."""
-    M = K = 4096
+@pytest.mark.parametrize("MK,N", [(4096, 4096), (1024, 2048)])
+def test_big_tile_identity_returns_every_weight(MK, N):
+    """qa = I with M = K: y = W^T bit-exactly for every weight, on 128x128
+    tiles (4096^3) and 64x128 tiles (1024 x 2048)."""
+    M = K = MK
     rng = np.random.Generator(np.random.PCG64(4096 + N))
     qw = _random_codes(rng, (N, K))
     say("big identity", M, N, K, "tiles256", _big_tiles(M, N))
@@ -262,9 +260,10 @@ def test_big_tile_identity_returns_every_weight(N):
     assert np.array_equal(y, want.T)
 
 
-@pytest.mark.parametrize("M,N,K", [(4096, 4096, 80), (4096, 8192, 80), (4100, 8200, 48)])
+@pytest.mark.parametrize("M,N,K", [(4096, 4096, 80), (4100, 12300, 48), (510, 8190, 80),
+                                   (500, 4000, 48)])
 def test_big_tile_small_integers_bit_exact(M, N, K):
-    """Small integers through both tile kernels; K = 80 and 48 leave a
+    """Small integers through every tile kernel; K = 80 and 48 leave a
     partial K step (out-of-range units read as zero)."""
     rng = np.random.Generator(np.random.PCG64(K + N))
     qa, qw = _small_int(rng, M, N, K)
@@ -275,7 +274,7 @@ def test_big_tile_small_integers_bit_exact(M, N, K):
 
 
 @pytest.mark.parametrize("M,N,K", [(2065, 8292, 4112), (4096, 4100, 272), (2040, 4090, 4112),
-                                   (2065, 14436, 4112), (4100, 8200, 272), (500, 4000, 1040)])
+                                   (4100, 12300, 272), (510, 8190, 1040), (500, 4000, 1040)])
 def test_big_tile_random_ragged_sampled(M, N, K):
     """Ragged M, N and K on both tile kernels; every output of 3 rows and 3
     columns plus 512 random pairs against the fp64 checker."""

@@ -153,3 +153,23 @@ def test_full_size_llama_shapes_sampled(M, K, N):
     ref8, ab8 = oracle.nested_fp8_ref(oqa.reshape(M, K)[rows], osa, ohi, ms, nn)
     out8 = oracle.f16_decode(host(y8)[rows][:, ns]).ravel()
     assert_within(out8, ref8, ab8, f"fp8 mode M={M} {K}->{N}", "fp16")
+
+
+def test_fp8_mode_large_grid_sampled():
+    """FP8 mode (E5M2 weights, fp16 output) on a large grid (3072 x 16384,
+    K = 1040, 3072 tiles of 128x128): 2 rows, 2 columns and 256 random
+    outputs against the fp64 checker."""
+    M, N, K = 3072, 16384, 1040
+    seed = synth.seed_for("nested-large", M, N, K)
+    a16, hi, _ = _operands(M, N, K, seed=seed)
+    qa, sa, _ = oracle.quantize(a16.ravel(), oracle.FP16)
+    qa = qa.reshape(M, K)
+    say("fp8 mode large grid", M, N, K)
+    y = fp8q.nested_gemm_fp8(to_dev_u8(qa), scalar_dev(sa), to_dev_u8(hi))
+    yb = host(y)
+    rng = np.random.Generator(np.random.PCG64(seed))
+    ms = np.concatenate([np.repeat([0, M - 1], N), np.tile(np.arange(M), 2), rng.integers(0, M, 256)])
+    ns = np.concatenate([np.tile(np.arange(N), 2), np.repeat([0, N - 1], M), rng.integers(0, N, 256)])
+    ref, ab = oracle.nested_fp8_ref(qa, sa, hi, ms, ns)
+    out = oracle.f16_decode(yb[ms, ns]).astype(np.float64)
+    assert_within(out, ref, ab, f"fp8 mode {M}x{N}x{K}", "fp16")
