@@ -154,7 +154,13 @@ fp8q_status fp8_linear(const void* x, int dtype, const uint8_t* qw, const float*
     if (M <= kRowkMaxM && M * K <= kFusedMaxMK)
         return finish("fp8_linear", launch_linear_fused(x, dtype, qw, sw, y, q, scale, amax,
                                                         (int)M, (int)N, (int)K, st));
-    hipError_t e = launch_quantize(x, dtype, M * K, q, scale, amax, st);
+    // y is written only by the GEMM, so until then it can hold the
+    // quantizer's per-workgroup partial maxima (unless it overlaps x)
+    const uintptr_t xb = reinterpret_cast<uintptr_t>(x), yb = reinterpret_cast<uintptr_t>(y);
+    const bool y_free = yb + (uintptr_t)(M * N * 2) <= xb || xb + (uintptr_t)(M * K * 2) <= yb;
+    hipError_t e = launch_quantize_scratch(x, dtype, M * K, q, scale, amax,
+                                           y_free ? reinterpret_cast<float*>(y) : nullptr,
+                                           M * N / 2, st);
     if (e == hipSuccess)
         e = dispatch_fp8(q, scale, qw, sw, y, (int)M, (int)N, (int)K, WF_E4M3, OUT_BF16, st);
     return finish("fp8_linear", e);

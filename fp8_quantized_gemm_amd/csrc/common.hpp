@@ -290,6 +290,12 @@ __device__ __forceinline__ float wave_sum(float v)
 // Each returns the hipError_t of hipGetLastError() after its launches.
 hipError_t launch_quantize(const void* x, int dtype, int64_t n, uint8_t* q, float* scale,
                            float* amax, hipStream_t stream);
+// Same result; for n above the one-workgroup size it uses scratch_floats
+// floats at `scratch` (device memory not overlapping x) for per-workgroup
+// partial maxima instead of an atomic, when that is enough room.
+hipError_t launch_quantize_scratch(const void* x, int dtype, int64_t n, uint8_t* q, float* scale,
+                                   float* amax, float* scratch, int64_t scratch_floats,
+                                   hipStream_t stream);
 
 // Row-contiguous decode path for M <= kRowkMaxM (see linear.hip).
 constexpr int kRowkMaxM = 2;

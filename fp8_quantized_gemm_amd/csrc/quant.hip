@@ -124,6 +124,71 @@ __global__ __launch_bounds__(kBigThreads) void quant_kernel(const uint16_t* __re
     }
 }
 
+// ---------------------------------------------------------------- large path, no atomics
+// For callers that can lend G floats of scratch (fp8_linear lends its output
+// y, which the GEMM writes only afterwards): each workgroup of the amax pass
+// writes its partial maximum to part[blockIdx.x]; every workgroup of the
+// quantize pass reduces the G partials itself (max is exact and
+// order-free, so all of them get the same amax) and quantizes its share.
+// Two launches instead of three, and no same-address atomics.
+template <int DT>
+__global__ __launch_bounds__(kBigThreads) void amax_partial_kernel(const uint16_t* __restrict__ x,
+                                                                   int64_t n, float* __restrict__ part)
+{
+    __shared__ float lds[kBigThreads / 64];
+    const int64_t nvec = n >> 3;
+    const v4i* xv = reinterpret_cast<const v4i*>(x);
+    const int64_t stride = (int64_t)gridDim.x * kBigThreads;
+    float m = 0.0f;
+    int64_t i = (int64_t)blockIdx.x * kBigThreads + threadIdx.x;
+    for (; i + (kBigUnroll - 1) * stride < nvec; i += kBigUnroll * stride) {
+        v4i v[kBigUnroll];
+#pragma unroll
+        for (int u = 0; u < kBigUnroll; ++u) v[u] = xv[i + u * stride];
+#pragma unroll
+        for (int u = 0; u < kBigUnroll; ++u) m = fmaxf(m, vec_absmax<DT>(v[u]));
+    }
+    for (; i < nvec; i += stride) m = fmaxf(m, vec_absmax<DT>(xv[i]));
+    if (blockIdx.x == 0 && threadIdx.x < (int)(n & 7))
+        m = fmaxf(m, fabsf(half_bits_to_f32<DT>(x[nvec * 8 + threadIdx.x])));
+    m = block_max<kBigThreads>(m, lds);
+    if (threadIdx.x == 0) part[blockIdx.x] = m;
+}
+
+template <int DT>
+__global__ __launch_bounds__(kBigThreads) void quant_partial_kernel(
+    const uint16_t* __restrict__ x, int64_t n, uint8_t* __restrict__ q, float* __restrict__ scale,
+    float* __restrict__ amax_out, const float* __restrict__ part)
+{
+    __shared__ float lds[kBigThreads / 64];
+    float m = 0.0f;
+    for (int i = threadIdx.x; i < (int)gridDim.x; i += kBigThreads) m = fmaxf(m, part[i]);
+    const float a = block_max<kBigThreads>(m, lds);
+    const float s = scale_from_amax(a);
+    const Quotient d(s);
+    const int64_t nvec = n >> 3;
+    const v4i* xv = reinterpret_cast<const v4i*>(x);
+    v2i* qv = reinterpret_cast<v2i*>(q);
+    const int64_t stride = (int64_t)gridDim.x * kBigThreads;
+    int64_t i = (int64_t)blockIdx.x * kBigThreads + threadIdx.x;
+    for (; i + (kBigUnroll - 1) * stride < nvec; i += kBigUnroll * stride) {
+        v4i v[kBigUnroll];
+#pragma unroll
+        for (int u = 0; u < kBigUnroll; ++u) v[u] = xv[i + u * stride];
+#pragma unroll
+        for (int u = 0; u < kBigUnroll; ++u) qv[i + u * stride] = vec_quantize<DT>(v[u], d);
+    }
+    for (; i < nvec; i += stride) qv[i] = vec_quantize<DT>(xv[i], d);
+    if (blockIdx.x == 0) {
+        if (threadIdx.x < (int)(n & 7))
+            q[nvec * 8 + threadIdx.x] = scalar_quantize<DT>(x[nvec * 8 + threadIdx.x], d);
+        if (threadIdx.x == 0) {
+            *scale = s;
+            *amax_out = a;
+        }
+    }
+}
+
 // ---------------------------------------------------------------- encoder export
 __global__ __launch_bounds__(256) void e4m3_encode_kernel(const float* __restrict__ v,
                                                           uint8_t* __restrict__ q, int64_t n)
@@ -162,6 +227,24 @@ hipError_t launch_quantize(const void* x, int dtype, int64_t n, uint8_t* q, floa
     } else {
         amax_kernel<DT_FP16><<<g, kBigThreads, 0, stream>>>(xs, n, amax);
         quant_kernel<DT_FP16><<<g, kBigThreads, 0, stream>>>(xs, n, q, scale, amax);
+    }
+    return hipGetLastError();
+}
+
+hipError_t launch_quantize_scratch(const void* x, int dtype, int64_t n, uint8_t* q, float* scale,
+                                   float* amax, float* scratch, int64_t scratch_floats,
+                                   hipStream_t stream)
+{
+    const int g = grid_for(n >> 3, kBigThreads * kBigUnroll);
+    if (n <= kSmallN || scratch == nullptr || scratch_floats < g)
+        return launch_quantize(x, dtype, n, q, scale, amax, stream);
+    const uint16_t* xs = static_cast<const uint16_t*>(x);
+    if (dtype == DT_BF16) {
+        amax_partial_kernel<DT_BF16><<<g, kBigThreads, 0, stream>>>(xs, n, scratch);
+        quant_partial_kernel<DT_BF16><<<g, kBigThreads, 0, stream>>>(xs, n, q, scale, amax, scratch);
+    } else {
+        amax_partial_kernel<DT_FP16><<<g, kBigThreads, 0, stream>>>(xs, n, scratch);
+        quant_partial_kernel<DT_FP16><<<g, kBigThreads, 0, stream>>>(xs, n, q, scale, amax, scratch);
     }
     return hipGetLastError();
 }

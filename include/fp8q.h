@@ -117,7 +117,9 @@ FP8Q_API fp8q_status fp8_gemm(const uint8_t* qa, const float* sa, const uint8_t*
  *   q[M,K], *scale, *amax out: the activation codes, scale and amax
  *   Size rules as fp8_gemm.  For M <= 2 and M*K <= 32768 the whole layer is
  *   one kernel (each workgroup quantizes the activation in LDS); otherwise it
- *   launches the quantizer and then the GEMM.
+ *   launches the quantizer and then the GEMM; while the quantizer runs, y
+ *   (not yet written) may hold its per-workgroup partial maxima, unless y
+ *   overlaps x.
  */
 FP8Q_API fp8q_status fp8_linear(const void* x, int dtype, const uint8_t* qw, const float* sw,
                        uint16_t* y, uint8_t* q, float* scale, float* amax, int64_t M,

@@ -210,11 +210,13 @@ def test_deterministic_and_stream_order():
 @pytest.mark.parametrize("M,N,K", [(1, 4096, 4096), (2, 300, 11008), (1, 37, 16), (1, 64, 32768),
                                    (2, 64, 16384), (2, 64, 32768),
                                    (1, 100, 65536), (2, 50, 33792), (3, 200, 1024), (16, 64, 4096),
-                                   (40, 96, 512)])
+                                   (40, 96, 512), (64, 256, 4096), (3, 16, 81920)])
 def test_linear_matches_quantize_then_gemm(M, N, K, dtype):
     """fp8_linear (fused for M <= 2, M*K <= 32768) returns the codes, scale and
     amax of fp8_quantize_act bit-exactly and the same y as fp8_gemm on them;
-    both agree with the oracle."""
+    both agree with the oracle.  Above 32768 elements fp8_linear keeps its
+    amax partials in y when y holds enough floats (64x256x4096) and falls
+    back to the atomic path when it does not (3x16x81920)."""
     seed = synth.seed_for("linear", M, N, K, dtype)
     x = synth.activation(M, K, seed=seed, dtype=dtype, outliers=M > 2)
     w = synth.normal((N, K), 0.02, "fp16", seed=seed + 1)
