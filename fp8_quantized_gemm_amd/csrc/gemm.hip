@@ -3,15 +3,14 @@
 //  - FP8: y = out( (qa . W^T) * scale ) with E4M3 activations and E4M3 (FP8
 //    GEMM, page "C++与FP8量化" §3.3) or E5M2 (NestedFP FP8 mode, page
 //    "NestedFP双精度推理框架" §2.1) weights: gemm_f8_kernel, 128x128 or
-//    64x128 tiles by grid size (launch_tile_fmt), 16x16x128 MFMAs, operands
-//    moved to LDS by direct-to-LDS loads in a 2-stage (activation) and a
-//    3-stage (weight) ring.
-//  - NestedFP FP16 mode (same page, §2.1-§2.2): gemm_nested16_tile_kernel,
-//    128x128 tiles; the weight tile is staged in LDS as its two byte planes
-//    and rebuilt as fp16 (hi<<8)|lo with v_perm while it is moved from LDS to
-//    registers, then v_mfma_f32_16x16x32_f16.  Each K step stages the next
-//    tiles in registers while the current LDS buffer feeds the MFMAs, so one
-//    barrier per step suffices.
+//    64x64 tiles by grid size (launch_tile_fmt), 16x16x128 MFMAs, operands
+//    moved to LDS by direct-to-LDS loads in an activation ring and a weight
+//    ring of 2-4 stages each.
+//  - NestedFP FP16 mode (same page, §2.1-§2.2): gemm_n16_kernel, 128x128 or
+//    64x64 tiles; the activation and the two weight byte planes reach LDS by
+//    direct-to-LDS loads, and the weight words are rebuilt as fp16
+//    (hi<<8)|lo with v_perm while they move from LDS to registers, then
+//    v_mfma_f32_16x16x32_f16.
 //
 // Rows of A and W are K-contiguous; LDS rows hold 16-byte units XOR-swizzled
 // by row so that 16 lanes reading the same unit of 16 consecutive rows hit
@@ -22,9 +21,8 @@
 namespace fp8q {
 namespace {
 
-constexpr int kBM = 128;
-constexpr int kBN = 128;
-constexpr int kThreads = 256;
+constexpr int kCUs = 256;                // compute units of an MI355X
+
 
 __device__ __forceinline__ v8i cat(const v4i& lo, const v4i& hi)
 {
@@ -78,15 +76,14 @@ __device__ __forceinline__ void wait_vm()
 
 
 // ---------------------------------------------------------------- FP8 tile GEMM
-// BM x BN output tile (128 x 128, or 64 x 128 for small grids) per 256-thread
+// BM x BN output tile (128 x 128, or 64 x 64 for small grids) per 256-thread
 // workgroup; the 4 waves form a 2 x 2 grid of (BM/2) x (BN/2) wave tiles of
 // 16x16x128 MFMAs, so each fragment read from LDS feeds BM/32 or BN/32
 // MFMAs.  K advances 128 bytes per step.  Both operands reach LDS through
 // direct global->LDS loads (buffer_load ... lds: no register staging, no LDS
 // store instructions), in two rings: the activation tile (small, reused by
-// every weight panel, L2-resident) has 2 stages, the weight tile (streamed
-// from HBM) WST = 3 stages, so its loads are issued two steps ahead and have
-// two steps of MFMAs to arrive.  Within a step the wave holds its A
+// every weight panel, L2-resident) has AST stages, the weight tile (streamed
+// from HBM) WST >= AST stages, so its loads are issued WST - 1 steps ahead.  Within a step the wave holds its A
 // fragments and double-buffers the W fragments column by column.  LDS rows
 // are 128 bytes, unit u of row r stored at position u ^ (r & 7), so the 16
 // lanes reading one unit of 16 consecutive rows hit distinct banks; a DMA
@@ -95,7 +92,7 @@ __device__ __forceinline__ void wait_vm()
 // that is 80 KiB of LDS: two workgroups per CU.  Loads past the last step are
 // still issued (with out-of-range offsets: zeros into a free stage) so the
 // wait counts are the same every step.
-template <int WFMT, int OUTF, int BM, int BN, int WST>
+template <int WFMT, int OUTF, int BM, int BN, int AST, int WST>
 __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2)))
 void gemm_f8_kernel(
     const uint8_t* __restrict__ qa, const float* __restrict__ sa,
@@ -107,10 +104,11 @@ void gemm_f8_kernel(
     constexpr int FM = TM / 16, FN = TN / 16;
     constexpr int ASTAGE = BM * BK, WSTAGE = BN * BK;
     constexpr int ABPW = BM / 32, WBPW = BN / 32;     // 1 KiB DMA blocks per wave per step
-    static_assert(WST == 3, "the wait counts below assume a 3-stage weight ring");
+    static_assert(AST >= 2 && WST >= AST, "ring depths");
+    constexpr int ALLOW = (AST < WST ? WBPW : 0) + (AST - 2) * (ABPW + WBPW);
     extern __shared__ __attribute__((aligned(16))) uint8_t lds[];
-    uint8_t* const a_lds = lds;                       // 2 stages
-    uint8_t* const w_lds = lds + 2 * ASTAGE;          // WST stages
+    uint8_t* const a_lds = lds;                       // AST stages
+    uint8_t* const w_lds = lds + AST * ASTAGE;        // WST stages
 
     const int tid = threadIdx.x;
     const int lane = tid & 63;
@@ -132,7 +130,7 @@ void gemm_f8_kernel(
     const int nk = (K + BK - 1) / BK;
     auto dma_a = [&](int kt) {
         const bool kin = kt < nk && kt * BK + du * 16 < K;
-        uint8_t* base = a_lds + (kt & 1) * ASTAGE + wave * ABPW * 1024;
+        uint8_t* base = a_lds + (kt % AST) * ASTAGE + wave * ABPW * 1024;
 #pragma unroll
         for (int j = 0; j < ABPW; ++j)
             dma_load16(ra, base + j * 1024,
@@ -153,18 +151,22 @@ void gemm_f8_kernel(
 #pragma unroll
         for (int j = 0; j < FN; ++j) acc[i][j] = v4f{0.f, 0.f, 0.f, 0.f};
 
-    // issue order: A0 W0 .. W(WST-2) A1, then after step k: A(k+2) W(k+WST)
-    dma_a(0);
+    // loads go out in groups: the group issued after step j holds A(j + AST)
+    // then W(j + WST); the prologue issues groups -WST .. -1 (skipping
+    // negative steps), and loads past the last step are still issued with
+    // out-of-range offsets, so the wait before every step is the same:
+    // A(k+1) sits in group k + 1 - AST, after which only that group's W and
+    // the AST - 2 later groups may still be in flight.
 #pragma unroll
-    for (int p = 0; p < WST - 1; ++p) dma_w(p);
-    dma_a(1);
-    dma_w(WST - 1);
-    // A0 and W0 done; outstanding: W1..W(WST-1), A1
-    wait_vm<(WST - 1) * WBPW + ABPW>();
+    for (int j = -WST; j < 0; ++j) {
+        if (j + AST >= 0) dma_a(j + AST);
+        dma_w(j + WST);
+    }
+    wait_vm<ALLOW + ABPW + WBPW>();            // the prologue has also issued group -1
     __syncthreads();
 
     for (int kt = 0; kt < nk; ++kt) {
-        const uint8_t* As = a_lds + (kt & 1) * ASTAGE;
+        const uint8_t* As = a_lds + (kt % AST) * ASTAGE;
         const uint8_t* Ws = w_lds + (kt % WST) * WSTAGE;
         v8i af[FM];
 #pragma unroll
@@ -188,12 +190,9 @@ void gemm_f8_kernel(
                 acc[i][j] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(
                     af[i], wf[j & 1], acc[i][j], WF_E4M3, WFMT, 0, 0, 0, 0);
         }
-        // issue order so far ends with ... W(k+1) A(k+1) W(k+2); A(k+1),
-        // needed next, was issued one group ago, so only W(k+2) may stay in
-        // flight (W(k+1) has had two steps)
-        wait_vm<WBPW>();
+        wait_vm<ALLOW>();
         __syncthreads();                       // stage k of both rings is free
-        dma_a(kt + 2);
+        dma_a(kt + AST);
         dma_w(kt + WST);
     }
     wait_vm<0>();                              // nothing left in flight into LDS
@@ -203,98 +202,112 @@ void gemm_f8_kernel(
     store_tile<OUTF, FM, FN>(y, acc, s, M, N, m0 + wm * TM, n0 + wn * TN, r, g);
 }
 
-// ---------------------------------------------------------------- NestedFP FP16 tile GEMM
-// K step = 64 elements: A tile 128 rows x 128 bytes, hi and lo tiles 128 rows
-// x 64 bytes each.  MFMA s (s = 0, 1) of a step covers elements
-// [32 s, 32 s + 32); lane group g supplies elements [32 s + 8 g, +8).
-__global__ __launch_bounds__(kThreads) void gemm_nested16_tile_kernel(
-    const uint16_t* __restrict__ a, const uint8_t* __restrict__ hi,
-    const uint8_t* __restrict__ lo, uint16_t* __restrict__ y, int M, int N, int K)
+// ---------------------------------------------------------------- NestedFP FP16 GEMM, DMA rings
+// The NestedFP FP16 mode on the structure of gemm_f8_kernel: BM x BN tiles,
+// 4 waves of (BM/2) x (BN/2), K steps of 64 elements.  The fp16 activation
+// tile (BM rows x 128 bytes) goes through an AST-stage ring and the weight
+// byte planes (hi then lo, BN rows x 64 bytes each) through a WST-stage ring
+// (WST >= AST >= 2), both filled by direct global->LDS loads.  MFMA s
+// (s = 0, 1) of a step covers elements [32 s, 32 s + 32): lane group g
+// supplies elements [32 s + 8 g, +8), i.e. unit 4 s + g of an activation row
+// and half (g & 1) of unit 2 s + (g >> 1) of each plane row; the weight words
+// are rebuilt as (hi << 8) | lo with v_perm while they move from LDS to
+// registers.  Activation rows use the 128-byte swizzle (u ^ (r & 7)), plane
+// rows the 64-byte one (u ^ ((r >> 1) & 3)); a DMA block is 8 activation rows
+// or 16 plane rows.
+//
+// Loads are issued in groups: the group issued after step j holds A(j + AST)
+// then W(j + WST) (the prologue issues groups j = -WST .. -1, skipping
+// negative steps), and loads past the last step are still issued with
+// out-of-range offsets, so before step k + 1 the wait is the same every
+// step: A(k+1) sits in group k + 1 - AST, after which only that group's W
+// and the AST - 2 later groups may still be in flight (when AST == WST the
+// group's W is needed too).
+template <int BM, int BN, int AST, int WST>
+__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2)))
+void gemm_n16_kernel(const uint16_t* __restrict__ a, const uint8_t* __restrict__ hi,
+                     const uint8_t* __restrict__ lo, uint16_t* __restrict__ y, int M, int N, int K)
 {
-    constexpr int BK = 64;                                   // elements
-    constexpr int A_BYTES = kBM * BK * 2;                    // 16 KiB
-    constexpr int P_BYTES = kBN * BK;                        // 8 KiB per plane
-    constexpr int STAGE = A_BYTES + 2 * P_BYTES;             // 32 KiB
-    __shared__ __attribute__((aligned(16))) uint8_t lds[2 * STAGE];
+    static_assert(AST >= 2 && WST >= AST, "ring depths");
+    constexpr int TM = BM / 2, TN = BN / 2;
+    constexpr int FM = TM / 16, FN = TN / 16;
+    constexpr int ASTAGE = BM * 128, PLANE = BN * 64, WSTAGE = 2 * PLANE;
+    constexpr int ABPW = BM / 32;                 // activation blocks per wave per step
+    constexpr int PBPW = BN / 64;                 // blocks per plane per wave per step
+    constexpr int WBPW = 2 * PBPW;
+    constexpr int ALLOW = (AST < WST ? WBPW : 0) + (AST - 2) * (ABPW + WBPW);
+    extern __shared__ __attribute__((aligned(16))) uint8_t lds[];
+    uint8_t* const a_lds = lds;
+    uint8_t* const w_lds = lds + AST * ASTAGE;
 
     const int tid = threadIdx.x;
-    const int lane = tid & 63, wave = tid >> 6;
+    const int lane = tid & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
     const int wm = wave >> 1, wn = wave & 1;
     const int r = lane & 15, g = lane >> 4;
 
-    const int tiles_m = (M + kBM - 1) / kBM;
+    const int tiles_m = (M + BM - 1) / BM;
     const int bid = xcd_remap(blockIdx.x, gridDim.x);
-    const int m0 = (bid % tiles_m) * kBM;
-    const int n0 = (bid / tiles_m) * kBN;
-
-    // A staging: unit (tid & 7) (8 elements) of rows (tid >> 3) + 32 j, j = 0..3
-    // plane staging: unit (tid & 3) (16 bytes) of rows (tid >> 2) + 64 j, j = 0..1
-    const int au = tid & 7, pu = tid & 3;
-    const int mrows = min(kBM, M - m0), nrows = min(kBN, N - n0);
-    const rsrc_t ra = make_rsrc(a + (size_t)m0 * K, (uint32_t)(mrows * K * 2));
+    const int m0 = (bid % tiles_m) * BM;
+    const int n0 = (bid / tiles_m) * BN;
+    const int nrows = min(BN, N - n0);
+    const rsrc_t ra = make_rsrc(a + (size_t)m0 * K, (uint32_t)(min(BM, M - m0) * K * 2));
     const rsrc_t rh = make_rsrc(hi + (size_t)n0 * K, (uint32_t)(nrows * K));
     const rsrc_t rl = make_rsrc(lo + (size_t)n0 * K, (uint32_t)(nrows * K));
-    uint32_t aoff[4], poff[2];
+
+    const int dua = (lane & 7) ^ (lane >> 3);         // activation unit landing in slot l
+    const int duw = (lane & 3) ^ ((lane >> 3) & 3);   // plane unit landing in slot l
+    const uint32_t aoff = (uint32_t)((lane >> 3) * K * 2 + dua * 16);
+    const uint32_t poff = (uint32_t)((lane >> 2) * K + duw * 16);
+    const int nk = (K + 63) / 64;
+    auto dma_a = [&](int kt) {
+        const bool kin = kt < nk && kt * 64 + dua * 8 < K;
+        uint8_t* base = a_lds + (kt % AST) * ASTAGE + wave * ABPW * 1024;
 #pragma unroll
-    for (int j = 0; j < 4; ++j) aoff[j] = (uint32_t)((((tid >> 3) + 32 * j) * K + au * 8) * 2);
-#pragma unroll
-    for (int j = 0; j < 2; ++j) poff[j] = (uint32_t)(((tid >> 2) + 64 * j) * K + pu * 16);
-    v4i ra_[4], rh_[2], rl_[2];
-    auto gload = [&](int kt) {
-        const bool ain = kt * BK + au * 8 < K;
-        const bool pin = kt * BK + pu * 16 < K;
-#pragma unroll
-        for (int j = 0; j < 4; ++j) ra_[j] = buf_load16(ra, ain ? aoff[j] + kt * BK * 2 : kOOB);
-#pragma unroll
-        for (int j = 0; j < 2; ++j) {
-            rh_[j] = buf_load16(rh, pin ? poff[j] + kt * BK : kOOB);
-            rl_[j] = buf_load16(rl, pin ? poff[j] + kt * BK : kOOB);
-        }
+        for (int j = 0; j < ABPW; ++j)
+            dma_load16(ra, base + j * 1024,
+                       kin ? (uint32_t)((wave * ABPW + j) * 8 * K * 2) + aoff + kt * 128 : kOOB);
     };
-    auto lstore = [&](int buf) {
-        uint8_t* As = lds + buf * STAGE;
-        uint8_t* Hs = As + A_BYTES;
-        uint8_t* Ls = Hs + P_BYTES;
+    auto dma_w = [&](int kt) {
+        const bool kin = kt < nk && kt * 64 + duw * 16 < K;
+        uint8_t* base = w_lds + (kt % WST) * WSTAGE + wave * PBPW * 1024;
 #pragma unroll
-        for (int j = 0; j < 4; ++j)
-            *reinterpret_cast<v4i*>(As + swz128((tid >> 3) + 32 * j, au)) = ra_[j];
-#pragma unroll
-        for (int j = 0; j < 2; ++j) {
-            const int row = (tid >> 2) + 64 * j;
-            *reinterpret_cast<v4i*>(Hs + swz64(row, pu)) = rh_[j];
-            *reinterpret_cast<v4i*>(Ls + swz64(row, pu)) = rl_[j];
+        for (int j = 0; j < PBPW; ++j) {
+            const uint32_t o = kin ? (uint32_t)((wave * PBPW + j) * 16 * K) + poff + kt * 64 : kOOB;
+            dma_load16(rh, base + j * 1024, o);
+            dma_load16(rl, base + PLANE + j * 1024, o);
         }
     };
 
-    v4f acc[4][4];
+    v4f acc[FM][FN];
 #pragma unroll
-    for (int i = 0; i < 4; ++i)
+    for (int i = 0; i < FM; ++i)
 #pragma unroll
-        for (int j = 0; j < 4; ++j) acc[i][j] = v4f{0.f, 0.f, 0.f, 0.f};
+        for (int j = 0; j < FN; ++j) acc[i][j] = v4f{0.f, 0.f, 0.f, 0.f};
 
-    const int nk = (K + BK - 1) / BK;
-    gload(0);
-    lstore(0);
+#pragma unroll
+    for (int j = -WST; j < 0; ++j) {
+        if (j + AST >= 0) dma_a(j + AST);
+        dma_w(j + WST);
+    }
+    wait_vm<ALLOW + ABPW + WBPW>();            // the prologue has also issued group -1
     __syncthreads();
+
     for (int kt = 0; kt < nk; ++kt) {
-        const int cur = kt & 1;
-        if (kt + 1 < nk) gload(kt + 1);
-        const uint8_t* As = lds + cur * STAGE;
-        const uint8_t* Hs = As + A_BYTES;
-        const uint8_t* Ls = Hs + P_BYTES;
+        const uint8_t* As = a_lds + (kt % AST) * ASTAGE;
+        const uint8_t* Hs = w_lds + (kt % WST) * WSTAGE;
+        const uint8_t* Ls = Hs + PLANE;
 #pragma unroll
         for (int s = 0; s < 2; ++s) {
-            // A: elements [32 s + 8 g, +8) = unit 4 s + g of the 128-byte row
-            v8h af[4], wf[4];
+            v8h af[FM], wf[FN];
 #pragma unroll
-            for (int i = 0; i < 4; ++i) {
-                const int row = wm * 64 + i * 16 + r;
+            for (int i = 0; i < FM; ++i) {
+                const int row = wm * TM + i * 16 + r;
                 af[i] = __builtin_bit_cast(v8h, *reinterpret_cast<const v4i*>(As + swz128(row, 4 * s + g)));
             }
-            // planes: bytes [32 s + 8 g, +8) = half (g & 1) of unit 2 s + (g >> 1)
 #pragma unroll
-            for (int j = 0; j < 4; ++j) {
-                const int row = wn * 64 + j * 16 + r;
+            for (int j = 0; j < FN; ++j) {
+                const int row = wn * TN + j * 16 + r;
                 const int off = swz64(row, 2 * s + (g >> 1)) + (g & 1) * 8;
                 const v2i h = *reinterpret_cast<const v2i*>(Hs + off);
                 const v2i l = *reinterpret_cast<const v2i*>(Ls + off);
@@ -304,31 +317,29 @@ __global__ __launch_bounds__(kThreads) void gemm_nested16_tile_kernel(
                 wf[j] = __builtin_bit_cast(v8h, v4i{(int)w0, (int)w1, (int)w2, (int)w3});
             }
 #pragma unroll
-            for (int i = 0; i < 4; ++i)
+            for (int i = 0; i < FM; ++i)
 #pragma unroll
-                for (int j = 0; j < 4; ++j)
+                for (int j = 0; j < FN; ++j)
                     acc[i][j] = __builtin_amdgcn_mfma_f32_16x16x32_f16(af[i], wf[j], acc[i][j], 0, 0, 0);
         }
-        if (kt + 1 < nk) lstore(cur ^ 1);
-        __syncthreads();
+        wait_vm<ALLOW>();
+        __syncthreads();                       // stage kt of both rings is free
+        dma_a(kt + AST);
+        dma_w(kt + WST);
     }
+    wait_vm<0>();
 
-    store_tile<OUT_FP16>(y, acc, 1.0f, M, N, m0 + wm * 64, n0 + wn * 64, r, g);
-}
-
-int tile_grid(int M, int N)
-{
-    return ((M + kBM - 1) / kBM) * ((N + kBN - 1) / kBN);
+    store_tile<OUT_FP16, FM, FN>(y, acc, 1.0f, M, N, m0 + wm * TM, n0 + wn * TN, r, g);
 }
 
 }  // namespace
 
-template <int WFMT, int OUTF, int BM, int BN, int WST>
+template <int WFMT, int OUTF, int BM, int BN, int AST, int WST>
 hipError_t launch_f8(const uint8_t* qa, const float* sa, const uint8_t* qw, const float* sw,
-                      uint16_t* y, int M, int N, int K, hipStream_t stream)
+                     uint16_t* y, int M, int N, int K, hipStream_t stream)
 {
-    auto kern = gemm_f8_kernel<WFMT, OUTF, BM, BN, WST>;
-    constexpr size_t lds = (2 * (size_t)BM + (size_t)WST * BN) * 128;
+    auto kern = gemm_f8_kernel<WFMT, OUTF, BM, BN, AST, WST>;
+    constexpr size_t lds = ((size_t)AST * BM + (size_t)WST * BN) * 128;
     static bool attr_set = false;        // idempotent host attribute, set on first use
     if (!attr_set) {
         const hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(kern),
@@ -346,12 +357,16 @@ template <int WFMT, int OUTF>
 hipError_t launch_tile_fmt(const uint8_t* qa, const float* sa, const uint8_t* qw, const float* sw,
                            uint16_t* y, int M, int N, int K, hipStream_t stream)
 {
-    // 128 x 128 tiles from 192 of them (measured faster from there on the
-    // Llama-7B / Qwen-32B prefill shapes, M = 256..2048, weights cold in
-    // HBM); below that 64 x 128, which doubles the workgroups per weight panel.
+    // From measurements on MI355X over the Llama-7B / Qwen-32B prefill shapes
+    // (M = 64..2048, weights cold in HBM): 128 x 128 tiles with 2 activation
+    // and 3 weight stages (80 KiB, two workgroups per CU) for more than one
+    // tile per CU; 128 x 128 with 3 + 3 stages (96 KiB) when every tile gets a
+    // CU of its own; below 192 tiles, 64 x 64 tiles with 4 + 4 stages, whose
+    // short K steps need the deeper lead.
     const int64_t t128 = (int64_t)((M + 127) / 128) * ((N + 127) / 128);
-    if (t128 >= 192) return launch_f8<WFMT, OUTF, 128, 128, 3>(qa, sa, qw, sw, y, M, N, K, stream);
-    return launch_f8<WFMT, OUTF, 64, 128, 3>(qa, sa, qw, sw, y, M, N, K, stream);
+    if (t128 > kCUs) return launch_f8<WFMT, OUTF, 128, 128, 2, 3>(qa, sa, qw, sw, y, M, N, K, stream);
+    if (t128 >= 192) return launch_f8<WFMT, OUTF, 128, 128, 3, 3>(qa, sa, qw, sw, y, M, N, K, stream);
+    return launch_f8<WFMT, OUTF, 64, 64, 4, 4>(qa, sa, qw, sw, y, M, N, K, stream);
 }
 
 hipError_t launch_tile_fp8(const uint8_t* qa, const float* sa, const uint8_t* qw, const float* sw,
@@ -365,12 +380,35 @@ hipError_t launch_tile_fp8(const uint8_t* qa, const float* sa, const uint8_t* qw
     return hipErrorInvalidValue;
 }
 
+template <int BM, int BN, int AST, int WST>
+hipError_t launch_n16(const uint16_t* a, const uint8_t* hi, const uint8_t* lo, uint16_t* y,
+                      int M, int N, int K, hipStream_t stream)
+{
+    auto kern = gemm_n16_kernel<BM, BN, AST, WST>;
+    constexpr size_t lds = ((size_t)AST * BM + (size_t)WST * BN) * 128;
+    static bool attr_set = false;        // idempotent host attribute, set on first use
+    if (!attr_set) {
+        const hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(kern),
+                                                 hipFuncAttributeMaxDynamicSharedMemorySize,
+                                                 (int)lds);
+        if (e != hipSuccess) return e;
+        attr_set = true;
+    }
+    const int grid = ((M + BM - 1) / BM) * ((N + BN - 1) / BN);
+    kern<<<grid, 256, lds, stream>>>(a, hi, lo, y, M, N, K);
+    return hipGetLastError();
+}
+
 hipError_t launch_tile_nested16(const uint16_t* a, const uint8_t* hi, const uint8_t* lo,
                                 uint16_t* y, int M, int N, int K, hipStream_t stream)
 {
-    gemm_nested16_tile_kernel<<<dim3(tile_grid(M, N)), dim3(kThreads), 0, stream>>>(a, hi, lo, y,
-                                                                                    M, N, K);
-    return hipGetLastError();
+    // 128 x 128 tiles (2-stage activation ring, 3-stage weight ring) from 192
+    // of them; below that 64 x 64 tiles with 4-stage rings, whose short K
+    // steps need the deeper lead (measured on the Llama-7B shapes at M = 256
+    // and 2048, weights cold in HBM)
+    const int64_t t128 = (int64_t)((M + 127) / 128) * ((N + 127) / 128);
+    if (t128 >= 192) return launch_n16<128, 128, 2, 3>(a, hi, lo, y, M, N, K, stream);
+    return launch_n16<64, 64, 4, 4>(a, hi, lo, y, M, N, K, stream);
 }
 
 }  // namespace fp8q

@@ -242,9 +242,10 @@ def test_linear_matches_quantize_then_gemm(M, N, K, dtype):
 
 
 # ------------------------------------------------------------------ big-tile path
-# The tile path uses 128x128 tiles from 192 of them (4096x4096, 2065x8292,
-# 510x8190, ...) and 64x128 tiles below (1024x2048, 500x4000); ragged M, N and
-# K (K % 128 != 0: the last step is partial) on both.
+# The tile path uses 128x128 tiles with 2+3 LDS stages above 256 tiles
+# (4096x4096, 2065x8292, ...), 128x128 with 3+3 stages from 192 to 256 tiles
+# (510x8190) and 64x64 tiles with 4+4 stages below (1024x2048, 500x4000);
+# ragged M, N and K (K % 128 != 0: the last step is partial) on all three.
 def _big_tiles(M, N):
     return -(-M // 256) * -(-N // 256)
 
@@ -252,7 +253,7 @@ def _big_tiles(M, N):
 @pytest.mark.parametrize("MK,N", [(4096, 4096), (1024, 2048)])
 def test_big_tile_identity_returns_every_weight(MK, N):
     """qa = I with M = K: y = W^T bit-exactly for every weight, on 128x128
-    tiles (4096^3) and 64x128 tiles (1024 x 2048)."""
+    tiles (4096^3) and 64x64 tiles (1024 x 2048)."""
     M = K = MK
     rng = np.random.Generator(np.random.PCG64(4096 + N))
     qw = _random_codes(rng, (N, K))
