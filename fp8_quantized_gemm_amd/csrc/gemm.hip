@@ -2,8 +2,9 @@
 //
 //  - FP8: y = out( (qa . W^T) * scale ) with E4M3 activations and E4M3 (FP8
 //    GEMM, page "C++与FP8量化" §3.3) or E5M2 (NestedFP FP8 mode, page
-//    "NestedFP双精度推理框架" §2.1) weights: gemm_f8_kernel, 128x128 or
-//    64x64 tiles by grid size (launch_tile_fmt), 16x16x128 MFMAs, operands
+//    "NestedFP双精度推理框架" §2.1) weights: gemm_f8_kernel, 256x256 or
+//    256x128 tiles with 8 waves on large grids, 128x128 or 64x64 tiles with
+//    4 waves on small ones (launch_tile_fmt), 16x16x128 MFMAs, operands
 //    moved to LDS by direct-to-LDS loads in an activation ring and a weight
 //    ring of 2-4 stages each.
 //  - NestedFP FP16 mode (same page, §2.1-§2.2): gemm_n16_kernel, 128x128 or
@@ -76,34 +77,42 @@ __device__ __forceinline__ void wait_vm()
 
 
 // ---------------------------------------------------------------- FP8 tile GEMM
-// BM x BN output tile (128 x 128, or 64 x 64 for small grids) per 256-thread
-// workgroup; the 4 waves form a 2 x 2 grid of (BM/2) x (BN/2) wave tiles of
-// 16x16x128 MFMAs, so each fragment read from LDS feeds BM/32 or BN/32
-// MFMAs.  K advances 128 bytes per step.  Both operands reach LDS through
-// direct global->LDS loads (buffer_load ... lds: no register staging, no LDS
-// store instructions), in two rings: the activation tile (small, reused by
-// every weight panel, L2-resident) has AST stages, the weight tile (streamed
-// from HBM) WST >= AST stages, so its loads are issued WST - 1 steps ahead.  Within a step the wave holds its A
-// fragments and double-buffers the W fragments column by column.  LDS rows
-// are 128 bytes, unit u of row r stored at position u ^ (r & 7), so the 16
-// lanes reading one unit of 16 consecutive rows hit distinct banks; a DMA
+// BM x BN output tile per workgroup of WM x WN waves, each wave owning a
+// (BM/WM) x (BN/WN) block of 16x16x128 MFMA tiles.  K advances 128 bytes per
+// step.  Both operands reach LDS through direct global->LDS loads
+// (buffer_load ... lds: no register staging, no LDS store instructions), in
+// two rings: the activation tile (reused by every weight panel, L2-resident)
+// has AST stages, the weight tile (streamed from HBM) WST >= AST stages, so
+// its loads are issued WST - 1 steps ahead.  Within a step the wave keeps the
+// fragments of the operand it has fewer of and streams the other one,
+// double-buffered, so every streamed fragment feeds min(FM, FN) MFMAs.  LDS
+// rows are 128 bytes, unit u of row r stored at position u ^ (r & 7), so the
+// 16 lanes reading one unit of 16 consecutive rows hit distinct banks; a DMA
 // load writes lane l's 16 bytes to slot l of a 1 KiB block (8 rows), so each
-// lane fetches the global unit that belongs in its slot.  For 128 x 128 tiles
-// that is 80 KiB of LDS: two workgroups per CU.  Loads past the last step are
-// still issued (with out-of-range offsets: zeros into a free stage) so the
-// wait counts are the same every step.
-template <int WFMT, int OUTF, int BM, int BN, int AST, int WST>
-__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2)))
+// lane fetches the global unit that belongs in its slot.  Loads past the last
+// step are still issued (with out-of-range offsets: zeros into a free stage)
+// so the wait counts are the same every step.
+//
+// The weight fragment is the MFMA's first operand, so a lane's four results
+// are four consecutive output columns of one row: one 8-byte store each.
+//
+// Shapes in use (launch_tile_fmt): 256 x 256 and 256 x 128 tiles with 8
+// waves (one workgroup per CU, 128 / 160 KiB of LDS), 128 x 128 and 64 x 64
+// tiles with 4 waves for grids too small to fill the chip with the big ones.
+template <int WFMT, int OUTF, int BM, int BN, int WM, int WN, int AST, int WST>
+__global__ __launch_bounds__(WM * WN * 64) __attribute__((amdgpu_waves_per_eu(2)))
 void gemm_f8_kernel(
     const uint8_t* __restrict__ qa, const float* __restrict__ sa,
     const uint8_t* __restrict__ qw, const float* __restrict__ sw,
     uint16_t* __restrict__ y, int M, int N, int K)
 {
+    constexpr int NW = WM * WN;
     constexpr int BK = 128;
-    constexpr int TM = BM / 2, TN = BN / 2;
+    constexpr int TM = BM / WM, TN = BN / WN;
     constexpr int FM = TM / 16, FN = TN / 16;
     constexpr int ASTAGE = BM * BK, WSTAGE = BN * BK;
-    constexpr int ABPW = BM / 32, WBPW = BN / 32;     // 1 KiB DMA blocks per wave per step
+    constexpr int ABPW = BM / 8 / NW, WBPW = BN / 8 / NW;   // 1 KiB DMA blocks per wave per step
+    static_assert(ABPW * 8 * NW == BM && WBPW * 8 * NW == BN, "whole DMA blocks per wave");
     static_assert(AST >= 2 && WST >= AST, "ring depths");
     constexpr int ALLOW = (AST < WST ? WBPW : 0) + (AST - 2) * (ABPW + WBPW);
     extern __shared__ __attribute__((aligned(16))) uint8_t lds[];
@@ -113,7 +122,7 @@ void gemm_f8_kernel(
     const int tid = threadIdx.x;
     const int lane = tid & 63;
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
-    const int wm = wave >> 1, wn = wave & 1;
+    const int wm = wave / WN, wn = wave % WN;
     const int r = lane & 15, g = lane >> 4;
 
     const int tiles_m = (M + BM - 1) / BM;
@@ -168,27 +177,40 @@ void gemm_f8_kernel(
     for (int kt = 0; kt < nk; ++kt) {
         const uint8_t* As = a_lds + (kt % AST) * ASTAGE;
         const uint8_t* Ws = w_lds + (kt % WST) * WSTAGE;
-        v8i af[FM];
-#pragma unroll
-        for (int i = 0; i < FM; ++i) {
-            const int row = wm * TM + i * 16 + r;
-            af[i] = cat(*reinterpret_cast<const v4i*>(As + swz128(row, g)),
-                        *reinterpret_cast<const v4i*>(As + swz128(row, g + 4)));
-        }
-        v8i wf[2];
-        auto read_w = [&](int j, v8i& f) {
-            const int row = wn * TN + j * 16 + r;
-            f = cat(*reinterpret_cast<const v4i*>(Ws + swz128(row, g)),
-                    *reinterpret_cast<const v4i*>(Ws + swz128(row, g + 4)));
+        auto frag = [&](const uint8_t* S, int row) {
+            return cat(*reinterpret_cast<const v4i*>(S + swz128(row, g)),
+                       *reinterpret_cast<const v4i*>(S + swz128(row, g + 4)));
         };
-        read_w(0, wf[0]);
+        if constexpr (FN <= FM) {
+            // keep the FN weight fragments, stream the activation fragments
+            v8i wf[FN];
 #pragma unroll
-        for (int j = 0; j < FN; ++j) {
-            if (j + 1 < FN) read_w(j + 1, wf[(j + 1) & 1]);
+            for (int j = 0; j < FN; ++j) wf[j] = frag(Ws, wn * TN + j * 16 + r);
+            v8i af[2];
+            af[0] = frag(As, wm * TM + r);
 #pragma unroll
-            for (int i = 0; i < FM; ++i)
-                acc[i][j] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(
-                    af[i], wf[j & 1], acc[i][j], WF_E4M3, WFMT, 0, 0, 0, 0);
+            for (int i = 0; i < FM; ++i) {
+                if (i + 1 < FM) af[(i + 1) & 1] = frag(As, wm * TM + (i + 1) * 16 + r);
+#pragma unroll
+                for (int j = 0; j < FN; ++j)
+                    acc[i][j] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(
+                        wf[j], af[i & 1], acc[i][j], WFMT, WF_E4M3, 0, 0, 0, 0);
+            }
+        } else {
+            // keep the FM activation fragments, stream the weight fragments
+            v8i af[FM];
+#pragma unroll
+            for (int i = 0; i < FM; ++i) af[i] = frag(As, wm * TM + i * 16 + r);
+            v8i wf[2];
+            wf[0] = frag(Ws, wn * TN + r);
+#pragma unroll
+            for (int j = 0; j < FN; ++j) {
+                if (j + 1 < FN) wf[(j + 1) & 1] = frag(Ws, wn * TN + (j + 1) * 16 + r);
+#pragma unroll
+                for (int i = 0; i < FM; ++i)
+                    acc[i][j] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(
+                        wf[j & 1], af[i], acc[i][j], WFMT, WF_E4M3, 0, 0, 0, 0);
+            }
         }
         wait_vm<ALLOW>();
         __syncthreads();                       // stage k of both rings is free
@@ -199,7 +221,30 @@ void gemm_f8_kernel(
 
     float s = *sa;
     if (sw != nullptr) s = s * *sw;
-    store_tile<OUTF, FM, FN>(y, acc, s, M, N, m0 + wm * TM, n0 + wn * TN, r, g);
+    // acc[i][j][e] is output row mb + 16 i + r, column nb + 16 j + 4 g + e
+    const int mb = m0 + wm * TM, nb = n0 + wn * TN;
+    const bool vec = (N & 3) == 0;             // 8-byte aligned groups of 4 columns
+#pragma unroll
+    for (int i = 0; i < FM; ++i) {
+        const int m = mb + i * 16 + r;
+        if (m >= M) continue;
+#pragma unroll
+        for (int j = 0; j < FN; ++j) {
+            const int n = nb + j * 16 + 4 * g;
+            uint16_t* dst = y + (size_t)m * N + n;
+            if (vec && n + 3 < N) {
+                const uint32_t lo = f32_to_out_bits<OUTF>(acc[i][j][0] * s) |
+                                    (f32_to_out_bits<OUTF>(acc[i][j][1] * s) << 16);
+                const uint32_t hi = f32_to_out_bits<OUTF>(acc[i][j][2] * s) |
+                                    (f32_to_out_bits<OUTF>(acc[i][j][3] * s) << 16);
+                *reinterpret_cast<v2i*>(dst) = v2i{(int)lo, (int)hi};
+            } else {
+#pragma unroll
+                for (int e = 0; e < 4; ++e)
+                    if (n + e < N) dst[e] = (uint16_t)f32_to_out_bits<OUTF>(acc[i][j][e] * s);
+            }
+        }
+    }
 }
 
 // ---------------------------------------------------------------- NestedFP FP16 GEMM, DMA rings
@@ -334,12 +379,13 @@ void gemm_n16_kernel(const uint16_t* __restrict__ a, const uint8_t* __restrict__
 
 }  // namespace
 
-template <int WFMT, int OUTF, int BM, int BN, int AST, int WST>
+template <int WFMT, int OUTF, int BM, int BN, int WM, int WN, int AST, int WST>
 hipError_t launch_f8(const uint8_t* qa, const float* sa, const uint8_t* qw, const float* sw,
                      uint16_t* y, int M, int N, int K, hipStream_t stream)
 {
-    auto kern = gemm_f8_kernel<WFMT, OUTF, BM, BN, AST, WST>;
+    auto kern = gemm_f8_kernel<WFMT, OUTF, BM, BN, WM, WN, AST, WST>;
     constexpr size_t lds = ((size_t)AST * BM + (size_t)WST * BN) * 128;
+    static_assert(lds <= 160 * 1024, "LDS of one CU");
     static bool attr_set = false;        // idempotent host attribute, set on first use
     if (!attr_set) {
         const hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(kern),
@@ -349,7 +395,7 @@ hipError_t launch_f8(const uint8_t* qa, const float* sa, const uint8_t* qw, cons
         attr_set = true;
     }
     const int grid = ((M + BM - 1) / BM) * ((N + BN - 1) / BN);
-    kern<<<grid, 256, lds, stream>>>(qa, sa, qw, sw, y, M, N, K);
+    kern<<<grid, WM * WN * 64, lds, stream>>>(qa, sa, qw, sw, y, M, N, K);
     return hipGetLastError();
 }
 
@@ -358,15 +404,28 @@ hipError_t launch_tile_fmt(const uint8_t* qa, const float* sa, const uint8_t* qw
                            uint16_t* y, int M, int N, int K, hipStream_t stream)
 {
     // From measurements on MI355X over the Llama-7B / Qwen-32B prefill shapes
-    // (M = 64..2048, weights cold in HBM): 128 x 128 tiles with 2 activation
-    // and 3 weight stages (80 KiB, two workgroups per CU) for more than one
-    // tile per CU; 128 x 128 with 3 + 3 stages (96 KiB) when every tile gets a
-    // CU of its own; below 192 tiles, 64 x 64 tiles with 4 + 4 stages, whose
-    // short K steps need the deeper lead.
+    // (M = 64..4096, weights cold in HBM).  From M = 256 and with at least
+    // 128 tiles of 256 x 128 the 8-wave kernels run one workgroup per CU; a 256 x 256 tile
+    // does the work of two 256 x 128 tiles in about 1.64 times the time, so
+    // it wins where it needs fewer rounds of 256 workgroups by that margin.
+    // Smaller grids keep 4-wave tiles: 128 x 128 with 2 activation and 3
+    // weight stages (two workgroups per CU) for more than one tile per CU,
+    // 3 + 3 stages when every tile gets a CU of its own, and below 192 of
+    // them 64 x 64 tiles with 4 + 4 stages, whose short K steps need the
+    // deeper lead.
+    const int64_t tm256 = (M + 255) / 256;
+    const int64_t t_256x128 = tm256 * ((N + 127) / 128);
+    if (M >= 256 && t_256x128 >= 128) {
+        const int64_t rounds_128 = (t_256x128 + kCUs - 1) / kCUs;
+        const int64_t rounds_256 = (tm256 * ((N + 255) / 256) + kCUs - 1) / kCUs;
+        if (rounds_256 * 164 < rounds_128 * 100)
+            return launch_f8<WFMT, OUTF, 256, 256, 2, 4, 2, 2>(qa, sa, qw, sw, y, M, N, K, stream);
+        return launch_f8<WFMT, OUTF, 256, 128, 4, 2, 3, 4>(qa, sa, qw, sw, y, M, N, K, stream);
+    }
     const int64_t t128 = (int64_t)((M + 127) / 128) * ((N + 127) / 128);
-    if (t128 > kCUs) return launch_f8<WFMT, OUTF, 128, 128, 2, 3>(qa, sa, qw, sw, y, M, N, K, stream);
-    if (t128 >= 192) return launch_f8<WFMT, OUTF, 128, 128, 3, 3>(qa, sa, qw, sw, y, M, N, K, stream);
-    return launch_f8<WFMT, OUTF, 64, 64, 4, 4>(qa, sa, qw, sw, y, M, N, K, stream);
+    if (t128 > kCUs) return launch_f8<WFMT, OUTF, 128, 128, 2, 2, 2, 3>(qa, sa, qw, sw, y, M, N, K, stream);
+    if (t128 >= 192) return launch_f8<WFMT, OUTF, 128, 128, 2, 2, 3, 3>(qa, sa, qw, sw, y, M, N, K, stream);
+    return launch_f8<WFMT, OUTF, 64, 64, 2, 2, 4, 4>(qa, sa, qw, sw, y, M, N, K, stream);
 }
 
 hipError_t launch_tile_fp8(const uint8_t* qa, const float* sa, const uint8_t* qw, const float* sw,
