@@ -2,9 +2,9 @@
 //
 //  - FP8: y = out( (qa . W^T) * scale ) with E4M3 activations and E4M3 (FP8
 //    GEMM, page "C++与FP8量化" §3.3) or E5M2 (NestedFP FP8 mode, page
-//    "NestedFP双精度推理框架" §2.1) weights: gemm_f8_kernel, 256x256 or
-//    256x128 tiles with 8 waves on large grids, 128x128 or 64x64 tiles with
-//    4 waves on small ones (launch_tile_fmt), 16x16x128 MFMAs, operands
+//    "NestedFP双精度推理框架" §2.1) weights: gemm_f8_kernel, tiles from
+//    256x256 (8 waves) down to 64x64 (4 waves) picked per shape by the cost
+//    of their rounds of workgroups (pick_tile_shape), 16x16x128 MFMAs, operands
 //    moved to LDS by direct-to-LDS loads in an activation ring and a weight
 //    ring of 2-4 stages each.
 //  - NestedFP FP16 mode (same page, §2.1-§2.2): gemm_n16_kernel, 128x128 or
@@ -96,9 +96,7 @@ __device__ __forceinline__ void wait_vm()
 // The weight fragment is the MFMA's first operand, so a lane's four results
 // are four consecutive output columns of one row: one 8-byte store each.
 //
-// Shapes in use (launch_tile_fmt): 256 x 256 and 256 x 128 tiles with 8
-// waves (one workgroup per CU, 128 / 160 KiB of LDS), 128 x 128 and 64 x 64
-// tiles with 4 waves for grids too small to fill the chip with the big ones.
+// Shapes in use: kTileShapes, chosen per call by pick_tile_shape.
 template <int WFMT, int OUTF, int BM, int BN, int WM, int WN, int AST, int WST>
 __global__ __launch_bounds__(WM * WN * 64) __attribute__((amdgpu_waves_per_eu(2)))
 void gemm_f8_kernel(
@@ -399,33 +397,51 @@ hipError_t launch_f8(const uint8_t* qa, const float* sa, const uint8_t* qw, cons
     return hipGetLastError();
 }
 
+// Tile shapes of the FP8 GEMM and the measured time of one round of their
+// workgroups (one per CU; two per CU for 64 x 64) at K = 4096 on MI355X,
+// weights cold in HBM, medians over the Llama-7B / Qwen-32B prefill shapes.
+struct TileShape { int bm, bn, per_cu; float round_us; };
+constexpr TileShape kTileShapes[] = {
+    {256, 256, 1, 55.8f},   // 8 waves of 128 x 64, 2 + 2 stages (128 KiB)
+    {256, 192, 1, 45.3f},   // 8 waves of 128 x 48, 2 + 3 stages (136 KiB)
+    {256, 128, 1, 33.9f},   // 8 waves of  64 x 64, 3 + 4 stages (160 KiB)
+    {128, 192, 1, 29.6f},   // 8 waves of  64 x 48, 3 + 4 stages (144 KiB)
+    {128, 128, 1, 22.9f},   // 8 waves of  64 x 32, 4 + 4 stages (128 KiB)
+    {128,  64, 1, 16.5f},   // 4 waves of  64 x 32, 4 + 4 stages ( 96 KiB)
+    { 64,  64, 2, 17.0f},   // 4 waves of  32 x 32, 4 + 4 stages ( 64 KiB)
+};
+
+// The shape whose rounds of workgroups cost least; tiles may not be taller
+// than M rounded up to 64 rows.
+inline int pick_tile_shape(int M, int N)
+{
+    const int64_t mcap = ((int64_t)M + 63) / 64 * 64;
+    int best = -1;
+    float best_us = 0.f;
+    for (int i = 0; i < (int)(sizeof(kTileShapes) / sizeof(kTileShapes[0])); ++i) {
+        const TileShape& t = kTileShapes[i];
+        if (t.bm > mcap) continue;
+        const int64_t tiles = (((int64_t)M + t.bm - 1) / t.bm) * (((int64_t)N + t.bn - 1) / t.bn);
+        const int64_t slots = (int64_t)kCUs * t.per_cu;
+        const float us = (float)((tiles + slots - 1) / slots) * t.round_us;
+        if (best < 0 || us < best_us) { best = i; best_us = us; }
+    }
+    return best;
+}
+
 template <int WFMT, int OUTF>
 hipError_t launch_tile_fmt(const uint8_t* qa, const float* sa, const uint8_t* qw, const float* sw,
                            uint16_t* y, int M, int N, int K, hipStream_t stream)
 {
-    // From measurements on MI355X over the Llama-7B / Qwen-32B prefill shapes
-    // (M = 64..4096, weights cold in HBM).  From M = 256 and with at least
-    // 128 tiles of 256 x 128 the 8-wave kernels run one workgroup per CU; a 256 x 256 tile
-    // does the work of two 256 x 128 tiles in about 1.64 times the time, so
-    // it wins where it needs fewer rounds of 256 workgroups by that margin.
-    // Smaller grids keep 4-wave tiles: 128 x 128 with 2 activation and 3
-    // weight stages (two workgroups per CU) for more than one tile per CU,
-    // 3 + 3 stages when every tile gets a CU of its own, and below 192 of
-    // them 64 x 64 tiles with 4 + 4 stages, whose short K steps need the
-    // deeper lead.
-    const int64_t tm256 = (M + 255) / 256;
-    const int64_t t_256x128 = tm256 * ((N + 127) / 128);
-    if (M >= 256 && t_256x128 >= 128) {
-        const int64_t rounds_128 = (t_256x128 + kCUs - 1) / kCUs;
-        const int64_t rounds_256 = (tm256 * ((N + 255) / 256) + kCUs - 1) / kCUs;
-        if (rounds_256 * 164 < rounds_128 * 100)
-            return launch_f8<WFMT, OUTF, 256, 256, 2, 4, 2, 2>(qa, sa, qw, sw, y, M, N, K, stream);
-        return launch_f8<WFMT, OUTF, 256, 128, 4, 2, 3, 4>(qa, sa, qw, sw, y, M, N, K, stream);
+    switch (pick_tile_shape(M, N)) {
+    case 0: return launch_f8<WFMT, OUTF, 256, 256, 2, 4, 2, 2>(qa, sa, qw, sw, y, M, N, K, stream);
+    case 1: return launch_f8<WFMT, OUTF, 256, 192, 2, 4, 2, 3>(qa, sa, qw, sw, y, M, N, K, stream);
+    case 2: return launch_f8<WFMT, OUTF, 256, 128, 4, 2, 3, 4>(qa, sa, qw, sw, y, M, N, K, stream);
+    case 3: return launch_f8<WFMT, OUTF, 128, 192, 2, 4, 3, 4>(qa, sa, qw, sw, y, M, N, K, stream);
+    case 4: return launch_f8<WFMT, OUTF, 128, 128, 2, 4, 4, 4>(qa, sa, qw, sw, y, M, N, K, stream);
+    case 5: return launch_f8<WFMT, OUTF, 128, 64, 2, 2, 4, 4>(qa, sa, qw, sw, y, M, N, K, stream);
+    default: return launch_f8<WFMT, OUTF, 64, 64, 2, 2, 4, 4>(qa, sa, qw, sw, y, M, N, K, stream);
     }
-    const int64_t t128 = (int64_t)((M + 127) / 128) * ((N + 127) / 128);
-    if (t128 > kCUs) return launch_f8<WFMT, OUTF, 128, 128, 2, 2, 2, 3>(qa, sa, qw, sw, y, M, N, K, stream);
-    if (t128 >= 192) return launch_f8<WFMT, OUTF, 128, 128, 2, 2, 3, 3>(qa, sa, qw, sw, y, M, N, K, stream);
-    return launch_f8<WFMT, OUTF, 64, 64, 2, 2, 4, 4>(qa, sa, qw, sw, y, M, N, K, stream);
 }
 
 hipError_t launch_tile_fp8(const uint8_t* qa, const float* sa, const uint8_t* qw, const float* sw,

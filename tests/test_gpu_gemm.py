@@ -242,12 +242,12 @@ def test_linear_matches_quantize_then_gemm(M, N, K, dtype):
 
 
 # ------------------------------------------------------------------ big-tile path
-# Tile kernels by shape: 256x256 tiles with 8 waves (4096x4096, 4100x12300),
-# 256x128 tiles with 8 waves (2065x8292, 4096x4100, 2040x4090, 510x8190),
-# 128x128 tiles with 2+3 stages (200x22000), 128x128 with 3+3 stages
-# (639x5370) and 64x64 tiles with 4+4 stages (1024x2048, 500x4000); ragged M,
-# N (N % 4 != 0 takes the 2-byte stores) and K (K % 128 != 0: the last step
-# is partial) on each of them.
+# The tile shape is picked per call from the cost of its rounds of
+# workgroups: 256x256 (4096x4096, 4100x12300), 256x192 (2000x12000,
+# 1000x10000), 256x128 (2040x4090, 1024x8192), 128x192 (2065x8292, 4096x4100,
+# 200x22000), 128x128 with 8 waves (510x8190, 639x5370), 128x64 (500x4000,
+# 1024x2048) and 64x64 (60x5000); ragged M, N (N % 4 != 0 takes the 2-byte
+# stores) and K (K % 128 != 0: the last step is partial) on each of them.
 def _big_tiles(M, N):
     return -(-M // 256) * -(-N // 256)
 
@@ -255,7 +255,7 @@ def _big_tiles(M, N):
 @pytest.mark.parametrize("MK,N", [(4096, 4096), (1024, 8192), (1024, 2048)])
 def test_big_tile_identity_returns_every_weight(MK, N):
     """qa = I with M = K: y = W^T bit-exactly for every weight, on 256x256
-    tiles (4096^3), 256x128 tiles (1024 x 8192) and 64x64 tiles (1024 x 2048)."""
+    tiles (4096^3), 256x128 tiles (1024 x 8192) and 128x64 tiles (1024 x 2048)."""
     M = K = MK
     rng = np.random.Generator(np.random.PCG64(4096 + N))
     qw = _random_codes(rng, (N, K))
@@ -265,8 +265,9 @@ def test_big_tile_identity_returns_every_weight(MK, N):
     assert np.array_equal(y, want.T)
 
 
-@pytest.mark.parametrize("M,N,K", [(4096, 4096, 80), (4100, 12300, 48), (510, 8190, 80),
-                                   (200, 22000, 48), (639, 5370, 80), (500, 4000, 48)])
+@pytest.mark.parametrize("M,N,K", [(4096, 4096, 80), (4100, 12300, 48), (2000, 12000, 80),
+                                   (2040, 4090, 48), (510, 8190, 80), (200, 22000, 48),
+                                   (639, 5370, 80), (500, 4000, 48), (60, 5000, 80)])
 def test_big_tile_small_integers_bit_exact(M, N, K):
     """Small integers through every tile kernel; K = 80 and 48 leave a
     partial K step (out-of-range units read as zero)."""
@@ -279,8 +280,9 @@ def test_big_tile_small_integers_bit_exact(M, N, K):
 
 
 @pytest.mark.parametrize("M,N,K", [(2065, 8292, 4112), (4096, 4100, 272), (2040, 4090, 4112),
-                                   (4100, 12300, 272), (510, 8190, 1040), (200, 22000, 1040),
-                                   (639, 5370, 4112), (500, 4000, 1040)])
+                                   (4100, 12300, 272), (1000, 10000, 1040), (510, 8190, 1040),
+                                   (200, 22000, 1040), (639, 5370, 4112), (500, 4000, 1040),
+                                   (60, 5000, 4112)])
 def test_big_tile_random_ragged_sampled(M, N, K):
     """Ragged M, N and K on both tile kernels; every output of 3 rows and 3
     columns plus 512 random pairs against the fp64 checker."""
