@@ -58,6 +58,9 @@ def parse():
                         "one captured HIP graph")
     p.add_argument("--cpu-seconds", type=float, default=10.0,
                    help="lower bound on the oracle's timed CPU work")
+    p.add_argument("--only-prefill", action="store_true",
+                   help="run only the prefill figures (M = 512, 2048) and print them: the "
+                        "command that the prefill GEMM's rocprofv3 summaries are taken on")
     p.add_argument("--copy-calibration-mib", type=int, default=0, metavar="MIB",
                    help="instead of the benchmark, run 5 launches of a plain elementwise "
                         "copy (read MIB MiB, write MIB MiB) so that HBM byte counters "
@@ -217,11 +220,11 @@ def cpu_baseline(torch, synth, dev, seconds):
                       f"{el:.1f} s of CPU work; same algorithmic bytes as the GPU metric"}
 
 
-def secondary(torch, fp8q, synth, model1, dev):
+def secondary(torch, fp8q, synth, model1, dev, parts=("decode", "prefill", "nested"), graph=True):
     """Prefill, M = 4/8 decode and NestedFP figures (a few steps each)."""
     out = {}
     # decode at M = 4, 8 on the same weights (activations re-drawn)
-    for M in (4, 8):
+    for M in ((4, 8) if "decode" in parts else ()):
         mm = Model.__new__(Model)
         mm.M = M
         mm.linears = []
@@ -240,7 +243,7 @@ def secondary(torch, fp8q, synth, model1, dev):
                                "ms_per_step": round(dt * 1e3, 3)}
         progress(f"decode M={M} done")
     # prefill M = 512, 2048 (activations with 0.1% outlier channels x50)
-    for M in (512, 2048):
+    for M in ((512, 2048) if "prefill" in parts else ()):
         mm = Model.__new__(Model)
         mm.M = M
         mm.linears = []
@@ -252,9 +255,9 @@ def secondary(torch, fp8q, synth, model1, dev):
             d["q"] = torch.empty((M, K), dtype=torch.uint8, device=dev)
             d["y"] = torch.empty((M, N), dtype=torch.bfloat16, device=dev)
             mm.linears.append(d)
-        dt, _ = time_steps(torch, fp8q, mm, steps=3, warmup=1)
+        dt, _ = time_steps(torch, fp8q, mm, steps=3, warmup=1, graph=graph)
         # the GEMM alone, on the codes and scales the timed steps left behind
-        _, gdev = time_steps(torch, fp8q, mm, steps=3, warmup=1, call=gemm_call)
+        _, gdev = time_steps(torch, fp8q, mm, steps=3, warmup=1, graph=graph, call=gemm_call)
         kern = gdev / len(mm.linears)
         fl = sum(mm.flops(L) for L in mm.linears)
         out[f"prefill_m{M}"] = {"TFLOP_per_s": round(fl / dt / 1e12, 1),
@@ -263,6 +266,8 @@ def secondary(torch, fp8q, synth, model1, dev):
                                 "ms_per_step": round(dt * 1e3, 3)}
         progress(f"prefill M={M} done")
         del mm
+    if "nested" not in parts:
+        return out
     # NestedFP at M = 1 and 256 on 8 layers of fp16 weights (hi/lo planes)
     nested = []
     for layer in range(8):
@@ -340,6 +345,10 @@ def main():
     torch.cuda.set_device(0)
     model = Model(torch, fp8q, synth, M=1, dev=dev)
     progress("decode model built (128 E4M3 weight matrices)")
+    if args.only_prefill:
+        print(json.dumps({"prefill": secondary(torch, fp8q, synth, model, dev, parts=("prefill",),
+                                               graph=not args.eager)}), flush=True)
+        return
     graph = not args.eager
     dt, dev_step = time_steps(torch, fp8q, model, args.steps, args.warmup, graph=graph)
     step_bytes = sum(model.gemm_bytes(L) + model.quant_bytes(L) for L in model.linears)
