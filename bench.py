@@ -291,8 +291,7 @@ def secondary(torch, fp8q, synth, model1, dev, parts=("decode", "prefill", "nest
 
         def step8():
             for (K, N, hi, lo), (a, q, s, am, y) in zip(nested, bufs):
-                fp8q.fp8_quantize_act(a, q, s, am)
-                fp8q.nested_gemm_fp8(q, s, hi, y)
+                fp8q.nested_linear_fp8(a, hi, y, q, s, am)
 
         for mode, fn, wbytes in (("fp16", step16, 2), ("fp8", step8, 1)):
             dt, _ = time_fn(torch, fn, steps=5, warmup=2)

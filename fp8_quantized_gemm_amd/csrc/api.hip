@@ -93,6 +93,26 @@ hipError_t dispatch_fp8(const uint8_t* qa, const float* sa, const uint8_t* qw, c
         if (s_ != FP8Q_OK) return s_;      \
     } while (0)
 
+// quantize + GEMM of fp8_linear / nested_linear_fp8 (pointers already checked)
+fp8q_status linear_common(const char* where, const void* x, int dtype, const uint8_t* qw,
+                          const float* sw, uint16_t* y, uint8_t* q, float* scale, float* amax,
+                          int64_t M, int64_t N, int64_t K, int wfmt, int outf, hipStream_t st)
+{
+    if (M <= kRowkMaxM && M * K <= kFusedMaxMK)
+        return finish(where, launch_linear_fused(x, dtype, qw, sw, y, q, scale, amax, (int)M,
+                                                 (int)N, (int)K, wfmt, outf, st));
+    // y is written only by the GEMM, so until then it can hold the
+    // quantizer's per-workgroup partial maxima (unless it overlaps x)
+    const uintptr_t xb = reinterpret_cast<uintptr_t>(x), yb = reinterpret_cast<uintptr_t>(y);
+    const bool y_free = yb + (uintptr_t)(M * N * 2) <= xb || xb + (uintptr_t)(M * K * 2) <= yb;
+    hipError_t e = launch_quantize_scratch(x, dtype, M * K, q, scale, amax,
+                                           y_free ? reinterpret_cast<float*>(y) : nullptr,
+                                           M * N / 2, st);
+    if (e == hipSuccess)
+        e = dispatch_fp8(q, scale, qw, sw, y, (int)M, (int)N, (int)K, wfmt, outf, st);
+    return finish(where, e);
+}
+
 }  // namespace
 
 extern "C" {
@@ -150,20 +170,22 @@ fp8q_status fp8_linear(const void* x, int dtype, const uint8_t* qw, const float*
         !aligned4(scale) || !aligned4(amax))
         return FP8Q_ERR_ALIGN;
     FP8Q_TRY(check_device());
-    hipStream_t st = (hipStream_t)stream;
-    if (M <= kRowkMaxM && M * K <= kFusedMaxMK)
-        return finish("fp8_linear", launch_linear_fused(x, dtype, qw, sw, y, q, scale, amax,
-                                                        (int)M, (int)N, (int)K, st));
-    // y is written only by the GEMM, so until then it can hold the
-    // quantizer's per-workgroup partial maxima (unless it overlaps x)
-    const uintptr_t xb = reinterpret_cast<uintptr_t>(x), yb = reinterpret_cast<uintptr_t>(y);
-    const bool y_free = yb + (uintptr_t)(M * N * 2) <= xb || xb + (uintptr_t)(M * K * 2) <= yb;
-    hipError_t e = launch_quantize_scratch(x, dtype, M * K, q, scale, amax,
-                                           y_free ? reinterpret_cast<float*>(y) : nullptr,
-                                           M * N / 2, st);
-    if (e == hipSuccess)
-        e = dispatch_fp8(q, scale, qw, sw, y, (int)M, (int)N, (int)K, WF_E4M3, OUT_BF16, st);
-    return finish("fp8_linear", e);
+    return linear_common("fp8_linear", x, dtype, qw, sw, y, q, scale, amax, M, N, K, WF_E4M3,
+                         OUT_BF16, (hipStream_t)stream);
+}
+
+fp8q_status nested_linear_fp8(const uint16_t* a, const uint8_t* hi, uint16_t* y, uint8_t* q,
+                              float* scale, float* amax, int64_t M, int64_t N, int64_t K,
+                              fp8q_stream stream)
+{
+    if (!a || !hi || !y || !q || !scale || !amax) return FP8Q_ERR_NULL;
+    FP8Q_TRY(check_gemm_sizes(M, N, K));
+    if (!aligned16(a) || !aligned16(hi) || !aligned16(y) || !aligned16(q) || !aligned4(scale) ||
+        !aligned4(amax))
+        return FP8Q_ERR_ALIGN;
+    FP8Q_TRY(check_device());
+    return linear_common("nested_linear_fp8", a, FP8Q_FP16, hi, nullptr, y, q, scale, amax, M, N,
+                         K, WF_E5M2, OUT_FP16, (hipStream_t)stream);
 }
 
 fp8q_status nested_split(const uint16_t* w, uint8_t* hi, uint8_t* lo, int64_t n,

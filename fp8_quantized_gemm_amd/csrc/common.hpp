@@ -308,7 +308,7 @@ hipError_t launch_rowk_nested16(const uint16_t* a, const uint8_t* hi, const uint
                                 uint16_t* y, int M, int N, int K, hipStream_t stream);
 hipError_t launch_linear_fused(const void* x, int dtype, const uint8_t* qw, const float* sw,
                                uint16_t* y, uint8_t* q, float* scale, float* amax, int M, int N,
-                               int K, hipStream_t stream);
+                               int K, int wfmt, int outf, hipStream_t stream);
 hipError_t launch_e4m3_encode_f32(const float* v, uint8_t* q, int64_t n, hipStream_t stream);
 
 // Decode path (M <= 16) and tile path (M > 16) of the FP8 GEMM; wfmt selects

@@ -398,8 +398,10 @@ hipError_t launch_f8(const uint8_t* qa, const float* sa, const uint8_t* qw, cons
 }
 
 // Tile shapes of the FP8 GEMM and the measured time of one round of their
-// workgroups (one per CU; two per CU for 64 x 64) at K = 4096 on MI355X,
+// workgroups (one per CU, or two per CU for 64 x 64) at K = 4096 on MI355X,
 // weights cold in HBM, medians over the Llama-7B / Qwen-32B prefill shapes.
+// 64 x 64 appears twice: a grid of at most one workgroup per CU finishes its
+// round much sooner than a full one.
 struct TileShape { int bm, bn, per_cu; float round_us; };
 constexpr TileShape kTileShapes[] = {
     {256, 256, 1, 55.8f},   // 8 waves of 128 x 64, 2 + 2 stages (128 KiB)
@@ -409,6 +411,7 @@ constexpr TileShape kTileShapes[] = {
     {128, 128, 1, 22.9f},   // 8 waves of  64 x 32, 4 + 4 stages (128 KiB)
     {128,  64, 1, 16.5f},   // 4 waves of  64 x 32, 4 + 4 stages ( 96 KiB)
     { 64,  64, 2, 17.0f},   // 4 waves of  32 x 32, 4 + 4 stages ( 64 KiB)
+    { 64,  64, 1, 10.2f},   // the same kernel, one workgroup per CU
 };
 
 // The shape whose rounds of workgroups cost least; tiles may not be taller

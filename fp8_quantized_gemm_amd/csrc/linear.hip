@@ -379,18 +379,26 @@ hipError_t launch_rowk_nested16(const uint16_t* a, const uint8_t* hi, const uint
 
 hipError_t launch_linear_fused(const void* x, int dtype, const uint8_t* qw, const float* sw,
                                uint16_t* y, uint8_t* q, float* scale, float* amax, int M, int N,
-                               int K, hipStream_t stream)
+                               int K, int wfmt, int outf, hipStream_t stream)
 {
-    if (dtype == DT_BF16) {
+    if (wfmt == WF_E4M3 && outf == OUT_BF16 && dtype == DT_BF16) {
         if (M == 1)
             launch_rowk<WF_E4M3, OUT_BF16, AS_BF16, 1>(x, nullptr, qw, sw, y, q, scale, amax, N, K, stream);
         else
             launch_rowk<WF_E4M3, OUT_BF16, AS_BF16, 2>(x, nullptr, qw, sw, y, q, scale, amax, N, K, stream);
-    } else {
+    } else if (wfmt == WF_E4M3 && outf == OUT_BF16 && dtype == DT_FP16) {
         if (M == 1)
             launch_rowk<WF_E4M3, OUT_BF16, AS_FP16, 1>(x, nullptr, qw, sw, y, q, scale, amax, N, K, stream);
         else
             launch_rowk<WF_E4M3, OUT_BF16, AS_FP16, 2>(x, nullptr, qw, sw, y, q, scale, amax, N, K, stream);
+    } else if (wfmt == WF_E5M2 && outf == OUT_FP16 && dtype == DT_FP16) {
+        // NestedFP FP8 mode: fp16 activation, hi plane as E5M2, no weight scale
+        if (M == 1)
+            launch_rowk<WF_E5M2, OUT_FP16, AS_FP16, 1>(x, nullptr, qw, sw, y, q, scale, amax, N, K, stream);
+        else
+            launch_rowk<WF_E5M2, OUT_FP16, AS_FP16, 2>(x, nullptr, qw, sw, y, q, scale, amax, N, K, stream);
+    } else {
+        return hipErrorInvalidValue;
     }
     return hipGetLastError();
 }

@@ -38,6 +38,7 @@ _SIGS = {
     "nested_rebuild_fp16": (_i, [_p, _p, _p, _i64, _p]),
     "nested_gemm_fp16": (_i, [_p, _p, _p, _p, _i64, _i64, _i64, _p]),
     "nested_gemm_fp8": (_i, [_p, _p, _p, _p, _i64, _i64, _i64, _p]),
+    "nested_linear_fp8": (_i, [_p, _p, _p, _p, _p, _p, _i64, _i64, _i64, _p]),
     "fp8q_e4m3_encode_f32": (_i, [_p, _p, _i64, _p]),
 }
 for _name, (_res, _args) in _SIGS.items():
@@ -216,6 +217,30 @@ def nested_gemm_fp8(qa: torch.Tensor, sa: torch.Tensor, hi: torch.Tensor,
         _dev(qa, "qa", torch.uint8), _scalar(sa, "sa"), _dev(hi, "hi", torch.uint8),
         _dev(y, "y", torch.float16, (M, N)), M, N, K, _stream(qa)))
     return y
+
+
+def nested_linear_fp8(a: torch.Tensor, hi: torch.Tensor, y: torch.Tensor | None = None,
+                      q: torch.Tensor | None = None, scale: torch.Tensor | None = None,
+                      amax: torch.Tensor | None = None):
+    """One NestedFP FP8-mode linear layer: quantize a[M,K] (fp16) per tensor,
+    then y[M,N] fp16 = (q . E5M2(hi)^T) * scale.  Returns (y, q, scale, amax)."""
+    if a.dtype != torch.float16:
+        raise TypeError(f"a must be float16, got {a.dtype}")
+    M, N, K = _mnk(a, hi)
+    dev = a.device
+    if y is None:
+        y = torch.empty((M, N), dtype=torch.float16, device=dev)
+    if q is None:
+        q = torch.empty((M, K), dtype=torch.uint8, device=dev)
+    if scale is None:
+        scale = torch.empty(1, dtype=torch.float32, device=dev)
+    if amax is None:
+        amax = torch.empty(1, dtype=torch.float32, device=dev)
+    _check("nested_linear_fp8", lib.nested_linear_fp8(
+        _dev(a, "a", torch.float16), _dev(hi, "hi", torch.uint8),
+        _dev(y, "y", torch.float16, (M, N)), _dev(q, "q", torch.uint8, (M, K)),
+        _scalar(scale, "scale"), _scalar(amax, "amax"), M, N, K, _stream(a)))
+    return y, q, scale, amax
 
 
 def e4m3_encode_f32(v: torch.Tensor, q: torch.Tensor | None = None) -> torch.Tensor:

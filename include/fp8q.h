@@ -168,6 +168,23 @@ FP8Q_API fp8q_status nested_gemm_fp8(const uint8_t* qa, const float* sa, const u
                             fp8q_stream stream);
 
 /*
+ * nested_linear_fp8 - one NestedFP FP8-mode linear layer ([NestedFP] §2.1):
+ *   fp8_quantize_act on the fp16 activation, then nested_gemm_fp8 on its
+ *   codes.  Results are bit-identical to the two calls made in sequence:
+ *
+ *   a[M,K]   in : fp16 activation bit patterns
+ *   hi[N,K]  in : hi byte plane of the fp16 weights, read as E5M2
+ *   y[M,N]   out: fp16 bit patterns
+ *   q[M,K], *scale, *amax out: the activation codes, scale and amax
+ *   Size rules as fp8_gemm.  As for fp8_linear, M <= 2 with M*K <= 32768 is
+ *   one kernel; otherwise the quantizer runs first and may keep its
+ *   per-workgroup partial maxima in y (not yet written) unless y overlaps a.
+ */
+FP8Q_API fp8q_status nested_linear_fp8(const uint16_t* a, const uint8_t* hi, uint16_t* y,
+                              uint8_t* q, float* scale, float* amax, int64_t M, int64_t N,
+                              int64_t K, fp8q_stream stream);
+
+/*
  * fp8q_e4m3_encode_f32 - the device E4M3 encoder used by fp8_quantize_act,
  *   applied to binary32 values directly: q[i] = E4M3_rne_sat(v[i]).  n >= 1.
  *   Exported so the encoder can be checked exhaustively; not on the hot path.

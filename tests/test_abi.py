@@ -28,7 +28,7 @@ def declared_functions():
 def test_header_declares_the_entry_points():
     names = declared_functions()
     for want in ["fp8_quantize_act", "fp8_gemm", "fp8_linear", "nested_split", "nested_rebuild_fp16",
-                 "nested_gemm_fp16", "nested_gemm_fp8", "fp8q_abi_version",
+                 "nested_gemm_fp16", "nested_gemm_fp8", "nested_linear_fp8", "fp8q_abi_version",
                  "fp8q_status_str", "fp8q_last_error", "fp8q_e4m3_encode_f32"]:
         assert want in names
 
@@ -110,6 +110,14 @@ GEMM_SIG = [P16, P16, P16, P16, P16]
     ("nested_gemm_fp8", [P16, NULL, P16, P16, 1, 1, 16, NULL], ERR_NULL),
     ("nested_gemm_fp8", [P16, P16, P16, P16, -3, 1, 16, NULL], ERR_SHAPE),
     ("nested_gemm_fp8", [P16, P16, P17, P16, 1, 1, 16, NULL], ERR_ALIGN),
+    # nested_linear_fp8(a, hi, y, q, scale, amax, M, N, K, stream)
+    ("nested_linear_fp8", [NULL, P16, P16, P16, P16, P16, 1, 1, 16, NULL], ERR_NULL),
+    ("nested_linear_fp8", [P16, P16, P16, P16, P16, NULL, 1, 1, 16, NULL], ERR_NULL),
+    ("nested_linear_fp8", [P16, P16, P16, P16, P16, P16, 1, 1, 24, NULL], ERR_SHAPE),
+    ("nested_linear_fp8", [P16, P16, P16, P16, P16, P16, 1, 0, 16, NULL], ERR_SHAPE),
+    ("nested_linear_fp8", [P16, P17, P16, P16, P16, P16, 1, 1, 16, NULL], ERR_ALIGN),
+    ("nested_linear_fp8", [P16, P16, P16, P16, ctypes.c_void_p(0x1002), P16, 1, 1, 16, NULL],
+     ERR_ALIGN),
     # fp8q_e4m3_encode_f32(v, q, n, stream)
     ("fp8q_e4m3_encode_f32", [NULL, P16, 4, NULL], ERR_NULL),
     ("fp8q_e4m3_encode_f32", [P16, P16, 0, NULL], ERR_SHAPE),

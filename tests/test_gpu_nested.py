@@ -173,3 +173,34 @@ def test_fp8_mode_large_grid_sampled():
     ref, ab = oracle.nested_fp8_ref(qa, sa, hi, ms, ns)
     out = oracle.f16_decode(yb[ms, ns]).astype(np.float64)
     assert_within(out, ref, ab, f"fp8 mode {M}x{N}x{K}", "fp16")
+
+
+@pytest.mark.parametrize("M,N,K", [(1, 4096, 4096), (2, 300, 11008), (1, 37, 16), (1, 64, 32768),
+                                   (3, 16, 81920), (64, 256, 4096), (256, 1000, 4112)])
+def test_fp8_mode_linear_matches_quantize_then_gemm(M, N, K):
+    """nested_linear_fp8 (one fused kernel for M <= 2 with M*K <= 32768, the
+    two-launch quantizer with partial maxima in y otherwise) writes the same
+    codes, scale, amax and output bits as fp8_quantize_act followed by
+    nested_gemm_fp8; codes equal the oracle's, sampled outputs within the
+    GEMM tolerance."""
+    seed = synth.seed_for("nested-linear", M, N, K)
+    a = synth.activation(M, K, seed=seed, dtype="fp16", device=DEV)
+    w = synth.normal((N, K), 0.02, "fp16", seed=seed + 1, device=DEV)
+    hi, _ = fp8q.nested_split(w)
+    say("nested linear fp8", M, N, K)
+    y, q, s, am = fp8q.nested_linear_fp8(a, hi)
+    q2, s2, am2 = fp8q.fp8_quantize_act(a)
+    y2 = fp8q.nested_gemm_fp8(q2, s2, hi)
+    torch.cuda.synchronize()
+    assert torch.equal(q, q2) and torch.equal(s, s2) and torch.equal(am, am2)
+    assert torch.equal(y, y2)
+    ab16 = synth.bits(a)
+    oq, os_, oa = oracle.quantize(ab16.ravel(), oracle.FP16)
+    assert np.array_equal(host(q).ravel(), oq)
+    assert float(host(s)[0]) == os_ and float(host(am)[0]) == oa
+    ohi, _ = oracle.nested_split(synth.bits(w))
+    ms = np.repeat(np.arange(min(M, 4)), min(N, 64))
+    ns = np.tile(np.arange(min(N, 64)), min(M, 4))
+    ref, ab = oracle.nested_fp8_ref(oq.reshape(M, K), os_, ohi, ms, ns)
+    out = oracle.f16_decode(host(y)[ms, ns]).astype(np.float64)
+    assert_within(out, ref, ab, f"nested linear fp8 {M}x{N}x{K}", "fp16")
