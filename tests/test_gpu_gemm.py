@@ -210,7 +210,9 @@ def test_deterministic_and_stream_order():
 @pytest.mark.parametrize("M,N,K", [(1, 4096, 4096), (2, 300, 11008), (1, 37, 16), (1, 64, 32768),
                                    (2, 64, 16384), (2, 64, 32768),
                                    (1, 100, 65536), (2, 50, 33792), (3, 200, 1024), (16, 64, 4096),
-                                   (40, 96, 512), (64, 256, 4096), (3, 16, 81920)])
+                                   (40, 96, 512), (64, 256, 4096), (3, 16, 81920),
+                                   (4, 4096, 4096), (8, 1000, 4096), (16, 300, 2048),
+                                   (5, 37, 6544), (3, 12300, 10912)])
 def test_linear_matches_quantize_then_gemm(M, N, K, dtype):
     """fp8_linear (fused for M <= 2, M*K <= 32768) returns the codes, scale and
     amax of fp8_quantize_act bit-exactly and the same y as fp8_gemm on them;
