@@ -75,7 +75,8 @@ def _quant_case(x: torch.Tensor, what: str, guard: int = 64):
     return q[:n]
 
 
-SIZES = [1, 7, 8, 9, 1000, 4096, 4103, 32767, 32768, 32769, 8 * 11008, 1_000_003]
+SIZES = [1, 7, 8, 9, 1000, 4096, 4103, 32767, 32768, 32769, 8 * 11008, 98303, 98304, 98305,
+         1_000_003]
 
 
 @pytest.mark.parametrize("n", SIZES)
@@ -97,7 +98,7 @@ def test_quantize_fp16_weights_full_size():
 
 
 @pytest.mark.parametrize("dtype", ["bf16", "fp16"])
-@pytest.mark.parametrize("n", [20_000, 70_000])
+@pytest.mark.parametrize("n", [20_000, 70_000, 120_000])
 def test_quantize_every_16bit_value_at_unit_scale(dtype, n):
     """All finite 16-bit values with |v| <= 448, plus 448 itself: amax = 448 so
     s = 1 and the codes are the plain encodings (small and large path)."""
@@ -105,7 +106,7 @@ def test_quantize_every_16bit_value_at_unit_scale(dtype, n):
     t = synth.from_bits(allv, dtype).to(torch.float32).numpy()
     keep = allv[np.isfinite(t) & (np.abs(t) <= 448.0)]
     rng = np.random.Generator(np.random.PCG64(n))
-    sel = np.concatenate([keep, keep])[:n] if n > keep.size else rng.choice(keep, n, replace=False)
+    sel = np.resize(keep, n) if n > keep.size else rng.choice(keep, n, replace=False)
     b = sel.copy()
     b[0] = synth.bits(synth.from_bits(np.array([0], np.uint16), dtype) + 448.0)[0]
     _quant_case(synth.from_bits(b, dtype), f"unit-scale {dtype} n={n}")
@@ -124,7 +125,7 @@ def test_quantize_scaled_midpoints():
     assert q[-1] == 0x7E
 
 
-@pytest.mark.parametrize("n", [5, 50_000])
+@pytest.mark.parametrize("n", [5, 50_000, 150_000])
 def test_quantize_zero_and_constant(n):
     _quant_case(torch.zeros(n, dtype=torch.bfloat16), f"zeros n={n}")
     _quant_case(-torch.zeros(n, dtype=torch.float16), f"neg zeros n={n}")
@@ -134,7 +135,7 @@ def test_quantize_zero_and_constant(n):
     _quant_case(tiny, f"tiny n={n}")
 
 
-@pytest.mark.parametrize("n", [600, 40_000])
+@pytest.mark.parametrize("n", [600, 40_000, 120_000])
 @pytest.mark.parametrize("below", [False, True])
 def test_quantize_scale_threshold(n, below):
     """The device divides by s with a reciprocal and an FMA correction for
