@@ -7,8 +7,9 @@
 //    of their rounds of workgroups (pick_tile_shape), 16x16x128 MFMAs, operands
 //    moved to LDS by direct-to-LDS loads in an activation ring and a weight
 //    ring of 2-4 stages each.
-//  - NestedFP FP16 mode (same page, §2.1-§2.2): gemm_n16_kernel, 128x128 or
-//    64x64 tiles; the activation and the two weight byte planes reach LDS by
+//  - NestedFP FP16 mode (same page, §2.1-§2.2): gemm_n16_kernel, tiles from
+//    256x256 (8 waves) to 64x64 (4 waves) picked the same way; the
+//    activation and the two weight byte planes reach LDS by
 //    direct-to-LDS loads, and the weight words are rebuilt as fp16
 //    (hi<<8)|lo with v_perm while they move from LDS to registers, then
 //    v_mfma_f32_16x16x32_f16.
@@ -247,7 +248,7 @@ void gemm_f8_kernel(
 
 // ---------------------------------------------------------------- NestedFP FP16 GEMM, DMA rings
 // The NestedFP FP16 mode on the structure of gemm_f8_kernel: BM x BN tiles,
-// 4 waves of (BM/2) x (BN/2), K steps of 64 elements.  The fp16 activation
+// WM x WN waves of (BM/WM) x (BN/WN), K steps of 64 elements.  The fp16 activation
 // tile (BM rows x 128 bytes) goes through an AST-stage ring and the weight
 // byte planes (hi then lo, BN rows x 64 bytes each) through a WST-stage ring
 // (WST >= AST >= 2), both filled by direct global->LDS loads.  MFMA s
@@ -266,17 +267,19 @@ void gemm_f8_kernel(
 // step: A(k+1) sits in group k + 1 - AST, after which only that group's W
 // and the AST - 2 later groups may still be in flight (when AST == WST the
 // group's W is needed too).
-template <int BM, int BN, int AST, int WST>
-__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2)))
+template <int BM, int BN, int WM, int WN, int AST, int WST>
+__global__ __launch_bounds__(WM * WN * 64) __attribute__((amdgpu_waves_per_eu(2)))
 void gemm_n16_kernel(const uint16_t* __restrict__ a, const uint8_t* __restrict__ hi,
                      const uint8_t* __restrict__ lo, uint16_t* __restrict__ y, int M, int N, int K)
 {
     static_assert(AST >= 2 && WST >= AST, "ring depths");
-    constexpr int TM = BM / 2, TN = BN / 2;
+    constexpr int NW = WM * WN;
+    constexpr int TM = BM / WM, TN = BN / WN;
     constexpr int FM = TM / 16, FN = TN / 16;
     constexpr int ASTAGE = BM * 128, PLANE = BN * 64, WSTAGE = 2 * PLANE;
-    constexpr int ABPW = BM / 32;                 // activation blocks per wave per step
-    constexpr int PBPW = BN / 64;                 // blocks per plane per wave per step
+    constexpr int ABPW = BM / 8 / NW;             // activation blocks per wave per step
+    constexpr int PBPW = BN / 16 / NW;            // blocks per plane per wave per step
+    static_assert(ABPW * 8 * NW == BM && PBPW * 16 * NW == BN, "whole DMA blocks per wave");
     constexpr int WBPW = 2 * PBPW;
     constexpr int ALLOW = (AST < WST ? WBPW : 0) + (AST - 2) * (ABPW + WBPW);
     extern __shared__ __attribute__((aligned(16))) uint8_t lds[];
@@ -286,7 +289,7 @@ void gemm_n16_kernel(const uint16_t* __restrict__ a, const uint8_t* __restrict__
     const int tid = threadIdx.x;
     const int lane = tid & 63;
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
-    const int wm = wave >> 1, wn = wave & 1;
+    const int wm = wave / WN, wn = wave % WN;
     const int r = lane & 15, g = lane >> 4;
 
     const int tiles_m = (M + BM - 1) / BM;
@@ -414,15 +417,15 @@ constexpr TileShape kTileShapes[] = {
     { 64,  64, 1, 10.2f},   // the same kernel, one workgroup per CU
 };
 
-// The shape whose rounds of workgroups cost least; tiles may not be taller
-// than M rounded up to 64 rows.
-inline int pick_tile_shape(int M, int N)
+// The shape of `shapes` whose rounds of workgroups cost least; tiles may not
+// be taller than M rounded up to 64 rows.
+inline int pick_tile_shape(const TileShape* shapes, int count, int M, int N)
 {
     const int64_t mcap = ((int64_t)M + 63) / 64 * 64;
     int best = -1;
     float best_us = 0.f;
-    for (int i = 0; i < (int)(sizeof(kTileShapes) / sizeof(kTileShapes[0])); ++i) {
-        const TileShape& t = kTileShapes[i];
+    for (int i = 0; i < count; ++i) {
+        const TileShape& t = shapes[i];
         if (t.bm > mcap) continue;
         const int64_t tiles = (((int64_t)M + t.bm - 1) / t.bm) * (((int64_t)N + t.bn - 1) / t.bn);
         const int64_t slots = (int64_t)kCUs * t.per_cu;
@@ -436,7 +439,7 @@ template <int WFMT, int OUTF>
 hipError_t launch_tile_fmt(const uint8_t* qa, const float* sa, const uint8_t* qw, const float* sw,
                            uint16_t* y, int M, int N, int K, hipStream_t stream)
 {
-    switch (pick_tile_shape(M, N)) {
+    switch (pick_tile_shape(kTileShapes, sizeof(kTileShapes) / sizeof(kTileShapes[0]), M, N)) {
     case 0: return launch_f8<WFMT, OUTF, 256, 256, 2, 4, 2, 2>(qa, sa, qw, sw, y, M, N, K, stream);
     case 1: return launch_f8<WFMT, OUTF, 256, 192, 2, 4, 2, 3>(qa, sa, qw, sw, y, M, N, K, stream);
     case 2: return launch_f8<WFMT, OUTF, 256, 128, 4, 2, 3, 4>(qa, sa, qw, sw, y, M, N, K, stream);
@@ -458,12 +461,13 @@ hipError_t launch_tile_fp8(const uint8_t* qa, const float* sa, const uint8_t* qw
     return hipErrorInvalidValue;
 }
 
-template <int BM, int BN, int AST, int WST>
+template <int BM, int BN, int WM, int WN, int AST, int WST>
 hipError_t launch_n16(const uint16_t* a, const uint8_t* hi, const uint8_t* lo, uint16_t* y,
                       int M, int N, int K, hipStream_t stream)
 {
-    auto kern = gemm_n16_kernel<BM, BN, AST, WST>;
+    auto kern = gemm_n16_kernel<BM, BN, WM, WN, AST, WST>;
     constexpr size_t lds = ((size_t)AST * BM + (size_t)WST * BN) * 128;
+    static_assert(lds <= 160 * 1024, "LDS of one CU");
     static bool attr_set = false;        // idempotent host attribute, set on first use
     if (!attr_set) {
         const hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(kern),
@@ -473,20 +477,30 @@ hipError_t launch_n16(const uint16_t* a, const uint8_t* hi, const uint8_t* lo, u
         attr_set = true;
     }
     const int grid = ((M + BM - 1) / BM) * ((N + BN - 1) / BN);
-    kern<<<grid, 256, lds, stream>>>(a, hi, lo, y, M, N, K);
+    kern<<<grid, WM * WN * 64, lds, stream>>>(a, hi, lo, y, M, N, K);
     return hipGetLastError();
 }
+
+// Tile shapes of the NestedFP FP16 GEMM with the measured time of one round
+// of their workgroups at K = 4096 (MI355X, planes cold in HBM; Llama-7B
+// shapes at M = 256 and 2048), picked like the FP8 shapes.
+constexpr TileShape kN16Shapes[] = {
+    {256, 256, 1, 115.0f},  // 8 waves of 128 x 64, 2 + 2 stages (128 KiB)
+    {256, 128, 1, 76.0f},   // 8 waves of  64 x 64, 3 + 4 stages (160 KiB)
+    {128, 128, 1, 48.5f},   // 8 waves of  64 x 32, 4 + 4 stages (128 KiB)
+    { 64,  64, 2, 39.0f},   // 4 waves of  32 x 32, 4 + 4 stages ( 64 KiB)
+    { 64,  64, 1, 25.0f},   // the same kernel, one workgroup per CU
+};
 
 hipError_t launch_tile_nested16(const uint16_t* a, const uint8_t* hi, const uint8_t* lo,
                                 uint16_t* y, int M, int N, int K, hipStream_t stream)
 {
-    // 128 x 128 tiles (2-stage activation ring, 3-stage weight ring) from 192
-    // of them; below that 64 x 64 tiles with 4-stage rings, whose short K
-    // steps need the deeper lead (measured on the Llama-7B shapes at M = 256
-    // and 2048, weights cold in HBM)
-    const int64_t t128 = (int64_t)((M + 127) / 128) * ((N + 127) / 128);
-    if (t128 >= 192) return launch_n16<128, 128, 2, 3>(a, hi, lo, y, M, N, K, stream);
-    return launch_n16<64, 64, 4, 4>(a, hi, lo, y, M, N, K, stream);
+    switch (pick_tile_shape(kN16Shapes, sizeof(kN16Shapes) / sizeof(kN16Shapes[0]), M, N)) {
+    case 0: return launch_n16<256, 256, 2, 4, 2, 2>(a, hi, lo, y, M, N, K, stream);
+    case 1: return launch_n16<256, 128, 4, 2, 3, 4>(a, hi, lo, y, M, N, K, stream);
+    case 2: return launch_n16<128, 128, 2, 4, 4, 4>(a, hi, lo, y, M, N, K, stream);
+    default: return launch_n16<64, 64, 2, 2, 4, 4>(a, hi, lo, y, M, N, K, stream);
+    }
 }
 
 }  // namespace fp8q

@@ -205,3 +205,23 @@ def test_fp8_mode_linear_matches_quantize_then_gemm(M, N, K):
     ref, ab = oracle.nested_fp8_ref(oq.reshape(M, K), os_, ohi, ms, ns)
     out = oracle.f16_decode(host(y)[ms, ns]).astype(np.float64)
     assert_within(out, ref, ab, f"nested linear fp8 {M}x{N}x{K}", "fp16")
+
+
+@pytest.mark.parametrize("M,N,K", [(250, 12290, 1040), (260, 12300, 1040), (2000, 12000, 1040),
+                                   (1000, 9000, 1040), (300, 5000, 1040)])
+def test_fp16_mode_tile_shapes_ragged_sampled(M, N, K):
+    """FP16 mode on each tile kernel with ragged M, N and K (K % 64 != 0):
+    128x128 with 8 waves (250x12290), 256x128 (260x12300, 2000x12000),
+    256x256 (1000x9000) and 64x64 (300x5000); the first and last rows and
+    columns plus 256 random outputs against the fp64 checker."""
+    seed = synth.seed_for("n16-tiles", M, N, K)
+    a16, hi, lo = _operands(M, N, K, seed=seed)
+    say("fp16 tile shapes", M, N, K)
+    y = fp8q.nested_gemm_fp16(to_dev_bits(a16, "fp16"), to_dev_u8(hi), to_dev_u8(lo))
+    yb = host(y)
+    rng = np.random.Generator(np.random.PCG64(seed))
+    ms = np.concatenate([np.repeat([0, M - 1], N), np.tile(np.arange(M), 2), rng.integers(0, M, 256)])
+    ns = np.concatenate([np.tile(np.arange(N), 2), np.repeat([0, N - 1], M), rng.integers(0, N, 256)])
+    ref, ab = oracle.nested_fp16_ref(a16, hi, lo, ms, ns)
+    out = oracle.f16_decode(yb[ms, ns]).astype(np.float64)
+    assert_within(out, ref, ab, f"fp16 mode {M}x{N}x{K}", "fp16")
