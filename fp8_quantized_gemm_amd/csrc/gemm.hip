@@ -124,7 +124,7 @@ void gemm_f8_kernel(
     const int wm = wave / WN, wn = wave % WN;
     const int r = lane & 15, g = lane >> 4;
 
-    const int tiles_m = (M + BM - 1) / BM;
+    const int tiles_m = (int)(((int64_t)M + BM - 1) / BM);
     const int bid = xcd_remap(blockIdx.x, gridDim.x);
     const int m0 = (bid % tiles_m) * BM;
     const int n0 = (bid / tiles_m) * BN;
@@ -292,7 +292,7 @@ void gemm_n16_kernel(const uint16_t* __restrict__ a, const uint8_t* __restrict__
     const int wm = wave / WN, wn = wave % WN;
     const int r = lane & 15, g = lane >> 4;
 
-    const int tiles_m = (M + BM - 1) / BM;
+    const int tiles_m = (int)(((int64_t)M + BM - 1) / BM);
     const int bid = xcd_remap(blockIdx.x, gridDim.x);
     const int m0 = (bid % tiles_m) * BM;
     const int n0 = (bid / tiles_m) * BN;
@@ -395,8 +395,9 @@ hipError_t launch_f8(const uint8_t* qa, const float* sa, const uint8_t* qw, cons
         if (e != hipSuccess) return e;
         attr_set = true;
     }
-    const int grid = ((M + BM - 1) / BM) * ((N + BN - 1) / BN);
-    kern<<<grid, WM * WN * 64, lds, stream>>>(qa, sa, qw, sw, y, M, N, K);
+    const int64_t grid = (((int64_t)M + BM - 1) / BM) * (((int64_t)N + BN - 1) / BN);
+    if (grid > 0x7fffffff) return hipErrorInvalidValue;
+    kern<<<(int)grid, WM * WN * 64, lds, stream>>>(qa, sa, qw, sw, y, M, N, K);
     return hipGetLastError();
 }
 
@@ -476,8 +477,9 @@ hipError_t launch_n16(const uint16_t* a, const uint8_t* hi, const uint8_t* lo, u
         if (e != hipSuccess) return e;
         attr_set = true;
     }
-    const int grid = ((M + BM - 1) / BM) * ((N + BN - 1) / BN);
-    kern<<<grid, WM * WN * 64, lds, stream>>>(a, hi, lo, y, M, N, K);
+    const int64_t grid = (((int64_t)M + BM - 1) / BM) * (((int64_t)N + BN - 1) / BN);
+    if (grid > 0x7fffffff) return hipErrorInvalidValue;
+    kern<<<(int)grid, WM * WN * 64, lds, stream>>>(a, hi, lo, y, M, N, K);
     return hipGetLastError();
 }
 

@@ -191,7 +191,7 @@ hipError_t launch_gemv_fp8(const uint8_t* qa, const float* sa, const uint8_t* qw
                            uint16_t* y, int M, int N, int K, int wfmt, int outf,
                            hipStream_t stream)
 {
-    const dim3 grid((N + 15) / 16), block(kGemvWaves * 64);
+    const dim3 grid((unsigned)(((int64_t)N + 15) / 16)), block(kGemvWaves * 64);
     if (wfmt == WF_E4M3 && outf == OUT_BF16)
         gemv_f8_kernel<WF_E4M3, OUT_BF16, kGemvWaves, kGemvUnroll, CP_DEFAULT>
             <<<grid, block, 0, stream>>>(qa, sa, qw, sw, y, M, N, K);
@@ -207,7 +207,7 @@ hipError_t launch_gemv_nested16(const uint16_t* a, const uint8_t* hi, const uint
                                 uint16_t* y, int M, int N, int K, hipStream_t stream)
 {
     gemv_nested16_kernel<kNestedWaves, kNestedUnroll, CP_NT>
-        <<<dim3((N + 15) / 16), dim3(kNestedWaves * 64), 0, stream>>>(a, hi, lo, y, M, N, K);
+        <<<dim3((unsigned)(((int64_t)N + 15) / 16)), dim3(kNestedWaves * 64), 0, stream>>>(a, hi, lo, y, M, N, K);
     return hipGetLastError();
 }
 

@@ -102,9 +102,10 @@ void rowk_f8_kernel(
 
     const int tid = threadIdx.x, lane = tid & 63;
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
-    const int ngroups = (N + ROWS - 1) / ROWS;
-    const int gpw = (ngroups + gridDim.x - 1) / gridDim.x;      // groups per workgroup
-    const int gend = min(ngroups, (int)(blockIdx.x + 1) * gpw);
+    const int ngroups = (int)(((int64_t)N + ROWS - 1) / ROWS);
+    // 64-bit group indices: ngroups may come within a workgroup's span of 2^31
+    const int64_t gpw = ((int64_t)ngroups + gridDim.x - 1) / gridDim.x;   // groups per workgroup
+    const int64_t gend = min((int64_t)ngroups, (int64_t)(blockIdx.x + 1) * gpw);
     const int nkb = (K + 1024 * U - 1) / (1024 * U);
 
     v4i w[ROWS][U];
@@ -152,8 +153,8 @@ void rowk_f8_kernel(
     }
     __builtin_amdgcn_sched_barrier(0);
 
-    int grp = blockIdx.x * gpw + wave;
-    load_w(min(grp, ngroups - 1) * ROWS, 0, grp < gend);   // unconditional: see load_w
+    int64_t grp = (int64_t)blockIdx.x * gpw + wave;
+    load_w((int)min(grp, (int64_t)ngroups - 1) * ROWS, 0, grp < gend);   // unconditional: see load_w
     __builtin_amdgcn_sched_barrier(0);
 
     float s_a;
@@ -196,7 +197,7 @@ void rowk_f8_kernel(
     const rsrc_t ra = make_rsrc(act, (uint32_t)(MR * K));
 
     for (; grp < gend; grp += W) {
-        const int row0 = grp * ROWS;
+        const int row0 = (int)(grp * ROWS);
         float acc[MR][ROWS];
 #pragma unroll
         for (int m = 0; m < MR; ++m)
@@ -245,7 +246,7 @@ void rowk_f8_kernel(
                     y[(size_t)m * N + row0 + j] = (uint16_t)f32_to_out_bits<OUTF>(v * s);
             }
         // next group's first batch
-        if (grp + W < gend) load_w((grp + W) * ROWS, 0, true);
+        if (grp + W < gend) load_w((int)(grp + W) * ROWS, 0, true);
     }
 }
 
@@ -261,9 +262,9 @@ __global__ __launch_bounds__(kThreads) void rowk_nested16_kernel(
 {
     const int lane = threadIdx.x & 63;
     const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
-    const int row0 = (blockIdx.x * (kThreads / 64) + wave) * ROWS;   // one group per wave
-    const int nrow = max(0, min(ROWS, N - row0));
-    const size_t base = (size_t)min(row0, N - 1) * K;
+    const int64_t row0 = ((int64_t)blockIdx.x * (kThreads / 64) + wave) * ROWS;   // one group per wave
+    const int nrow = (int)max((int64_t)0, min((int64_t)ROWS, (int64_t)N - row0));
+    const size_t base = (size_t)min(row0, (int64_t)N - 1) * K;
     const rsrc_t rh = make_rsrc(hi + base, (uint32_t)(nrow * K));
     const rsrc_t rl = make_rsrc(lo + base, (uint32_t)(nrow * K));
     const rsrc_t ra = make_rsrc(a, (uint32_t)(MR * K * 2));
@@ -321,7 +322,7 @@ __global__ __launch_bounds__(kThreads) void rowk_nested16_kernel(
         }
 }
 
-int rowk_grid(int N) { return (N + kRows * (kThreads / 64) - 1) / (kRows * (kThreads / 64)); }
+int rowk_grid(int N) { return (int)(((int64_t)N + kRows * (kThreads / 64) - 1) / (kRows * (kThreads / 64))); }
 
 template <int WFMT, int OUTF, int AS, int MR>
 void launch_rowk(const void* act, const float* sa_in, const uint8_t* qw, const float* sw,
@@ -330,7 +331,7 @@ void launch_rowk(const void* act, const float* sa_in, const uint8_t* qw, const f
 {
     using C = RowkCfg<MR>;
     const size_t lds = AS != AS_GLOBAL ? (size_t)MR * K : 0;
-    const int ngroups = (N + C::ROWS - 1) / C::ROWS;
+    const int ngroups = (int)(((int64_t)N + C::ROWS - 1) / C::ROWS);
     const int grid = min(ngroups, kCUs * C::WPC);
     rowk_f8_kernel<WFMT, OUTF, AS, MR, C::ROWS, C::U, CP_NT, C::WPC>
         <<<grid, kWgThreads, lds, st>>>(act, sa_in, qw, sw, y, q, sa_out, amax, N, K);
