@@ -93,12 +93,13 @@ def load_traffic(src_hash: str):
 class Model:
     """Device-resident weights and per-linear buffers of one decode workload."""
 
-    def __init__(self, torch, fp8q, synth, M: int, dev: str):
+    def __init__(self, torch, fp8q, synth, M: int, dev: str, spec=None, layers: int = LAYERS,
+                 sigma: float = 0.02, tag: str = "w"):
         self.M = M
         self.linears = []
-        for layer in range(LAYERS):
-            for name, K, N in synth.LLAMA7B_LINEARS:
-                w = synth.normal((N, K), 0.02, "fp16", seed=synth.seed_for("w", layer, name),
+        for layer in range(layers):
+            for name, K, N in (spec if spec is not None else synth.LLAMA7B_LINEARS):
+                w = synth.normal((N, K), sigma, "fp16", seed=synth.seed_for(tag, layer, name),
                                  device=dev)
                 qw, sw, _ = fp8q.fp8_quantize_act(w)      # offline static quantization
                 del w
@@ -220,52 +221,69 @@ def cpu_baseline(torch, synth, dev, seconds):
                       f"{el:.1f} s of CPU work; same algorithmic bytes as the GPU metric"}
 
 
-def secondary(torch, fp8q, synth, model1, dev, parts=("decode", "prefill", "nested"), graph=True):
-    """Prefill, M = 4/8 decode and NestedFP figures (a few steps each)."""
+def with_activations(torch, synth, model1, M, dev, tag, outliers=False):
+    """The weights of `model1` with fresh M-row activations and outputs."""
+    mm = Model.__new__(Model)
+    mm.M = M
+    mm.linears = []
+    for L in model1.linears:
+        K, N = L["K"], L["N"]
+        d = dict(L)
+        d["x"] = synth.activation(M, K, seed=synth.seed_for(tag, M, L["layer"], L["name"]),
+                                  outliers=outliers, device=dev)
+        d["q"] = torch.empty((M, K), dtype=torch.uint8, device=dev)
+        d["y"] = torch.empty((M, N), dtype=torch.bfloat16, device=dev)
+        mm.linears.append(d)
+    return mm
+
+
+def decode_figures(torch, fp8q, mm, graph=True):
+    dt, _ = time_steps(torch, fp8q, mm, steps=5, warmup=2, graph=graph)
+    byts = sum(mm.gemm_bytes(L) + mm.quant_bytes(L) for L in mm.linears)
+    return {"GB_per_s": round(byts / dt / 1e9, 1),
+            "frac_hbm": round(byts / dt / 1e9 / HBM_PEAK_GBS, 4),
+            "ms_per_step": round(dt * 1e3, 3)}
+
+
+def prefill_figures(torch, fp8q, mm, graph=True):
+    dt, _ = time_steps(torch, fp8q, mm, steps=3, warmup=1, graph=graph)
+    # the GEMM alone, on the codes and scales the timed steps left behind
+    _, gdev = time_steps(torch, fp8q, mm, steps=3, warmup=1, graph=graph, call=gemm_call)
+    fl = sum(mm.flops(L) for L in mm.linears)
+    return {"TFLOP_per_s": round(fl / dt / 1e12, 1),
+            "frac_fp8_mfma": round(fl / dt / 1e12 / FP8_PEAK_TFLOPS, 4),
+            "gemm_only_TFLOP_per_s": round(fl / gdev / 1e12, 1),
+            "ms_per_step": round(dt * 1e3, 3)}
+
+
+def secondary(torch, fp8q, synth, model1, dev, parts=("decode", "prefill", "qwen", "nested"),
+              graph=True):
+    """Prefill, M = 4/8 decode, Qwen-32B and NestedFP figures (a few steps each)."""
     out = {}
     # decode at M = 4, 8 on the same weights (activations re-drawn)
     for M in ((4, 8) if "decode" in parts else ()):
-        mm = Model.__new__(Model)
-        mm.M = M
-        mm.linears = []
-        for L in model1.linears:
-            K, N = L["K"], L["N"]
-            d = dict(L)
-            d["x"] = synth.activation(M, K, seed=synth.seed_for("x", M, L["layer"], L["name"]),
-                                      device=dev)
-            d["q"] = torch.empty((M, K), dtype=torch.uint8, device=dev)
-            d["y"] = torch.empty((M, N), dtype=torch.bfloat16, device=dev)
-            mm.linears.append(d)
-        dt, _ = time_steps(torch, fp8q, mm, steps=5, warmup=2)
-        byts = sum(mm.gemm_bytes(L) + mm.quant_bytes(L) for L in mm.linears)
-        out[f"decode_m{M}"] = {"GB_per_s": round(byts / dt / 1e9, 1),
-                               "frac_hbm": round(byts / dt / 1e9 / HBM_PEAK_GBS, 4),
-                               "ms_per_step": round(dt * 1e3, 3)}
+        out[f"decode_m{M}"] = decode_figures(torch, fp8q, with_activations(torch, synth, model1, M,
+                                                                           dev, "x"))
         progress(f"decode M={M} done")
     # prefill M = 512, 2048 (activations with 0.1% outlier channels x50)
     for M in ((512, 2048) if "prefill" in parts else ()):
-        mm = Model.__new__(Model)
-        mm.M = M
-        mm.linears = []
-        for L in model1.linears:
-            K, N = L["K"], L["N"]
-            d = dict(L)
-            d["x"] = synth.activation(M, K, seed=synth.seed_for("xp", M, L["layer"], L["name"]),
-                                      outliers=True, device=dev)
-            d["q"] = torch.empty((M, K), dtype=torch.uint8, device=dev)
-            d["y"] = torch.empty((M, N), dtype=torch.bfloat16, device=dev)
-            mm.linears.append(d)
-        dt, _ = time_steps(torch, fp8q, mm, steps=3, warmup=1, graph=graph)
-        # the GEMM alone, on the codes and scales the timed steps left behind
-        _, gdev = time_steps(torch, fp8q, mm, steps=3, warmup=1, graph=graph, call=gemm_call)
-        kern = gdev / len(mm.linears)
-        fl = sum(mm.flops(L) for L in mm.linears)
-        out[f"prefill_m{M}"] = {"TFLOP_per_s": round(fl / dt / 1e12, 1),
-                                "frac_fp8_mfma": round(fl / dt / 1e12 / FP8_PEAK_TFLOPS, 4),
-                                "gemm_only_TFLOP_per_s": round(fl / (kern * len(mm.linears)) / 1e12, 1),
-                                "ms_per_step": round(dt * 1e3, 3)}
+        mm = with_activations(torch, synth, model1, M, dev, "xp", outliers=True)
+        out[f"prefill_m{M}"] = prefill_figures(torch, fp8q, mm, graph)
         progress(f"prefill M={M} done")
         del mm
+    # Qwen-32B linears (weights N(0, 0.015)) on 8 of the 64 layers: 3.9 GB of
+    # E4M3 weights, still cold in HBM on every step; decode M = 1, 16, prefill
+    # M = 1024
+    if "qwen" in parts:
+        mq = Model(torch, fp8q, synth, M=1, dev=dev, spec=synth.QWEN32B_LINEARS, layers=8,
+                   sigma=0.015, tag="wq")
+        out["qwen32b_decode_m1"] = dict(decode_figures(torch, fp8q, mq, graph), layers=8)
+        out["qwen32b_decode_m16"] = dict(decode_figures(
+            torch, fp8q, with_activations(torch, synth, mq, 16, dev, "xq"), graph), layers=8)
+        out["qwen32b_prefill_m1024"] = dict(prefill_figures(
+            torch, fp8q, with_activations(torch, synth, mq, 1024, dev, "xqp"), graph), layers=8)
+        progress("qwen-32b done")
+        del mq
     if "nested" not in parts:
         return out
     # NestedFP at M = 1 and 256 on 8 layers of fp16 weights (hi/lo planes)

@@ -154,7 +154,7 @@ LAYER_SHAPES = [(K, N) for _, K, N in synth.LLAMA7B_LINEARS] + \
                [(K, N) for _, K, N in synth.QWEN32B_LINEARS]
 
 
-@pytest.mark.parametrize("M", [1, 8, 16, 512, 2048])
+@pytest.mark.parametrize("M", [1, 8, 16, 512, 1024, 2048])
 @pytest.mark.parametrize("K,N", LAYER_SHAPES)
 def test_full_size_layers_sampled(M, K, N):
     """Full Llama-7B / Qwen-32B linear shapes, GPU quantization + GEMM: codes of
