@@ -302,3 +302,24 @@ def test_big_tile_random_ragged_sampled(M, N, K):
     ref, ab = oracle.gemm_fp8_ref(qa, sa, qw, sw, ms, ns)
     out = oracle.bf16_decode(y[ms, ns]).astype(np.float64)
     assert_within(out, ref, ab, f"big {M}x{N}x{K}", "bf16")
+
+
+# ------------------------------------------------------------------ largest K
+KMAX = 1 << 22
+
+
+@pytest.mark.parametrize("M", [1, 8, 40])
+def test_largest_k_bit_exact(M):
+    """K = 2^22 (the largest the boundary accepts) on the row kernel (M = 1,
+    codes read from L2), the MFMA GEMV (M = 8) and a tile kernel (M = 40):
+    codes of 0, +-1, +-2 keep every partial sum an integer below 2^24, so the
+    fp32 accumulation is exact in any order and the bf16 output equals the
+    oracle's bit for bit.  32-bit offsets reach 2^30 on the tile kernel."""
+    rng = np.random.Generator(np.random.PCG64(M + KMAX))
+    table = np.array([0x00, 0x38, 0x40, 0xB8, 0xC0], np.uint8)      # 0, 1, 2, -1, -2
+    qa = table[rng.integers(0, 5, size=(M, KMAX))]
+    qw = table[rng.integers(0, 5, size=(16, KMAX))]
+    say("largest K", M, 16, KMAX)
+    y = _run_gemm(qa, 1.0, qw, 1.0)
+    want = oracle.gemm_fp8_f32(qa, 1.0, qw, 1.0)
+    assert np.array_equal(y, want)

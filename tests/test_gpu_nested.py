@@ -225,3 +225,18 @@ def test_fp16_mode_tile_shapes_ragged_sampled(M, N, K):
     ref, ab = oracle.nested_fp16_ref(a16, hi, lo, ms, ns)
     out = oracle.f16_decode(yb[ms, ns]).astype(np.float64)
     assert_within(out, ref, ab, f"fp16 mode {M}x{N}x{K}", "fp16")
+
+
+def test_largest_k_fp16_mode_sampled():
+    """NestedFP FP16 mode at K = 2^22 (activation rows of 8 MiB, tile path):
+    sampled outputs within tolerance of the fp64 checker."""
+    M, N, K = 20, 16, 1 << 22
+    a16, hi, lo = _operands(M, N, K, seed=K + 5)
+    say("fp16 mode largest K", M, N, K)
+    y = fp8q.nested_gemm_fp16(to_dev_bits(a16, "fp16"), to_dev_u8(hi), to_dev_u8(lo))
+    yb = host(y)
+    ms = np.repeat(np.arange(M), N)
+    ns = np.tile(np.arange(N), M)
+    ref, ab = oracle.nested_fp16_ref(a16, hi, lo, ms, ns)
+    assert_within(oracle.f16_decode(yb[ms, ns]).astype(np.float64), ref, ab,
+                  f"fp16 mode {M}x{N}x{K}", "fp16")
