@@ -32,12 +32,13 @@ constexpr int kUnroll = 4;        // 1 KiB chunks per row in flight per wave
 constexpr int kWgThreads = 1024;  // FP8 kernel: 16 waves per workgroup
 constexpr int kCUs = 256;         // compute units of an MI355X
 // FP8 kernel configuration, measured on MI355X over the Llama-7B / Qwen-32B
-// decode shapes: one activation row runs one weight row per wave, 2 KiB
-// batches and two workgroups per CU (57 VGPRs, 32 waves per CU); two
-// activation rows need more registers and run one workgroup per CU.
+// decode shapes: one activation row runs 2 KiB batches and two workgroups per
+// CU (57 VGPRs, 32 waves per CU); two activation rows need more registers and
+// run one workgroup per CU.
 template <int MR> struct RowkCfg;
-template <> struct RowkCfg<1> { static constexpr int ROWS = 1, U = 2, WPC = 2; };
-template <> struct RowkCfg<2> { static constexpr int ROWS = 1, U = 2, WPC = 1; };
+template <> struct RowkCfg<1> { static constexpr int U = 2, WPC = 2; };
+template <> struct RowkCfg<2> { static constexpr int U = 2, WPC = 1; };
+constexpr int kPartMax = 1024;    // per-workgroup partial sums of the split-K decode kernel
 
 typedef float v2f __attribute__((ext_vector_type(2)));
 typedef _Float16 h2 __attribute__((ext_vector_type(2)));
@@ -75,23 +76,28 @@ enum : int {
 // y[m, n] = out( sum_k dec(a[m,k]) * dec(W[n,k]) * s_a * (*sw or 1) ).
 //
 // At most WPC 1024-thread workgroups per CU: the activation prologue (copy or
-// quantization into LDS) is paid once per workgroup and spread over 16 waves.  The
-// weight rows are cut into groups of ROWS rows and each workgroup takes one
-// contiguous span of groups, its 16 waves taking consecutive groups of the
-// span in turn, so that at any moment a workgroup streams one compact window
-// of the weight matrix: measured on MI355X, block-contiguous streaming with
-// non-temporal loads sustains about 7.1 TB/s where grid-strided streaming
-// stays near 6 TB/s.  Per group a wave streams K in batches of U 1 KiB chunks
-// per row; the 4 waves per SIMD overlap each other's loads and arithmetic.
-// The activation and then the first weight batch are requested before the
-// prologue.
-template <int WFMT, int OUTF, int AS, int MR, int ROWS, int U, int CP, int WPC = 1>
+// quantization into LDS) is paid once per workgroup and spread over 16 waves.
+// Each workgroup takes one contiguous span of weight rows, so that at any
+// moment it streams one compact window of the weight matrix: measured on
+// MI355X, block-contiguous streaming with non-temporal loads sustains about
+// 7.1 TB/s where grid-strided streaming stays near 6 TB/s.  The K range of a
+// row is cut into S = 2^ls equal segments (a multiple of 128 bytes each), so
+// that a span holds S units per row; the 16 waves take consecutive units in
+// turn, which keeps wave w on segment w % S.  A wave streams its segment in
+// batches of U 1 KiB chunks; the 4 waves per SIMD overlap each other's loads
+// and arithmetic.  With S = 1 a wave finishes a row itself; with S > 1 the
+// per-segment sums go to LDS and are added in segment order after one
+// barrier, so the result is deterministic.  The host picks S (see
+// rowk_split_shift): splitting pays where a span has fewer rows than waves or
+// a row's last batch is mostly empty.  The activation and then the first
+// weight batch are requested before the prologue.
+template <int WFMT, int OUTF, int AS, int MR, int U, int CP, int WPC = 1>
 __global__ __launch_bounds__(kWgThreads) __attribute__((amdgpu_waves_per_eu(4 * WPC)))
 void rowk_f8_kernel(
     const void* __restrict__ act, const float* __restrict__ sa_in,
     const uint8_t* __restrict__ qw, const float* __restrict__ sw,
     uint16_t* __restrict__ y, uint8_t* __restrict__ q_out, float* __restrict__ sa_out,
-    float* __restrict__ amax_out, int N, int K)
+    float* __restrict__ amax_out, int N, int K, int rpw, int ls, int kseg)
 {
     constexpr bool FUSED = AS == AS_BF16 || AS == AS_FP16;
     constexpr bool IN_LDS = AS != AS_GLOBAL;
@@ -99,30 +105,33 @@ void rowk_f8_kernel(
     constexpr int W = kWgThreads / 64;
     extern __shared__ __attribute__((aligned(16))) uint8_t codes_lds[];   // IN_LDS: MR*K codes
     __shared__ float red[W];
+    __shared__ float part[kPartMax];   // S > 1: [m][row of the span][segment]
 
     const int tid = threadIdx.x, lane = tid & 63;
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
-    const int ngroups = (int)(((int64_t)N + ROWS - 1) / ROWS);
-    // 64-bit group indices: ngroups may come within a workgroup's span of 2^31
-    const int64_t gpw = ((int64_t)ngroups + gridDim.x - 1) / gridDim.x;   // groups per workgroup
-    const int64_t gend = min((int64_t)ngroups, (int64_t)(blockIdx.x + 1) * gpw);
-    const int nkb = (K + 1024 * U - 1) / (1024 * U);
+    const int S = 1 << ls;
+    const int seg = wave & (S - 1);
+    // rows [rbeg, rbeg + nrows) of this workgroup (rpw rows per workgroup;
+    // 64-bit: N may come within a span of 2^31); the host computes rpw and
+    // the segment length kseg, so that the setup every wave runs before its
+    // first load (on the CU's one scalar unit) stays short
+    const int64_t rbeg = (int64_t)blockIdx.x * rpw;
+    const int nrows = (int)max((int64_t)0, min((int64_t)rpw, (int64_t)N - rbeg));
+    const int nunits = nrows << ls;    // S > 1 only when MR * nrows * S <= kPartMax
+    const int klo = min(K, seg * kseg), khi = min(K, klo + kseg);
+    const int nkb = (khi - klo + 1024 * U - 1) / (1024 * U);
 
-    v4i w[ROWS][U];
-    // weights of rows [row0, row0 + ROWS) at K slice kb; the resource covers
-    // only the valid rows, so padded rows and the K tail read zero, and an
-    // empty resource (!valid) makes every load read zero: the loads are still
-    // issued without a branch, which keeps the compiler's wait counts exact
-    // for the activation loads issued before them
-    auto load_w = [&](int row0, int kb, bool valid) {
-        const int nrow = valid ? min(ROWS, N - row0) : 0;
-        const rsrc_t rw = make_rsrc(qw + (size_t)row0 * K, (uint32_t)(nrow * K));
+    v4i w[U];
+    // weights of `row` at K offsets [kb, kb + U KiB) clipped to the segment;
+    // an empty resource (!valid) makes every load read zero, and the loads
+    // are still issued without a branch, which keeps the compiler's wait
+    // counts exact for the activation loads issued before them
+    auto load_w = [&](int64_t row, int kb, bool valid) {
+        const rsrc_t rw = make_rsrc(qw + (size_t)row * K, valid ? (uint32_t)K : 0u);
 #pragma unroll
         for (int u = 0; u < U; ++u) {
             const int k = kb + u * 1024 + lane * 16;
-#pragma unroll
-            for (int j = 0; j < ROWS; ++j)
-                w[j][u] = buf_load16<CP>(rw, k < K ? (uint32_t)(j * K + k) : kOOB);
+            w[u] = buf_load16<CP>(rw, k < khi ? (uint32_t)k : kOOB);
         }
     };
 
@@ -153,8 +162,8 @@ void rowk_f8_kernel(
     }
     __builtin_amdgcn_sched_barrier(0);
 
-    int64_t grp = (int64_t)blockIdx.x * gpw + wave;
-    load_w((int)min(grp, (int64_t)ngroups - 1) * ROWS, 0, grp < gend);   // unconditional: see load_w
+    const int u0 = wave;
+    load_w(rbeg + (min(u0, max(nunits - 1, 0)) >> ls), klo, u0 < nunits);   // unconditional: see load_w
     __builtin_amdgcn_sched_barrier(0);
 
     float s_a;
@@ -196,57 +205,62 @@ void rowk_f8_kernel(
     const float s = (sw != nullptr) ? s_a * *sw : s_a;
     const rsrc_t ra = make_rsrc(act, (uint32_t)(MR * K));
 
-    for (; grp < gend; grp += W) {
-        const int row0 = (int)(grp * ROWS);
-        float acc[MR][ROWS];
+    for (int u = u0; u < nunits; u += W) {
+        const int lr = u >> ls;
+        const int64_t row = rbeg + lr;
+        float acc[MR];
 #pragma unroll
-        for (int m = 0; m < MR; ++m)
-#pragma unroll
-            for (int j = 0; j < ROWS; ++j) acc[m][j] = 0.0f;
+        for (int m = 0; m < MR; ++m) acc[m] = 0.0f;
         for (int kbi = 0; kbi < nkb; ++kbi) {
-            const int kb = kbi * 1024 * U;
-            if (kbi > 0) load_w(row0, kb, true);   // (the first batch is already in flight)
+            const int kb = klo + kbi * 1024 * U;
+            if (kbi > 0) load_w(row, kb, true);   // (the first batch is already in flight)
             v4i a[MR][U];
 #pragma unroll
-            for (int u = 0; u < U; ++u) {
-                const int k = kb + u * 1024 + lane * 16;
-                const bool in = k < K;
+            for (int uu = 0; uu < U; ++uu) {
+                const int k = kb + uu * 1024 + lane * 16;
+                const bool in = k < khi;
 #pragma unroll
                 for (int m = 0; m < MR; ++m) {
                     if constexpr (IN_LDS) {
                         const v4i v = *reinterpret_cast<const v4i*>(codes_lds + m * K + (in ? k : 0));
-                        a[m][u] = in ? v : v4i{0, 0, 0, 0};
+                        a[m][uu] = in ? v : v4i{0, 0, 0, 0};
                     } else {
-                        a[m][u] = buf_load16(ra, in ? (uint32_t)(m * K + k) : kOOB);
+                        a[m][uu] = buf_load16(ra, in ? (uint32_t)(m * K + k) : kOOB);
                     }
                 }
             }
 #pragma unroll
-            for (int u = 0; u < U; ++u) {
+            for (int uu = 0; uu < U; ++uu) {
                 float af[MR][16];
 #pragma unroll
-                for (int m = 0; m < MR; ++m) decode16<WF_E4M3>(a[m][u], af[m]);
+                for (int m = 0; m < MR; ++m) decode16<WF_E4M3>(a[m][uu], af[m]);
+                float wf[16];
+                decode16<WFMT>(w[uu], wf);
 #pragma unroll
-                for (int j = 0; j < ROWS; ++j) {
-                    float wf[16];
-                    decode16<WFMT>(w[j][u], wf);
+                for (int m = 0; m < MR; ++m)
 #pragma unroll
-                    for (int m = 0; m < MR; ++m)
-#pragma unroll
-                        for (int e = 0; e < 16; ++e) acc[m][j] += af[m][e] * wf[e];
-                }
+                    for (int e = 0; e < 16; ++e) acc[m] += af[m][e] * wf[e];
             }
         }
 #pragma unroll
-        for (int m = 0; m < MR; ++m)
-#pragma unroll
-            for (int j = 0; j < ROWS; ++j) {
-                const float v = wave_sum(acc[m][j]);
-                if (lane == 0 && row0 + j < N)
-                    y[(size_t)m * N + row0 + j] = (uint16_t)f32_to_out_bits<OUTF>(v * s);
+        for (int m = 0; m < MR; ++m) {
+            const float v = wave_sum(acc[m]);
+            if (lane == 0) {
+                if (S == 1) y[(size_t)m * N + row] = (uint16_t)f32_to_out_bits<OUTF>(v * s);
+                else part[(m * nrows + lr) * S + seg] = v;
             }
-        // next group's first batch
-        if (grp + W < gend) load_w((int)(grp + W) * ROWS, 0, true);
+        }
+        // next unit's first batch
+        if (u + W < nunits) load_w(rbeg + ((u + W) >> ls), klo, true);
+    }
+    if (S > 1) {
+        __syncthreads();
+        for (int t = tid; t < MR * nrows; t += kWgThreads) {
+            float v = 0.0f;
+            for (int j = 0; j < S; ++j) v += part[t * S + j];
+            const int m = t / nrows, lr = t - m * nrows;
+            y[(size_t)m * N + rbeg + lr] = (uint16_t)f32_to_out_bits<OUTF>(v * s);
+        }
     }
 }
 
@@ -324,6 +338,29 @@ __global__ __launch_bounds__(kThreads) void rowk_nested16_kernel(
 
 int rowk_grid(int N) { return (int)(((int64_t)N + kRows * (kThreads / 64) - 1) / (kRows * (kThreads / 64))); }
 
+// Split of each weight row's K range over S = 2^ls waves.  A wave's work is
+// ceil(units / 16) units of ceil(segment / batch) batches each.  A split is
+// taken only where it at least halves the longest wave and that wave has at
+// least 4 batches, and only while the partial sums fit in LDS.  Measured on
+// MI355X inside the Llama-7B decode step: the down projection (8 rows of
+// 11008 per workgroup, half the waves idle without a split) gains 10% with
+// S = 2, while QKV (24 rows of 4096: 4 -> 3 batches) and O (8 rows of 4096:
+// 2 -> 1 batch) lose about 4%, and S = 4 at 10-20 rows of 5120..8192 (Qwen-32B)
+// loses although it shortens the longest wave a little.
+int rowk_split_shift(int64_t rows_per_wg, int K, int MR, int U)
+{
+    auto cost = [&](int ls) {
+        const int64_t units = rows_per_wg << ls;
+        const int64_t kseg = ((((int64_t)K + (1 << ls) - 1) >> ls) + 127) & ~(int64_t)127;
+        return ((units + 15) / 16) * ((kseg + 1024 * U - 1) / (1024 * U));
+    };
+    int best = 0;
+    if (cost(0) < 4) return best;
+    for (int ls = 1; ls <= 4; ++ls)
+        if ((int64_t)MR * (rows_per_wg << ls) <= kPartMax && 2 * cost(ls) <= cost(best)) best = ls;
+    return best;
+}
+
 template <int WFMT, int OUTF, int AS, int MR>
 void launch_rowk(const void* act, const float* sa_in, const uint8_t* qw, const float* sw,
                  uint16_t* y, uint8_t* q, float* sa_out, float* amax, int N, int K,
@@ -331,10 +368,12 @@ void launch_rowk(const void* act, const float* sa_in, const uint8_t* qw, const f
 {
     using C = RowkCfg<MR>;
     const size_t lds = AS != AS_GLOBAL ? (size_t)MR * K : 0;
-    const int ngroups = (int)(((int64_t)N + C::ROWS - 1) / C::ROWS);
-    const int grid = min(ngroups, kCUs * C::WPC);
-    rowk_f8_kernel<WFMT, OUTF, AS, MR, C::ROWS, C::U, CP_NT, C::WPC>
-        <<<grid, kWgThreads, lds, st>>>(act, sa_in, qw, sw, y, q, sa_out, amax, N, K);
+    const int grid = min(N, kCUs * C::WPC);
+    const int rpw = (int)(((int64_t)N + grid - 1) / grid);
+    const int ls = rowk_split_shift(rpw, K, MR, C::U);
+    const int kseg = (int)(((((int64_t)K + (1 << ls) - 1) >> ls) + 127) & ~(int64_t)127);
+    rowk_f8_kernel<WFMT, OUTF, AS, MR, C::U, CP_NT, C::WPC>
+        <<<grid, kWgThreads, lds, st>>>(act, sa_in, qw, sw, y, q, sa_out, amax, N, K, rpw, ls, kseg);
 }
 
 // Unfused FP8 weights: codes staged in LDS when they fit, else read from L2.

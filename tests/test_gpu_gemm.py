@@ -323,3 +323,54 @@ def test_largest_k_bit_exact(M):
     y = _run_gemm(qa, 1.0, qw, 1.0)
     want = oracle.gemm_fp8_f32(qa, 1.0, qw, 1.0)
     assert np.array_equal(y, want)
+
+
+# ------------------------------------------------------------------ split-K rows
+# The M <= 2 row kernel cuts each weight row's K range over 2..16 waves when
+# its workgroups hold few rows of long K (partial sums added through LDS).
+# These shapes take that path with full and ragged last segments, workgroups
+# without rows (N = 4000 over 512 workgroups of 8 rows), codes staged in LDS
+# (M * K <= 32768) and read from L2 (M = 1, K = 65536).
+SPLIT_SHAPES = [(1, 4096, 11008), (1, 4000, 11008), (1, 3, 32752), (2, 16, 16384),
+                (2, 300, 16000), (1, 5, 65536), (2, 300, 11008)]
+
+
+@pytest.mark.parametrize("M,N,K", SPLIT_SHAPES)
+def test_split_k_rows_small_integers_bit_exact(M, N, K):
+    """Codes of 0, +-1, +-2, +-4 and a few +-448 keep every partial sum an
+    integer far below 2^24: exact in any summation order, so the split
+    kernel's output equals the oracle's bit for bit."""
+    rng = np.random.Generator(np.random.PCG64(M * 31 + N * 7 + K))
+    table = np.array([0x00, 0x38, 0x40, 0x48, 0xB8, 0xC0, 0xC8], np.uint8)   # 0, 1, 2, 4, -1, -2, -4
+    qa = table[rng.integers(0, 7, size=(M, K))]
+    qw = table[rng.integers(0, 7, size=(N, K))]
+    qa.flat[rng.integers(qa.size, size=2)] = 0x7E                             # 448
+    qw.flat[rng.integers(qw.size, size=4)] = 0xFE                             # -448
+    say("split-K rows small int", M, N, K)
+    y = _run_gemm(qa, 1.0, qw, 1.0)
+    assert np.array_equal(y, oracle.gemm_fp8_f32(qa, 1.0, qw, 1.0))
+
+
+@pytest.mark.parametrize("M,N,K", SPLIT_SHAPES)
+def test_split_k_rows_random_within_tolerance(M, N, K):
+    qa, sa, qw, sw = _quantized_operands(M, N, K, seed=M * 17 + N * 5 + K)
+    say("split-K rows random", M, N, K)
+    y = _run_gemm(qa, sa, qw, sw)
+    ref, ab = oracle.gemm_fp8_ref(qa, sa, qw, sw)
+    assert_within(oracle.bf16_decode(y).astype(np.float64).ravel(), ref, ab, f"{M}x{N}x{K}", "bf16")
+
+
+@pytest.mark.parametrize("M,N,K", [(1, 9, 32752), (2, 5, 16384)])
+def test_split_k_rows_identity_returns_every_weight(M, N, K):
+    """One-hot activations on the columns around every 2048-byte boundary
+    (where the split kernel's segments start and end) read the weights back
+    bit-exactly."""
+    rng = np.random.Generator(np.random.PCG64(N * K + M))
+    qw = _random_codes(rng, (N, K))
+    want = oracle.bf16_encode((oracle.e4m3_decode(qw) + 0.0).astype(np.float32))
+    cols = sorted({c for b in range(0, K + 1, 2048) for c in (b - 1, b) if 0 <= c < K} | {K - 1})
+    for c0 in range(0, len(cols), M):
+        cc = cols[c0:c0 + M]
+        say("split-K identity", M, N, K, cc[0])
+        y = _run_gemm(_ident_act(len(cc), K, np.array(cc)), 1.0, qw, 1.0)
+        assert np.array_equal(y, want[:, cc].T), f"columns {cc}"
