@@ -80,11 +80,13 @@ fp8q_status check_gemm_sizes(int64_t M, int64_t N, int64_t K)
 // FP8-operand GEMM dispatch on M: row-contiguous VALU path (M <= 2),
 // MFMA GEMV (M <= 16), MFMA tile GEMM (larger M).
 hipError_t dispatch_fp8(const uint8_t* qa, const float* sa, const uint8_t* qw, const float* sw,
-                        uint16_t* y, int M, int N, int K, int wfmt, int outf, hipStream_t st)
+                        uint16_t* y, int M, int N, int K, int wfmt, int outf, int rowscale,
+                        hipStream_t st)
 {
-    if (M <= kRowkMaxM) return launch_rowk_fp8(qa, sa, qw, sw, y, M, N, K, wfmt, outf, st);
-    if (M <= kDecodeMaxM) return launch_gemv_fp8(qa, sa, qw, sw, y, M, N, K, wfmt, outf, st);
-    return launch_tile_fp8(qa, sa, qw, sw, y, M, N, K, wfmt, outf, st);
+    if (M <= kRowkMaxM) return launch_rowk_fp8(qa, sa, qw, sw, y, M, N, K, wfmt, outf, rowscale, st);
+    if (M <= kDecodeMaxM)
+        return launch_gemv_fp8(qa, sa, qw, sw, y, M, N, K, wfmt, outf, rowscale, st);
+    return launch_tile_fp8(qa, sa, qw, sw, y, M, N, K, wfmt, outf, rowscale, st);
 }
 
 #define FP8Q_TRY(expr)                     \
@@ -96,11 +98,18 @@ hipError_t dispatch_fp8(const uint8_t* qa, const float* sa, const uint8_t* qw, c
 // quantize + GEMM of fp8_linear / nested_linear_fp8 (pointers already checked)
 fp8q_status linear_common(const char* where, const void* x, int dtype, const uint8_t* qw,
                           const float* sw, uint16_t* y, uint8_t* q, float* scale, float* amax,
-                          int64_t M, int64_t N, int64_t K, int wfmt, int outf, hipStream_t st)
+                          int64_t M, int64_t N, int64_t K, int wfmt, int outf, int rowscale,
+                          hipStream_t st)
 {
     if (M <= kRowkMaxM && M * K <= kFusedMaxMK)
         return finish(where, launch_linear_fused(x, dtype, qw, sw, y, q, scale, amax, (int)M,
-                                                 (int)N, (int)K, wfmt, outf, st));
+                                                 (int)N, (int)K, wfmt, outf, rowscale, st));
+    if (rowscale) {
+        hipError_t e = launch_quantize_rows(x, dtype, M, K, q, scale, amax, st);
+        if (e == hipSuccess)
+            e = dispatch_fp8(q, scale, qw, sw, y, (int)M, (int)N, (int)K, wfmt, outf, 1, st);
+        return finish(where, e);
+    }
     // y is written only by the GEMM, so until then it can hold the
     // quantizer's per-workgroup partial maxima (unless it overlaps x)
     const uintptr_t xb = reinterpret_cast<uintptr_t>(x), yb = reinterpret_cast<uintptr_t>(y);
@@ -109,7 +118,7 @@ fp8q_status linear_common(const char* where, const void* x, int dtype, const uin
                                            y_free ? reinterpret_cast<float*>(y) : nullptr,
                                            M * N / 2, st);
     if (e == hipSuccess)
-        e = dispatch_fp8(q, scale, qw, sw, y, (int)M, (int)N, (int)K, wfmt, outf, st);
+        e = dispatch_fp8(q, scale, qw, sw, y, (int)M, (int)N, (int)K, wfmt, outf, 0, st);
     return finish(where, e);
 }
 
@@ -156,7 +165,7 @@ fp8q_status fp8_gemm(const uint8_t* qa, const float* sa, const uint8_t* qw, cons
         return FP8Q_ERR_ALIGN;
     FP8Q_TRY(check_device());
     return finish("fp8_gemm", dispatch_fp8(qa, sa, qw, sw, y, (int)M, (int)N, (int)K, WF_E4M3,
-                                           OUT_BF16, (hipStream_t)stream));
+                                           OUT_BF16, 0, (hipStream_t)stream));
 }
 
 fp8q_status fp8_linear(const void* x, int dtype, const uint8_t* qw, const float* sw, uint16_t* y,
@@ -171,7 +180,48 @@ fp8q_status fp8_linear(const void* x, int dtype, const uint8_t* qw, const float*
         return FP8Q_ERR_ALIGN;
     FP8Q_TRY(check_device());
     return linear_common("fp8_linear", x, dtype, qw, sw, y, q, scale, amax, M, N, K, WF_E4M3,
-                         OUT_BF16, (hipStream_t)stream);
+                         OUT_BF16, 0, (hipStream_t)stream);
+}
+
+fp8q_status fp8_quantize_rows(const void* x, int dtype, int64_t rows, int64_t cols, uint8_t* q,
+                              float* scale, float* amax, fp8q_stream stream)
+{
+    if (!x || !q || !scale || !amax) return FP8Q_ERR_NULL;
+    if (dtype != FP8Q_BF16 && dtype != FP8Q_FP16) return FP8Q_ERR_DTYPE;
+    if (rows < 1 || rows > kMaxDim || cols < 16 || (cols % 16) != 0 || cols > kMaxK)
+        return FP8Q_ERR_SHAPE;
+    if (!aligned16(x) || !aligned16(q) || !aligned4(scale) || !aligned4(amax)) return FP8Q_ERR_ALIGN;
+    FP8Q_TRY(check_device());
+    return finish("fp8_quantize_rows",
+                  launch_quantize_rows(x, dtype, rows, cols, q, scale, amax, (hipStream_t)stream));
+}
+
+fp8q_status fp8_gemm_rowwise(const uint8_t* qa, const float* sa, const uint8_t* qw,
+                             const float* sw, uint16_t* y, int64_t M, int64_t N, int64_t K,
+                             fp8q_stream stream)
+{
+    if (!qa || !sa || !qw || !sw || !y) return FP8Q_ERR_NULL;
+    FP8Q_TRY(check_gemm_sizes(M, N, K));
+    if (!aligned16(qa) || !aligned16(qw) || !aligned16(y) || !aligned4(sa) || !aligned4(sw))
+        return FP8Q_ERR_ALIGN;
+    FP8Q_TRY(check_device());
+    return finish("fp8_gemm_rowwise", dispatch_fp8(qa, sa, qw, sw, y, (int)M, (int)N, (int)K,
+                                                   WF_E4M3, OUT_BF16, 1, (hipStream_t)stream));
+}
+
+fp8q_status fp8_linear_rowwise(const void* x, int dtype, const uint8_t* qw, const float* sw,
+                               uint16_t* y, uint8_t* q, float* sa, float* amax, int64_t M,
+                               int64_t N, int64_t K, fp8q_stream stream)
+{
+    if (!x || !qw || !sw || !y || !q || !sa || !amax) return FP8Q_ERR_NULL;
+    if (dtype != FP8Q_BF16 && dtype != FP8Q_FP16) return FP8Q_ERR_DTYPE;
+    FP8Q_TRY(check_gemm_sizes(M, N, K));
+    if (!aligned16(x) || !aligned16(qw) || !aligned16(y) || !aligned16(q) || !aligned4(sw) ||
+        !aligned4(sa) || !aligned4(amax))
+        return FP8Q_ERR_ALIGN;
+    FP8Q_TRY(check_device());
+    return linear_common("fp8_linear_rowwise", x, dtype, qw, sw, y, q, sa, amax, M, N, K, WF_E4M3,
+                         OUT_BF16, 1, (hipStream_t)stream);
 }
 
 fp8q_status nested_linear_fp8(const uint16_t* a, const uint8_t* hi, uint16_t* y, uint8_t* q,
@@ -185,7 +235,7 @@ fp8q_status nested_linear_fp8(const uint16_t* a, const uint8_t* hi, uint16_t* y,
         return FP8Q_ERR_ALIGN;
     FP8Q_TRY(check_device());
     return linear_common("nested_linear_fp8", a, FP8Q_FP16, hi, nullptr, y, q, scale, amax, M, N,
-                         K, WF_E5M2, OUT_FP16, (hipStream_t)stream);
+                         K, WF_E5M2, OUT_FP16, 0, (hipStream_t)stream);
 }
 
 fp8q_status nested_split(const uint16_t* w, uint8_t* hi, uint8_t* lo, int64_t n,
@@ -230,7 +280,7 @@ fp8q_status nested_gemm_fp8(const uint8_t* qa, const float* sa, const uint8_t* h
     if (!aligned16(qa) || !aligned16(hi) || !aligned16(y) || !aligned4(sa)) return FP8Q_ERR_ALIGN;
     FP8Q_TRY(check_device());
     return finish("nested_gemm_fp8", dispatch_fp8(qa, sa, hi, nullptr, y, (int)M, (int)N, (int)K,
-                                                  WF_E5M2, OUT_FP16, (hipStream_t)stream));
+                                                  WF_E5M2, OUT_FP16, 0, (hipStream_t)stream));
 }
 
 fp8q_status fp8q_e4m3_encode_f32(const float* v, uint8_t* q, int64_t n, fp8q_stream stream)

@@ -297,29 +297,36 @@ hipError_t launch_quantize_scratch(const void* x, int dtype, int64_t n, uint8_t*
                                    float* amax, float* scratch, int64_t scratch_floats,
                                    hipStream_t stream);
 
+// One scale per row of a [rows, cols] matrix (cols % 16 == 0): scale[r],
+// amax[r] and the codes of row r as fp8_quantize_act would give for that row.
+hipError_t launch_quantize_rows(const void* x, int dtype, int64_t rows, int64_t cols, uint8_t* q,
+                                float* scale, float* amax, hipStream_t stream);
+
 // Row-contiguous decode path for M <= kRowkMaxM (see linear.hip).
 constexpr int kRowkMaxM = 2;
 // Largest M*K the fused decode linear quantizes in LDS.
 constexpr int64_t kFusedMaxMK = 32768;
 hipError_t launch_rowk_fp8(const uint8_t* qa, const float* sa, const uint8_t* qw, const float* sw,
-                           uint16_t* y, int M, int N, int K, int wfmt, int outf,
+                           uint16_t* y, int M, int N, int K, int wfmt, int outf, int rowscale,
                            hipStream_t stream);
 hipError_t launch_rowk_nested16(const uint16_t* a, const uint8_t* hi, const uint8_t* lo,
                                 uint16_t* y, int M, int N, int K, hipStream_t stream);
 hipError_t launch_linear_fused(const void* x, int dtype, const uint8_t* qw, const float* sw,
                                uint16_t* y, uint8_t* q, float* scale, float* amax, int M, int N,
-                               int K, int wfmt, int outf, hipStream_t stream);
+                               int K, int wfmt, int outf, int rowscale, hipStream_t stream);
 hipError_t launch_e4m3_encode_f32(const float* v, uint8_t* q, int64_t n, hipStream_t stream);
 
 // Decode path (M <= 16) and tile path (M > 16) of the FP8 GEMM; wfmt selects
 // the weight format (E4M3 / E5M2), outf the output format (bf16 / fp16), and
-// sw == nullptr means the scale is *sa alone.
+// sw == nullptr means the scale is *sa alone.  With rowscale (E4M3 / bf16
+// only) sa holds M scales and sw N scales, and element (m, n) is scaled by
+// fl32(sa[m] * sw[n]).
 hipError_t launch_gemv_fp8(const uint8_t* qa, const float* sa, const uint8_t* qw,
                            const float* sw, uint16_t* y, int M, int N, int K, int wfmt,
-                           int outf, hipStream_t stream);
+                           int outf, int rowscale, hipStream_t stream);
 hipError_t launch_tile_fp8(const uint8_t* qa, const float* sa, const uint8_t* qw,
                            const float* sw, uint16_t* y, int M, int N, int K, int wfmt,
-                           int outf, hipStream_t stream);
+                           int outf, int rowscale, hipStream_t stream);
 
 hipError_t launch_nested_split(const uint16_t* w, uint8_t* hi, uint8_t* lo, int64_t n,
                                hipStream_t stream);

@@ -103,7 +103,7 @@ __global__ __launch_bounds__(WM * WN * 64) __attribute__((amdgpu_waves_per_eu(2)
 void gemm_f8_kernel(
     const uint8_t* __restrict__ qa, const float* __restrict__ sa,
     const uint8_t* __restrict__ qw, const float* __restrict__ sw,
-    uint16_t* __restrict__ y, int M, int N, int K)
+    uint16_t* __restrict__ y, int M, int N, int K, int rowscale)
 {
     constexpr int NW = WM * WN;
     constexpr int BK = 128;
@@ -218,31 +218,39 @@ void gemm_f8_kernel(
     }
     wait_vm<0>();                              // nothing left in flight into LDS
 
-    float s = *sa;
-    if (sw != nullptr) s = s * *sw;
-    // acc[i][j][e] is output row mb + 16 i + r, column nb + 16 j + 4 g + e
+    // acc[i][j][e] is output row mb + 16 i + r, column nb + 16 j + 4 g + e;
+    // scale_of(m, n) is the output scale of element (m, n)
     const int mb = m0 + wm * TM, nb = n0 + wn * TN;
     const bool vec = (N & 3) == 0;             // 8-byte aligned groups of 4 columns
+    auto store = [&](auto scale_of) {
 #pragma unroll
-    for (int i = 0; i < FM; ++i) {
-        const int m = mb + i * 16 + r;
-        if (m >= M) continue;
+        for (int i = 0; i < FM; ++i) {
+            const int m = mb + i * 16 + r;
+            if (m >= M) continue;
 #pragma unroll
-        for (int j = 0; j < FN; ++j) {
-            const int n = nb + j * 16 + 4 * g;
-            uint16_t* dst = y + (size_t)m * N + n;
-            if (vec && n + 3 < N) {
-                const uint32_t lo = f32_to_out_bits<OUTF>(acc[i][j][0] * s) |
-                                    (f32_to_out_bits<OUTF>(acc[i][j][1] * s) << 16);
-                const uint32_t hi = f32_to_out_bits<OUTF>(acc[i][j][2] * s) |
-                                    (f32_to_out_bits<OUTF>(acc[i][j][3] * s) << 16);
-                *reinterpret_cast<v2i*>(dst) = v2i{(int)lo, (int)hi};
-            } else {
+            for (int j = 0; j < FN; ++j) {
+                const int n = nb + j * 16 + 4 * g;
+                uint16_t* dst = y + (size_t)m * N + n;
+                if (vec && n + 3 < N) {
+                    const uint32_t lo = f32_to_out_bits<OUTF>(acc[i][j][0] * scale_of(m, n)) |
+                                        (f32_to_out_bits<OUTF>(acc[i][j][1] * scale_of(m, n + 1)) << 16);
+                    const uint32_t hi = f32_to_out_bits<OUTF>(acc[i][j][2] * scale_of(m, n + 2)) |
+                                        (f32_to_out_bits<OUTF>(acc[i][j][3] * scale_of(m, n + 3)) << 16);
+                    *reinterpret_cast<v2i*>(dst) = v2i{(int)lo, (int)hi};
+                } else {
 #pragma unroll
-                for (int e = 0; e < 4; ++e)
-                    if (n + e < N) dst[e] = (uint16_t)f32_to_out_bits<OUTF>(acc[i][j][e] * s);
+                    for (int e = 0; e < 4; ++e)
+                        if (n + e < N)
+                            dst[e] = (uint16_t)f32_to_out_bits<OUTF>(acc[i][j][e] * scale_of(m, n + e));
+                }
             }
         }
+    };
+    if (rowscale) {
+        store([&](int m, int n) { return sa[m] * sw[n]; });
+    } else {
+        const float s = (sw != nullptr) ? *sa * *sw : *sa;
+        store([&](int, int) { return s; });
     }
 }
 
@@ -382,7 +390,7 @@ void gemm_n16_kernel(const uint16_t* __restrict__ a, const uint8_t* __restrict__
 
 template <int WFMT, int OUTF, int BM, int BN, int WM, int WN, int AST, int WST>
 hipError_t launch_f8(const uint8_t* qa, const float* sa, const uint8_t* qw, const float* sw,
-                     uint16_t* y, int M, int N, int K, hipStream_t stream)
+                     uint16_t* y, int M, int N, int K, int rowscale, hipStream_t stream)
 {
     auto kern = gemm_f8_kernel<WFMT, OUTF, BM, BN, WM, WN, AST, WST>;
     constexpr size_t lds = ((size_t)AST * BM + (size_t)WST * BN) * 128;
@@ -397,7 +405,7 @@ hipError_t launch_f8(const uint8_t* qa, const float* sa, const uint8_t* qw, cons
     }
     const int64_t grid = (((int64_t)M + BM - 1) / BM) * (((int64_t)N + BN - 1) / BN);
     if (grid > 0x7fffffff) return hipErrorInvalidValue;
-    kern<<<(int)grid, WM * WN * 64, lds, stream>>>(qa, sa, qw, sw, y, M, N, K);
+    kern<<<(int)grid, WM * WN * 64, lds, stream>>>(qa, sa, qw, sw, y, M, N, K, rowscale);
     return hipGetLastError();
 }
 
@@ -438,27 +446,27 @@ inline int pick_tile_shape(const TileShape* shapes, int count, int M, int N)
 
 template <int WFMT, int OUTF>
 hipError_t launch_tile_fmt(const uint8_t* qa, const float* sa, const uint8_t* qw, const float* sw,
-                           uint16_t* y, int M, int N, int K, hipStream_t stream)
+                           uint16_t* y, int M, int N, int K, int rowscale, hipStream_t stream)
 {
     switch (pick_tile_shape(kTileShapes, sizeof(kTileShapes) / sizeof(kTileShapes[0]), M, N)) {
-    case 0: return launch_f8<WFMT, OUTF, 256, 256, 2, 4, 2, 2>(qa, sa, qw, sw, y, M, N, K, stream);
-    case 1: return launch_f8<WFMT, OUTF, 256, 192, 2, 4, 2, 3>(qa, sa, qw, sw, y, M, N, K, stream);
-    case 2: return launch_f8<WFMT, OUTF, 256, 128, 4, 2, 3, 4>(qa, sa, qw, sw, y, M, N, K, stream);
-    case 3: return launch_f8<WFMT, OUTF, 128, 192, 2, 4, 3, 4>(qa, sa, qw, sw, y, M, N, K, stream);
-    case 4: return launch_f8<WFMT, OUTF, 128, 128, 2, 4, 4, 4>(qa, sa, qw, sw, y, M, N, K, stream);
-    case 5: return launch_f8<WFMT, OUTF, 128, 64, 2, 2, 4, 4>(qa, sa, qw, sw, y, M, N, K, stream);
-    default: return launch_f8<WFMT, OUTF, 64, 64, 2, 2, 4, 4>(qa, sa, qw, sw, y, M, N, K, stream);
+    case 0: return launch_f8<WFMT, OUTF, 256, 256, 2, 4, 2, 2>(qa, sa, qw, sw, y, M, N, K, rowscale, stream);
+    case 1: return launch_f8<WFMT, OUTF, 256, 192, 2, 4, 2, 3>(qa, sa, qw, sw, y, M, N, K, rowscale, stream);
+    case 2: return launch_f8<WFMT, OUTF, 256, 128, 4, 2, 3, 4>(qa, sa, qw, sw, y, M, N, K, rowscale, stream);
+    case 3: return launch_f8<WFMT, OUTF, 128, 192, 2, 4, 3, 4>(qa, sa, qw, sw, y, M, N, K, rowscale, stream);
+    case 4: return launch_f8<WFMT, OUTF, 128, 128, 2, 4, 4, 4>(qa, sa, qw, sw, y, M, N, K, rowscale, stream);
+    case 5: return launch_f8<WFMT, OUTF, 128, 64, 2, 2, 4, 4>(qa, sa, qw, sw, y, M, N, K, rowscale, stream);
+    default: return launch_f8<WFMT, OUTF, 64, 64, 2, 2, 4, 4>(qa, sa, qw, sw, y, M, N, K, rowscale, stream);
     }
 }
 
 hipError_t launch_tile_fp8(const uint8_t* qa, const float* sa, const uint8_t* qw, const float* sw,
-                           uint16_t* y, int M, int N, int K, int wfmt, int outf,
+                           uint16_t* y, int M, int N, int K, int wfmt, int outf, int rowscale,
                            hipStream_t stream)
 {
     if (wfmt == WF_E4M3 && outf == OUT_BF16)
-        return launch_tile_fmt<WF_E4M3, OUT_BF16>(qa, sa, qw, sw, y, M, N, K, stream);
-    if (wfmt == WF_E5M2 && outf == OUT_FP16)
-        return launch_tile_fmt<WF_E5M2, OUT_FP16>(qa, sa, qw, sw, y, M, N, K, stream);
+        return launch_tile_fmt<WF_E4M3, OUT_BF16>(qa, sa, qw, sw, y, M, N, K, rowscale, stream);
+    if (wfmt == WF_E5M2 && outf == OUT_FP16 && !rowscale)
+        return launch_tile_fmt<WF_E5M2, OUT_FP16>(qa, sa, qw, sw, y, M, N, K, 0, stream);
     return hipErrorInvalidValue;
 }
 

@@ -38,8 +38,9 @@ __device__ __forceinline__ v8i cat(const v4i& lo, const v4i& hi)
 }
 
 // ---------------------------------------------------------------- FP8 GEMV
-// y[m, n] = out( sum_k qa[m,k] * W[n,k] * scale ),  scale = *sa * *sw (or *sa
-// when sw == nullptr).
+// y[m, n] = out( sum_k qa[m,k] * W[n,k] * scale(m, n) ), scale(m, n) =
+// fl32(*sa * *sw) (*sa when sw == nullptr), or fl32(sa[m] * sw[n]) with
+// rowscale (a scale per activation row and per weight row).
 //
 // All loads are raw buffer loads: the weight resource spans only the valid
 // rows of this workgroup's 16-row tile and the activation resource only the
@@ -51,7 +52,7 @@ template <int WFMT, int OUTF, int WAVES, int U, int CP>
 __global__ __launch_bounds__(WAVES * 64) void gemv_f8_kernel(
     const uint8_t* __restrict__ qa, const float* __restrict__ sa,
     const uint8_t* __restrict__ qw, const float* __restrict__ sw,
-    uint16_t* __restrict__ y, int M, int N, int K)
+    uint16_t* __restrict__ y, int M, int N, int K, int rowscale)
 {
     __shared__ float red[WAVES][16][17];
     const int lane = threadIdx.x & 63;
@@ -92,14 +93,14 @@ __global__ __launch_bounds__(WAVES * 64) void gemv_f8_kernel(
     for (int i = 0; i < 4; ++i) red[wave][4 * g + i][r] = acc[i];
     __syncthreads();
 
-    float s = *sa;
-    if (sw != nullptr) s = s * *sw;
+    const float s_w = (sw != nullptr) ? *sw : 1.0f;
     for (int t = threadIdx.x; t < M * 16; t += WAVES * 64) {
         const int m = t >> 4, c = t & 15;
         if (c >= rows) continue;
         float v = red[0][m][c];
 #pragma unroll
         for (int w = 1; w < WAVES; ++w) v += red[w][m][c];
+        const float s = rowscale ? sa[m] * sw[n0 + c] : *sa * s_w;
         y[(size_t)m * N + n0 + c] = (uint16_t)f32_to_out_bits<OUTF>(v * s);
     }
 }
@@ -188,16 +189,16 @@ constexpr int kNestedUnroll = 4;
 }  // namespace
 
 hipError_t launch_gemv_fp8(const uint8_t* qa, const float* sa, const uint8_t* qw, const float* sw,
-                           uint16_t* y, int M, int N, int K, int wfmt, int outf,
+                           uint16_t* y, int M, int N, int K, int wfmt, int outf, int rowscale,
                            hipStream_t stream)
 {
     const dim3 grid((unsigned)(((int64_t)N + 15) / 16)), block(kGemvWaves * 64);
     if (wfmt == WF_E4M3 && outf == OUT_BF16)
         gemv_f8_kernel<WF_E4M3, OUT_BF16, kGemvWaves, kGemvUnroll, CP_DEFAULT>
-            <<<grid, block, 0, stream>>>(qa, sa, qw, sw, y, M, N, K);
-    else if (wfmt == WF_E5M2 && outf == OUT_FP16)
+            <<<grid, block, 0, stream>>>(qa, sa, qw, sw, y, M, N, K, rowscale);
+    else if (wfmt == WF_E5M2 && outf == OUT_FP16 && !rowscale)
         gemv_f8_kernel<WF_E5M2, OUT_FP16, kGemvWaves, kGemvUnroll, CP_DEFAULT>
-            <<<grid, block, 0, stream>>>(qa, sa, qw, sw, y, M, N, K);
+            <<<grid, block, 0, stream>>>(qa, sa, qw, sw, y, M, N, K, 0);
     else
         return hipErrorInvalidValue;
     return hipGetLastError();

@@ -21,6 +21,8 @@
 // waits only for the activation and HBM is busy while it runs.  The FP8 GEMM is the one
 // of page "C++与FP8量化" §3.3; the quantization follows the page on a 7B
 // model on an RTX 4060, §2.2 and §6.1.
+#include <type_traits>
+
 #include "common.hpp"
 
 namespace fp8q {
@@ -73,7 +75,11 @@ enum : int {
     AS_FP16 = 3,     // fp16 activation quantized into LDS once per workgroup (fused)
 };
 
-// y[m, n] = out( sum_k dec(a[m,k]) * dec(W[n,k]) * s_a * (*sw or 1) ).
+// y[m, n] = out( sum_k dec(a[m,k]) * dec(W[n,k]) * scale(m, n) ), where
+// scale(m, n) = fl32(s_a * s_w) with one activation scale and one weight scale
+// (*sw, or 1 without weight scales), or, with rowscale set, fl32(s_a[m] *
+// s_w[n]) with a scale per activation row (token) and per weight row (output
+// channel).  The fused prologue then reduces amax per activation row.
 //
 // At most WPC 1024-thread workgroups per CU: the activation prologue (copy or
 // quantization into LDS) is paid once per workgroup and spread over 16 waves.
@@ -91,20 +97,20 @@ enum : int {
 // rowk_split_shift): splitting pays where a span has fewer rows than waves or
 // a row's last batch is mostly empty.  The activation and then the first
 // weight batch are requested before the prologue.
-template <int WFMT, int OUTF, int AS, int MR, int U, int CP, int WPC = 1>
+template <int WFMT, int OUTF, int AS, int MR, int U, int CP, int WPC, int XV>
 __global__ __launch_bounds__(kWgThreads) __attribute__((amdgpu_waves_per_eu(4 * WPC)))
 void rowk_f8_kernel(
     const void* __restrict__ act, const float* __restrict__ sa_in,
     const uint8_t* __restrict__ qw, const float* __restrict__ sw,
     uint16_t* __restrict__ y, uint8_t* __restrict__ q_out, float* __restrict__ sa_out,
-    float* __restrict__ amax_out, int N, int K, int rpw, int ls, int kseg)
+    float* __restrict__ amax_out, int N, int K, int rpw, int ls, int kseg, int rowscale)
 {
     constexpr bool FUSED = AS == AS_BF16 || AS == AS_FP16;
     constexpr bool IN_LDS = AS != AS_GLOBAL;
     constexpr int DT = AS == AS_BF16 ? DT_BF16 : DT_FP16;
     constexpr int W = kWgThreads / 64;
     extern __shared__ __attribute__((aligned(16))) uint8_t codes_lds[];   // IN_LDS: MR*K codes
-    __shared__ float red[W];
+    __shared__ float red[MR][W];
     __shared__ float part[kPartMax];   // S > 1: [m][row of the span][segment]
 
     const int tid = threadIdx.x, lane = tid & 63;
@@ -139,8 +145,12 @@ void rowk_f8_kernel(
     // requested before the first weight batch, so its (L2-resident) lines
     // return first and the prologue waits for them alone while the weights
     // are still in flight.
-    constexpr int VPT = (int)(kFusedMaxMK / 8 / kWgThreads);
-    constexpr int CPT = (int)(kFusedMaxMK / 16 / kWgThreads);
+    // XV 16-byte activation vectors per thread cover the activation: 8
+    // elements each for the fused prologue, 16 codes each for AS_COPY (the
+    // host picks the smallest of 1, 2, 4 that fits, which keeps registers
+    // free for the prologue)
+    constexpr int VPT = XV;
+    constexpr int CPT = XV;
     const int nunit = MR * K / 8;
     const int ncopy = MR * K / 16;
     v4i xr[VPT];
@@ -166,32 +176,60 @@ void rowk_f8_kernel(
     load_w(rbeg + (min(u0, max(nunits - 1, 0)) >> ls), klo, u0 < nunits);   // unconditional: see load_w
     __builtin_amdgcn_sched_barrier(0);
 
-    float s_a;
+    float s_a[MR];                    // the activation scale of each row (all equal without rowscale)
     if constexpr (FUSED) {
-        float m = 0.0f;
+        // per-row maxima (unit v belongs to row v / (K/8)), then one barrier
+        // for all rows; without rowscale every row takes the overall max
+        float mx[MR];
 #pragma unroll
-        for (int i = 0; i < VPT; ++i) m = fmaxf(m, vec_absmax<DT>(xr[i]));
-        const float amax = block_max<kWgThreads>(m, red);
-        s_a = scale_from_amax(amax);
-        const Quotient d(s_a);
+        for (int m = 0; m < MR; ++m) mx[m] = 0.0f;
+#pragma unroll
+        for (int i = 0; i < VPT; ++i) {
+            const float a = vec_absmax<DT>(xr[i]);
+            if (MR == 1 || tid + i * kWgThreads < nunit / MR) mx[0] = fmaxf(mx[0], a);
+            else mx[MR - 1] = fmaxf(mx[MR - 1], a);
+        }
+#pragma unroll
+        for (int m = 0; m < MR; ++m) {
+            mx[m] = wave_max(mx[m]);
+            if (lane == 0) red[m][wave] = mx[m];
+        }
+        __syncthreads();
+        float amax[MR];
+#pragma unroll
+        for (int m = 0; m < MR; ++m) {
+            amax[m] = red[m][0];
+#pragma unroll
+            for (int i = 1; i < W; ++i) amax[m] = fmaxf(amax[m], red[m][i]);
+        }
+        if (!rowscale) {
+#pragma unroll
+            for (int m = 1; m < MR; ++m) amax[0] = fmaxf(amax[0], amax[m]);
+#pragma unroll
+            for (int m = 1; m < MR; ++m) amax[m] = amax[0];
+        }
+#pragma unroll
+        for (int m = 0; m < MR; ++m) s_a[m] = scale_from_amax(amax[m]);
+        const Quotient d0(s_a[0]), d1(s_a[MR - 1]);
         v2i* cl = reinterpret_cast<v2i*>(codes_lds);
         v2i* qg = reinterpret_cast<v2i*>(q_out);
 #pragma unroll
         for (int i = 0; i < VPT; ++i) {
             const int v = tid + i * kWgThreads;
             if (v < nunit) {
-                const v2i c = vec_quantize<DT>(xr[i], d);
+                const v2i c = vec_quantize<DT>(xr[i], (MR == 1 || v < nunit / MR) ? d0 : d1);
                 cl[v] = c;
                 if (blockIdx.x == 0) qg[v] = c;
             }
         }
-        if (blockIdx.x == 0 && tid == 0) {
-            *sa_out = s_a;
-            *amax_out = amax;
+        if (blockIdx.x == 0 && tid < (rowscale ? MR : 1)) {
+            sa_out[tid] = s_a[tid];
+            amax_out[tid] = amax[tid];
         }
         __syncthreads();
     } else {
-        s_a = *sa_in;
+#pragma unroll
+        for (int m = 0; m < MR; ++m) s_a[m] = sa_in[rowscale ? m : 0];
         if constexpr (AS == AS_COPY) {
             v4i* dst = reinterpret_cast<v4i*>(codes_lds);
 #pragma unroll
@@ -202,7 +240,11 @@ void rowk_f8_kernel(
             __syncthreads();
         }
     }
-    const float s = (sw != nullptr) ? s_a * *sw : s_a;
+    // output scale of activation row m and weight row `row`
+    const float s_w = (sw != nullptr) ? *sw : 1.0f;
+    auto out_scale = [&](int m, int64_t row) {
+        return rowscale ? s_a[m] * sw[row] : s_a[m] * s_w;
+    };
     const rsrc_t ra = make_rsrc(act, (uint32_t)(MR * K));
 
     for (int u = u0; u < nunits; u += W) {
@@ -246,7 +288,7 @@ void rowk_f8_kernel(
         for (int m = 0; m < MR; ++m) {
             const float v = wave_sum(acc[m]);
             if (lane == 0) {
-                if (S == 1) y[(size_t)m * N + row] = (uint16_t)f32_to_out_bits<OUTF>(v * s);
+                if (S == 1) y[(size_t)m * N + row] = (uint16_t)f32_to_out_bits<OUTF>(v * out_scale(m, row));
                 else part[(m * nrows + lr) * S + seg] = v;
             }
         }
@@ -259,7 +301,7 @@ void rowk_f8_kernel(
             float v = 0.0f;
             for (int j = 0; j < S; ++j) v += part[t * S + j];
             const int m = t / nrows, lr = t - m * nrows;
-            y[(size_t)m * N + rbeg + lr] = (uint16_t)f32_to_out_bits<OUTF>(v * s);
+            y[(size_t)m * N + rbeg + lr] = (uint16_t)f32_to_out_bits<OUTF>(v * out_scale(m, rbeg + lr));
         }
     }
 }
@@ -364,7 +406,7 @@ int rowk_split_shift(int64_t rows_per_wg, int K, int MR, int U)
 template <int WFMT, int OUTF, int AS, int MR>
 void launch_rowk(const void* act, const float* sa_in, const uint8_t* qw, const float* sw,
                  uint16_t* y, uint8_t* q, float* sa_out, float* amax, int N, int K,
-                 hipStream_t st)
+                 int rowscale, hipStream_t st)
 {
     using C = RowkCfg<MR>;
     const size_t lds = AS != AS_GLOBAL ? (size_t)MR * K : 0;
@@ -372,33 +414,42 @@ void launch_rowk(const void* act, const float* sa_in, const uint8_t* qw, const f
     const int rpw = (int)(((int64_t)N + grid - 1) / grid);
     const int ls = rowk_split_shift(rpw, K, MR, C::U);
     const int kseg = (int)(((((int64_t)K + (1 << ls) - 1) >> ls) + 127) & ~(int64_t)127);
-    rowk_f8_kernel<WFMT, OUTF, AS, MR, C::U, CP_NT, C::WPC>
-        <<<grid, kWgThreads, lds, st>>>(act, sa_in, qw, sw, y, q, sa_out, amax, N, K, rpw, ls, kseg);
+    // 16-byte activation vectors per thread: MR*K/8 bf16/fp16 vectors for the
+    // fused prologue, MR*K/16 code vectors for AS_COPY (none for AS_GLOBAL)
+    const int64_t vecs = AS == AS_GLOBAL ? 0 : (int64_t)MR * K / (AS == AS_COPY ? 16 : 8);
+    auto go = [&](auto xv) {
+        rowk_f8_kernel<WFMT, OUTF, AS, MR, C::U, CP_NT, C::WPC, decltype(xv)::value>
+            <<<grid, kWgThreads, lds, st>>>(act, sa_in, qw, sw, y, q, sa_out, amax, N, K, rpw, ls,
+                                             kseg, rowscale);
+    };
+    if (vecs <= kWgThreads) go(std::integral_constant<int, 1>{});
+    else if (vecs <= 2 * kWgThreads) go(std::integral_constant<int, 2>{});
+    else go(std::integral_constant<int, 4>{});
 }
 
 // Unfused FP8 weights: codes staged in LDS when they fit, else read from L2.
 template <int WFMT, int OUTF, int MR>
 void launch_rowk_codes(const uint8_t* qa, const float* sa, const uint8_t* qw, const float* sw,
-                       uint16_t* y, int N, int K, hipStream_t st)
+                       uint16_t* y, int N, int K, int rowscale, hipStream_t st)
 {
     if ((int64_t)MR * K <= kFusedMaxMK)
-        launch_rowk<WFMT, OUTF, AS_COPY, MR>(qa, sa, qw, sw, y, nullptr, nullptr, nullptr, N, K, st);
+        launch_rowk<WFMT, OUTF, AS_COPY, MR>(qa, sa, qw, sw, y, nullptr, nullptr, nullptr, N, K, rowscale, st);
     else
-        launch_rowk<WFMT, OUTF, AS_GLOBAL, MR>(qa, sa, qw, sw, y, nullptr, nullptr, nullptr, N, K, st);
+        launch_rowk<WFMT, OUTF, AS_GLOBAL, MR>(qa, sa, qw, sw, y, nullptr, nullptr, nullptr, N, K, rowscale, st);
 }
 
 }  // namespace
 
 hipError_t launch_rowk_fp8(const uint8_t* qa, const float* sa, const uint8_t* qw, const float* sw,
-                           uint16_t* y, int M, int N, int K, int wfmt, int outf,
+                           uint16_t* y, int M, int N, int K, int wfmt, int outf, int rowscale,
                            hipStream_t stream)
 {
     if (wfmt == WF_E4M3 && outf == OUT_BF16) {
-        if (M == 1) launch_rowk_codes<WF_E4M3, OUT_BF16, 1>(qa, sa, qw, sw, y, N, K, stream);
-        else launch_rowk_codes<WF_E4M3, OUT_BF16, 2>(qa, sa, qw, sw, y, N, K, stream);
-    } else if (wfmt == WF_E5M2 && outf == OUT_FP16) {
-        if (M == 1) launch_rowk_codes<WF_E5M2, OUT_FP16, 1>(qa, sa, qw, sw, y, N, K, stream);
-        else launch_rowk_codes<WF_E5M2, OUT_FP16, 2>(qa, sa, qw, sw, y, N, K, stream);
+        if (M == 1) launch_rowk_codes<WF_E4M3, OUT_BF16, 1>(qa, sa, qw, sw, y, N, K, rowscale, stream);
+        else launch_rowk_codes<WF_E4M3, OUT_BF16, 2>(qa, sa, qw, sw, y, N, K, rowscale, stream);
+    } else if (wfmt == WF_E5M2 && outf == OUT_FP16 && !rowscale) {
+        if (M == 1) launch_rowk_codes<WF_E5M2, OUT_FP16, 1>(qa, sa, qw, sw, y, N, K, 0, stream);
+        else launch_rowk_codes<WF_E5M2, OUT_FP16, 2>(qa, sa, qw, sw, y, N, K, 0, stream);
     } else {
         return hipErrorInvalidValue;
     }
@@ -419,24 +470,25 @@ hipError_t launch_rowk_nested16(const uint16_t* a, const uint8_t* hi, const uint
 
 hipError_t launch_linear_fused(const void* x, int dtype, const uint8_t* qw, const float* sw,
                                uint16_t* y, uint8_t* q, float* scale, float* amax, int M, int N,
-                               int K, int wfmt, int outf, hipStream_t stream)
+                               int K, int wfmt, int outf, int rowscale, hipStream_t stream)
 {
+    if (rowscale && !(wfmt == WF_E4M3 && outf == OUT_BF16)) return hipErrorInvalidValue;
     if (wfmt == WF_E4M3 && outf == OUT_BF16 && dtype == DT_BF16) {
         if (M == 1)
-            launch_rowk<WF_E4M3, OUT_BF16, AS_BF16, 1>(x, nullptr, qw, sw, y, q, scale, amax, N, K, stream);
+            launch_rowk<WF_E4M3, OUT_BF16, AS_BF16, 1>(x, nullptr, qw, sw, y, q, scale, amax, N, K, rowscale, stream);
         else
-            launch_rowk<WF_E4M3, OUT_BF16, AS_BF16, 2>(x, nullptr, qw, sw, y, q, scale, amax, N, K, stream);
+            launch_rowk<WF_E4M3, OUT_BF16, AS_BF16, 2>(x, nullptr, qw, sw, y, q, scale, amax, N, K, rowscale, stream);
     } else if (wfmt == WF_E4M3 && outf == OUT_BF16 && dtype == DT_FP16) {
         if (M == 1)
-            launch_rowk<WF_E4M3, OUT_BF16, AS_FP16, 1>(x, nullptr, qw, sw, y, q, scale, amax, N, K, stream);
+            launch_rowk<WF_E4M3, OUT_BF16, AS_FP16, 1>(x, nullptr, qw, sw, y, q, scale, amax, N, K, rowscale, stream);
         else
-            launch_rowk<WF_E4M3, OUT_BF16, AS_FP16, 2>(x, nullptr, qw, sw, y, q, scale, amax, N, K, stream);
+            launch_rowk<WF_E4M3, OUT_BF16, AS_FP16, 2>(x, nullptr, qw, sw, y, q, scale, amax, N, K, rowscale, stream);
     } else if (wfmt == WF_E5M2 && outf == OUT_FP16 && dtype == DT_FP16) {
         // NestedFP FP8 mode: fp16 activation, hi plane as E5M2, no weight scale
         if (M == 1)
-            launch_rowk<WF_E5M2, OUT_FP16, AS_FP16, 1>(x, nullptr, qw, sw, y, q, scale, amax, N, K, stream);
+            launch_rowk<WF_E5M2, OUT_FP16, AS_FP16, 1>(x, nullptr, qw, sw, y, q, scale, amax, N, K, rowscale, stream);
         else
-            launch_rowk<WF_E5M2, OUT_FP16, AS_FP16, 2>(x, nullptr, qw, sw, y, q, scale, amax, N, K, stream);
+            launch_rowk<WF_E5M2, OUT_FP16, AS_FP16, 2>(x, nullptr, qw, sw, y, q, scale, amax, N, K, rowscale, stream);
     } else {
         return hipErrorInvalidValue;
     }

@@ -189,6 +189,54 @@ __global__ __launch_bounds__(kBigThreads) void quant_partial_kernel(
     }
 }
 
+// ---------------------------------------------------------------- per-row scales
+// One scale per row of a [rows, cols] matrix: the activation scale per token
+// and the weight scale per output channel of the TensorRT-LLM build the page
+// "C++与FP8量化" shows in §4.2 (its per-token and per-channel options).  One
+// workgroup per row: the first kRowVec vectors of 8 elements per thread stay
+// in registers between the amax pass and the quantization pass, the rest of a
+// longer row is read again (from L2).  Codes and scales are those of
+// fp8_quantize_act applied to each row on its own.
+constexpr int kRowThreads = 256;
+constexpr int kRowVec = 4;
+
+template <int DT>
+__global__ __launch_bounds__(kRowThreads) void quant_rows_kernel(
+    const uint16_t* __restrict__ x, int64_t cols, uint8_t* __restrict__ q,
+    float* __restrict__ scale, float* __restrict__ amax_out)
+{
+    __shared__ float lds[kRowThreads / 64];
+    const int64_t row = blockIdx.x;
+    const int nvec = (int)(cols >> 3);                     // cols % 16 == 0
+    const v4i* xv = reinterpret_cast<const v4i*>(x + row * cols);
+    v2i* qv = reinterpret_cast<v2i*>(q + row * cols);
+    const int t = threadIdx.x;
+    v4i v[kRowVec];
+    float m = 0.0f;
+#pragma unroll
+    for (int u = 0; u < kRowVec; ++u) {
+        const int i = t + u * kRowThreads;
+        v[u] = i < nvec ? xv[i] : v4i{0, 0, 0, 0};
+        m = fmaxf(m, vec_absmax<DT>(v[u]));
+    }
+    for (int i = t + kRowVec * kRowThreads; i < nvec; i += kRowThreads)
+        m = fmaxf(m, vec_absmax<DT>(xv[i]));
+    const float a = block_max<kRowThreads>(m, lds);
+    const float s = scale_from_amax(a);
+    const Quotient d(s);
+#pragma unroll
+    for (int u = 0; u < kRowVec; ++u) {
+        const int i = t + u * kRowThreads;
+        if (i < nvec) qv[i] = vec_quantize<DT>(v[u], d);
+    }
+    for (int i = t + kRowVec * kRowThreads; i < nvec; i += kRowThreads)
+        qv[i] = vec_quantize<DT>(xv[i], d);
+    if (t == 0) {
+        scale[row] = s;
+        amax_out[row] = a;
+    }
+}
+
 // ---------------------------------------------------------------- encoder export
 __global__ __launch_bounds__(256) void e4m3_encode_kernel(const float* __restrict__ v,
                                                           uint8_t* __restrict__ q, int64_t n)
@@ -246,6 +294,18 @@ hipError_t launch_quantize_scratch(const void* x, int dtype, int64_t n, uint8_t*
         amax_partial_kernel<DT_FP16><<<g, kBigThreads, 0, stream>>>(xs, n, scratch);
         quant_partial_kernel<DT_FP16><<<g, kBigThreads, 0, stream>>>(xs, n, q, scale, amax, scratch);
     }
+    return hipGetLastError();
+}
+
+hipError_t launch_quantize_rows(const void* x, int dtype, int64_t rows, int64_t cols, uint8_t* q,
+                                float* scale, float* amax, hipStream_t stream)
+{
+    if (rows < 1 || rows > 0x7fffffff || cols < 16 || (cols & 15) != 0) return hipErrorInvalidValue;
+    const uint16_t* xs = static_cast<const uint16_t*>(x);
+    if (dtype == DT_BF16)
+        quant_rows_kernel<DT_BF16><<<(unsigned)rows, kRowThreads, 0, stream>>>(xs, cols, q, scale, amax);
+    else
+        quant_rows_kernel<DT_FP16><<<(unsigned)rows, kRowThreads, 0, stream>>>(xs, cols, q, scale, amax);
     return hipGetLastError();
 }
 

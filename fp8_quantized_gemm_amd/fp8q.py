@@ -40,6 +40,9 @@ _SIGS = {
     "nested_gemm_fp8": (_i, [_p, _p, _p, _p, _i64, _i64, _i64, _p]),
     "nested_linear_fp8": (_i, [_p, _p, _p, _p, _p, _p, _i64, _i64, _i64, _p]),
     "fp8q_e4m3_encode_f32": (_i, [_p, _p, _i64, _p]),
+    "fp8_quantize_rows": (_i, [_p, _i, _i64, _i64, _p, _p, _p, _p]),
+    "fp8_gemm_rowwise": (_i, [_p, _p, _p, _p, _p, _i64, _i64, _i64, _p]),
+    "fp8_linear_rowwise": (_i, [_p, _i, _p, _p, _p, _p, _p, _p, _i64, _i64, _i64, _p]),
 }
 for _name, (_res, _args) in _SIGS.items():
     _fn = getattr(lib, _name)
@@ -163,6 +166,77 @@ def fp8_linear(x: torch.Tensor, qw: torch.Tensor, sw: torch.Tensor,
         _dev(y, "y", torch.bfloat16, (M, N)), _dev(q, "q", torch.uint8, (M, K)),
         _scalar(scale, "scale"), _scalar(amax, "amax"), M, N, K, _stream(x)))
     return y, q, scale, amax
+
+
+def _vector(t: torch.Tensor, name: str, n: int):
+    if t.numel() != n:
+        raise ValueError(f"{name} must hold {n} float32 values, got {t.numel()}")
+    return _dev(t, name, torch.float32)
+
+
+def _dtype_code(x: torch.Tensor) -> int:
+    if x.dtype == torch.bfloat16:
+        return BF16
+    if x.dtype == torch.float16:
+        return FP16
+    raise TypeError(f"x must be bfloat16 or float16, got {x.dtype}")
+
+
+def fp8_quantize_rows(x: torch.Tensor, q: torch.Tensor | None = None,
+                      scale: torch.Tensor | None = None, amax: torch.Tensor | None = None):
+    """One E4M3 scale per row of x[rows, cols] (bf16/fp16): per-token activation
+    or per-channel weight scales.  Returns (q uint8 [rows, cols], scale float32
+    [rows], amax float32 [rows])."""
+    code = _dtype_code(x)
+    if x.dim() != 2:
+        raise ValueError(f"x must be 2-D [rows, cols], got {tuple(x.shape)}")
+    rows, cols = x.shape
+    if q is None:
+        q = torch.empty((rows, cols), dtype=torch.uint8, device=x.device)
+    if scale is None:
+        scale = torch.empty(rows, dtype=torch.float32, device=x.device)
+    if amax is None:
+        amax = torch.empty(rows, dtype=torch.float32, device=x.device)
+    _check("fp8_quantize_rows", lib.fp8_quantize_rows(
+        _dev(x, "x"), code, rows, cols, _dev(q, "q", torch.uint8, (rows, cols)),
+        _vector(scale, "scale", rows), _vector(amax, "amax", rows), _stream(x)))
+    return q, scale, amax
+
+
+def fp8_gemm_rowwise(qa: torch.Tensor, sa: torch.Tensor, qw: torch.Tensor, sw: torch.Tensor,
+                     y: torch.Tensor | None = None) -> torch.Tensor:
+    """y[M,N] bf16 = (qa . qw^T)[m,n] * fl32(sa[m] * sw[n]): per-token activation
+    and per-channel weight scales, fp32 accumulation."""
+    M, N, K = _mnk(qa, qw)
+    if y is None:
+        y = torch.empty((M, N), dtype=torch.bfloat16, device=qa.device)
+    _check("fp8_gemm_rowwise", lib.fp8_gemm_rowwise(
+        _dev(qa, "qa", torch.uint8), _vector(sa, "sa", M), _dev(qw, "qw", torch.uint8),
+        _vector(sw, "sw", N), _dev(y, "y", torch.bfloat16, (M, N)), M, N, K, _stream(qa)))
+    return y
+
+
+def fp8_linear_rowwise(x: torch.Tensor, qw: torch.Tensor, sw: torch.Tensor,
+                       y: torch.Tensor | None = None, q: torch.Tensor | None = None,
+                       sa: torch.Tensor | None = None, amax: torch.Tensor | None = None):
+    """fp8_quantize_rows on x[M,K], then fp8_gemm_rowwise with the per-channel
+    weight scales sw[N].  Returns (y, q, sa, amax)."""
+    code = _dtype_code(x)
+    M, N, K = _mnk(x, qw)
+    dev = x.device
+    if y is None:
+        y = torch.empty((M, N), dtype=torch.bfloat16, device=dev)
+    if q is None:
+        q = torch.empty((M, K), dtype=torch.uint8, device=dev)
+    if sa is None:
+        sa = torch.empty(M, dtype=torch.float32, device=dev)
+    if amax is None:
+        amax = torch.empty(M, dtype=torch.float32, device=dev)
+    _check("fp8_linear_rowwise", lib.fp8_linear_rowwise(
+        _dev(x, "x"), code, _dev(qw, "qw", torch.uint8), _vector(sw, "sw", N),
+        _dev(y, "y", torch.bfloat16, (M, N)), _dev(q, "q", torch.uint8, (M, K)),
+        _vector(sa, "sa", M), _vector(amax, "amax", M), M, N, K, _stream(x)))
+    return y, q, sa, amax
 
 
 def nested_split(w: torch.Tensor, hi: torch.Tensor | None = None,

@@ -1,5 +1,6 @@
 /*
- * fp8q.h - C ABI of libfp8q: FP8 E4M3 per-tensor-scaled linear layers and the
+ * fp8q.h - C ABI of libfp8q: FP8 E4M3 linear layers (per-tensor scales, or per-token
+ * activation and per-channel weight scales) and the
  * NestedFP dual-precision GEMM on AMD MI355X (gfx950).
  *
  * Pages whose statement of the problem these calls follow:
@@ -124,6 +125,54 @@ FP8Q_API fp8q_status fp8_gemm(const uint8_t* qa, const float* sa, const uint8_t*
 FP8Q_API fp8q_status fp8_linear(const void* x, int dtype, const uint8_t* qw, const float* sw,
                        uint16_t* y, uint8_t* q, float* scale, float* amax, int64_t M,
                        int64_t N, int64_t K, fp8q_stream stream);
+
+/*
+ * fp8_quantize_rows - one E4M3 scale per row of x[rows, cols]: per-token
+ *   activation scales, or per-channel weight scales when x is a weight
+ *   matrix [N, K] (the per-token / per-channel options of the TensorRT-LLM
+ *   build in [C++FP8] §4.2).  Row r is quantized exactly as fp8_quantize_act
+ *   quantizes it on its own:
+ *
+ *   x[rows,cols]  in : bf16/fp16 bit patterns (dtype as for fp8_quantize_act)
+ *   q[rows,cols]  out: E4M3 codes of row r with scale[r]
+ *   scale[rows]   out: fl32(amax[r] / 448), or 1.0 when amax[r] == 0
+ *   amax[rows]    out: max over row r of |x|
+ *   1 <= rows <= 2^31-1;  16 <= cols <= 2^22 and cols % 16 == 0.
+ */
+FP8Q_API fp8q_status fp8_quantize_rows(const void* x, int dtype, int64_t rows, int64_t cols,
+                                       uint8_t* q, float* scale, float* amax,
+                                       fp8q_stream stream);
+
+/*
+ * fp8_gemm_rowwise - fp8_gemm with a scale per activation row and per weight
+ *   row: y[m,n] = bf16( (sum_k dec(qa[m,k]) dec(qw[n,k])) * fl32(sa[m] * sw[n]) ),
+ *   fp32 accumulation, the epilogue applied once per element.
+ *
+ *   qa[M,K], sa[M] in: E4M3 activation codes and per-token scales
+ *   qw[N,K], sw[N] in: E4M3 weight codes and per-channel scales
+ *   y[M,N]         out: bf16 bit patterns
+ *   Size rules and dispatch as fp8_gemm.
+ */
+FP8Q_API fp8q_status fp8_gemm_rowwise(const uint8_t* qa, const float* sa, const uint8_t* qw,
+                                      const float* sw, uint16_t* y, int64_t M, int64_t N,
+                                      int64_t K, fp8q_stream stream);
+
+/*
+ * fp8_linear_rowwise - fp8_quantize_rows on the activation, then
+ *   fp8_gemm_rowwise on its codes; bit-identical to the two calls made in
+ *   sequence.
+ *
+ *   x[M,K]    in : bf16/fp16 activation
+ *   qw[N,K], sw[N] in: E4M3 weight codes and per-channel scales
+ *   y[M,N]    out: bf16 bit patterns
+ *   q[M,K], sa[M], amax[M] out: activation codes, per-token scales and amax
+ *   Size rules as fp8_gemm.  For M <= 2 and M*K <= 32768 one kernel (each
+ *   workgroup quantizes both rows in LDS); otherwise two launches.
+ */
+FP8Q_API fp8q_status fp8_linear_rowwise(const void* x, int dtype, const uint8_t* qw,
+                                        const float* sw, uint16_t* y, uint8_t* q, float* sa,
+                                        float* amax, int64_t M, int64_t N, int64_t K,
+                                        fp8q_stream stream);
 
 /*
  * nested_split - NestedFP byte split of fp16 weights ([NestedFP] §2.1):

@@ -40,6 +40,10 @@ def _load():
         "orc_scale_from_amax": (_c.c_float, [_c.c_float]),
         "orc_quantize_with_scale": (None, [_p, _c.c_int, _i64, _c.c_float, _p]),
         "orc_quantize": (None, [_p, _c.c_int, _i64, _p, _p, _p]),
+        "orc_quantize_rows": (None, [_p, _c.c_int, _i64, _i64, _p, _p, _p]),
+        "orc_gemm_fp8_rowwise_ref": (None, [_p, _p, _p, _p, _i64, _i64, _i64,
+                                            _p, _p, _i64, _p, _p]),
+        "orc_gemm_fp8_rowwise_f32": (None, [_p, _p, _p, _p, _i64, _i64, _i64, _p, _c.c_int]),
         "orc_nested_split": (None, [_p, _p, _p, _i64]),
         "orc_nested_rebuild": (None, [_p, _p, _p, _i64]),
         "orc_gemm_fp8_ref": (None, [_p, _c.c_float, _p, _c.c_float, _i64, _i64, _i64,
@@ -166,6 +170,19 @@ def quantize(x_bits, dtype: int):
     return q, float(s[0]), float(a[0])
 
 
+def quantize_rows(x_bits, dtype: int):
+    """Per-row quantization of a [rows, cols] bf16/fp16 matrix (uint16 bits):
+    returns (codes [rows, cols], scale float32 [rows], amax float32 [rows])."""
+    x = _c_arr(x_bits, np.uint16)
+    assert x.ndim == 2
+    rows, cols = x.shape
+    q = np.empty(x.shape, np.uint8)
+    s = np.zeros(rows, np.float32)
+    a = np.zeros(rows, np.float32)
+    lib.orc_quantize_rows(_ptr(x), dtype, rows, cols, _ptr(q), _ptr(s), _ptr(a))
+    return q, s, a
+
+
 # ---------------------------------------------------------------- NestedFP
 def nested_split(w_bits):
     w = _c_arr(w_bits, np.uint16)
@@ -238,6 +255,41 @@ def nested_fp8_ref(qa, sa, hi, ms=None, ns=None):
     lib.orc_nested_fp8_ref(_ptr(qa), sa, _ptr(hi), M, N, K, _ptr(ms), _ptr(ns), ms.size,
                            _ptr(ref), _ptr(ab))
     return ref, ab
+
+
+def gemm_fp8_rowwise_ref(qa, sa, qw, sw, ms=None, ns=None):
+    """fp64 (ref, absref) of the FP8 GEMM with scales sa[M] per activation row
+    and sw[N] per weight row, at (ms[i], ns[i]) (all of [M,N] if None)."""
+    qa = _c_arr(qa, np.uint8)
+    qw = _c_arr(qw, np.uint8)
+    M, K = qa.shape
+    N, K2 = qw.shape
+    assert K == K2
+    sa = _c_arr(sa, np.float32)
+    sw = _c_arr(sw, np.float32)
+    assert sa.shape == (M,) and sw.shape == (N,)
+    ms, ns = _pairs(M, N, ms, ns)
+    ref = np.empty(ms.size, np.float64)
+    ab = np.empty(ms.size, np.float64)
+    lib.orc_gemm_fp8_rowwise_ref(_ptr(qa), _ptr(sa), _ptr(qw), _ptr(sw), M, N, K, _ptr(ms),
+                                 _ptr(ns), ms.size, _ptr(ref), _ptr(ab))
+    return ref, ab
+
+
+def gemm_fp8_rowwise_f32(qa, sa, qw, sw, nthreads=None):
+    """The plain fp32-accumulating FP8 GEMM with scales sa[M] and sw[N]:
+    y[m,n] = bf16(acc * fl32(sa[m] * sw[n])); returns bf16 bits [M,N]."""
+    qa = _c_arr(qa, np.uint8)
+    qw = _c_arr(qw, np.uint8)
+    M, K = qa.shape
+    N, _ = qw.shape
+    sa = _c_arr(sa, np.float32)
+    sw = _c_arr(sw, np.float32)
+    assert sa.shape == (M,) and sw.shape == (N,)
+    y = np.empty((M, N), np.uint16)
+    lib.orc_gemm_fp8_rowwise_f32(_ptr(qa), _ptr(sa), _ptr(qw), _ptr(sw), M, N, K, _ptr(y),
+                                 nthreads or default_threads())
+    return y
 
 
 def default_threads() -> int:

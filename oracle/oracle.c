@@ -236,6 +236,17 @@ void orc_quantize(const uint16_t* x, int dtype, int64_t n, uint8_t* q, float* sc
     *amax = a;
 }
 
+/* One scale per row of a [rows, cols] matrix: per-token activation scales   */
+/* and per-channel weight scales (the per-token / per-channel options of the */
+/* TensorRT-LLM build in [C++FP8] §4.2).  Each row is quantized on its own   */
+/* with the three steps above.                                               */
+void orc_quantize_rows(const uint16_t* x, int dtype, int64_t rows, int64_t cols, uint8_t* q,
+                       float* scale, float* amax)
+{
+    for (int64_t r = 0; r < rows; ++r)
+        orc_quantize(x + r * cols, dtype, cols, q + r * cols, scale + r, amax + r);
+}
+
 /* ------------------------------------------------------------------------ */
 /* NestedFP byte split and rebuild ([NestedFP] §2.1): an fp16 word is kept   */
 /* as its upper byte and its lower byte; FP16 mode rebuilds (upper<<8)|lower */
@@ -273,6 +284,7 @@ typedef struct {
     const int64_t* ms; const int64_t* ns;
     int64_t t0, t1;
     double* ref; double* absref;
+    const float* sav; const float* swv;   /* FP8 with a scale per row of a and of w */
 } ref_job;
 
 static void ref_pair(const ref_job* j, int64_t t)
@@ -288,7 +300,7 @@ static void ref_pair(const ref_job* j, int64_t t)
             sum += p;
             sabs += fabs(p);
         }
-        scale = (double)j->sa * (double)j->sw;
+        scale = (double)(j->sav ? j->sav[m] : j->sa) * (double)(j->swv ? j->swv[n] : j->sw);
     } else if (j->kind == 1) {
         /* NestedFP FP16 mode: fp16 activation x fp16 word (hi<<8)|lo, no scale */
         const uint16_t* a = (const uint16_t*)j->a + m * K;
@@ -357,7 +369,19 @@ void orc_gemm_fp8_ref(const uint8_t* qa, float sa, const uint8_t* qw, float sw,
                       double* ref, double* absref)
 {
     (void)M; (void)N;
-    ref_job j = {0, qa, qw, NULL, sa, sw, K, ms, ns, 0, 0, ref, absref};
+    ref_job j = {0, qa, qw, NULL, sa, sw, K, ms, ns, 0, 0, ref, absref, NULL, NULL};
+    run_ref(j, count);
+}
+
+/* FP8 GEMM with a scale per activation row (sa[M]) and per weight row (sw[N]):
+   the pair (m, n) is scaled by sa[m] * sw[n]. */
+void orc_gemm_fp8_rowwise_ref(const uint8_t* qa, const float* sa, const uint8_t* qw,
+                              const float* sw, int64_t M, int64_t N, int64_t K,
+                              const int64_t* ms, const int64_t* ns, int64_t count,
+                              double* ref, double* absref)
+{
+    (void)M; (void)N;
+    ref_job j = {0, qa, qw, NULL, 0.0f, 0.0f, K, ms, ns, 0, 0, ref, absref, sa, sw};
     run_ref(j, count);
 }
 
@@ -368,7 +392,7 @@ void orc_nested_fp16_ref(const uint16_t* a16, const uint8_t* hi, const uint8_t* 
                          double* ref, double* absref)
 {
     (void)M; (void)N;
-    ref_job j = {1, a16, hi, lo, 1.0f, 1.0f, K, ms, ns, 0, 0, ref, absref};
+    ref_job j = {1, a16, hi, lo, 1.0f, 1.0f, K, ms, ns, 0, 0, ref, absref, NULL, NULL};
     run_ref(j, count);
 }
 
@@ -379,7 +403,7 @@ void orc_nested_fp8_ref(const uint8_t* qa, float sa, const uint8_t* hi,
                         double* ref, double* absref)
 {
     (void)M; (void)N;
-    ref_job j = {2, qa, hi, NULL, sa, 1.0f, K, ms, ns, 0, 0, ref, absref};
+    ref_job j = {2, qa, hi, NULL, sa, 1.0f, K, ms, ns, 0, 0, ref, absref, NULL, NULL};
     run_ref(j, count);
 }
 
@@ -397,6 +421,7 @@ typedef struct {
     float sa, sw;
     int64_t M, N, K, n0, n1;
     uint16_t* y;
+    const float* sav; const float* swv;   /* KIND_FP8 with per-row scales, else NULL */
 } gemm_job;
 
 static void* gemm_worker(void* arg)
@@ -410,7 +435,8 @@ static void* gemm_worker(void* arg)
                 const uint8_t* w = j->w + n * j->K;
                 for (int64_t k = 0; k < j->K; ++k)
                     acc += (float)orc_e4m3_decode(a[k]) * (float)orc_e4m3_decode(w[k]);
-                float s = j->sa * j->sw;                    /* fl32(s_a * s_w) */
+                float s = (j->sav ? j->sav[m] : j->sa) *
+                          (j->swv ? j->swv[n] : j->sw);     /* fl32(s_a * s_w) */
                 j->y[m * j->N + n] = orc_bf16_encode(acc * s);
             } else if (j->kind == KIND_NESTED_FP16) {
                 const uint16_t* a = (const uint16_t*)j->a + m * j->K;
@@ -433,9 +459,9 @@ static void* gemm_worker(void* arg)
     return NULL;
 }
 
-static void run_gemm(int kind, const void* a, const uint8_t* w, const uint8_t* w2,
-                     float sa, float sw, int64_t M, int64_t N, int64_t K,
-                     uint16_t* y, int nthreads)
+static void run_gemm_scaled(int kind, const void* a, const uint8_t* w, const uint8_t* w2,
+                            float sa, float sw, const float* sav, const float* swv,
+                            int64_t M, int64_t N, int64_t K, uint16_t* y, int nthreads)
 {
     if (nthreads < 1) nthreads = 1;
     if (nthreads > 256) nthreads = 256;
@@ -447,7 +473,7 @@ static void run_gemm(int kind, const void* a, const uint8_t* w, const uint8_t* w
     for (int t = 0; t < nthreads; ++t) {
         int64_t n0 = t * chunk, n1 = n0 + chunk < N ? n0 + chunk : N;
         if (n0 >= n1) break;
-        jobs[t] = (gemm_job){kind, a, w, w2, sa, sw, M, N, K, n0, n1, y};
+        jobs[t] = (gemm_job){kind, a, w, w2, sa, sw, M, N, K, n0, n1, y, sav, swv};
         if (pthread_create(&th[t], NULL, gemm_worker, &jobs[t]) != 0) {
             gemm_worker(&jobs[t]);                           /* run inline if no thread */
             th[t] = 0;
@@ -456,6 +482,21 @@ static void run_gemm(int kind, const void* a, const uint8_t* w, const uint8_t* w
     }
     for (int t = 0; t < started; ++t)
         if (th[t]) pthread_join(th[t], NULL);
+}
+
+static void run_gemm(int kind, const void* a, const uint8_t* w, const uint8_t* w2,
+                     float sa, float sw, int64_t M, int64_t N, int64_t K,
+                     uint16_t* y, int nthreads)
+{
+    run_gemm_scaled(kind, a, w, w2, sa, sw, NULL, NULL, M, N, K, y, nthreads);
+}
+
+/* y[M,N] bf16 = bf16(fl32(acc) * fl32(s_a[m]*s_w[n])), acc = fp32 sum over k. */
+void orc_gemm_fp8_rowwise_f32(const uint8_t* qa, const float* sa, const uint8_t* qw,
+                              const float* sw, int64_t M, int64_t N, int64_t K, uint16_t* y,
+                              int nthreads)
+{
+    run_gemm_scaled(KIND_FP8, qa, qw, NULL, 0.0f, 0.0f, sa, sw, M, N, K, y, nthreads);
 }
 
 /* y[M,N] bf16 = bf16(fl32(acc) * fl32(s_a*s_w)), acc = fp32 sum over k. */

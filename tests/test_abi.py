@@ -29,7 +29,8 @@ def test_header_declares_the_entry_points():
     names = declared_functions()
     for want in ["fp8_quantize_act", "fp8_gemm", "fp8_linear", "nested_split", "nested_rebuild_fp16",
                  "nested_gemm_fp16", "nested_gemm_fp8", "nested_linear_fp8", "fp8q_abi_version",
-                 "fp8q_status_str", "fp8q_last_error", "fp8q_e4m3_encode_f32"]:
+                 "fp8q_status_str", "fp8q_last_error", "fp8q_e4m3_encode_f32",
+                 "fp8_quantize_rows", "fp8_gemm_rowwise", "fp8_linear_rowwise"]:
         assert want in names
 
 
@@ -118,6 +119,28 @@ GEMM_SIG = [P16, P16, P16, P16, P16]
     ("nested_linear_fp8", [P16, P17, P16, P16, P16, P16, 1, 1, 16, NULL], ERR_ALIGN),
     ("nested_linear_fp8", [P16, P16, P16, P16, ctypes.c_void_p(0x1002), P16, 1, 1, 16, NULL],
      ERR_ALIGN),
+    # fp8_quantize_rows(x, dtype, rows, cols, q, scale, amax, stream)
+    ("fp8_quantize_rows", [NULL, 0, 1, 16, P16, P16, P16, NULL], ERR_NULL),
+    ("fp8_quantize_rows", [P16, 0, 1, 16, P16, NULL, P16, NULL], ERR_NULL),
+    ("fp8_quantize_rows", [P16, 2, 1, 16, P16, P16, P16, NULL], ERR_DTYPE),
+    ("fp8_quantize_rows", [P16, 0, 0, 16, P16, P16, P16, NULL], ERR_SHAPE),
+    ("fp8_quantize_rows", [P16, 0, 1, 8, P16, P16, P16, NULL], ERR_SHAPE),
+    ("fp8_quantize_rows", [P16, 0, 1, 24, P16, P16, P16, NULL], ERR_SHAPE),
+    ("fp8_quantize_rows", [P16, 0, 2**31, 16, P16, P16, P16, NULL], ERR_SHAPE),
+    ("fp8_quantize_rows", [P16, 0, 1, 2**22 + 16, P16, P16, P16, NULL], ERR_SHAPE),
+    ("fp8_quantize_rows", [P17, 0, 1, 16, P16, P16, P16, NULL], ERR_ALIGN),
+    ("fp8_quantize_rows", [P16, 1, 1, 16, P16, P16, ctypes.c_void_p(0x1002), NULL], ERR_ALIGN),
+    # fp8_gemm_rowwise(qa, sa, qw, sw, y, M, N, K, stream)
+    ("fp8_gemm_rowwise", [P16, P16, P16, NULL, P16, 1, 1, 16, NULL], ERR_NULL),
+    ("fp8_gemm_rowwise", [P16, P16, P16, P16, P16, 1, 1, 40, NULL], ERR_SHAPE),
+    ("fp8_gemm_rowwise", [P16, P16, P16, P16, P16, 0, 1, 16, NULL], ERR_SHAPE),
+    ("fp8_gemm_rowwise", [P16, P16, P16, P16, P17, 1, 1, 16, NULL], ERR_ALIGN),
+    ("fp8_gemm_rowwise", [P16, ctypes.c_void_p(0x1002), P16, P16, P16, 1, 1, 16, NULL], ERR_ALIGN),
+    # fp8_linear_rowwise(x, dtype, qw, sw, y, q, sa, amax, M, N, K, stream)
+    ("fp8_linear_rowwise", [P16, 0, P16, P16, P16, P16, NULL, P16, 1, 1, 16, NULL], ERR_NULL),
+    ("fp8_linear_rowwise", [P16, 5, P16, P16, P16, P16, P16, P16, 1, 1, 16, NULL], ERR_DTYPE),
+    ("fp8_linear_rowwise", [P16, 0, P16, P16, P16, P16, P16, P16, 1, 1, 8, NULL], ERR_SHAPE),
+    ("fp8_linear_rowwise", [P16, 0, P16, P16, P16, P17, P16, P16, 1, 1, 16, NULL], ERR_ALIGN),
     # fp8q_e4m3_encode_f32(v, q, n, stream)
     ("fp8q_e4m3_encode_f32", [NULL, P16, 4, NULL], ERR_NULL),
     ("fp8q_e4m3_encode_f32", [P16, P16, 0, NULL], ERR_SHAPE),
