@@ -94,23 +94,26 @@ class Model:
     """Device-resident weights and per-linear buffers of one decode workload."""
 
     def __init__(self, torch, fp8q, synth, M: int, dev: str, spec=None, layers: int = LAYERS,
-                 sigma: float = 0.02, tag: str = "w"):
+                 sigma: float = 0.02, tag: str = "w", rowwise: bool = False):
         self.M = M
         self.linears = []
         for layer in range(layers):
             for name, K, N in (spec if spec is not None else synth.LLAMA7B_LINEARS):
                 w = synth.normal((N, K), sigma, "fp16", seed=synth.seed_for(tag, layer, name),
                                  device=dev)
-                qw, sw, _ = fp8q.fp8_quantize_act(w)      # offline static quantization
+                # offline static quantization: one scale per tensor, or per
+                # output channel
+                qw, sw, _ = fp8q.fp8_quantize_rows(w) if rowwise else fp8q.fp8_quantize_act(w)
                 del w
-                self.linears.append(dict(layer=layer, name=name, K=K, N=N, qw=qw, sw=sw))
+                self.linears.append(dict(layer=layer, name=name, K=K, N=N, qw=qw, sw=sw,
+                                         rowwise=rowwise))
         for L in self.linears:
             K, N = L["K"], L["N"]
             L["x"] = synth.activation(M, K, seed=synth.seed_for("x", M, L["layer"], L["name"]),
                                       device=dev)
             L["q"] = torch.empty((M, K), dtype=torch.uint8, device=dev)
-            L["sa"] = torch.empty(1, dtype=torch.float32, device=dev)
-            L["amax"] = torch.empty(1, dtype=torch.float32, device=dev)
+            L["sa"] = torch.empty(M if rowwise else 1, dtype=torch.float32, device=dev)
+            L["amax"] = torch.empty(M if rowwise else 1, dtype=torch.float32, device=dev)
             L["y"] = torch.empty((M, N), dtype=torch.bfloat16, device=dev)
         torch.cuda.synchronize()
 
@@ -126,11 +129,13 @@ class Model:
 
 
 def linear_call(fp8q, L):
-    fp8q.fp8_linear(L["x"], L["qw"], L["sw"], L["y"], L["q"], L["sa"], L["amax"])
+    fn = fp8q.fp8_linear_rowwise if L["rowwise"] else fp8q.fp8_linear
+    fn(L["x"], L["qw"], L["sw"], L["y"], L["q"], L["sa"], L["amax"])
 
 
 def gemm_call(fp8q, L):
-    fp8q.fp8_gemm(L["q"], L["sa"], L["qw"], L["sw"], L["y"])
+    fn = fp8q.fp8_gemm_rowwise if L["rowwise"] else fp8q.fp8_gemm
+    fn(L["q"], L["sa"], L["qw"], L["sw"], L["y"])
 
 
 def run_step(fp8q, model, events=None, call=linear_call):
@@ -233,6 +238,9 @@ def with_activations(torch, synth, model1, M, dev, tag, outliers=False):
                                   outliers=outliers, device=dev)
         d["q"] = torch.empty((M, K), dtype=torch.uint8, device=dev)
         d["y"] = torch.empty((M, N), dtype=torch.bfloat16, device=dev)
+        if L["rowwise"]:
+            d["sa"] = torch.empty(M, dtype=torch.float32, device=dev)
+            d["amax"] = torch.empty(M, dtype=torch.float32, device=dev)
         mm.linears.append(d)
     return mm
 
@@ -256,9 +264,10 @@ def prefill_figures(torch, fp8q, mm, graph=True):
             "ms_per_step": round(dt * 1e3, 3)}
 
 
-def secondary(torch, fp8q, synth, model1, dev, parts=("decode", "prefill", "qwen", "nested"),
-              graph=True):
-    """Prefill, M = 4/8 decode, Qwen-32B and NestedFP figures (a few steps each)."""
+def secondary(torch, fp8q, synth, model1, dev,
+              parts=("decode", "prefill", "qwen", "rowwise", "nested"), graph=True):
+    """Prefill, M = 4/8 decode, Qwen-32B, per-token/per-channel and NestedFP
+    figures (a few steps each)."""
     out = {}
     # decode at M = 4, 8 on the same weights (activations re-drawn)
     for M in ((4, 8) if "decode" in parts else ()):
@@ -284,6 +293,16 @@ def secondary(torch, fp8q, synth, model1, dev, parts=("decode", "prefill", "qwen
             torch, fp8q, with_activations(torch, synth, mq, 1024, dev, "xqp"), graph), layers=8)
         progress("qwen-32b done")
         del mq
+    # per-token activation and per-channel weight scales (fp8_linear_rowwise)
+    # on 8 Llama-7B layers: 1.6 GB of E4M3 weights, cold in HBM on every step
+    if "rowwise" in parts:
+        mr = Model(torch, fp8q, synth, M=1, dev=dev, layers=8, tag="w", rowwise=True)
+        out["rowwise_decode_m1"] = dict(decode_figures(torch, fp8q, mr, graph), layers=8)
+        out["rowwise_prefill_m512"] = dict(prefill_figures(
+            torch, fp8q, with_activations(torch, synth, mr, 512, dev, "xp", outliers=True), graph),
+            layers=8)
+        progress("per-token / per-channel done")
+        del mr
     if "nested" not in parts:
         return out
     # NestedFP at M = 1 and 256 on 8 layers of fp16 weights (hi/lo planes)

@@ -219,7 +219,7 @@ void gemm_f8_kernel(
     wait_vm<0>();                              // nothing left in flight into LDS
 
     // acc[i][j][e] is output row mb + 16 i + r, column nb + 16 j + 4 g + e;
-    // scale_of(m, n) is the output scale of element (m, n)
+    // scale_of(i, j, e) is the output scale of that element
     const int mb = m0 + wm * TM, nb = n0 + wn * TN;
     const bool vec = (N & 3) == 0;             // 8-byte aligned groups of 4 columns
     auto store = [&](auto scale_of) {
@@ -232,25 +232,40 @@ void gemm_f8_kernel(
                 const int n = nb + j * 16 + 4 * g;
                 uint16_t* dst = y + (size_t)m * N + n;
                 if (vec && n + 3 < N) {
-                    const uint32_t lo = f32_to_out_bits<OUTF>(acc[i][j][0] * scale_of(m, n)) |
-                                        (f32_to_out_bits<OUTF>(acc[i][j][1] * scale_of(m, n + 1)) << 16);
-                    const uint32_t hi = f32_to_out_bits<OUTF>(acc[i][j][2] * scale_of(m, n + 2)) |
-                                        (f32_to_out_bits<OUTF>(acc[i][j][3] * scale_of(m, n + 3)) << 16);
+                    const uint32_t lo = f32_to_out_bits<OUTF>(acc[i][j][0] * scale_of(i, j, 0)) |
+                                        (f32_to_out_bits<OUTF>(acc[i][j][1] * scale_of(i, j, 1)) << 16);
+                    const uint32_t hi = f32_to_out_bits<OUTF>(acc[i][j][2] * scale_of(i, j, 2)) |
+                                        (f32_to_out_bits<OUTF>(acc[i][j][3] * scale_of(i, j, 3)) << 16);
                     *reinterpret_cast<v2i*>(dst) = v2i{(int)lo, (int)hi};
                 } else {
 #pragma unroll
                     for (int e = 0; e < 4; ++e)
                         if (n + e < N)
-                            dst[e] = (uint16_t)f32_to_out_bits<OUTF>(acc[i][j][e] * scale_of(m, n + e));
+                            dst[e] = (uint16_t)f32_to_out_bits<OUTF>(acc[i][j][e] * scale_of(i, j, e));
                 }
             }
         }
     };
     if (rowscale) {
-        store([&](int m, int n) { return sa[m] * sw[n]; });
+        // the tile's row and column scales, loaded before the first store so
+        // that no load waits behind the output stores
+        float sam[FM], swn[FN][4];
+#pragma unroll
+        for (int i = 0; i < FM; ++i) {
+            const int m = mb + i * 16 + r;
+            sam[i] = m < M ? sa[m] : 0.0f;
+        }
+#pragma unroll
+        for (int j = 0; j < FN; ++j)
+#pragma unroll
+            for (int e = 0; e < 4; ++e) {
+                const int n = nb + j * 16 + 4 * g + e;
+                swn[j][e] = n < N ? sw[n] : 0.0f;
+            }
+        store([&](int i, int j, int e) { return sam[i] * swn[j][e]; });
     } else {
         const float s = (sw != nullptr) ? *sa * *sw : *sa;
-        store([&](int, int) { return s; });
+        store([&](int, int, int) { return s; });
     }
 }
 
