@@ -41,6 +41,7 @@ def _load():
         "orc_quantize_with_scale": (None, [_p, _c.c_int, _i64, _c.c_float, _p]),
         "orc_quantize": (None, [_p, _c.c_int, _i64, _p, _p, _p]),
         "orc_quantize_rows": (None, [_p, _c.c_int, _i64, _i64, _p, _p, _p]),
+        "orc_quantize_delayed": (None, [_p, _c.c_int, _i64, _p, _p, _p, _p, _i64, _p]),
         "orc_gemm_fp8_rowwise_ref": (None, [_p, _p, _p, _p, _i64, _i64, _i64,
                                             _p, _p, _i64, _p, _p]),
         "orc_gemm_fp8_rowwise_f32": (None, [_p, _p, _p, _p, _i64, _i64, _i64, _p, _c.c_int]),
@@ -181,6 +182,35 @@ def quantize_rows(x_bits, dtype: int):
     a = np.zeros(rows, np.float32)
     lib.orc_quantize_rows(_ptr(x), dtype, rows, cols, _ptr(q), _ptr(s), _ptr(a))
     return q, s, a
+
+
+class DelayedScaling:
+    """Delayed scaling with an amax history of `length` calls (state kept on
+    the host): each call quantizes with the scale the earlier calls' amax
+    history gives (1 before any call), then records its own amax."""
+
+    def __init__(self, length: int):
+        assert length >= 1
+        self.history = np.zeros(length, np.float32)
+        self.state = np.zeros(4, np.uint32)          # [next scale bits, 0, position, 0]
+
+    @property
+    def next_scale(self) -> float:
+        return float(self.state[:1].view(np.float32)[0])
+
+    @property
+    def position(self) -> int:
+        return int(self.state[2])
+
+    def quantize(self, x_bits, dtype: int):
+        """Returns (codes, scale used, amax of x) and advances the history."""
+        x = _c_arr(x_bits, np.uint16)
+        q = np.empty(x.shape, np.uint8)
+        s = np.zeros(1, np.float32)
+        a = np.zeros(1, np.float32)
+        lib.orc_quantize_delayed(_ptr(x), dtype, x.size, _ptr(q), _ptr(s), _ptr(a),
+                                 _ptr(self.history), self.history.size, _ptr(self.state))
+        return q, float(s[0]), float(a[0])
 
 
 # ---------------------------------------------------------------- NestedFP

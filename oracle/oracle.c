@@ -247,6 +247,39 @@ void orc_quantize_rows(const uint16_t* x, int dtype, int64_t rows, int64_t cols,
         orc_quantize(x + r * cols, dtype, cols, q + r * cols, scale + r, amax + r);
 }
 
+/* Delayed scaling with an amax history ([RTX4060] §6.1 asks that the amax   */
+/* history be at least 1024 long).  Reading: history[L] holds the amax of    */
+/* the last L calls on this tensor (zeros before any call), state[0] is the  */
+/* scale the next call uses (0 = no history yet, meaning 1) and state[2] the */
+/* ring position (as an integer).  One call:                                 */
+/*   1. s = state[0] > 0 ? state[0] : 1                                      */
+/*   2. q_i = E4M3_rne_sat(fl32(x_i / s))   (values beyond 448 s saturate)    */
+/*   3. a = max |x_i|                                                        */
+/*   4. history[pos] = a; pos = (pos + 1) mod L                              */
+/*   5. state[0] = scale_from_amax(max over history)                         */
+/* and the call reports s and a.  state[1] and state[3] are the device's     */
+/* accumulators; the oracle leaves them at 0, as the device does between    */
+/* calls.                                                                    */
+void orc_quantize_delayed(const uint16_t* x, int dtype, int64_t n, uint8_t* q, float* scale,
+                          float* amax, float* history, int64_t L, uint32_t* state)
+{
+    float next;
+    memcpy(&next, &state[0], 4);
+    float s = next > 0.0f ? next : 1.0f;
+    orc_quantize_with_scale(x, dtype, n, s, q);
+    float a = orc_amax(x, dtype, n);
+    uint32_t pos = state[2];
+    history[pos] = a;
+    state[2] = (uint32_t)((pos + 1) % (uint64_t)L);
+    float hmax = 0.0f;
+    for (int64_t i = 0; i < L; ++i)
+        if (history[i] > hmax) hmax = history[i];
+    next = orc_scale_from_amax(hmax);
+    memcpy(&state[0], &next, 4);
+    *scale = s;
+    *amax = a;
+}
+
 /* ------------------------------------------------------------------------ */
 /* NestedFP byte split and rebuild ([NestedFP] §2.1): an fp16 word is kept   */
 /* as its upper byte and its lower byte; FP16 mode rebuilds (upper<<8)|lower */
