@@ -133,6 +133,10 @@ def linear_call(fp8q, L):
     fn(L["x"], L["qw"], L["sw"], L["y"], L["q"], L["sa"], L["amax"])
 
 
+def delayed_call(fp8q, L):
+    fp8q.fp8_linear_delayed(L["x"], L["qw"], L["sw"], L["ds"], L["y"], L["q"], L["sa"], L["amax"])
+
+
 def gemm_call(fp8q, L):
     fn = fp8q.fp8_gemm_rowwise if L["rowwise"] else fp8q.fp8_gemm
     fn(L["q"], L["sa"], L["qw"], L["sw"], L["y"])
@@ -245,16 +249,16 @@ def with_activations(torch, synth, model1, M, dev, tag, outliers=False):
     return mm
 
 
-def decode_figures(torch, fp8q, mm, graph=True):
-    dt, _ = time_steps(torch, fp8q, mm, steps=5, warmup=2, graph=graph)
+def decode_figures(torch, fp8q, mm, graph=True, call=linear_call):
+    dt, _ = time_steps(torch, fp8q, mm, steps=5, warmup=2, graph=graph, call=call)
     byts = sum(mm.gemm_bytes(L) + mm.quant_bytes(L) for L in mm.linears)
     return {"GB_per_s": round(byts / dt / 1e9, 1),
             "frac_hbm": round(byts / dt / 1e9 / HBM_PEAK_GBS, 4),
             "ms_per_step": round(dt * 1e3, 3)}
 
 
-def prefill_figures(torch, fp8q, mm, graph=True):
-    dt, _ = time_steps(torch, fp8q, mm, steps=3, warmup=1, graph=graph)
+def prefill_figures(torch, fp8q, mm, graph=True, call=linear_call):
+    dt, _ = time_steps(torch, fp8q, mm, steps=3, warmup=1, graph=graph, call=call)
     # the GEMM alone, on the codes and scales the timed steps left behind
     _, gdev = time_steps(torch, fp8q, mm, steps=3, warmup=1, graph=graph, call=gemm_call)
     fl = sum(mm.flops(L) for L in mm.linears)
@@ -265,9 +269,9 @@ def prefill_figures(torch, fp8q, mm, graph=True):
 
 
 def secondary(torch, fp8q, synth, model1, dev,
-              parts=("decode", "prefill", "qwen", "rowwise", "nested"), graph=True):
-    """Prefill, M = 4/8 decode, Qwen-32B, per-token/per-channel and NestedFP
-    figures (a few steps each)."""
+              parts=("decode", "prefill", "delayed", "qwen", "rowwise", "nested"), graph=True):
+    """Prefill, M = 4/8 decode, delayed scaling, Qwen-32B, per-token/per-channel
+    and NestedFP figures (a few steps each)."""
     out = {}
     # decode at M = 4, 8 on the same weights (activations re-drawn)
     for M in ((4, 8) if "decode" in parts else ()):
@@ -280,6 +284,18 @@ def secondary(torch, fp8q, synth, model1, dev,
         out[f"prefill_m{M}"] = prefill_figures(torch, fp8q, mm, graph)
         progress(f"prefill M={M} done")
         del mm
+    # delayed scaling (amax history of 1024 per linear) on the same 32 layers:
+    # the activation is quantized in one pass with the history's scale
+    if "delayed" in parts:
+        for L in model1.linears:
+            L["ds"] = fp8q.DelayedScaling(1024, device=dev)
+        out["delayed_decode_m1"] = decode_figures(torch, fp8q, model1, graph, call=delayed_call)
+        mm = with_activations(torch, synth, model1, 512, dev, "xp", outliers=True)
+        out["delayed_prefill_m512"] = prefill_figures(torch, fp8q, mm, graph, call=delayed_call)
+        progress("delayed scaling done")
+        del mm
+        for L in model1.linears:
+            del L["ds"]
     # Qwen-32B linears (weights N(0, 0.015)) on 8 of the 64 layers: 3.9 GB of
     # E4M3 weights, still cold in HBM on every step; decode M = 1, 16, prefill
     # M = 1024

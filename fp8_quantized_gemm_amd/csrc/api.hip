@@ -183,6 +183,52 @@ fp8q_status fp8_linear(const void* x, int dtype, const uint8_t* qw, const float*
                          OUT_BF16, 0, (hipStream_t)stream);
 }
 
+// History lengths the delayed-scaling calls accept.
+constexpr int64_t kMaxHistory = (int64_t)1 << 24;
+
+fp8q_status fp8_quantize_act_delayed(const void* x, int dtype, int64_t n, uint8_t* q,
+                                     float* scale, float* amax, float* history,
+                                     int64_t history_len, uint32_t* state, fp8q_stream stream)
+{
+    if (!x || !q || !scale || !amax || !history || !state) return FP8Q_ERR_NULL;
+    if (dtype != FP8Q_BF16 && dtype != FP8Q_FP16) return FP8Q_ERR_DTYPE;
+    if (n < 1 || n > ((int64_t)1 << 40) || history_len < 1 || history_len > kMaxHistory)
+        return FP8Q_ERR_SHAPE;
+    if (!aligned16(x) || !aligned16(q) || !aligned4(scale) || !aligned4(amax) ||
+        !aligned4(history) || !aligned16(state))
+        return FP8Q_ERR_ALIGN;
+    FP8Q_TRY(check_device());
+    return finish("fp8_quantize_act_delayed",
+                  launch_quantize_delayed(x, dtype, n, q, scale, amax, history, history_len, state,
+                                          (hipStream_t)stream));
+}
+
+fp8q_status fp8_linear_delayed(const void* x, int dtype, const uint8_t* qw, const float* sw,
+                               uint16_t* y, uint8_t* q, float* scale, float* amax,
+                               float* history, int64_t history_len, uint32_t* state, int64_t M,
+                               int64_t N, int64_t K, fp8q_stream stream)
+{
+    if (!x || !qw || !sw || !y || !q || !scale || !amax || !history || !state)
+        return FP8Q_ERR_NULL;
+    if (dtype != FP8Q_BF16 && dtype != FP8Q_FP16) return FP8Q_ERR_DTYPE;
+    FP8Q_TRY(check_gemm_sizes(M, N, K));
+    if (history_len < 1 || history_len > kMaxHistory) return FP8Q_ERR_SHAPE;
+    if (!aligned16(x) || !aligned16(qw) || !aligned16(y) || !aligned16(q) || !aligned4(sw) ||
+        !aligned4(scale) || !aligned4(amax) || !aligned4(history) || !aligned16(state))
+        return FP8Q_ERR_ALIGN;
+    FP8Q_TRY(check_device());
+    hipStream_t st = (hipStream_t)stream;
+    if (M <= kRowkMaxM && M * K <= kFusedMaxMK)
+        return finish("fp8_linear_delayed",
+                      launch_linear_fused_delayed(x, dtype, qw, sw, y, q, scale, amax, history,
+                                                  history_len, state, (int)M, (int)N, (int)K, st));
+    hipError_t e = launch_quantize_delayed(x, dtype, M * K, q, scale, amax, history, history_len,
+                                           state, st);
+    if (e == hipSuccess)
+        e = dispatch_fp8(q, scale, qw, sw, y, (int)M, (int)N, (int)K, WF_E4M3, OUT_BF16, 0, st);
+    return finish("fp8_linear_delayed", e);
+}
+
 fp8q_status fp8_quantize_rows(const void* x, int dtype, int64_t rows, int64_t cols, uint8_t* q,
                               float* scale, float* amax, fp8q_stream stream)
 {

@@ -286,6 +286,43 @@ __device__ __forceinline__ float wave_sum(float v)
     return v;
 }
 
+// ---------------------------------------------------------------- delayed scaling
+// Delayed scaling with an amax history ([RTX4060] §6.1 asks for a history of
+// at least 1024 values).  A call quantizes with the scale that the earlier
+// calls' history gives, then records its own amax:
+//   history[L]  the amax of the last L calls (zeros before any call)
+//   state[0]    float bits of the scale the next call uses (0: none yet -> 1)
+//   state[1]    float bits of the running max of the current call
+//   state[2]    ring position
+//   state[3]    workgroups of the current call that have arrived
+// state[1] and state[3] are back at 0 when a call ends, so the caller only
+// zero-fills state and history once.  Calls on one state must not overlap.
+__device__ __forceinline__ float delayed_scale(const uint32_t* state)
+{
+    const float s = __uint_as_float(state[0]);
+    return s > 0.0f ? s : 1.0f;
+}
+
+// Run by every thread of the one workgroup that ends a call: history[pos] =
+// amax, the next scale from the maximum of the new history, pos advanced,
+// the accumulators cleared.
+template <int NT>
+__device__ __forceinline__ void delayed_publish(float amax, float* history, int64_t L,
+                                                uint32_t* state, float* lds)
+{
+    const uint32_t pos = (int64_t)state[2] < L ? state[2] : 0u;   // a corrupted position stays in range
+    float m = 0.0f;
+    for (int64_t i = threadIdx.x; i < L; i += NT) m = fmaxf(m, i == pos ? amax : history[i]);
+    m = block_max<NT>(m, lds);
+    if (threadIdx.x == 0) {
+        history[pos] = amax;
+        state[0] = __float_as_uint(scale_from_amax(m));
+        state[1] = 0u;
+        state[2] = (int64_t)pos + 1 == L ? 0u : pos + 1;
+        state[3] = 0u;
+    }
+}
+
 // ---------------------------------------------------------------- launchers
 // Each returns the hipError_t of hipGetLastError() after its launches.
 hipError_t launch_quantize(const void* x, int dtype, int64_t n, uint8_t* q, float* scale,
@@ -302,6 +339,12 @@ hipError_t launch_quantize_scratch(const void* x, int dtype, int64_t n, uint8_t*
 hipError_t launch_quantize_rows(const void* x, int dtype, int64_t rows, int64_t cols, uint8_t* q,
                                 float* scale, float* amax, hipStream_t stream);
 
+// Delayed-scaling quantizer (see delayed_scale): q, the scale it used and the
+// amax of x; history and state advanced by one call.
+hipError_t launch_quantize_delayed(const void* x, int dtype, int64_t n, uint8_t* q, float* scale,
+                                   float* amax, float* history, int64_t L, uint32_t* state,
+                                   hipStream_t stream);
+
 // Row-contiguous decode path for M <= kRowkMaxM (see linear.hip).
 constexpr int kRowkMaxM = 2;
 // Largest M*K the fused decode linear quantizes in LDS.
@@ -314,6 +357,11 @@ hipError_t launch_rowk_nested16(const uint16_t* a, const uint8_t* hi, const uint
 hipError_t launch_linear_fused(const void* x, int dtype, const uint8_t* qw, const float* sw,
                                uint16_t* y, uint8_t* q, float* scale, float* amax, int M, int N,
                                int K, int wfmt, int outf, int rowscale, hipStream_t stream);
+// The fused decode linear with delayed scaling (E4M3 weights, bf16 output).
+hipError_t launch_linear_fused_delayed(const void* x, int dtype, const uint8_t* qw, const float* sw,
+                                       uint16_t* y, uint8_t* q, float* scale, float* amax,
+                                       float* history, int64_t L, uint32_t* state, int M, int N,
+                                       int K, hipStream_t stream);
 hipError_t launch_e4m3_encode_f32(const float* v, uint8_t* q, int64_t n, hipStream_t stream);
 
 // Decode path (M <= 16) and tile path (M > 16) of the FP8 GEMM; wfmt selects

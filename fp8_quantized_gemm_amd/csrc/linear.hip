@@ -97,15 +97,23 @@ enum : int {
 // rowk_split_shift): splitting pays where a span has fewer rows than waves or
 // a row's last batch is mostly empty.  The activation and then the first
 // weight batch are requested before the prologue.
-template <int WFMT, int OUTF, int AS, int MR, int U, int CP, int WPC, int XV>
+//
+// With DS (delayed scaling, fused prologue only) the activation scale is the
+// one the amax history gives (delayed_scale), so the prologue quantizes as
+// soon as the activation arrives, without a block-wide amax first; each
+// workgroup counts itself in state[3] after its prologue, and the one that
+// arrives last reduces the amax at its end and publishes the call.
+template <int WFMT, int OUTF, int AS, int MR, int U, int CP, int WPC, int XV, bool DS = false>
 __global__ __launch_bounds__(kWgThreads) __attribute__((amdgpu_waves_per_eu(4 * WPC)))
 void rowk_f8_kernel(
     const void* __restrict__ act, const float* __restrict__ sa_in,
     const uint8_t* __restrict__ qw, const float* __restrict__ sw,
     uint16_t* __restrict__ y, uint8_t* __restrict__ q_out, float* __restrict__ sa_out,
-    float* __restrict__ amax_out, int N, int K, int rpw, int ls, int kseg, int rowscale)
+    float* __restrict__ amax_out, int N, int K, int rpw, int ls, int kseg, int rowscale,
+    float* __restrict__ history, int64_t hist_len, uint32_t* __restrict__ state)
 {
     constexpr bool FUSED = AS == AS_BF16 || AS == AS_FP16;
+    static_assert(!DS || FUSED, "delayed scaling belongs to the fused prologue");
     constexpr bool IN_LDS = AS != AS_GLOBAL;
     constexpr int DT = AS == AS_BF16 ? DT_BF16 : DT_FP16;
     constexpr int W = kWgThreads / 64;
@@ -177,7 +185,35 @@ void rowk_f8_kernel(
     __builtin_amdgcn_sched_barrier(0);
 
     float s_a[MR];                    // the activation scale of each row (all equal without rowscale)
-    if constexpr (FUSED) {
+    bool arrived_last = false;        // DS: thread 0 of the workgroup that ends the call
+    if constexpr (DS) {
+        float xmax = 0.0f;
+        const float sd = delayed_scale(state);
+#pragma unroll
+        for (int m = 0; m < MR; ++m) s_a[m] = sd;
+        const Quotient d(sd);
+        v2i* cl = reinterpret_cast<v2i*>(codes_lds);
+        v2i* qg = reinterpret_cast<v2i*>(q_out);
+#pragma unroll
+        for (int i = 0; i < VPT; ++i) {
+            const int v = tid + i * kWgThreads;
+            xmax = fmaxf(xmax, vec_absmax<DT>(xr[i]));
+            if (v < nunit) {
+                const v2i c = vec_quantize<DT>(xr[i], d);
+                cl[v] = c;
+                if (blockIdx.x == 0) qg[v] = c;
+            }
+        }
+        if (blockIdx.x == 0 && tid == 0) sa_out[0] = sd;
+        // the waves' maxima wait in red[0] (untouched until the end) for the
+        // workgroup that ends the call; the codes barrier publishes them too
+        xmax = wave_max(xmax);
+        if (lane == 0) red[0][wave] = xmax;
+        __syncthreads();
+        // every wave has read state[0] and passed the barrier: count this
+        // workgroup (the result is needed only at the end)
+        if (tid == 0) arrived_last = atomicAdd(&state[3], 1u) == gridDim.x - 1;
+    } else if constexpr (FUSED) {
         // per-row maxima (unit v belongs to row v / (K/8)), then one barrier
         // for all rows; without rowscale every row takes the overall max
         float mx[MR];
@@ -304,6 +340,19 @@ void rowk_f8_kernel(
             y[(size_t)m * N + rbeg + lr] = (uint16_t)f32_to_out_bits<OUTF>(v * out_scale(m, rbeg + lr));
         }
     }
+    if constexpr (DS) {
+        __shared__ int last;
+        if (tid == 0) last = arrived_last;
+        __syncthreads();
+        if (last) {
+            float a = red[0][0];
+#pragma unroll
+            for (int i = 1; i < W; ++i) a = fmaxf(a, red[0][i]);
+            __syncthreads();                           // red is reused below
+            delayed_publish<kWgThreads>(a, history, hist_len, state, &red[0][0]);
+            if (tid == 0) amax_out[0] = a;
+        }
+    }
 }
 
 // ---------------------------------------------------------------- NestedFP FP16 mode
@@ -403,10 +452,11 @@ int rowk_split_shift(int64_t rows_per_wg, int K, int MR, int U)
     return best;
 }
 
-template <int WFMT, int OUTF, int AS, int MR>
+template <int WFMT, int OUTF, int AS, int MR, bool DS = false>
 void launch_rowk(const void* act, const float* sa_in, const uint8_t* qw, const float* sw,
                  uint16_t* y, uint8_t* q, float* sa_out, float* amax, int N, int K,
-                 int rowscale, hipStream_t st)
+                 int rowscale, hipStream_t st, float* history = nullptr, int64_t hist_len = 0,
+                 uint32_t* state = nullptr)
 {
     using C = RowkCfg<MR>;
     const size_t lds = AS != AS_GLOBAL ? (size_t)MR * K : 0;
@@ -418,9 +468,9 @@ void launch_rowk(const void* act, const float* sa_in, const uint8_t* qw, const f
     // fused prologue, MR*K/16 code vectors for AS_COPY (none for AS_GLOBAL)
     const int64_t vecs = AS == AS_GLOBAL ? 0 : (int64_t)MR * K / (AS == AS_COPY ? 16 : 8);
     auto go = [&](auto xv) {
-        rowk_f8_kernel<WFMT, OUTF, AS, MR, C::U, CP_NT, C::WPC, decltype(xv)::value>
+        rowk_f8_kernel<WFMT, OUTF, AS, MR, C::U, CP_NT, C::WPC, decltype(xv)::value, DS>
             <<<grid, kWgThreads, lds, st>>>(act, sa_in, qw, sw, y, q, sa_out, amax, N, K, rpw, ls,
-                                             kseg, rowscale);
+                                             kseg, rowscale, history, hist_len, state);
     };
     if (vecs <= kWgThreads) go(std::integral_constant<int, 1>{});
     else if (vecs <= 2 * kWgThreads) go(std::integral_constant<int, 2>{});
@@ -465,6 +515,29 @@ hipError_t launch_rowk_nested16(const uint16_t* a, const uint8_t* hi, const uint
     else
         rowk_nested16_kernel<2, kRows, kUnroll, CP_NT>
             <<<rowk_grid(N), kThreads, 0, stream>>>(a, hi, lo, y, N, K);
+    return hipGetLastError();
+}
+
+hipError_t launch_linear_fused_delayed(const void* x, int dtype, const uint8_t* qw, const float* sw,
+                                       uint16_t* y, uint8_t* q, float* scale, float* amax,
+                                       float* history, int64_t L, uint32_t* state, int M, int N,
+                                       int K, hipStream_t stream)
+{
+    if (dtype == DT_BF16) {
+        if (M == 1)
+            launch_rowk<WF_E4M3, OUT_BF16, AS_BF16, 1, true>(x, nullptr, qw, sw, y, q, scale, amax, N,
+                                                             K, 0, stream, history, L, state);
+        else
+            launch_rowk<WF_E4M3, OUT_BF16, AS_BF16, 2, true>(x, nullptr, qw, sw, y, q, scale, amax, N,
+                                                             K, 0, stream, history, L, state);
+    } else {
+        if (M == 1)
+            launch_rowk<WF_E4M3, OUT_BF16, AS_FP16, 1, true>(x, nullptr, qw, sw, y, q, scale, amax, N,
+                                                             K, 0, stream, history, L, state);
+        else
+            launch_rowk<WF_E4M3, OUT_BF16, AS_FP16, 2, true>(x, nullptr, qw, sw, y, q, scale, amax, N,
+                                                             K, 0, stream, history, L, state);
+    }
     return hipGetLastError();
 }
 

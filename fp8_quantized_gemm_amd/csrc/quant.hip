@@ -15,6 +15,8 @@
 // fl32(x / s) is the correctly rounded binary32 quotient (see Quotient in
 // common.hpp), so codes are a function of (x, s) alone and independent of the
 // launch shape.
+#include <algorithm>
+
 #include "common.hpp"
 
 namespace fp8q {
@@ -189,6 +191,107 @@ __global__ __launch_bounds__(kBigThreads) void quant_partial_kernel(
     }
 }
 
+// ---------------------------------------------------------------- delayed scaling
+// One pass over x: the scale comes from the amax history of earlier calls
+// (delayed_scale), so every element is quantized as soon as it is loaded and
+// the amax of x is only recorded.  Small n: one workgroup, which ends the
+// call itself.  Larger n: a grid-stride pass in which every workgroup folds
+// its maximum into state[1] with an integer atomicMax on the float bits
+// (monotone for non-negative floats) and then counts itself in state[3]; the
+// workgroup that arrives last publishes the call (delayed_publish).  Nothing
+// waits for another workgroup, so the grid needs no co-residency.
+template <int DT>
+__global__ __launch_bounds__(kSmallThreads) void quant_small_delayed_kernel(
+    const uint16_t* __restrict__ x, int64_t n, uint8_t* __restrict__ q,
+    float* __restrict__ scale, float* __restrict__ amax_out, float* __restrict__ history,
+    int64_t L, uint32_t* __restrict__ state)
+{
+    __shared__ float lds[kSmallThreads / 64];
+    const int tid = threadIdx.x;
+    const int64_t nvec = n >> 3;
+    const int tail = (int)(n & 7);
+    const v4i* xv = reinterpret_cast<const v4i*>(x);
+    const float s = delayed_scale(state);
+    const Quotient d(s);
+    v2i* qv = reinterpret_cast<v2i*>(q);
+    float m = 0.0f;
+#pragma unroll
+    for (int j = 0; j < kSmallVecPerThread; ++j) {
+        const int64_t i = tid + (int64_t)j * kSmallThreads;
+        if (i < nvec) {
+            const v4i v = xv[i];
+            m = fmaxf(m, vec_absmax<DT>(v));
+            qv[i] = vec_quantize<DT>(v, d);
+        }
+    }
+    if (tid < tail) {
+        const uint16_t th = x[nvec * 8 + tid];
+        m = fmaxf(m, fabsf(half_bits_to_f32<DT>(th)));
+        q[nvec * 8 + tid] = scalar_quantize<DT>(th, d);
+    }
+    const float a = block_max<kSmallThreads>(m, lds);
+    __syncthreads();                                   // lds is reused below
+    delayed_publish<kSmallThreads>(a, history, L, state, lds);
+    if (tid == 0) {
+        *scale = s;
+        *amax_out = a;
+    }
+}
+
+template <int DT>
+__global__ __launch_bounds__(kBigThreads) void quant_delayed_kernel(
+    const uint16_t* __restrict__ x, int64_t n, uint8_t* __restrict__ q,
+    float* __restrict__ scale, float* __restrict__ amax_out, float* __restrict__ history,
+    int64_t L, uint32_t* __restrict__ state)
+{
+    __shared__ float lds[kBigThreads / 64];
+    __shared__ int last;
+    const float s = delayed_scale(state);
+    const Quotient d(s);
+    const int64_t nvec = n >> 3;
+    const v4i* xv = reinterpret_cast<const v4i*>(x);
+    v2i* qv = reinterpret_cast<v2i*>(q);
+    const int64_t stride = (int64_t)gridDim.x * kBigThreads;
+    float m = 0.0f;
+    int64_t i = (int64_t)blockIdx.x * kBigThreads + threadIdx.x;
+    for (; i + (kBigUnroll - 1) * stride < nvec; i += kBigUnroll * stride) {
+        v4i v[kBigUnroll];
+#pragma unroll
+        for (int u = 0; u < kBigUnroll; ++u) v[u] = xv[i + u * stride];
+#pragma unroll
+        for (int u = 0; u < kBigUnroll; ++u) {
+            m = fmaxf(m, vec_absmax<DT>(v[u]));
+            qv[i + u * stride] = vec_quantize<DT>(v[u], d);
+        }
+    }
+    for (; i < nvec; i += stride) {
+        const v4i v = xv[i];
+        m = fmaxf(m, vec_absmax<DT>(v));
+        qv[i] = vec_quantize<DT>(v, d);
+    }
+    if (blockIdx.x == 0 && threadIdx.x < (int)(n & 7)) {
+        const uint16_t th = x[nvec * 8 + threadIdx.x];
+        m = fmaxf(m, fabsf(half_bits_to_f32<DT>(th)));
+        q[nvec * 8 + threadIdx.x] = scalar_quantize<DT>(th, d);
+    }
+    m = block_max<kBigThreads>(m, lds);
+    if (threadIdx.x == 0) {
+        atomicMax(&state[1], __float_as_uint(m));
+        __threadfence();                               // the max lands before the arrival
+        last = atomicAdd(&state[3], 1u) == gridDim.x - 1;
+    }
+    __syncthreads();
+    if (last) {
+        __threadfence();
+        const float a = __uint_as_float(atomicMax(&state[1], 0u));   // every workgroup's max
+        delayed_publish<kBigThreads>(a, history, L, state, lds);
+        if (threadIdx.x == 0) {
+            *scale = s;
+            *amax_out = a;
+        }
+    }
+}
+
 // ---------------------------------------------------------------- per-row scales
 // One scale per row of a [rows, cols] matrix: the activation scale per token
 // and the weight scale per output channel of the TensorRT-LLM build the page
@@ -306,6 +409,34 @@ hipError_t launch_quantize_rows(const void* x, int dtype, int64_t rows, int64_t 
         quant_rows_kernel<DT_BF16><<<(unsigned)rows, kRowThreads, 0, stream>>>(xs, cols, q, scale, amax);
     else
         quant_rows_kernel<DT_FP16><<<(unsigned)rows, kRowThreads, 0, stream>>>(xs, cols, q, scale, amax);
+    return hipGetLastError();
+}
+
+hipError_t launch_quantize_delayed(const void* x, int dtype, int64_t n, uint8_t* q, float* scale,
+                                   float* amax, float* history, int64_t L, uint32_t* state,
+                                   hipStream_t stream)
+{
+    const uint16_t* xs = static_cast<const uint16_t*>(x);
+    if (n <= kSmallN) {
+        if (dtype == DT_BF16)
+            quant_small_delayed_kernel<DT_BF16><<<1, kSmallThreads, 0, stream>>>(
+                xs, n, q, scale, amax, history, L, state);
+        else
+            quant_small_delayed_kernel<DT_FP16><<<1, kSmallThreads, 0, stream>>>(
+                xs, n, q, scale, amax, history, L, state);
+        return hipGetLastError();
+    }
+    // every workgroup ends with two same-address device atomics, which
+    // serialize (measured on MI355X: 2048 workgroups take 3x longer than 256
+    // on a 22.5 M-element tensor), so the grid is one workgroup per 2048
+    // vectors, 64 to 256 workgroups
+    const int64_t g = std::min<int64_t>(256, std::max<int64_t>(64, (n >> 3) / 2048));
+    if (dtype == DT_BF16)
+        quant_delayed_kernel<DT_BF16><<<g, kBigThreads, 0, stream>>>(xs, n, q, scale, amax, history,
+                                                                     L, state);
+    else
+        quant_delayed_kernel<DT_FP16><<<g, kBigThreads, 0, stream>>>(xs, n, q, scale, amax, history,
+                                                                     L, state);
     return hipGetLastError();
 }
 

@@ -43,6 +43,9 @@ _SIGS = {
     "fp8_quantize_rows": (_i, [_p, _i, _i64, _i64, _p, _p, _p, _p]),
     "fp8_gemm_rowwise": (_i, [_p, _p, _p, _p, _p, _i64, _i64, _i64, _p]),
     "fp8_linear_rowwise": (_i, [_p, _i, _p, _p, _p, _p, _p, _p, _i64, _i64, _i64, _p]),
+    "fp8_quantize_act_delayed": (_i, [_p, _i, _i64, _p, _p, _p, _p, _i64, _p, _p]),
+    "fp8_linear_delayed": (_i, [_p, _i, _p, _p, _p, _p, _p, _p, _p, _i64, _p, _i64, _i64, _i64,
+                                _p]),
 }
 for _name, (_res, _args) in _SIGS.items():
     _fn = getattr(lib, _name)
@@ -237,6 +240,76 @@ def fp8_linear_rowwise(x: torch.Tensor, qw: torch.Tensor, sw: torch.Tensor,
         _dev(y, "y", torch.bfloat16, (M, N)), _dev(q, "q", torch.uint8, (M, K)),
         _vector(sa, "sa", M), _vector(amax, "amax", M), M, N, K, _stream(x)))
     return y, q, sa, amax
+
+
+class DelayedScaling:
+    """Device state of delayed scaling for one tensor: the amax of its last
+    `length` quantizations (zeros at first) and the scale the next one uses.
+    Use one object per tensor and issue its calls on one stream."""
+
+    def __init__(self, length: int = 1024, device="cuda"):
+        if length < 1:
+            raise ValueError("the amax history needs at least one entry")
+        self.history = torch.zeros(length, dtype=torch.float32, device=device)
+        self.state = torch.zeros(4, dtype=torch.int32, device=device)
+
+    def _args(self):
+        return (_dev(self.history, "history", torch.float32), self.history.numel(),
+                _dev(self.state, "state", torch.int32, (4,)))
+
+    @property
+    def next_scale(self) -> float:
+        """The scale the next call will use (1.0 before any history)."""
+        s = float(self.state[:1].view(torch.float32).item())
+        return s if s > 0 else 1.0
+
+    @property
+    def position(self) -> int:
+        return int(self.state[2].item())
+
+
+def fp8_quantize_act_delayed(x: torch.Tensor, ds: DelayedScaling, q: torch.Tensor | None = None,
+                             scale: torch.Tensor | None = None,
+                             amax: torch.Tensor | None = None):
+    """fp8_quantize_act with delayed scaling: codes with the scale of ds's amax
+    history, then x's amax recorded in it.  Returns (q, scale used, amax of x)."""
+    code = _dtype_code(x)
+    if q is None:
+        q = torch.empty(x.shape, dtype=torch.uint8, device=x.device)
+    if scale is None:
+        scale = torch.empty(1, dtype=torch.float32, device=x.device)
+    if amax is None:
+        amax = torch.empty(1, dtype=torch.float32, device=x.device)
+    if q.numel() != x.numel():
+        raise ValueError("q must have as many elements as x")
+    _check("fp8_quantize_act_delayed", lib.fp8_quantize_act_delayed(
+        _dev(x, "x"), code, x.numel(), _dev(q, "q", torch.uint8), _scalar(scale, "scale"),
+        _scalar(amax, "amax"), *ds._args(), _stream(x)))
+    return q, scale, amax
+
+
+def fp8_linear_delayed(x: torch.Tensor, qw: torch.Tensor, sw: torch.Tensor, ds: DelayedScaling,
+                       y: torch.Tensor | None = None, q: torch.Tensor | None = None,
+                       scale: torch.Tensor | None = None, amax: torch.Tensor | None = None):
+    """fp8_linear with delayed activation scaling (ds holds the amax history).
+    Returns (y, q, scale used, amax of x)."""
+    code = _dtype_code(x)
+    M, N, K = _mnk(x, qw)
+    dev = x.device
+    if y is None:
+        y = torch.empty((M, N), dtype=torch.bfloat16, device=dev)
+    if q is None:
+        q = torch.empty((M, K), dtype=torch.uint8, device=dev)
+    if scale is None:
+        scale = torch.empty(1, dtype=torch.float32, device=dev)
+    if amax is None:
+        amax = torch.empty(1, dtype=torch.float32, device=dev)
+    hist, hlen, state = ds._args()
+    _check("fp8_linear_delayed", lib.fp8_linear_delayed(
+        _dev(x, "x"), code, _dev(qw, "qw", torch.uint8), _scalar(sw, "sw"),
+        _dev(y, "y", torch.bfloat16, (M, N)), _dev(q, "q", torch.uint8, (M, K)),
+        _scalar(scale, "scale"), _scalar(amax, "amax"), hist, hlen, state, M, N, K, _stream(x)))
+    return y, q, scale, amax
 
 
 def nested_split(w: torch.Tensor, hi: torch.Tensor | None = None,

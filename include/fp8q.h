@@ -175,6 +175,49 @@ FP8Q_API fp8q_status fp8_linear_rowwise(const void* x, int dtype, const uint8_t*
                                         fp8q_stream stream);
 
 /*
+ * Delayed scaling with an amax history ([RTX4060] §6.1: the history should be
+ * at least 1024 long).  A call quantizes with the scale that the amax of the
+ * earlier calls gives, then records its own amax, so the activation is read
+ * once and no reduction precedes the quantization:
+ *
+ *   history[L]  in/out: the amax of the last L calls on this tensor (ring)
+ *   state[4]    in/out: [0] float bits of the scale the next call uses
+ *               (0 = no history yet, meaning 1), [1] and [3] accumulators of
+ *               a call in progress (0 between calls), [2] ring position
+ *   Both are device memory owned by the caller, zero-filled once before the
+ *   first call; state is 16-byte aligned.  Calls on one (history, state)
+ *   must not overlap in time (issue them on one stream).  1 <= L <= 2^24.
+ *
+ *   Call t: s = scale from state[0] (1 if 0); q_i = E4M3_rne_sat(fl32(x_i / s)),
+ *   so values beyond 448 s saturate to +-448; a = max_i |x_i|;
+ *   history[pos] = a; pos = (pos + 1) mod L; state[0] = fl32(max(history) / 448)
+ *   (1.0 when the history holds only zeros).
+ */
+
+/*
+ * fp8_quantize_act_delayed - fp8_quantize_act with delayed scaling:
+ *   x[n] in; q[n] out; *scale out: the scale s used; *amax out: max_i |x_i|.
+ *   One launch (a grid-stride pass whose last workgroup updates the history).
+ */
+FP8Q_API fp8q_status fp8_quantize_act_delayed(const void* x, int dtype, int64_t n, uint8_t* q,
+                                              float* scale, float* amax, float* history,
+                                              int64_t history_len, uint32_t* state,
+                                              fp8q_stream stream);
+
+/*
+ * fp8_linear_delayed - fp8_linear with delayed activation scaling: the
+ *   activation is quantized as fp8_quantize_act_delayed does, then multiplied
+ *   with fp8_gemm; bit-identical to the two calls in sequence.  For M <= 2
+ *   and M*K <= 32768 one kernel, whose quantization needs no reduction over
+ *   the activation first.  Size rules as fp8_gemm.
+ */
+FP8Q_API fp8q_status fp8_linear_delayed(const void* x, int dtype, const uint8_t* qw,
+                                        const float* sw, uint16_t* y, uint8_t* q, float* scale,
+                                        float* amax, float* history, int64_t history_len,
+                                        uint32_t* state, int64_t M, int64_t N, int64_t K,
+                                        fp8q_stream stream);
+
+/*
  * nested_split - NestedFP byte split of fp16 weights ([NestedFP] §2.1):
  *   hi[i] = w[i] >> 8, lo[i] = w[i] & 0xFF.   n >= 1.
  */

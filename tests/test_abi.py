@@ -30,7 +30,8 @@ def test_header_declares_the_entry_points():
     for want in ["fp8_quantize_act", "fp8_gemm", "fp8_linear", "nested_split", "nested_rebuild_fp16",
                  "nested_gemm_fp16", "nested_gemm_fp8", "nested_linear_fp8", "fp8q_abi_version",
                  "fp8q_status_str", "fp8q_last_error", "fp8q_e4m3_encode_f32",
-                 "fp8_quantize_rows", "fp8_gemm_rowwise", "fp8_linear_rowwise"]:
+                 "fp8_quantize_rows", "fp8_gemm_rowwise", "fp8_linear_rowwise",
+                 "fp8_quantize_act_delayed", "fp8_linear_delayed"]:
         assert want in names
 
 
@@ -141,6 +142,26 @@ GEMM_SIG = [P16, P16, P16, P16, P16]
     ("fp8_linear_rowwise", [P16, 5, P16, P16, P16, P16, P16, P16, 1, 1, 16, NULL], ERR_DTYPE),
     ("fp8_linear_rowwise", [P16, 0, P16, P16, P16, P16, P16, P16, 1, 1, 8, NULL], ERR_SHAPE),
     ("fp8_linear_rowwise", [P16, 0, P16, P16, P16, P17, P16, P16, 1, 1, 16, NULL], ERR_ALIGN),
+    # fp8_quantize_act_delayed(x, dtype, n, q, scale, amax, history, L, state, stream)
+    ("fp8_quantize_act_delayed", [P16, 0, 8, P16, P16, P16, NULL, 4, P16, NULL], ERR_NULL),
+    ("fp8_quantize_act_delayed", [P16, 0, 8, P16, P16, P16, P16, 4, NULL, NULL], ERR_NULL),
+    ("fp8_quantize_act_delayed", [P16, 9, 8, P16, P16, P16, P16, 4, P16, NULL], ERR_DTYPE),
+    ("fp8_quantize_act_delayed", [P16, 0, 0, P16, P16, P16, P16, 4, P16, NULL], ERR_SHAPE),
+    ("fp8_quantize_act_delayed", [P16, 0, 8, P16, P16, P16, P16, 0, P16, NULL], ERR_SHAPE),
+    ("fp8_quantize_act_delayed", [P16, 0, 8, P16, P16, P16, P16, 2**24 + 1, P16, NULL], ERR_SHAPE),
+    ("fp8_quantize_act_delayed", [P16, 0, 8, P16, P16, P16, P16, 4, ctypes.c_void_p(0x1004), NULL],
+     ERR_ALIGN),
+    ("fp8_quantize_act_delayed", [P16, 0, 8, P16, P16, P16, ctypes.c_void_p(0x1002), 4, P16, NULL],
+     ERR_ALIGN),
+    # fp8_linear_delayed(x, dtype, qw, sw, y, q, scale, amax, history, L, state, M, N, K, stream)
+    ("fp8_linear_delayed", [P16, 0, P16, P16, P16, P16, P16, P16, NULL, 4, P16, 1, 1, 16, NULL],
+     ERR_NULL),
+    ("fp8_linear_delayed", [P16, 0, P16, P16, P16, P16, P16, P16, P16, 4, P16, 1, 1, 24, NULL],
+     ERR_SHAPE),
+    ("fp8_linear_delayed", [P16, 0, P16, P16, P16, P16, P16, P16, P16, -1, P16, 1, 1, 16, NULL],
+     ERR_SHAPE),
+    ("fp8_linear_delayed", [P16, 1, P16, P16, P16, P17, P16, P16, P16, 4, P16, 1, 1, 16, NULL],
+     ERR_ALIGN),
     # fp8q_e4m3_encode_f32(v, q, n, stream)
     ("fp8q_e4m3_encode_f32", [NULL, P16, 4, NULL], ERR_NULL),
     ("fp8q_e4m3_encode_f32", [P16, P16, 0, NULL], ERR_SHAPE),

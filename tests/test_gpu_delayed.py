@@ -1,0 +1,133 @@
+"""GPU parity of delayed scaling with an amax history (fp8_quantize_act_delayed,
+fp8_linear_delayed) against the oracle, call by call.
+
+Every call is compared bit-exactly: codes, the scale used, the amax, and after
+the sequence the history ring and the state (next scale, position, and the
+accumulators back at 0).  Magnitudes change from call to call, so later calls
+saturate and the window maximum moves; the history is short (wraps) and long.
+Covers the single-workgroup quantizer (n <= 32768), the grid-stride one (its
+last workgroup publishes the call), the fused decode linear (M <= 2) and the
+two-launch linear, and HIP-graph replays (each replay is one more call).
+"""
+import numpy as np
+import pytest
+import torch
+
+import oracle
+from fp8_quantized_gemm_amd import fp8q, synth
+from gpu_helpers import DEV, host, say
+
+pytestmark = pytest.mark.gpu
+
+MAGS = [1.0, 3.0, 0.25, 40.0, 0.5, 0.5, 2.0, 0.125]
+
+
+def _inputs(M, K, dtype, seed):
+    return [(synth.activation(M, K, seed=seed + t, dtype=dtype, outliers=True).to(torch.float32)
+             * mag).to(torch.bfloat16 if dtype == "bf16" else torch.float16) for t, mag in
+            enumerate(MAGS)]
+
+
+def _check_state(ds: fp8q.DelayedScaling, od: oracle.DelayedScaling, what):
+    assert np.array_equal(host(ds.history), od.history), f"{what}: history"
+    st = host(ds.state).view(np.uint32)
+    assert st[0] == od.state[0] and st[2] == od.state[2], f"{what}: next scale / position"
+    assert st[1] == 0 and st[3] == 0, f"{what}: accumulators not cleared"
+
+
+@pytest.mark.parametrize("dtype", ["bf16", "fp16"])
+@pytest.mark.parametrize("M,K,L", [(1, 4096, 3), (4, 8192, 1024), (300, 5120, 3),
+                                   (2048, 11008, 5), (3, 17, 2)])
+def test_quantize_delayed_sequence(M, K, L, dtype):
+    xs = _inputs(M, K, dtype, seed=synth.seed_for("dq", M, K, L, dtype))
+    code = oracle.BF16 if dtype == "bf16" else oracle.FP16
+    od = oracle.DelayedScaling(L)
+    ds = fp8q.DelayedScaling(L, device=DEV)
+    for t, x in enumerate(xs):
+        want_q, want_s, want_a = od.quantize(synth.bits(x).ravel(), code)
+        say("quantize delayed", dtype, M, K, L, "call", t)
+        q, s, a = fp8q.fp8_quantize_act_delayed(x.to(DEV), ds)
+        assert np.array_equal(host(q).ravel(), want_q), f"call {t}: codes"
+        assert host(s)[0] == np.float32(want_s) and host(a)[0] == np.float32(want_a), f"call {t}"
+    _check_state(ds, od, f"{M}x{K} L={L}")
+
+
+@pytest.mark.parametrize("M,K,N", [(1, 4096, 4096), (2, 11008, 300), (1, 32752, 64),
+                                   (16, 4096, 1000), (512, 4096, 300)])
+def test_linear_delayed_sequence(M, K, N):
+    L = 4
+    xs = _inputs(M, K, "bf16", seed=synth.seed_for("dl", M, K, N))
+    w = synth.normal((N, K), 0.02, "fp16", seed=synth.seed_for("dlw", M, K, N), device=DEV)
+    qw, sw, _ = fp8q.fp8_quantize_act(w)
+    od = oracle.DelayedScaling(L)
+    ds = fp8q.DelayedScaling(L, device=DEV)
+    for t, x in enumerate(xs):
+        want_q, want_s, want_a = od.quantize(synth.bits(x).ravel(), oracle.BF16)
+        say("linear delayed", M, K, N, "call", t)
+        y, q, s, a = fp8q.fp8_linear_delayed(x.to(DEV), qw, sw, ds)
+        assert np.array_equal(host(q).ravel(), want_q), f"call {t}: codes"
+        assert host(s)[0] == np.float32(want_s) and host(a)[0] == np.float32(want_a), f"call {t}"
+        y2 = fp8q.fp8_gemm(q, s, qw, sw)                      # the GEMM on the same codes
+        assert torch.equal(y.view(torch.int16), y2.view(torch.int16)), f"call {t}: y"
+    _check_state(ds, od, f"linear {M}x{K}x{N}")
+
+
+def test_linear_delayed_fp16_and_two_states_independent():
+    K, N = 4096, 512
+    w = synth.normal((N, K), 0.02, "fp16", seed=7, device=DEV)
+    qw, sw, _ = fp8q.fp8_quantize_act(w)
+    xa = _inputs(1, K, "fp16", seed=70)
+    xb = _inputs(2, K, "fp16", seed=80)
+    oa, ob = oracle.DelayedScaling(8), oracle.DelayedScaling(2)
+    da, db = fp8q.DelayedScaling(8, device=DEV), fp8q.DelayedScaling(2, device=DEV)
+    for t in range(len(MAGS)):
+        for x, od, ds, tag in ((xa[t], oa, da, "a"), (xb[t], ob, db, "b")):
+            want_q, want_s, _ = od.quantize(synth.bits(x).ravel(), oracle.FP16)
+            say("linear delayed fp16", tag, "call", t)
+            y, q, s, _ = fp8q.fp8_linear_delayed(x.to(DEV), qw, sw, ds)
+            assert np.array_equal(host(q).ravel(), want_q) and host(s)[0] == np.float32(want_s)
+    _check_state(da, oa, "state a")
+    _check_state(db, ob, "state b")
+
+
+@pytest.mark.parametrize("M,K,N", [(1, 4096, 4096), (300, 5120, 256)])
+def test_delayed_graph_replays_advance_the_history(M, K, N):
+    """A captured call replayed R times is R more calls: the scale of each
+    replay follows the oracle's sequence on the same input."""
+    L, R = 3, 4
+    x = (synth.activation(M, K, seed=91, outliers=True).to(torch.float32) * 5.0).to(torch.bfloat16)
+    w = synth.normal((N, K), 0.02, "fp16", seed=92, device=DEV)
+    qw, sw, _ = fp8q.fp8_quantize_act(w)
+    xd = x.to(DEV)
+    y = torch.empty((M, N), dtype=torch.bfloat16, device=DEV)
+    q = torch.empty((M, K), dtype=torch.uint8, device=DEV)
+    s = torch.empty(1, device=DEV)
+    a = torch.empty(1, device=DEV)
+    ds = fp8q.DelayedScaling(L, device=DEV)
+    od = oracle.DelayedScaling(L)
+    # warm-up call on the capture stream (one call), then capture one call
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    say("delayed graph", M, K, N)
+    with torch.cuda.stream(side):
+        fp8q.fp8_linear_delayed(xd, qw, sw, ds, y, q, s, a)
+    torch.cuda.current_stream().wait_stream(side)
+    torch.cuda.synchronize()
+    od.quantize(synth.bits(x).ravel(), oracle.BF16)
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        fp8q.fp8_linear_delayed(xd, qw, sw, ds, y, q, s, a)
+    # capture records without running: the state is unchanged
+    _check_state(ds, od, "after capture")
+    for rep in range(R):
+        want_q, want_s, want_a = od.quantize(synth.bits(x).ravel(), oracle.BF16)
+        q.fill_(0)
+        torch.cuda.synchronize()
+        g.replay()
+        torch.cuda.synchronize()
+        assert np.array_equal(host(q).ravel(), want_q), f"replay {rep}: codes"
+        assert host(s)[0] == np.float32(want_s) and host(a)[0] == np.float32(want_a), f"replay {rep}"
+        y2 = fp8q.fp8_gemm(q, s, qw, sw)
+        assert torch.equal(y.view(torch.int16), y2.view(torch.int16)), f"replay {rep}: y"
+    _check_state(ds, od, "after replays")
+    del g
