@@ -42,6 +42,7 @@ def _load():
         "orc_quantize": (None, [_p, _c.c_int, _i64, _p, _p, _p]),
         "orc_quantize_rows": (None, [_p, _c.c_int, _i64, _i64, _p, _p, _p]),
         "orc_quantize_delayed": (None, [_p, _c.c_int, _i64, _p, _p, _p, _p, _i64, _p]),
+        "orc_quantize_kv": (None, [_p, _c.c_int, _i64, _i64, _i64, _p, _p, _p]),
         "orc_gemm_fp8_rowwise_ref": (None, [_p, _p, _p, _p, _i64, _i64, _i64,
                                             _p, _p, _i64, _p, _p]),
         "orc_gemm_fp8_rowwise_f32": (None, [_p, _p, _p, _p, _i64, _i64, _i64, _p, _c.c_int]),
@@ -181,6 +182,19 @@ def quantize_rows(x_bits, dtype: int):
     s = np.zeros(rows, np.float32)
     a = np.zeros(rows, np.float32)
     lib.orc_quantize_rows(_ptr(x), dtype, rows, cols, _ptr(q), _ptr(s), _ptr(a))
+    return q, s, a
+
+
+def quantize_kv(x_bits, dtype: int):
+    """Per-head quantization of a K or V block [T, H, D] (uint16 bits): returns
+    (codes [T, H, D], scale float32 [H], amax float32 [H])."""
+    x = _c_arr(x_bits, np.uint16)
+    assert x.ndim == 3
+    T, H, D = x.shape
+    q = np.empty(x.shape, np.uint8)
+    s = np.zeros(H, np.float32)
+    a = np.zeros(H, np.float32)
+    lib.orc_quantize_kv(_ptr(x), dtype, T, H, D, _ptr(q), _ptr(s), _ptr(a))
     return q, s, a
 
 

@@ -247,6 +247,28 @@ void orc_quantize_rows(const uint16_t* x, int dtype, int64_t rows, int64_t cols,
         orc_quantize(x + r * cols, dtype, cols, q + r * cols, scale + r, amax + r);
 }
 
+/* FP8 KV cache ([RTX4060] §1 stores the KV cache in FP8; [C++FP8] §4.2 builds */
+/* with an FP8 KV-cache type): a K or V block x[T, H, D] (token-major, then   */
+/* heads, then head dimension) with one scale per head h over all tokens and */
+/* all D elements of that head.  Head h is gathered into a plain vector and   */
+/* quantized by the three steps above; the codes go back to their places.  */
+void orc_quantize_kv(const uint16_t* x, int dtype, int64_t T, int64_t H, int64_t D, uint8_t* q,
+                     float* scale, float* amax)
+{
+    uint16_t* g = (uint16_t*)malloc((size_t)(T * D) * sizeof(uint16_t));
+    uint8_t* c = (uint8_t*)malloc((size_t)(T * D));
+    if (!g || !c) { free(g); free(c); return; }
+    for (int64_t h = 0; h < H; ++h) {
+        for (int64_t t = 0; t < T; ++t)
+            for (int64_t d = 0; d < D; ++d) g[t * D + d] = x[(t * H + h) * D + d];
+        orc_quantize(g, dtype, T * D, c, scale + h, amax + h);
+        for (int64_t t = 0; t < T; ++t)
+            for (int64_t d = 0; d < D; ++d) q[(t * H + h) * D + d] = c[t * D + d];
+    }
+    free(g);
+    free(c);
+}
+
 /* Delayed scaling with an amax history ([RTX4060] §6.1 asks that the amax   */
 /* history be at least 1024 long).  Reading: history[L] holds the amax of    */
 /* the last L calls on this tensor (zeros before any call), state[0] is the  */
