@@ -269,7 +269,8 @@ def prefill_figures(torch, fp8q, mm, graph=True, call=linear_call):
 
 
 def secondary(torch, fp8q, synth, model1, dev,
-              parts=("decode", "prefill", "delayed", "qwen", "rowwise", "nested"), graph=True):
+              parts=("decode", "prefill", "delayed", "qwen", "rowwise", "kv", "nested"),
+              graph=True):
     """Prefill, M = 4/8 decode, delayed scaling, Qwen-32B, per-token/per-channel
     and NestedFP figures (a few steps each)."""
     out = {}
@@ -319,6 +320,20 @@ def secondary(torch, fp8q, synth, model1, dev,
             layers=8)
         progress("per-token / per-channel done")
         del mr
+    # FP8 KV cache: one layer's K block of 4096 tokens x 32 heads x 128 (bf16,
+    # 32 MiB), one scale per head; algorithmic bytes 2 read + 1 written per element
+    if "kv" in parts:
+        kv = synth.activation(4096, 32 * 128, seed=77, device=dev).reshape(4096, 32, 128)
+        qkv = torch.empty((4096, 32, 128), dtype=torch.uint8, device=dev)
+        skv = torch.empty(32, dtype=torch.float32, device=dev)
+        akv = torch.empty(32, dtype=torch.float32, device=dev)
+        dt, _ = time_fn(torch, lambda: fp8q.fp8_quantize_kv(kv, qkv, skv, akv), steps=20, warmup=3)
+        byts = 3 * kv.numel()
+        out["kv_quantize_4096x32x128"] = {"GB_per_s": round(byts / dt / 1e9, 1),
+                                          "frac_hbm": round(byts / dt / 1e9 / HBM_PEAK_GBS, 4),
+                                          "us": round(dt * 1e6, 2)}
+        progress("kv cache done")
+        del kv, qkv
     if "nested" not in parts:
         return out
     # NestedFP at M = 1 and 256 on 8 layers of fp16 weights (hi/lo planes)

@@ -183,6 +183,22 @@ fp8q_status fp8_linear(const void* x, int dtype, const uint8_t* qw, const float*
                          OUT_BF16, 0, (hipStream_t)stream);
 }
 
+fp8q_status fp8_quantize_kv(const void* x, int dtype, int64_t tokens, int64_t heads,
+                            int64_t head_dim, uint8_t* q, float* scale, float* amax,
+                            fp8q_stream stream)
+{
+    if (!x || !q || !scale || !amax) return FP8Q_ERR_NULL;
+    if (dtype != FP8Q_BF16 && dtype != FP8Q_FP16) return FP8Q_ERR_DTYPE;
+    if (tokens < 1 || heads < 1 || heads > ((int64_t)1 << 20) || head_dim < 8 ||
+        (head_dim % 8) != 0 || head_dim > ((int64_t)1 << 16) ||
+        tokens > ((int64_t)1 << 40) / (heads * head_dim))
+        return FP8Q_ERR_SHAPE;
+    if (!aligned16(x) || !aligned16(q) || !aligned4(scale) || !aligned4(amax)) return FP8Q_ERR_ALIGN;
+    FP8Q_TRY(check_device());
+    return finish("fp8_quantize_kv", launch_quantize_kv(x, dtype, tokens, heads, head_dim, q, scale,
+                                                        amax, (hipStream_t)stream));
+}
+
 // History lengths the delayed-scaling calls accept.
 constexpr int64_t kMaxHistory = (int64_t)1 << 24;
 

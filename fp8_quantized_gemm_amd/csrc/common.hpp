@@ -339,6 +339,10 @@ hipError_t launch_quantize_scratch(const void* x, int dtype, int64_t n, uint8_t*
 hipError_t launch_quantize_rows(const void* x, int dtype, int64_t rows, int64_t cols, uint8_t* q,
                                 float* scale, float* amax, hipStream_t stream);
 
+// FP8 KV-cache quantizer: x[T, H, D] with one scale per head (D % 8 == 0).
+hipError_t launch_quantize_kv(const void* x, int dtype, int64_t T, int64_t H, int64_t D,
+                              uint8_t* q, float* scale, float* amax, hipStream_t stream);
+
 // Delayed-scaling quantizer (see delayed_scale): q, the scale it used and the
 // amax of x; history and state advanced by one call.
 hipError_t launch_quantize_delayed(const void* x, int dtype, int64_t n, uint8_t* q, float* scale,

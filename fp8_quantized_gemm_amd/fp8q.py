@@ -44,6 +44,7 @@ _SIGS = {
     "fp8_gemm_rowwise": (_i, [_p, _p, _p, _p, _p, _i64, _i64, _i64, _p]),
     "fp8_linear_rowwise": (_i, [_p, _i, _p, _p, _p, _p, _p, _p, _i64, _i64, _i64, _p]),
     "fp8_quantize_act_delayed": (_i, [_p, _i, _i64, _p, _p, _p, _p, _i64, _p, _p]),
+    "fp8_quantize_kv": (_i, [_p, _i, _i64, _i64, _i64, _p, _p, _p, _p]),
     "fp8_linear_delayed": (_i, [_p, _i, _p, _p, _p, _p, _p, _p, _p, _i64, _p, _i64, _i64, _i64,
                                 _p]),
 }
@@ -240,6 +241,26 @@ def fp8_linear_rowwise(x: torch.Tensor, qw: torch.Tensor, sw: torch.Tensor,
         _dev(y, "y", torch.bfloat16, (M, N)), _dev(q, "q", torch.uint8, (M, K)),
         _vector(sa, "sa", M), _vector(amax, "amax", M), M, N, K, _stream(x)))
     return y, q, sa, amax
+
+
+def fp8_quantize_kv(x: torch.Tensor, q: torch.Tensor | None = None,
+                    scale: torch.Tensor | None = None, amax: torch.Tensor | None = None):
+    """FP8 KV cache: E4M3 codes of a K or V block x[T, H, D] (bf16/fp16) with one
+    scale per head.  Returns (q uint8 [T, H, D], scale float32 [H], amax float32 [H])."""
+    code = _dtype_code(x)
+    if x.dim() != 3:
+        raise ValueError(f"x must be [tokens, heads, head_dim], got {tuple(x.shape)}")
+    T, H, D = x.shape
+    if q is None:
+        q = torch.empty((T, H, D), dtype=torch.uint8, device=x.device)
+    if scale is None:
+        scale = torch.empty(H, dtype=torch.float32, device=x.device)
+    if amax is None:
+        amax = torch.empty(H, dtype=torch.float32, device=x.device)
+    _check("fp8_quantize_kv", lib.fp8_quantize_kv(
+        _dev(x, "x"), code, T, H, D, _dev(q, "q", torch.uint8, (T, H, D)),
+        _vector(scale, "scale", H), _vector(amax, "amax", H), _stream(x)))
+    return q, scale, amax
 
 
 class DelayedScaling:

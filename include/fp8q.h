@@ -175,6 +175,25 @@ FP8Q_API fp8q_status fp8_linear_rowwise(const void* x, int dtype, const uint8_t*
                                         fp8q_stream stream);
 
 /*
+ * fp8_quantize_kv - FP8 KV cache: E4M3 codes of a K or V block with one scale
+ *   per head ([RTX4060] §1 stores the KV cache in FP8, [C++FP8] §4.2 builds
+ *   with an FP8 KV-cache type; attention itself is not part of this library).
+ *
+ *   x[T,H,D]  in : bf16/fp16 bit patterns, tokens x heads x head dimension
+ *   q[T,H,D]  out: E4M3 codes; head h quantized with scale[h]
+ *   scale[H]  out: fl32(amax[h] / 448), or 1.0 when amax[h] == 0
+ *   amax[H]   out: max over all tokens and the head dimension of |x[:,h,:]|
+ *   Head h is quantized exactly as fp8_quantize_act would quantize the
+ *   gathered x[:,h,:].  T, H >= 1 (H <= 2^20); 8 <= D <= 2^16, D % 8 == 0;
+ *   T*H*D <= 2^40.  Heads of at most 32768 elements: one launch; larger:
+ *   three (partial maxima, kept in q until the last pass; per-head amax and
+ *   scale; quantization).
+ */
+FP8Q_API fp8q_status fp8_quantize_kv(const void* x, int dtype, int64_t tokens, int64_t heads,
+                                     int64_t head_dim, uint8_t* q, float* scale, float* amax,
+                                     fp8q_stream stream);
+
+/*
  * Delayed scaling with an amax history ([RTX4060] §6.1: the history should be
  * at least 1024 long).  A call quantizes with the scale that the amax of the
  * earlier calls gives, then records its own amax, so the activation is read

@@ -31,7 +31,7 @@ def test_header_declares_the_entry_points():
                  "nested_gemm_fp16", "nested_gemm_fp8", "nested_linear_fp8", "fp8q_abi_version",
                  "fp8q_status_str", "fp8q_last_error", "fp8q_e4m3_encode_f32",
                  "fp8_quantize_rows", "fp8_gemm_rowwise", "fp8_linear_rowwise",
-                 "fp8_quantize_act_delayed", "fp8_linear_delayed"]:
+                 "fp8_quantize_act_delayed", "fp8_linear_delayed", "fp8_quantize_kv"]:
         assert want in names
 
 
@@ -162,6 +162,15 @@ GEMM_SIG = [P16, P16, P16, P16, P16]
      ERR_SHAPE),
     ("fp8_linear_delayed", [P16, 1, P16, P16, P16, P17, P16, P16, P16, 4, P16, 1, 1, 16, NULL],
      ERR_ALIGN),
+    # fp8_quantize_kv(x, dtype, tokens, heads, head_dim, q, scale, amax, stream)
+    ("fp8_quantize_kv", [P16, 0, 1, 1, 8, P16, NULL, P16, NULL], ERR_NULL),
+    ("fp8_quantize_kv", [P16, 3, 1, 1, 8, P16, P16, P16, NULL], ERR_DTYPE),
+    ("fp8_quantize_kv", [P16, 0, 0, 1, 8, P16, P16, P16, NULL], ERR_SHAPE),
+    ("fp8_quantize_kv", [P16, 0, 1, 0, 8, P16, P16, P16, NULL], ERR_SHAPE),
+    ("fp8_quantize_kv", [P16, 0, 1, 1, 12, P16, P16, P16, NULL], ERR_SHAPE),
+    ("fp8_quantize_kv", [P16, 0, 1, 1, 4, P16, P16, P16, NULL], ERR_SHAPE),
+    ("fp8_quantize_kv", [P16, 0, 2**40, 2, 8, P16, P16, P16, NULL], ERR_SHAPE),
+    ("fp8_quantize_kv", [P16, 0, 1, 1, 8, P17, P16, P16, NULL], ERR_ALIGN),
     # fp8q_e4m3_encode_f32(v, q, n, stream)
     ("fp8q_e4m3_encode_f32", [NULL, P16, 4, NULL], ERR_NULL),
     ("fp8q_e4m3_encode_f32", [P16, P16, 0, NULL], ERR_SHAPE),
