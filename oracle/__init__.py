@@ -43,6 +43,10 @@ def _load():
         "orc_quantize_rows": (None, [_p, _c.c_int, _i64, _i64, _p, _p, _p]),
         "orc_quantize_delayed": (None, [_p, _c.c_int, _i64, _p, _p, _p, _p, _i64, _p]),
         "orc_quantize_kv": (None, [_p, _c.c_int, _i64, _i64, _i64, _p, _p, _p]),
+        "orc_nested_split_e4m3": (_i64, [_p, _p, _p, _i64]),
+        "orc_nested_rebuild_e4m3": (None, [_p, _p, _p, _i64]),
+        "orc_gemm_fp8_f32_fp16out": (None, [_p, _c.c_float, _p, _c.c_float, _i64, _i64, _i64,
+                                            _p, _c.c_int]),
         "orc_gemm_fp8_rowwise_ref": (None, [_p, _p, _p, _p, _i64, _i64, _i64,
                                             _p, _p, _i64, _p, _p]),
         "orc_gemm_fp8_rowwise_f32": (None, [_p, _p, _p, _p, _i64, _i64, _i64, _p, _c.c_int]),
@@ -243,6 +247,41 @@ def nested_rebuild(hi, lo):
     w = np.empty(hi.shape, np.uint16)
     lib.orc_nested_rebuild(_ptr(hi), _ptr(lo), _ptr(w), hi.size)
     return w
+
+
+def nested_split_e4m3(w_bits):
+    """E4M3 upper-byte split: returns (hi, lo, number of words outside the FP8
+    mode's range |w| < 1.875)."""
+    w = _c_arr(w_bits, np.uint16)
+    hi = np.empty(w.shape, np.uint8)
+    lo = np.empty(w.shape, np.uint8)
+    bad = lib.orc_nested_split_e4m3(_ptr(w), _ptr(hi), _ptr(lo), w.size)
+    return hi, lo, int(bad)
+
+
+def nested_rebuild_e4m3(hi, lo):
+    hi = _c_arr(hi, np.uint8)
+    lo = _c_arr(lo, np.uint8)
+    assert hi.shape == lo.shape
+    w = np.empty(hi.shape, np.uint16)
+    lib.orc_nested_rebuild_e4m3(_ptr(hi), _ptr(lo), _ptr(w), hi.size)
+    return w
+
+
+NESTED_E4M3_SCALE = 2.0 ** -8      # weight scale of the E4M3 upper byte
+
+
+def gemm_fp8_f32_fp16out(qa, sa, qw, sw, nthreads=None):
+    """The fp32-accumulating E4M3 x E4M3 GEMM with fp16 output:
+    y = fp16(acc * fl32(sa * sw)); returns fp16 bits [M,N]."""
+    qa = _c_arr(qa, np.uint8)
+    qw = _c_arr(qw, np.uint8)
+    M, K = qa.shape
+    N, _ = qw.shape
+    y = np.empty((M, N), np.uint16)
+    lib.orc_gemm_fp8_f32_fp16out(_ptr(qa), sa, _ptr(qw), sw, M, N, K, _ptr(y),
+                                 nthreads or default_threads())
+    return y
 
 
 # ---------------------------------------------------------------- GEMM checkers

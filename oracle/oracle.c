@@ -321,6 +321,37 @@ void orc_nested_rebuild(const uint8_t* hi, const uint8_t* lo, uint16_t* w, int64
     for (int64_t i = 0; i < n; ++i) w[i] = (uint16_t)(((uint16_t)hi[i] << 8) | lo[i]);
 }
 
+/* The E4M3 upper-byte split ([NestedFP] §2.1 says the upper byte "becomes    */
+/* E4M3").  Reading: an fp16 word s|e4..e0|m9..m0 with e4 = 0 (|w| < 2) keeps  */
+/* s|e3..e0|m9..m7 in the upper byte, which is then the E4M3 code of w * 2^8    */
+/* truncated to 3 mantissa bits (fp16 subnormals land on E4M3 subnormals), and */
+/* e4|m6..m0 in the lower byte, so the rebuild is exact for every fp16 word.   */
+/* The FP8 mode (upper byte as E4M3, scale 2^-8) holds for finite |w| < 1.875; */
+/* beyond that e4 = 1 or the code would read as NaN.  Returns how many words   */
+/* break that range.                                                           */
+int64_t orc_nested_split_e4m3(const uint16_t* w, uint8_t* hi, uint8_t* lo, int64_t n)
+{
+    int64_t bad = 0;
+    for (int64_t i = 0; i < n; ++i) {
+        uint16_t v = w[i];
+        uint16_t s = (uint16_t)(v >> 15);
+        uint16_t e4 = (uint16_t)((v >> 14) & 1);
+        uint16_t rest = (uint16_t)((v >> 7) & 0x7F);       /* e3..e0 m9 m8 m7 */
+        hi[i] = (uint8_t)((s << 7) | rest);
+        lo[i] = (uint8_t)((e4 << 7) | (v & 0x7F));
+        double a = fabs(orc_f16_decode(v));
+        if (e4 || !(a < 1.875)) ++bad;
+    }
+    return bad;
+}
+
+void orc_nested_rebuild_e4m3(const uint8_t* hi, const uint8_t* lo, uint16_t* w, int64_t n)
+{
+    for (int64_t i = 0; i < n; ++i)
+        w[i] = (uint16_t)(((hi[i] & 0x80) << 8) | ((lo[i] & 0x80) << 7) | ((hi[i] & 0x7F) << 7) |
+                          (lo[i] & 0x7F));
+}
+
 /* ------------------------------------------------------------------------ */
 /* GEMM checkers (fp64).  All matrices are row-major: activations [M,K],     */
 /* weights [N,K] (K contiguous: the "tn" layout of the FP8 GEMM named in     */
@@ -468,7 +499,7 @@ void orc_nested_fp8_ref(const uint8_t* qa, float sa, const uint8_t* hi,
 /* These are what the CPU baseline times.  Threads only split the N range.   */
 /* ------------------------------------------------------------------------ */
 
-enum { KIND_FP8 = 0, KIND_NESTED_FP16 = 1, KIND_NESTED_FP8 = 2 };
+enum { KIND_FP8 = 0, KIND_NESTED_FP16 = 1, KIND_NESTED_FP8 = 2, KIND_FP8_FP16OUT = 3 };
 
 typedef struct {
     int kind;
@@ -502,12 +533,20 @@ static void* gemm_worker(void* arg)
                     acc += (float)orc_f16_decode(a[k]) * (float)orc_f16_decode(wbits);
                 }
                 j->y[m * j->N + n] = orc_f16_encode(acc);
-            } else {
+            } else if (j->kind == KIND_NESTED_FP8) {
                 const uint8_t* a = (const uint8_t*)j->a + m * j->K;
                 const uint8_t* h = j->w + n * j->K;
                 for (int64_t k = 0; k < j->K; ++k)
                     acc += (float)orc_e4m3_decode(a[k]) * (float)orc_e5m2_decode(h[k]);
                 j->y[m * j->N + n] = orc_f16_encode(acc * j->sa);
+            } else {
+                /* E4M3 x E4M3, fp16 output: the NestedFP FP8 mode of the E4M3 split */
+                const uint8_t* a = (const uint8_t*)j->a + m * j->K;
+                const uint8_t* h = j->w + n * j->K;
+                for (int64_t k = 0; k < j->K; ++k)
+                    acc += (float)orc_e4m3_decode(a[k]) * (float)orc_e4m3_decode(h[k]);
+                float s = j->sa * j->sw;                    /* fl32(s_a * s_w) */
+                j->y[m * j->N + n] = orc_f16_encode(acc * s);
             }
         }
     }
@@ -573,6 +612,13 @@ void orc_nested_fp8_f32(const uint8_t* qa, float sa, const uint8_t* hi,
                         int64_t M, int64_t N, int64_t K, uint16_t* y, int nthreads)
 {
     run_gemm(KIND_NESTED_FP8, qa, hi, NULL, sa, 1.0f, M, N, K, y, nthreads);
+}
+
+/* y[M,N] fp16 = fp16(acc * fl32(s_a*s_w)), acc = fp32 sum of E4M3(qa) * E4M3(hi). */
+void orc_gemm_fp8_f32_fp16out(const uint8_t* qa, float sa, const uint8_t* hi, float sw,
+                              int64_t M, int64_t N, int64_t K, uint16_t* y, int nthreads)
+{
+    run_gemm(KIND_FP8_FP16OUT, qa, hi, NULL, sa, sw, M, N, K, y, nthreads);
 }
 
 /* Reports the rounding mode the oracle runs under (must be FE_TONEAREST). */
