@@ -338,12 +338,15 @@ def secondary(torch, fp8q, synth, model1, dev,
         return out
     # NestedFP at M = 1 and 256 on 8 layers of fp16 weights (hi/lo planes)
     nested = []
+    nested4 = []                       # planes of the E4M3 upper-byte split
     for layer in range(8):
         for name, K, N in synth.LLAMA7B_LINEARS:
             w = synth.normal((N, K), 0.02, "fp16", seed=synth.seed_for("w", layer, name), device=dev)
             hi, lo = fp8q.nested_split(w)
+            hi4, lo4, _ = fp8q.nested_split_e4m3(w)
             del w
             nested.append((K, N, hi, lo))
+            nested4.append((hi4, lo4))
     for M in (1, 256):
         bufs = []
         for K, N, hi, lo in nested:
@@ -361,10 +364,19 @@ def secondary(torch, fp8q, synth, model1, dev,
             for (K, N, hi, lo), (a, q, s, am, y) in zip(nested, bufs):
                 fp8q.nested_linear_fp8(a, hi, y, q, s, am)
 
-        for mode, fn, wbytes in (("fp16", step16, 2), ("fp8", step8, 1)):
+        def step16e():
+            for (K, N, _, _), (hi4, lo4), (a, q, s, am, y) in zip(nested, nested4, bufs):
+                fp8q.nested_gemm_fp16_e4m3(a, hi4, lo4, y)
+
+        def step8e():
+            for (K, N, _, _), (hi4, _), (a, q, s, am, y) in zip(nested, nested4, bufs):
+                fp8q.nested_linear_fp8_e4m3(a, hi4, y, q, s, am)
+
+        for mode, fn, wbytes in (("fp16", step16, 2), ("fp8", step8, 1),
+                                 ("fp16_e4m3split", step16e, 2), ("fp8_e4m3split", step8e, 1)):
             dt, _ = time_fn(torch, fn, steps=5, warmup=2)
             byts = sum(wbytes * N * K + 2 * M * K + 2 * M * N for K, N, _, _ in nested)
-            if mode == "fp8":
+            if mode.startswith("fp8"):
                 byts = sum(N * K + M * K + 2 * M * N + 3 * M * K for K, N, _, _ in nested)
             fl = sum(2 * M * N * K for K, N, _, _ in nested)
             out[f"nested_{mode}_m{M}"] = {"GB_per_s": round(byts / dt / 1e9, 1),

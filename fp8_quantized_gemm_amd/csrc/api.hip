@@ -307,7 +307,8 @@ fp8q_status nested_split(const uint16_t* w, uint8_t* hi, uint8_t* lo, int64_t n,
     if (n < 1 || n > ((int64_t)1 << 40)) return FP8Q_ERR_SHAPE;
     if (!aligned16(w) || !aligned16(hi) || !aligned16(lo)) return FP8Q_ERR_ALIGN;
     FP8Q_TRY(check_device());
-    return finish("nested_split", launch_nested_split(w, hi, lo, n, (hipStream_t)stream));
+    return finish("nested_split", launch_nested_split(w, hi, lo, n, SP_PLAIN, nullptr,
+                                                      (hipStream_t)stream));
 }
 
 fp8q_status nested_rebuild_fp16(const uint8_t* hi, const uint8_t* lo, uint16_t* w, int64_t n,
@@ -317,8 +318,20 @@ fp8q_status nested_rebuild_fp16(const uint8_t* hi, const uint8_t* lo, uint16_t* 
     if (n < 1 || n > ((int64_t)1 << 40)) return FP8Q_ERR_SHAPE;
     if (!aligned16(w) || !aligned16(hi) || !aligned16(lo)) return FP8Q_ERR_ALIGN;
     FP8Q_TRY(check_device());
-    return finish("nested_rebuild_fp16", launch_nested_rebuild(hi, lo, w, n, (hipStream_t)stream));
+    return finish("nested_rebuild_fp16",
+                  launch_nested_rebuild(hi, lo, w, n, SP_PLAIN, (hipStream_t)stream));
 }
+
+namespace {
+// NestedFP FP16 mode on either split, dispatched on M like the FP8 GEMM.
+hipError_t dispatch_nested16(const uint16_t* a, const uint8_t* hi, const uint8_t* lo, uint16_t* y,
+                             int64_t M, int64_t N, int64_t K, int sp, hipStream_t st)
+{
+    return M <= kRowkMaxM     ? launch_rowk_nested16(a, hi, lo, y, (int)M, (int)N, (int)K, sp, st)
+           : M <= kDecodeMaxM ? launch_gemv_nested16(a, hi, lo, y, (int)M, (int)N, (int)K, sp, st)
+                              : launch_tile_nested16(a, hi, lo, y, (int)M, (int)N, (int)K, sp, st);
+}
+}  // namespace
 
 fp8q_status nested_gemm_fp16(const uint16_t* a, const uint8_t* hi, const uint8_t* lo, uint16_t* y,
                              int64_t M, int64_t N, int64_t K, fp8q_stream stream)
@@ -327,11 +340,8 @@ fp8q_status nested_gemm_fp16(const uint16_t* a, const uint8_t* hi, const uint8_t
     FP8Q_TRY(check_gemm_sizes(M, N, K));
     if (!aligned16(a) || !aligned16(hi) || !aligned16(lo) || !aligned16(y)) return FP8Q_ERR_ALIGN;
     FP8Q_TRY(check_device());
-    hipStream_t st = (hipStream_t)stream;
-    hipError_t e = M <= kRowkMaxM     ? launch_rowk_nested16(a, hi, lo, y, (int)M, (int)N, (int)K, st)
-                   : M <= kDecodeMaxM ? launch_gemv_nested16(a, hi, lo, y, (int)M, (int)N, (int)K, st)
-                                      : launch_tile_nested16(a, hi, lo, y, (int)M, (int)N, (int)K, st);
-    return finish("nested_gemm_fp16", e);
+    return finish("nested_gemm_fp16",
+                  dispatch_nested16(a, hi, lo, y, M, N, K, SP_PLAIN, (hipStream_t)stream));
 }
 
 fp8q_status nested_gemm_fp8(const uint8_t* qa, const float* sa, const uint8_t* hi, uint16_t* y,
@@ -343,6 +353,69 @@ fp8q_status nested_gemm_fp8(const uint8_t* qa, const float* sa, const uint8_t* h
     FP8Q_TRY(check_device());
     return finish("nested_gemm_fp8", dispatch_fp8(qa, sa, hi, nullptr, y, (int)M, (int)N, (int)K,
                                                   WF_E5M2, OUT_FP16, 0, (hipStream_t)stream));
+}
+
+fp8q_status nested_split_e4m3(const uint16_t* w, uint8_t* hi, uint8_t* lo, int64_t n,
+                              uint64_t* out_of_range, fp8q_stream stream)
+{
+    if (!w || !hi || !lo) return FP8Q_ERR_NULL;
+    if (n < 1 || n > ((int64_t)1 << 40)) return FP8Q_ERR_SHAPE;
+    if (!aligned16(w) || !aligned16(hi) || !aligned16(lo) ||
+        (out_of_range != nullptr && (reinterpret_cast<uintptr_t>(out_of_range) & 7u) != 0))
+        return FP8Q_ERR_ALIGN;
+    FP8Q_TRY(check_device());
+    return finish("nested_split_e4m3",
+                  launch_nested_split(w, hi, lo, n, SP_E4M3,
+                                      reinterpret_cast<unsigned long long*>(out_of_range),
+                                      (hipStream_t)stream));
+}
+
+fp8q_status nested_rebuild_e4m3(const uint8_t* hi, const uint8_t* lo, uint16_t* w, int64_t n,
+                                fp8q_stream stream)
+{
+    if (!w || !hi || !lo) return FP8Q_ERR_NULL;
+    if (n < 1 || n > ((int64_t)1 << 40)) return FP8Q_ERR_SHAPE;
+    if (!aligned16(w) || !aligned16(hi) || !aligned16(lo)) return FP8Q_ERR_ALIGN;
+    FP8Q_TRY(check_device());
+    return finish("nested_rebuild_e4m3",
+                  launch_nested_rebuild(hi, lo, w, n, SP_E4M3, (hipStream_t)stream));
+}
+
+fp8q_status nested_gemm_fp16_e4m3(const uint16_t* a, const uint8_t* hi, const uint8_t* lo,
+                                  uint16_t* y, int64_t M, int64_t N, int64_t K, fp8q_stream stream)
+{
+    if (!a || !hi || !lo || !y) return FP8Q_ERR_NULL;
+    FP8Q_TRY(check_gemm_sizes(M, N, K));
+    if (!aligned16(a) || !aligned16(hi) || !aligned16(lo) || !aligned16(y)) return FP8Q_ERR_ALIGN;
+    FP8Q_TRY(check_device());
+    return finish("nested_gemm_fp16_e4m3",
+                  dispatch_nested16(a, hi, lo, y, M, N, K, SP_E4M3, (hipStream_t)stream));
+}
+
+fp8q_status nested_gemm_fp8_e4m3(const uint8_t* qa, const float* sa, const uint8_t* hi,
+                                 uint16_t* y, int64_t M, int64_t N, int64_t K, fp8q_stream stream)
+{
+    if (!qa || !sa || !hi || !y) return FP8Q_ERR_NULL;
+    FP8Q_TRY(check_gemm_sizes(M, N, K));
+    if (!aligned16(qa) || !aligned16(hi) || !aligned16(y) || !aligned4(sa)) return FP8Q_ERR_ALIGN;
+    FP8Q_TRY(check_device());
+    return finish("nested_gemm_fp8_e4m3",
+                  dispatch_fp8(qa, sa, hi, nullptr, y, (int)M, (int)N, (int)K, WF_E4M3_SC8,
+                               OUT_FP16, 0, (hipStream_t)stream));
+}
+
+fp8q_status nested_linear_fp8_e4m3(const uint16_t* a, const uint8_t* hi, uint16_t* y, uint8_t* q,
+                                   float* scale, float* amax, int64_t M, int64_t N, int64_t K,
+                                   fp8q_stream stream)
+{
+    if (!a || !hi || !y || !q || !scale || !amax) return FP8Q_ERR_NULL;
+    FP8Q_TRY(check_gemm_sizes(M, N, K));
+    if (!aligned16(a) || !aligned16(hi) || !aligned16(y) || !aligned16(q) || !aligned4(scale) ||
+        !aligned4(amax))
+        return FP8Q_ERR_ALIGN;
+    FP8Q_TRY(check_device());
+    return linear_common("nested_linear_fp8_e4m3", a, FP8Q_FP16, hi, nullptr, y, q, scale, amax, M,
+                         N, K, WF_E4M3_SC8, OUT_FP16, 0, (hipStream_t)stream);
 }
 
 fp8q_status fp8q_e4m3_encode_f32(const float* v, uint8_t* q, int64_t n, fp8q_stream stream)

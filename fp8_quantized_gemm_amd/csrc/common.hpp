@@ -16,9 +16,16 @@ typedef _Float16 v8h __attribute__((ext_vector_type(8)));
 
 // Input dtype tags (same numbering as fp8q_dtype in the public header).
 enum : int { DT_BF16 = 0, DT_FP16 = 1 };
-// Weight-operand format of the FP8 MFMA (the cbsz/blgp format selector of
-// v_mfma_*_f8f6f4): 0 = FP8 E4M3, 1 = BF8 E5M2.
-enum : int { WF_E4M3 = 0, WF_E5M2 = 1 };
+// Weight format of the FP8 GEMMs: E4M3 codes, E5M2 codes (the NestedFP upper
+// byte of the plain split), or E4M3 codes of w * 2^8 (the NestedFP upper byte
+// of the E4M3 split), whose 2^-8 the epilogue applies when no weight scale is
+// given.
+enum : int { WF_E4M3 = 0, WF_E5M2 = 1, WF_E4M3_SC8 = 2 };
+// The format selector (cbsz/blgp) of v_mfma_*_f8f6f4 for a weight format:
+// 0 = FP8 E4M3, 1 = BF8 E5M2.
+constexpr int mfma_format(int wf) { return wf == WF_E5M2 ? 1 : 0; }
+// The weight scale a format implies when the call passes none.
+constexpr float implied_wscale(int wf) { return wf == WF_E4M3_SC8 ? 0x1p-8f : 1.0f; }
 // Output format of the GEMM epilogues.
 enum : int { OUT_BF16 = 0, OUT_FP16 = 1 };
 
@@ -192,10 +199,34 @@ __device__ __forceinline__ float scale_from_amax(float amax)
 // Interleave four upper bytes (h) and four lower bytes (l) into two dwords
 // holding the fp16 words (h_i << 8) | l_i, i = 0..3, little-endian.
 // v_perm_b32 selects bytes from {src0 (bytes 4..7), src1 (bytes 0..3)}.
+// With SP_E4M3 the planes come from the E4M3 split (hi = sign | bits 13..7,
+// lo = bit 14 | bits 6..0), and each interleaved word hi << 8 | lo is put
+// back in place: sign and bits 6..0 stay, hi's 7 bits move down by one, lo's
+// top bit moves up to bit 14.
+enum : int { SP_PLAIN = 0, SP_E4M3 = 1 };
+// v_bfi_b32: (mask & a) | (~mask & b), one VALU instruction (the compiler
+// does not form it from the C expression here); register operands only
+__device__ __forceinline__ uint32_t bit_insert(uint32_t mask, uint32_t a, uint32_t b)
+{
+    uint32_t d;
+    asm("v_bfi_b32 %0, %1, %2, %3" : "=v"(d) : "s"(mask), "v"(a), "v"(b));
+    return d;
+}
+__device__ __forceinline__ uint32_t e4m3_split_words(uint32_t u)
+{
+    // bits 13..7 from u >> 1, then bit 14 from u << 7
+    const uint32_t w = bit_insert(0x3F803F80u, u >> 1, u);
+    return bit_insert(0x40004000u, u << 7, w);
+}
+template <int SP = SP_PLAIN>
 __device__ __forceinline__ void nested_rebuild4(uint32_t h, uint32_t l, uint32_t& w01, uint32_t& w23)
 {
     w01 = __builtin_amdgcn_perm(h, l, 0x05010400u);  // [l0, h0, l1, h1]
     w23 = __builtin_amdgcn_perm(h, l, 0x07030602u);  // [l2, h2, l3, h3]
+    if constexpr (SP == SP_E4M3) {
+        w01 = e4m3_split_words(w01);
+        w23 = e4m3_split_words(w23);
+    }
 }
 
 // ---------------------------------------------------------------- buffer loads
@@ -286,6 +317,21 @@ __device__ __forceinline__ float wave_sum(float v)
     return v;
 }
 
+// Block-wide integer sum for blockDim.x = NT threads; valid in every thread.
+template <int NT>
+__device__ __forceinline__ int block_sum_int(int v, int* lds)
+{
+    constexpr int W = NT / 64;
+#pragma unroll
+    for (int off = 32; off >= 1; off >>= 1) v += __shfl_xor(v, off);
+    if ((threadIdx.x & 63) == 0) lds[threadIdx.x >> 6] = v;
+    __syncthreads();
+    int t = 0;
+#pragma unroll
+    for (int i = 0; i < W; ++i) t += lds[i];
+    return t;
+}
+
 // ---------------------------------------------------------------- delayed scaling
 // Delayed scaling with an amax history ([RTX4060] §6.1 asks for a history of
 // at least 1024 values).  A call quantizes with the scale that the earlier
@@ -357,7 +403,7 @@ hipError_t launch_rowk_fp8(const uint8_t* qa, const float* sa, const uint8_t* qw
                            uint16_t* y, int M, int N, int K, int wfmt, int outf, int rowscale,
                            hipStream_t stream);
 hipError_t launch_rowk_nested16(const uint16_t* a, const uint8_t* hi, const uint8_t* lo,
-                                uint16_t* y, int M, int N, int K, hipStream_t stream);
+                                uint16_t* y, int M, int N, int K, int sp, hipStream_t stream);
 hipError_t launch_linear_fused(const void* x, int dtype, const uint8_t* qw, const float* sw,
                                uint16_t* y, uint8_t* q, float* scale, float* amax, int M, int N,
                                int K, int wfmt, int outf, int rowscale, hipStream_t stream);
@@ -380,13 +426,15 @@ hipError_t launch_tile_fp8(const uint8_t* qa, const float* sa, const uint8_t* qw
                            const float* sw, uint16_t* y, int M, int N, int K, int wfmt,
                            int outf, int rowscale, hipStream_t stream);
 
-hipError_t launch_nested_split(const uint16_t* w, uint8_t* hi, uint8_t* lo, int64_t n,
-                               hipStream_t stream);
+// sp selects the split (SP_PLAIN / SP_E4M3); with SP_E4M3 the split adds the
+// number of words outside |w| < 1.875 to *bad (when bad is not null).
+hipError_t launch_nested_split(const uint16_t* w, uint8_t* hi, uint8_t* lo, int64_t n, int sp,
+                               unsigned long long* bad, hipStream_t stream);
 hipError_t launch_nested_rebuild(const uint8_t* hi, const uint8_t* lo, uint16_t* w, int64_t n,
-                                 hipStream_t stream);
+                                 int sp, hipStream_t stream);
 hipError_t launch_gemv_nested16(const uint16_t* a, const uint8_t* hi, const uint8_t* lo,
-                                uint16_t* y, int M, int N, int K, hipStream_t stream);
+                                uint16_t* y, int M, int N, int K, int sp, hipStream_t stream);
 hipError_t launch_tile_nested16(const uint16_t* a, const uint8_t* hi, const uint8_t* lo,
-                                uint16_t* y, int M, int N, int K, hipStream_t stream);
+                                uint16_t* y, int M, int N, int K, int sp, hipStream_t stream);
 
 }  // namespace fp8q

@@ -105,6 +105,7 @@ void gemm_f8_kernel(
     const uint8_t* __restrict__ qw, const float* __restrict__ sw,
     uint16_t* __restrict__ y, int M, int N, int K, int rowscale)
 {
+    constexpr int WF_MF = mfma_format(WFMT);   // MFMA format selector of the weight operand
     constexpr int NW = WM * WN;
     constexpr int BK = 128;
     constexpr int TM = BM / WM, TN = BN / WN;
@@ -193,7 +194,7 @@ void gemm_f8_kernel(
 #pragma unroll
                 for (int j = 0; j < FN; ++j)
                     acc[i][j] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(
-                        wf[j], af[i & 1], acc[i][j], WFMT, WF_E4M3, 0, 0, 0, 0);
+                        wf[j], af[i & 1], acc[i][j], WF_MF, WF_E4M3, 0, 0, 0, 0);
             }
         } else {
             // keep the FM activation fragments, stream the weight fragments
@@ -208,7 +209,7 @@ void gemm_f8_kernel(
 #pragma unroll
                 for (int i = 0; i < FM; ++i)
                     acc[i][j] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(
-                        wf[j & 1], af[i], acc[i][j], WFMT, WF_E4M3, 0, 0, 0, 0);
+                        wf[j & 1], af[i], acc[i][j], WF_MF, WF_E4M3, 0, 0, 0, 0);
             }
         }
         wait_vm<ALLOW>();
@@ -264,7 +265,7 @@ void gemm_f8_kernel(
             }
         store([&](int i, int j, int e) { return sam[i] * swn[j][e]; });
     } else {
-        const float s = (sw != nullptr) ? *sa * *sw : *sa;
+        const float s = *sa * ((sw != nullptr) ? *sw : implied_wscale(WFMT));
         store([&](int, int, int) { return s; });
     }
 }
@@ -290,7 +291,7 @@ void gemm_f8_kernel(
 // step: A(k+1) sits in group k + 1 - AST, after which only that group's W
 // and the AST - 2 later groups may still be in flight (when AST == WST the
 // group's W is needed too).
-template <int BM, int BN, int WM, int WN, int AST, int WST>
+template <int BM, int BN, int WM, int WN, int AST, int WST, int SP>
 __global__ __launch_bounds__(WM * WN * 64) __attribute__((amdgpu_waves_per_eu(2)))
 void gemm_n16_kernel(const uint16_t* __restrict__ a, const uint8_t* __restrict__ hi,
                      const uint8_t* __restrict__ lo, uint16_t* __restrict__ y, int M, int N, int K)
@@ -381,8 +382,8 @@ void gemm_n16_kernel(const uint16_t* __restrict__ a, const uint8_t* __restrict__
                 const v2i h = *reinterpret_cast<const v2i*>(Hs + off);
                 const v2i l = *reinterpret_cast<const v2i*>(Ls + off);
                 uint32_t w0, w1, w2, w3;
-                nested_rebuild4((uint32_t)h[0], (uint32_t)l[0], w0, w1);
-                nested_rebuild4((uint32_t)h[1], (uint32_t)l[1], w2, w3);
+                nested_rebuild4<SP>((uint32_t)h[0], (uint32_t)l[0], w0, w1);
+                nested_rebuild4<SP>((uint32_t)h[1], (uint32_t)l[1], w2, w3);
                 wf[j] = __builtin_bit_cast(v8h, v4i{(int)w0, (int)w1, (int)w2, (int)w3});
             }
 #pragma unroll
@@ -482,14 +483,16 @@ hipError_t launch_tile_fp8(const uint8_t* qa, const float* sa, const uint8_t* qw
         return launch_tile_fmt<WF_E4M3, OUT_BF16>(qa, sa, qw, sw, y, M, N, K, rowscale, stream);
     if (wfmt == WF_E5M2 && outf == OUT_FP16 && !rowscale)
         return launch_tile_fmt<WF_E5M2, OUT_FP16>(qa, sa, qw, sw, y, M, N, K, 0, stream);
+    if (wfmt == WF_E4M3_SC8 && outf == OUT_FP16 && !rowscale)
+        return launch_tile_fmt<WF_E4M3_SC8, OUT_FP16>(qa, sa, qw, sw, y, M, N, K, 0, stream);
     return hipErrorInvalidValue;
 }
 
-template <int BM, int BN, int WM, int WN, int AST, int WST>
+template <int BM, int BN, int WM, int WN, int AST, int WST, int SP>
 hipError_t launch_n16(const uint16_t* a, const uint8_t* hi, const uint8_t* lo, uint16_t* y,
                       int M, int N, int K, hipStream_t stream)
 {
-    auto kern = gemm_n16_kernel<BM, BN, WM, WN, AST, WST>;
+    auto kern = gemm_n16_kernel<BM, BN, WM, WN, AST, WST, SP>;
     constexpr size_t lds = ((size_t)AST * BM + (size_t)WST * BN) * 128;
     static_assert(lds <= 160 * 1024, "LDS of one CU");
     static bool attr_set = false;        // idempotent host attribute, set on first use
@@ -517,15 +520,23 @@ constexpr TileShape kN16Shapes[] = {
     { 64,  64, 1, 25.0f},   // the same kernel, one workgroup per CU
 };
 
-hipError_t launch_tile_nested16(const uint16_t* a, const uint8_t* hi, const uint8_t* lo,
-                                uint16_t* y, int M, int N, int K, hipStream_t stream)
+template <int SP>
+hipError_t launch_tile_nested16_sp(const uint16_t* a, const uint8_t* hi, const uint8_t* lo,
+                                   uint16_t* y, int M, int N, int K, hipStream_t stream)
 {
     switch (pick_tile_shape(kN16Shapes, sizeof(kN16Shapes) / sizeof(kN16Shapes[0]), M, N)) {
-    case 0: return launch_n16<256, 256, 2, 4, 2, 2>(a, hi, lo, y, M, N, K, stream);
-    case 1: return launch_n16<256, 128, 4, 2, 3, 4>(a, hi, lo, y, M, N, K, stream);
-    case 2: return launch_n16<128, 128, 2, 4, 4, 4>(a, hi, lo, y, M, N, K, stream);
-    default: return launch_n16<64, 64, 2, 2, 4, 4>(a, hi, lo, y, M, N, K, stream);
+    case 0: return launch_n16<256, 256, 2, 4, 2, 2, SP>(a, hi, lo, y, M, N, K, stream);
+    case 1: return launch_n16<256, 128, 4, 2, 3, 4, SP>(a, hi, lo, y, M, N, K, stream);
+    case 2: return launch_n16<128, 128, 2, 4, 4, 4, SP>(a, hi, lo, y, M, N, K, stream);
+    default: return launch_n16<64, 64, 2, 2, 4, 4, SP>(a, hi, lo, y, M, N, K, stream);
     }
+}
+
+hipError_t launch_tile_nested16(const uint16_t* a, const uint8_t* hi, const uint8_t* lo,
+                                uint16_t* y, int M, int N, int K, int sp, hipStream_t stream)
+{
+    return sp == SP_E4M3 ? launch_tile_nested16_sp<SP_E4M3>(a, hi, lo, y, M, N, K, stream)
+                         : launch_tile_nested16_sp<SP_PLAIN>(a, hi, lo, y, M, N, K, stream);
 }
 
 }  // namespace fp8q

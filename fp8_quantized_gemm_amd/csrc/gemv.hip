@@ -29,7 +29,8 @@ template <int WFMT>
 __device__ __forceinline__ v4f mfma_f8(const v8i& a, const v8i& b, const v4f& c)
 {
     // A (activations) is always E4M3; B (weights) is E4M3 or E5M2.
-    return __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(a, b, c, WF_E4M3, WFMT, 0, 0, 0, 0);
+    constexpr int BF = mfma_format(WFMT);
+    return __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(a, b, c, WF_E4M3, BF, 0, 0, 0, 0);
 }
 
 __device__ __forceinline__ v8i cat(const v4i& lo, const v4i& hi)
@@ -93,7 +94,7 @@ __global__ __launch_bounds__(WAVES * 64) void gemv_f8_kernel(
     for (int i = 0; i < 4; ++i) red[wave][4 * g + i][r] = acc[i];
     __syncthreads();
 
-    const float s_w = (sw != nullptr) ? *sw : 1.0f;
+    const float s_w = (sw != nullptr) ? *sw : implied_wscale(WFMT);
     for (int t = threadIdx.x; t < M * 16; t += WAVES * 64) {
         const int m = t >> 4, c = t & 15;
         if (c >= rows) continue;
@@ -110,7 +111,7 @@ __global__ __launch_bounds__(WAVES * 64) void gemv_f8_kernel(
 // A K block is 64 elements: lane group g takes elements [16g, 16g+16) (16
 // bytes of hi, 16 of lo, 32 of a) and feeds two 16x16x32 MFMAs.  Same
 // buffer-load scheme as the FP8 GEMV.
-template <int WAVES, int U, int CP>
+template <int WAVES, int U, int CP, int SP>
 __global__ __launch_bounds__(WAVES * 64) void gemv_nested16_kernel(
     const uint16_t* __restrict__ a, const uint8_t* __restrict__ hi,
     const uint8_t* __restrict__ lo, uint16_t* __restrict__ y, int M, int N, int K)
@@ -148,10 +149,10 @@ __global__ __launch_bounds__(WAVES * 64) void gemv_nested16_kernel(
 #pragma unroll
         for (int u = 0; u < U; ++u) {
             uint32_t w[8];
-            nested_rebuild4((uint32_t)hv[u][0], (uint32_t)lv[u][0], w[0], w[1]);
-            nested_rebuild4((uint32_t)hv[u][1], (uint32_t)lv[u][1], w[2], w[3]);
-            nested_rebuild4((uint32_t)hv[u][2], (uint32_t)lv[u][2], w[4], w[5]);
-            nested_rebuild4((uint32_t)hv[u][3], (uint32_t)lv[u][3], w[6], w[7]);
+            nested_rebuild4<SP>((uint32_t)hv[u][0], (uint32_t)lv[u][0], w[0], w[1]);
+            nested_rebuild4<SP>((uint32_t)hv[u][1], (uint32_t)lv[u][1], w[2], w[3]);
+            nested_rebuild4<SP>((uint32_t)hv[u][2], (uint32_t)lv[u][2], w[4], w[5]);
+            nested_rebuild4<SP>((uint32_t)hv[u][3], (uint32_t)lv[u][3], w[6], w[7]);
             const v4i wlo = {(int)w[0], (int)w[1], (int)w[2], (int)w[3]};
             const v4i whi = {(int)w[4], (int)w[5], (int)w[6], (int)w[7]};
             acc = __builtin_amdgcn_mfma_f32_16x16x32_f16(__builtin_bit_cast(v8h, a0[u]),
@@ -199,16 +200,24 @@ hipError_t launch_gemv_fp8(const uint8_t* qa, const float* sa, const uint8_t* qw
     else if (wfmt == WF_E5M2 && outf == OUT_FP16 && !rowscale)
         gemv_f8_kernel<WF_E5M2, OUT_FP16, kGemvWaves, kGemvUnroll, CP_DEFAULT>
             <<<grid, block, 0, stream>>>(qa, sa, qw, sw, y, M, N, K, 0);
+    else if (wfmt == WF_E4M3_SC8 && outf == OUT_FP16 && !rowscale)
+        gemv_f8_kernel<WF_E4M3_SC8, OUT_FP16, kGemvWaves, kGemvUnroll, CP_DEFAULT>
+            <<<grid, block, 0, stream>>>(qa, sa, qw, sw, y, M, N, K, 0);
     else
         return hipErrorInvalidValue;
     return hipGetLastError();
 }
 
 hipError_t launch_gemv_nested16(const uint16_t* a, const uint8_t* hi, const uint8_t* lo,
-                                uint16_t* y, int M, int N, int K, hipStream_t stream)
+                                uint16_t* y, int M, int N, int K, int sp, hipStream_t stream)
 {
-    gemv_nested16_kernel<kNestedWaves, kNestedUnroll, CP_NT>
-        <<<dim3((unsigned)(((int64_t)N + 15) / 16)), dim3(kNestedWaves * 64), 0, stream>>>(a, hi, lo, y, M, N, K);
+    const dim3 grid((unsigned)(((int64_t)N + 15) / 16)), block(kNestedWaves * 64);
+    if (sp == SP_E4M3)
+        gemv_nested16_kernel<kNestedWaves, kNestedUnroll, CP_NT, SP_E4M3>
+            <<<grid, block, 0, stream>>>(a, hi, lo, y, M, N, K);
+    else
+        gemv_nested16_kernel<kNestedWaves, kNestedUnroll, CP_NT, SP_PLAIN>
+            <<<grid, block, 0, stream>>>(a, hi, lo, y, M, N, K);
     return hipGetLastError();
 }
 

@@ -52,7 +52,7 @@ __device__ __forceinline__ void decode16(const v4i& v, float (&f)[16])
 #pragma unroll
     for (int d = 0; d < 4; ++d) {
         v2f lo, hi;
-        if constexpr (FMT == WF_E4M3) {
+        if constexpr (mfma_format(FMT) == 0) {      // E4M3 codes
             lo = __builtin_amdgcn_cvt_pk_f32_fp8(v[d], false);
             hi = __builtin_amdgcn_cvt_pk_f32_fp8(v[d], true);
         } else {
@@ -277,7 +277,7 @@ void rowk_f8_kernel(
         }
     }
     // output scale of activation row m and weight row `row`
-    const float s_w = (sw != nullptr) ? *sw : 1.0f;
+    const float s_w = (sw != nullptr) ? *sw : implied_wscale(WFMT);
     auto out_scale = [&](int m, int64_t row) {
         return rowscale ? s_a[m] * sw[row] : s_a[m] * s_w;
     };
@@ -360,7 +360,7 @@ void rowk_f8_kernel(
 // reads 16 bytes of each plane (1 KiB of a plane row per instruction),
 // rebuilds 16 fp16 words with v_perm and accumulates fp16 pairs with
 // v_dot2_f32_f16 (fp32 accumulation).
-template <int MR, int ROWS, int U, int CP>
+template <int MR, int ROWS, int U, int CP, int SP>
 __global__ __launch_bounds__(kThreads) void rowk_nested16_kernel(
     const uint16_t* __restrict__ a, const uint8_t* __restrict__ hi,
     const uint8_t* __restrict__ lo, uint16_t* __restrict__ y, int N, int K)
@@ -405,7 +405,7 @@ __global__ __launch_bounds__(kThreads) void rowk_nested16_kernel(
                 uint32_t wv[8];
 #pragma unroll
                 for (int d = 0; d < 4; ++d)
-                    nested_rebuild4((uint32_t)hv[j][u][d], (uint32_t)lv[j][u][d], wv[2 * d],
+                    nested_rebuild4<SP>((uint32_t)hv[j][u][d], (uint32_t)lv[j][u][d], wv[2 * d],
                                     wv[2 * d + 1]);
 #pragma unroll
                 for (int m = 0; m < MR; ++m)
@@ -500,6 +500,9 @@ hipError_t launch_rowk_fp8(const uint8_t* qa, const float* sa, const uint8_t* qw
     } else if (wfmt == WF_E5M2 && outf == OUT_FP16 && !rowscale) {
         if (M == 1) launch_rowk_codes<WF_E5M2, OUT_FP16, 1>(qa, sa, qw, sw, y, N, K, 0, stream);
         else launch_rowk_codes<WF_E5M2, OUT_FP16, 2>(qa, sa, qw, sw, y, N, K, 0, stream);
+    } else if (wfmt == WF_E4M3_SC8 && outf == OUT_FP16 && !rowscale) {
+        if (M == 1) launch_rowk_codes<WF_E4M3_SC8, OUT_FP16, 1>(qa, sa, qw, sw, y, N, K, 0, stream);
+        else launch_rowk_codes<WF_E4M3_SC8, OUT_FP16, 2>(qa, sa, qw, sw, y, N, K, 0, stream);
     } else {
         return hipErrorInvalidValue;
     }
@@ -507,14 +510,18 @@ hipError_t launch_rowk_fp8(const uint8_t* qa, const float* sa, const uint8_t* qw
 }
 
 hipError_t launch_rowk_nested16(const uint16_t* a, const uint8_t* hi, const uint8_t* lo,
-                                uint16_t* y, int M, int N, int K, hipStream_t stream)
+                                uint16_t* y, int M, int N, int K, int sp, hipStream_t stream)
 {
-    if (M == 1)
-        rowk_nested16_kernel<1, kRows, kUnroll, CP_NT>
+    auto go = [&](auto mr, auto spc) {
+        rowk_nested16_kernel<decltype(mr)::value, kRows, kUnroll, CP_NT, decltype(spc)::value>
             <<<rowk_grid(N), kThreads, 0, stream>>>(a, hi, lo, y, N, K);
-    else
-        rowk_nested16_kernel<2, kRows, kUnroll, CP_NT>
-            <<<rowk_grid(N), kThreads, 0, stream>>>(a, hi, lo, y, N, K);
+    };
+    using I1 = std::integral_constant<int, 1>;
+    using I2 = std::integral_constant<int, 2>;
+    using P0 = std::integral_constant<int, SP_PLAIN>;
+    using P1 = std::integral_constant<int, SP_E4M3>;
+    if (M == 1) (sp == SP_E4M3) ? go(I1{}, P1{}) : go(I1{}, P0{});
+    else (sp == SP_E4M3) ? go(I2{}, P1{}) : go(I2{}, P0{});
     return hipGetLastError();
 }
 
@@ -562,6 +569,12 @@ hipError_t launch_linear_fused(const void* x, int dtype, const uint8_t* qw, cons
             launch_rowk<WF_E5M2, OUT_FP16, AS_FP16, 1>(x, nullptr, qw, sw, y, q, scale, amax, N, K, rowscale, stream);
         else
             launch_rowk<WF_E5M2, OUT_FP16, AS_FP16, 2>(x, nullptr, qw, sw, y, q, scale, amax, N, K, rowscale, stream);
+    } else if (wfmt == WF_E4M3_SC8 && outf == OUT_FP16 && dtype == DT_FP16) {
+        // the same mode on the E4M3 split: hi plane = E4M3 codes of w * 2^8
+        if (M == 1)
+            launch_rowk<WF_E4M3_SC8, OUT_FP16, AS_FP16, 1>(x, nullptr, qw, sw, y, q, scale, amax, N, K, rowscale, stream);
+        else
+            launch_rowk<WF_E4M3_SC8, OUT_FP16, AS_FP16, 2>(x, nullptr, qw, sw, y, q, scale, amax, N, K, rowscale, stream);
     } else {
         return hipErrorInvalidValue;
     }

@@ -45,6 +45,11 @@ _SIGS = {
     "fp8_linear_rowwise": (_i, [_p, _i, _p, _p, _p, _p, _p, _p, _i64, _i64, _i64, _p]),
     "fp8_quantize_act_delayed": (_i, [_p, _i, _i64, _p, _p, _p, _p, _i64, _p, _p]),
     "fp8_quantize_kv": (_i, [_p, _i, _i64, _i64, _i64, _p, _p, _p, _p]),
+    "nested_split_e4m3": (_i, [_p, _p, _p, _i64, _p, _p]),
+    "nested_rebuild_e4m3": (_i, [_p, _p, _p, _i64, _p]),
+    "nested_gemm_fp16_e4m3": (_i, [_p, _p, _p, _p, _i64, _i64, _i64, _p]),
+    "nested_gemm_fp8_e4m3": (_i, [_p, _p, _p, _p, _i64, _i64, _i64, _p]),
+    "nested_linear_fp8_e4m3": (_i, [_p, _p, _p, _p, _p, _p, _i64, _i64, _i64, _p]),
     "fp8_linear_delayed": (_i, [_p, _i, _p, _p, _p, _p, _p, _p, _p, _i64, _p, _i64, _i64, _i64,
                                 _p]),
 }
@@ -405,6 +410,87 @@ def nested_linear_fp8(a: torch.Tensor, hi: torch.Tensor, y: torch.Tensor | None 
     if amax is None:
         amax = torch.empty(1, dtype=torch.float32, device=dev)
     _check("nested_linear_fp8", lib.nested_linear_fp8(
+        _dev(a, "a", torch.float16), _dev(hi, "hi", torch.uint8),
+        _dev(y, "y", torch.float16, (M, N)), _dev(q, "q", torch.uint8, (M, K)),
+        _scalar(scale, "scale"), _scalar(amax, "amax"), M, N, K, _stream(a)))
+    return y, q, scale, amax
+
+
+def nested_split_e4m3(w: torch.Tensor, hi: torch.Tensor | None = None,
+                      lo: torch.Tensor | None = None):
+    """NestedFP planes with an E4M3 upper byte: hi = sign | bits 13..7 (the E4M3
+    code of w * 2^8 when |w| < 2), lo = bit 14 | bits 6..0.  Returns (hi, lo,
+    out_of_range), the last an int64 device tensor counting the words outside
+    the FP8 mode's range |w| < 1.875."""
+    if hi is None:
+        hi = torch.empty(w.shape, dtype=torch.uint8, device=w.device)
+    if lo is None:
+        lo = torch.empty(w.shape, dtype=torch.uint8, device=w.device)
+    if hi.numel() != w.numel() or lo.numel() != w.numel():
+        raise ValueError("hi and lo must have as many elements as w")
+    bad = torch.zeros(1, dtype=torch.int64, device=w.device)
+    _check("nested_split_e4m3", lib.nested_split_e4m3(
+        _dev(w, "w", torch.float16), _dev(hi, "hi", torch.uint8), _dev(lo, "lo", torch.uint8),
+        w.numel(), _dev(bad, "out_of_range", torch.int64), _stream(w)))
+    return hi, lo, bad
+
+
+def nested_rebuild_e4m3(hi: torch.Tensor, lo: torch.Tensor,
+                        w: torch.Tensor | None = None) -> torch.Tensor:
+    """fp16 words rebuilt from the E4M3-split planes."""
+    if hi.shape != lo.shape:
+        raise ValueError("hi and lo must have the same shape")
+    if w is None:
+        w = torch.empty(hi.shape, dtype=torch.float16, device=hi.device)
+    _check("nested_rebuild_e4m3", lib.nested_rebuild_e4m3(
+        _dev(hi, "hi", torch.uint8), _dev(lo, "lo", torch.uint8),
+        _dev(w, "w", torch.float16, hi.shape), hi.numel(), _stream(hi)))
+    return w
+
+
+def nested_gemm_fp16_e4m3(a: torch.Tensor, hi: torch.Tensor, lo: torch.Tensor,
+                          y: torch.Tensor | None = None) -> torch.Tensor:
+    """NestedFP FP16 mode on E4M3-split planes: y fp16 = a . rebuilt(hi, lo)^T."""
+    M, N, K = _mnk(a, hi)
+    if lo.shape != hi.shape:
+        raise ValueError("hi and lo must have the same shape")
+    if y is None:
+        y = torch.empty((M, N), dtype=torch.float16, device=a.device)
+    _check("nested_gemm_fp16_e4m3", lib.nested_gemm_fp16_e4m3(
+        _dev(a, "a", torch.float16), _dev(hi, "hi", torch.uint8), _dev(lo, "lo", torch.uint8),
+        _dev(y, "y", torch.float16, (M, N)), M, N, K, _stream(a)))
+    return y
+
+
+def nested_gemm_fp8_e4m3(qa: torch.Tensor, sa: torch.Tensor, hi: torch.Tensor,
+                         y: torch.Tensor | None = None) -> torch.Tensor:
+    """NestedFP FP8 mode on E4M3-split planes: y fp16 = (qa . E4M3(hi)^T) * sa * 2^-8."""
+    M, N, K = _mnk(qa, hi)
+    if y is None:
+        y = torch.empty((M, N), dtype=torch.float16, device=qa.device)
+    _check("nested_gemm_fp8_e4m3", lib.nested_gemm_fp8_e4m3(
+        _dev(qa, "qa", torch.uint8), _scalar(sa, "sa"), _dev(hi, "hi", torch.uint8),
+        _dev(y, "y", torch.float16, (M, N)), M, N, K, _stream(qa)))
+    return y
+
+
+def nested_linear_fp8_e4m3(a: torch.Tensor, hi: torch.Tensor, y: torch.Tensor | None = None,
+                           q: torch.Tensor | None = None, scale: torch.Tensor | None = None,
+                           amax: torch.Tensor | None = None):
+    """nested_linear_fp8 on E4M3-split planes.  Returns (y, q, scale, amax)."""
+    if a.dtype != torch.float16:
+        raise TypeError(f"a must be float16, got {a.dtype}")
+    M, N, K = _mnk(a, hi)
+    dev = a.device
+    if y is None:
+        y = torch.empty((M, N), dtype=torch.float16, device=dev)
+    if q is None:
+        q = torch.empty((M, K), dtype=torch.uint8, device=dev)
+    if scale is None:
+        scale = torch.empty(1, dtype=torch.float32, device=dev)
+    if amax is None:
+        amax = torch.empty(1, dtype=torch.float32, device=dev)
+    _check("nested_linear_fp8_e4m3", lib.nested_linear_fp8_e4m3(
         _dev(a, "a", torch.float16), _dev(hi, "hi", torch.uint8),
         _dev(y, "y", torch.float16, (M, N)), _dev(q, "q", torch.uint8, (M, K)),
         _scalar(scale, "scale"), _scalar(amax, "amax"), M, N, K, _stream(a)))

@@ -296,6 +296,42 @@ FP8Q_API fp8q_status nested_linear_fp8(const uint16_t* a, const uint8_t* hi, uin
                               int64_t K, fp8q_stream stream);
 
 /*
+ * NestedFP with an E4M3 upper byte ([NestedFP] §2.1 says the upper byte
+ * "becomes E4M3").  Reading: the fp16 word s|e4..e0|m9..m0 is split into
+ *   hi = s | e3..e0 | m9..m7   (the E4M3 code of w * 2^8, truncated toward
+ *                               zero, whenever e4 == 0; fp16 subnormals land
+ *                               on E4M3 subnormals, so nothing underflows)
+ *   lo = e4 | m6..m0
+ * so the rebuild is exact for every fp16 word, and the FP8 mode (hi as E4M3,
+ * scale 2^-8) holds for finite |w| < 1.875 (beyond, e4 == 1 or hi would read
+ * as NaN).  One more mantissa bit than the plain split's E5M2 upper byte.
+ *
+ * nested_split_e4m3 - the split above.  *out_of_range (device, 8-byte
+ *   aligned, zero-filled by the caller; may be NULL) gains the number of
+ *   words outside |w| < 1.875 (NaN and inf included).   n >= 1.
+ * nested_rebuild_e4m3 - w = (hi & 0x80) << 8 | (lo & 0x80) << 7 |
+ *   (hi & 0x7F) << 7 | (lo & 0x7F), the FP16-mode rebuild on its own.
+ * nested_gemm_fp16_e4m3 - nested_gemm_fp16 on planes of this split.
+ * nested_gemm_fp8_e4m3 - y = fp16((qa . E4M3(hi)^T) * fl32(*sa * 2^-8)).
+ * nested_linear_fp8_e4m3 - fp8_quantize_act on the fp16 activation, then
+ *   nested_gemm_fp8_e4m3; bit-identical to the two calls in sequence.
+ *   Size rules and dispatch as the plain-split calls.
+ */
+FP8Q_API fp8q_status nested_split_e4m3(const uint16_t* w, uint8_t* hi, uint8_t* lo, int64_t n,
+                                       uint64_t* out_of_range, fp8q_stream stream);
+FP8Q_API fp8q_status nested_rebuild_e4m3(const uint8_t* hi, const uint8_t* lo, uint16_t* w,
+                                         int64_t n, fp8q_stream stream);
+FP8Q_API fp8q_status nested_gemm_fp16_e4m3(const uint16_t* a, const uint8_t* hi,
+                                           const uint8_t* lo, uint16_t* y, int64_t M, int64_t N,
+                                           int64_t K, fp8q_stream stream);
+FP8Q_API fp8q_status nested_gemm_fp8_e4m3(const uint8_t* qa, const float* sa, const uint8_t* hi,
+                                          uint16_t* y, int64_t M, int64_t N, int64_t K,
+                                          fp8q_stream stream);
+FP8Q_API fp8q_status nested_linear_fp8_e4m3(const uint16_t* a, const uint8_t* hi, uint16_t* y,
+                                            uint8_t* q, float* scale, float* amax, int64_t M,
+                                            int64_t N, int64_t K, fp8q_stream stream);
+
+/*
  * fp8q_e4m3_encode_f32 - the device E4M3 encoder used by fp8_quantize_act,
  *   applied to binary32 values directly: q[i] = E4M3_rne_sat(v[i]).  n >= 1.
  *   Exported so the encoder can be checked exhaustively; not on the hot path.

@@ -31,7 +31,9 @@ def test_header_declares_the_entry_points():
                  "nested_gemm_fp16", "nested_gemm_fp8", "nested_linear_fp8", "fp8q_abi_version",
                  "fp8q_status_str", "fp8q_last_error", "fp8q_e4m3_encode_f32",
                  "fp8_quantize_rows", "fp8_gemm_rowwise", "fp8_linear_rowwise",
-                 "fp8_quantize_act_delayed", "fp8_linear_delayed", "fp8_quantize_kv"]:
+                 "fp8_quantize_act_delayed", "fp8_linear_delayed", "fp8_quantize_kv",
+                 "nested_split_e4m3", "nested_rebuild_e4m3", "nested_gemm_fp16_e4m3",
+                 "nested_gemm_fp8_e4m3", "nested_linear_fp8_e4m3"]:
         assert want in names
 
 
@@ -171,6 +173,14 @@ GEMM_SIG = [P16, P16, P16, P16, P16]
     ("fp8_quantize_kv", [P16, 0, 1, 1, 4, P16, P16, P16, NULL], ERR_SHAPE),
     ("fp8_quantize_kv", [P16, 0, 2**40, 2, 8, P16, P16, P16, NULL], ERR_SHAPE),
     ("fp8_quantize_kv", [P16, 0, 1, 1, 8, P17, P16, P16, NULL], ERR_ALIGN),
+    # nested_split_e4m3(w, hi, lo, n, out_of_range, stream) and the E4M3-split calls
+    ("nested_split_e4m3", [P16, NULL, P16, 8, NULL, NULL], ERR_NULL),
+    ("nested_split_e4m3", [P16, P16, P16, 0, NULL, NULL], ERR_SHAPE),
+    ("nested_split_e4m3", [P16, P16, P16, 8, ctypes.c_void_p(0x1004), NULL], ERR_ALIGN),
+    ("nested_rebuild_e4m3", [P16, P16, P17, 8, NULL], ERR_ALIGN),
+    ("nested_gemm_fp16_e4m3", [P16, P16, P16, P16, 1, 1, 24, NULL], ERR_SHAPE),
+    ("nested_gemm_fp8_e4m3", [P16, NULL, P16, P16, 1, 1, 16, NULL], ERR_NULL),
+    ("nested_linear_fp8_e4m3", [P16, P16, P16, P16, P16, P16, 1, 0, 16, NULL], ERR_SHAPE),
     # fp8q_e4m3_encode_f32(v, q, n, stream)
     ("fp8q_e4m3_encode_f32", [NULL, P16, 4, NULL], ERR_NULL),
     ("fp8q_e4m3_encode_f32", [P16, P16, 0, NULL], ERR_SHAPE),

@@ -46,3 +46,16 @@ def test_fp16out_gemm_small_integers_exact():
     y = oracle.gemm_fp8_f32_fp16out(oracle.e4m3_encode(a), 1.0, oracle.e4m3_encode(w), 0.25)
     exact = (a.astype(np.int64) @ w.astype(np.int64).T).astype(np.float64) * 0.25
     assert np.array_equal(y, oracle.f16_encode(exact.astype(np.float32)))
+
+
+def test_e4m3_upper_byte_never_worse_than_e5m2():
+    """One more mantissa bit: for every fp16 word in range the FP8-mode value of
+    the E4M3 split is at least as close to w as the plain split's E5M2 value."""
+    hi4, _, _ = oracle.nested_split_e4m3(ALL)
+    hi5, _ = oracle.nested_split(ALL)
+    w = ALL.view(np.float16).astype(np.float64)
+    ok = np.isfinite(w) & (np.abs(w) < 1.875)
+    v4 = torch.from_numpy(hi4[ok].copy()).view(torch.float8_e4m3fn).to(torch.float64).numpy() * 2.0 ** -8
+    v5 = oracle.e5m2_decode(hi5[ok])
+    assert np.all(np.abs(w[ok] - v4) <= np.abs(w[ok] - v5))
+    assert np.sum(np.abs(w[ok] - v4) < np.abs(w[ok] - v5)) > ok.sum() // 3
