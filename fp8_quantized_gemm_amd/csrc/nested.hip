@@ -1,7 +1,7 @@
 // NestedFP byte planes (page "NestedFP双精度推理框架" §2.1): an fp16 weight
 // word is stored as its upper byte (sign, 5 exponent bits, 2 mantissa bits:
 // bit for bit an E5M2 code) and its lower byte (the remaining 8 mantissa
-// bits).  The E4M3 split (the page's "upper byte becomes E4M3") keeps sign |
+// bits).  The E4M3 split (the page also names E4M3 for the upper byte) keeps sign |
 // bits 13..7 in the upper byte, the E4M3 code of w * 2^8 truncated to 3
 // mantissa bits while the top exponent bit is clear, and bit 14 | bits 6..0
 // in the lower byte, so the rebuild stays exact for every word; the FP8 mode

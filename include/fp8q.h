@@ -296,8 +296,8 @@ FP8Q_API fp8q_status nested_linear_fp8(const uint16_t* a, const uint8_t* hi, uin
                               int64_t K, fp8q_stream stream);
 
 /*
- * NestedFP with an E4M3 upper byte ([NestedFP] §2.1 says the upper byte
- * "becomes E4M3").  Reading: the fp16 word s|e4..e0|m9..m0 is split into
+ * NestedFP with an E4M3 upper byte ([NestedFP] §2.1 also names E4M3 as the
+ * upper byte's format).  Reading: the fp16 word s|e4..e0|m9..m0 is split into
  *   hi = s | e3..e0 | m9..m7   (the E4M3 code of w * 2^8, truncated toward
  *                               zero, whenever e4 == 0; fp16 subnormals land
  *                               on E4M3 subnormals, so nothing underflows)

@@ -321,8 +321,8 @@ void orc_nested_rebuild(const uint8_t* hi, const uint8_t* lo, uint16_t* w, int64
     for (int64_t i = 0; i < n; ++i) w[i] = (uint16_t)(((uint16_t)hi[i] << 8) | lo[i]);
 }
 
-/* The E4M3 upper-byte split ([NestedFP] §2.1 says the upper byte "becomes    */
-/* E4M3").  Reading: an fp16 word s|e4..e0|m9..m0 with e4 = 0 (|w| < 2) keeps  */
+/* The E4M3 upper-byte split ([NestedFP] §2.1 also names E4M3 as the upper  */
+/* byte's format).  Reading: an fp16 word s|e4..e0|m9..m0 with e4 = 0 (|w| < 2) keeps  */
 /* s|e3..e0|m9..m7 in the upper byte, which is then the E4M3 code of w * 2^8    */
 /* truncated to 3 mantissa bits (fp16 subnormals land on E4M3 subnormals), and */
 /* e4|m6..m0 in the lower byte, so the rebuild is exact for every fp16 word.   */

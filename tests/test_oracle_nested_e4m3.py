@@ -1,6 +1,6 @@
 """Pins for the oracle's E4M3 upper-byte NestedFP split (CPU only).
 
-The NestedFP page (§2.1) says the upper byte "becomes E4M3"; the reading (an
+The NestedFP page (§2.1) also names E4M3 as the upper byte's format; the reading (an
 fp16 word with a clear top exponent bit keeps sign + 4 exponent + 3 mantissa
 bits in the upper byte, and the freed bit with the 7 low mantissa bits in the
 lower byte) is fixed here against numpy over all 65,536 fp16 words:
