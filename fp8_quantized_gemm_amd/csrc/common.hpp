@@ -294,6 +294,15 @@ __device__ __forceinline__ float wave_max(float v)
     return __int_as_float(__builtin_amdgcn_readlane(__float_as_int(v), 63));
 }
 
+// Workgroup barrier for data exchanged through LDS only.  __syncthreads()
+// also waits for every global load and store the wave still has in flight
+// (s_waitcnt vmcnt(0) before s_barrier), which would hold a prologue behind
+// weight loads issued ahead of it; LDS writes are complete once lgkmcnt is 0.
+__device__ __forceinline__ void lds_barrier()
+{
+    asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
+}
+
 // Block-wide max for blockDim.x = NT threads; result valid in every thread.
 template <int NT>
 __device__ __forceinline__ float block_max(float v, float* lds)

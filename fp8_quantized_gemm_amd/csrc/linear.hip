@@ -230,7 +230,7 @@ void rowk_f8_kernel(
             mx[m] = wave_max(mx[m]);
             if (lane == 0) red[m][wave] = mx[m];
         }
-        __syncthreads();
+        lds_barrier();
         float amax[MR];
 #pragma unroll
         for (int m = 0; m < MR; ++m) {
@@ -262,7 +262,7 @@ void rowk_f8_kernel(
             sa_out[tid] = s_a[tid];
             amax_out[tid] = amax[tid];
         }
-        __syncthreads();
+        lds_barrier();
     } else {
 #pragma unroll
         for (int m = 0; m < MR; ++m) s_a[m] = sa_in[rowscale ? m : 0];
@@ -273,7 +273,7 @@ void rowk_f8_kernel(
                 const int v = tid + i * kWgThreads;
                 if (v < ncopy) dst[v] = cr[i];
             }
-            __syncthreads();
+            lds_barrier();
         }
     }
     // output scale of activation row m and weight row `row`
@@ -332,7 +332,7 @@ void rowk_f8_kernel(
         if (u + W < nunits) load_w(rbeg + ((u + W) >> ls), klo, true);
     }
     if (S > 1) {
-        __syncthreads();
+        lds_barrier();
         for (int t = tid; t < MR * nrows; t += kWgThreads) {
             float v = 0.0f;
             for (int j = 0; j < S; ++j) v += part[t * S + j];
