@@ -318,6 +318,55 @@ __global__ __launch_bounds__(kBigThreads) void kv_quant_kernel(
     }
 }
 
+// Token-major quantization pass, for blocks whose tokens hold VT = H*D/8 >=
+// 256 vectors: workgroup w quantizes whole tokens [w*tpw, (w+1)*tpw), which
+// are contiguous in memory, so every wave reads and writes one contiguous
+// stretch.  Thread tid takes vectors tid + 256 i (i < RPT) of each token;
+// their heads, and so their scales, are the same for every token.  The codes
+// go out with non-temporal stores (they are not read again here): measured on
+// MI355X on a 4096 x 32 x 128 block this pass takes 9.9 us against 11.7 us for
+// the head-major pass with ordinary stores.
+template <int DT, int RPT>
+__global__ __launch_bounds__(kBigThreads) void kv_quant_tokens_kernel(
+    const uint16_t* __restrict__ x, int64_t T, uint32_t VT, uint32_t dv, int64_t tpw,
+    uint8_t* __restrict__ q, const float* __restrict__ scale)
+{
+    const int tid = threadIdx.x;
+    float s[RPT];
+    bool in[RPT];
+#pragma unroll
+    for (int i = 0; i < RPT; ++i) {
+        const uint32_t v = tid + i * kBigThreads;
+        in[i] = v < VT;
+        s[i] = scale[in[i] ? v / dv : 0];
+    }
+    const int64_t t0 = (int64_t)blockIdx.x * tpw;
+    const int64_t nt = max((int64_t)0, min(T - t0, tpw));
+    // per-workgroup resources: at most tpw * VT * 16 bytes of x
+    const rsrc_t rx = make_rsrc(x + t0 * VT * 8, (uint32_t)(nt * VT * 16));
+    const rsrc_t rq = make_rsrc(q + t0 * VT * 8, (uint32_t)(nt * VT * 8));
+    for (int64_t t = 0; t < nt; t += 2) {
+        v4i xv[2][RPT];
+#pragma unroll
+        for (int u = 0; u < 2; ++u)
+#pragma unroll
+            for (int i = 0; i < RPT; ++i) {
+                const uint32_t v = (uint32_t)((t + u) * VT) + tid + i * kBigThreads;
+                xv[u][i] = buf_load16(rx, in[i] ? v * 16 : kOOB);   // past nt: out of range
+            }
+#pragma unroll
+        for (int i = 0; i < RPT; ++i) {
+            const Quotient d(s[i]);
+#pragma unroll
+            for (int u = 0; u < 2; ++u) {
+                const uint32_t v = (uint32_t)((t + u) * VT) + tid + i * kBigThreads;
+                __builtin_amdgcn_raw_buffer_store_b64(vec_quantize<DT>(xv[u][i], d), rq,
+                                                      in[i] ? v * 8 : kOOB, 0, CP_NT);
+            }
+        }
+    }
+}
+
 // ---------------------------------------------------------------- delayed scaling
 // One pass over x: the scale comes from the amax history of earlier calls
 // (delayed_scale), so every element is quantized as soon as it is loaded and
@@ -596,10 +645,30 @@ hipError_t launch_quantize_kv(const void* x, int dtype, int64_t T, int64_t H, in
     else
         kv_amax_partial_kernel<DT_FP16><<<(unsigned)grid, kBigThreads, 0, stream>>>(xs, T, H, D, shift, C, tpw, part);
     kv_combine_kernel<<<(unsigned)H, kBigThreads, 0, stream>>>(part, C, scale, amax);
-    if (dtype == DT_BF16)
+    // quantization: token-major for 256 .. 2048 vectors per token (two tokens
+    // per workgroup), else head-major like the partial maxima
+    const int64_t VT = H * dv;
+    if (VT >= kBigThreads && VT <= 8 * kBigThreads) {
+        const int64_t g2 = (T + 1) / 2;
+        if (g2 > 0x7fffffff) return hipErrorInvalidValue;
+        auto go = [&](auto rpt) {
+            constexpr int R = decltype(rpt)::value;
+            if (dtype == DT_BF16)
+                kv_quant_tokens_kernel<DT_BF16, R><<<(unsigned)g2, kBigThreads, 0, stream>>>(
+                    xs, T, (uint32_t)VT, (uint32_t)dv, 2, q, scale);
+            else
+                kv_quant_tokens_kernel<DT_FP16, R><<<(unsigned)g2, kBigThreads, 0, stream>>>(
+                    xs, T, (uint32_t)VT, (uint32_t)dv, 2, q, scale);
+        };
+        if (VT <= kBigThreads) go(std::integral_constant<int, 1>{});
+        else if (VT <= 2 * kBigThreads) go(std::integral_constant<int, 2>{});
+        else if (VT <= 4 * kBigThreads) go(std::integral_constant<int, 4>{});
+        else go(std::integral_constant<int, 8>{});
+    } else if (dtype == DT_BF16) {
         kv_quant_kernel<DT_BF16><<<(unsigned)grid, kBigThreads, 0, stream>>>(xs, T, H, D, shift, C, tpw, q, scale);
-    else
+    } else {
         kv_quant_kernel<DT_FP16><<<(unsigned)grid, kBigThreads, 0, stream>>>(xs, T, H, D, shift, C, tpw, q, scale);
+    }
     return hipGetLastError();
 }
 
