@@ -18,6 +18,8 @@
 // by row so that 16 lanes reading the same unit of 16 consecutive rows hit
 // distinct banks.  Workgroup ids are remapped so that consecutive tiles
 // (which share the weight tile) land on the same XCD and its L2.
+#include <atomic>
+
 #include "common.hpp"
 
 namespace fp8q {
@@ -65,6 +67,22 @@ __device__ __forceinline__ void store_tile(uint16_t* __restrict__ y, const v4f (
 }
 
 // ---------------------------------------------------------------- shared pieces
+// Raises a kernel's dynamic LDS limit to `lds` bytes once per device (the
+// attribute is set for the current device).  `done` holds one bit per device
+// id below 64; two threads racing on a first call both set it, which is
+// harmless; devices 64 and up set it on every call.
+inline hipError_t set_lds_limit_once(const void* kern, size_t lds, std::atomic<uint64_t>& done)
+{
+    int dev = 0;
+    hipError_t e = hipGetDevice(&dev);
+    if (e != hipSuccess) return e;
+    const uint64_t bit = (dev >= 0 && dev < 64) ? (uint64_t)1 << dev : 0;
+    if (bit != 0 && (done.load(std::memory_order_acquire) & bit) != 0) return hipSuccess;
+    e = hipFuncSetAttribute(kern, hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
+    if (e == hipSuccess && bit != 0) done.fetch_or(bit, std::memory_order_release);
+    return e;
+}
+
 // The compiler does not order LDS reads after asynchronous direct-to-LDS
 // loads, so a kernel that uses them waits explicitly (s_waitcnt vmcnt) for
 // its own loads and then synchronizes the workgroup before reading.
@@ -411,14 +429,10 @@ hipError_t launch_f8(const uint8_t* qa, const float* sa, const uint8_t* qw, cons
     auto kern = gemm_f8_kernel<WFMT, OUTF, BM, BN, WM, WN, AST, WST>;
     constexpr size_t lds = ((size_t)AST * BM + (size_t)WST * BN) * 128;
     static_assert(lds <= 160 * 1024, "LDS of one CU");
-    static bool attr_set = false;        // idempotent host attribute, set on first use
-    if (!attr_set) {
-        const hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(kern),
-                                                 hipFuncAttributeMaxDynamicSharedMemorySize,
-                                                 (int)lds);
-        if (e != hipSuccess) return e;
-        attr_set = true;
-    }
+    static std::atomic<uint64_t> attr_devices{0};
+    if (const hipError_t e = set_lds_limit_once(reinterpret_cast<const void*>(kern), lds, attr_devices);
+        e != hipSuccess)
+        return e;
     const int64_t grid = (((int64_t)M + BM - 1) / BM) * (((int64_t)N + BN - 1) / BN);
     if (grid > 0x7fffffff) return hipErrorInvalidValue;
     kern<<<(int)grid, WM * WN * 64, lds, stream>>>(qa, sa, qw, sw, y, M, N, K, rowscale);
@@ -495,14 +509,10 @@ hipError_t launch_n16(const uint16_t* a, const uint8_t* hi, const uint8_t* lo, u
     auto kern = gemm_n16_kernel<BM, BN, WM, WN, AST, WST, SP>;
     constexpr size_t lds = ((size_t)AST * BM + (size_t)WST * BN) * 128;
     static_assert(lds <= 160 * 1024, "LDS of one CU");
-    static bool attr_set = false;        // idempotent host attribute, set on first use
-    if (!attr_set) {
-        const hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(kern),
-                                                 hipFuncAttributeMaxDynamicSharedMemorySize,
-                                                 (int)lds);
-        if (e != hipSuccess) return e;
-        attr_set = true;
-    }
+    static std::atomic<uint64_t> attr_devices{0};
+    if (const hipError_t e = set_lds_limit_once(reinterpret_cast<const void*>(kern), lds, attr_devices);
+        e != hipSuccess)
+        return e;
     const int64_t grid = (((int64_t)M + BM - 1) / BM) * (((int64_t)N + BN - 1) / BN);
     if (grid > 0x7fffffff) return hipErrorInvalidValue;
     kern<<<(int)grid, WM * WN * 64, lds, stream>>>(a, hi, lo, y, M, N, K);
