@@ -227,7 +227,21 @@ def cpu_baseline(torch, synth, dev, seconds):
     return {"value": round(done_bytes / el / 1e9, 3), "unit": "GB/s", "cores": threads,
             "kind": "oracle",
             "sample": f"layers 0-1 of the 32 (8 linears, M=1), {passes} pass(es), "
-                      f"{el:.1f} s of CPU work; same algorithmic bytes as the GPU metric"}
+                      f"{el:.1f} s of CPU work on {threads} threads of {host_cpu()} "
+                      f"({os.cpu_count()} logical CPUs visible); same algorithmic bytes as "
+                      f"the GPU metric"}
+
+
+def host_cpu() -> str:
+    """The host CPU's model name (Linux), for the record of the oracle's timing."""
+    try:
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                if line.startswith("model name"):
+                    return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return "an unknown CPU"
 
 
 def with_activations(torch, synth, model1, M, dev, tag, outliers=False):
