@@ -10,6 +10,7 @@ nested_linear_fp8_e4m3) against the oracle.
 - FP8 mode: bit-exact on small-integer operands, within
   |y - ref| <= 2e-3 * sum|a*b| + 1e-6 on random ones, on each path.
 - nested_linear_fp8_e4m3 equals fp8_quantize_act + nested_gemm_fp8_e4m3.
+- Full Llama-7B shapes at M = 1 and 256, both modes, sampled outputs.
 """
 import numpy as np
 import pytest
@@ -111,3 +112,40 @@ def test_linear_fp8_e4m3_matches_quantize_then_gemm(M, N, K):
     y2 = fp8q.nested_gemm_fp8_e4m3(q2, s2, hi)
     assert torch.equal(q.view(-1), q2.view(-1)) and torch.equal(s, s2)
     assert torch.equal(y.view(torch.int16), y2.view(torch.int16))
+
+
+@pytest.mark.parametrize("M", [1, 256])
+@pytest.mark.parametrize("K,N", [(K, N) for _, K, N in synth.LLAMA7B_LINEARS])
+def test_full_size_llama_shapes_sampled(M, K, N):
+    """Both modes on the Llama-7B linear shapes as the benchmark runs them (GPU
+    split; FP8 mode through nested_linear_fp8_e4m3, which quantizes the fp16
+    activation itself): the split of 256 sampled weight rows bit-exact, the
+    sampled outputs within tolerance of the oracle, the codes bit-exact."""
+    seed = synth.seed_for("nested-e4m3-full", M, K, N)
+    a = synth.activation(M, K, seed=seed, dtype="fp16", device=DEV)
+    w = synth.normal((N, K), 0.02, "fp16", seed=seed + 1, device=DEV)
+    say("nested e4m3 full", M, K, N)
+    hi, lo, bad = fp8q.nested_split_e4m3(w)
+    y16 = fp8q.nested_gemm_fp16_e4m3(a, hi, lo)
+    y8, qa, sa, _ = fp8q.nested_linear_fp8_e4m3(a, hi)
+    torch.cuda.synchronize()
+    assert int(bad.item()) == 0
+    rng = np.random.Generator(np.random.PCG64(seed))
+    ns = np.sort(rng.choice(N, 256, replace=False))
+    rows = np.arange(M) if M <= 16 else np.sort(rng.choice(M, 4, replace=False))
+    wb = synth.bits(w.cpu())[ns]
+    ohi, olo, _ = oracle.nested_split_e4m3(wb)
+    assert np.array_equal(host(hi)[ns], ohi) and np.array_equal(host(lo)[ns], olo)
+    ab16 = synth.bits(a.cpu())
+    ms = np.repeat(np.arange(rows.size), ns.size)
+    nn = np.tile(np.arange(ns.size), rows.size)
+    phi, plo = oracle.nested_split(wb)              # the same words, plain planes
+    ref, ab = oracle.nested_fp16_ref(ab16[rows], phi, plo, ms, nn)
+    out = oracle.f16_decode(host(y16)[rows][:, ns]).ravel()
+    assert_within(out, ref, ab, f"fp16 e4m3 M={M} {K}->{N}", "fp16")
+    oqa, osa, _ = oracle.quantize(ab16.ravel(), oracle.FP16)
+    assert np.array_equal(host(qa).ravel(), oqa) and host(sa)[0] == np.float32(osa)
+    ref8, ab8 = oracle.gemm_fp8_ref(oqa.reshape(M, K)[rows], osa, ohi, oracle.NESTED_E4M3_SCALE,
+                                    ms, nn)
+    out8 = oracle.f16_decode(host(y8)[rows][:, ns]).ravel()
+    assert_within(out8, ref8, ab8, f"fp8 e4m3 M={M} {K}->{N}", "fp16")
