@@ -8,6 +8,8 @@ saturate and the window maximum moves; the history is short (wraps) and long.
 Covers the single-workgroup quantizer (n <= 32768), the grid-stride one (its
 last workgroup publishes the call), the fused decode linear (M <= 2) and the
 two-launch linear, and HIP-graph replays (each replay is one more call).
+Full Llama-7B shapes at M = 1 and 512 with a history of 1024: three calls,
+sampled outputs of the last within tolerance of the oracle.
 """
 import numpy as np
 import pytest
@@ -15,7 +17,7 @@ import torch
 
 import oracle
 from fp8_quantized_gemm_amd import fp8q, synth
-from gpu_helpers import DEV, host, say
+from gpu_helpers import DEV, assert_within, host, say
 
 pytestmark = pytest.mark.gpu
 
@@ -131,3 +133,36 @@ def test_delayed_graph_replays_advance_the_history(M, K, N):
         assert torch.equal(y.view(torch.int16), y2.view(torch.int16)), f"replay {rep}: y"
     _check_state(ds, od, "after replays")
     del g
+
+
+@pytest.mark.parametrize("M", [1, 512])
+@pytest.mark.parametrize("K,N", [(K, N) for _, K, N in synth.LLAMA7B_LINEARS])
+def test_full_size_llama_shapes_sequence(M, K, N):
+    """fp8_linear_delayed on the Llama-7B linear shapes with the benchmark's
+    history length (1024): three calls with rising magnitudes, so the third
+    saturates against the second's amax.  Codes, scale and amax bit-exact on
+    every call; sampled outputs of the last call within tolerance."""
+    seed = synth.seed_for("delayed-full", M, K, N)
+    w = synth.normal((N, K), 0.02, "fp16", seed=seed + 1)
+    oqw, osw, _ = oracle.quantize(synth.bits(w).ravel(), oracle.FP16)   # offline, by the oracle
+    oqw = oqw.reshape(N, K)
+    qw = torch.from_numpy(oqw).to(DEV)
+    sw = torch.tensor([osw], dtype=torch.float32, device=DEV)
+    od = oracle.DelayedScaling(1024)
+    ds = fp8q.DelayedScaling(1024, device=DEV)
+    for t, mag in enumerate((1.0, 0.5, 4.0)):
+        x = (synth.activation(M, K, seed=seed + 10 + t, outliers=M > 16).to(torch.float32)
+             * mag).to(torch.bfloat16)
+        want_q, want_s, want_a = od.quantize(synth.bits(x).ravel(), oracle.BF16)
+        say("delayed full", M, K, N, "call", t)
+        y, q, s, a = fp8q.fp8_linear_delayed(x.to(DEV), qw, sw, ds)
+        assert np.array_equal(host(q).ravel(), want_q), f"call {t}: codes"
+        assert host(s)[0] == np.float32(want_s) and host(a)[0] == np.float32(want_a), f"call {t}"
+    rng = np.random.Generator(np.random.PCG64(seed))
+    ns = np.sort(rng.choice(N, 256, replace=False))
+    rows = np.arange(M) if M <= 16 else np.sort(rng.choice(M, 4, replace=False))
+    ms = np.repeat(np.arange(rows.size), ns.size)
+    nn = np.tile(np.arange(ns.size), rows.size)
+    ref, ab = oracle.gemm_fp8_ref(want_q.reshape(M, K)[rows], want_s, oqw[ns], osw, ms, nn)
+    out = oracle.bf16_decode(host(y)[rows][:, ns]).astype(np.float64).ravel()
+    assert_within(out, ref, ab, f"delayed M={M} {K}->{N}", "bf16")

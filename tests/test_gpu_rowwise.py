@@ -10,6 +10,8 @@ fp8_gemm_rowwise, fp8_linear_rowwise) against the oracle.
   and unsplit; M <= 16 GEMV; tile shapes) and ragged N.
 - Equal scales give exactly what the per-tensor fp8_gemm gives.
 - fp8_linear_rowwise equals fp8_quantize_rows + fp8_gemm_rowwise bit for bit.
+- Full Llama-7B shapes at M = 1 and 512 through fp8_linear_rowwise: codes and
+  scales bit-exact, sampled outputs within tolerance.
 """
 import numpy as np
 import pytest
@@ -198,3 +200,32 @@ def test_linear_rowwise_graph_replays():
         for o, w_ in zip(outs, want):
             assert torch.equal(o.view(torch.uint8), w_.view(torch.uint8)), f"replay {rep}"
     del g
+
+
+@pytest.mark.parametrize("M", [1, 512])
+@pytest.mark.parametrize("K,N", [(K, N) for _, K, N in synth.LLAMA7B_LINEARS])
+def test_full_size_llama_shapes_sampled(M, K, N):
+    """fp8_linear_rowwise on the Llama-7B linear shapes as the benchmark calls
+    it (weights quantized per channel on the GPU, activations per token with
+    outlier channels): per-channel codes and scales of 256 sampled weight rows
+    and all activation codes and scales bit-exact; sampled outputs within
+    tolerance of the oracle."""
+    seed = synth.seed_for("rowwise-full", M, K, N)
+    x = synth.activation(M, K, seed=seed, outliers=True, device=DEV)
+    w = synth.normal((N, K), 0.02, "fp16", seed=seed + 1, device=DEV)
+    say("rowwise full", M, K, N)
+    qw, sw, _ = fp8q.fp8_quantize_rows(w)
+    y, q, sa, _ = fp8q.fp8_linear_rowwise(x, qw, sw)
+    torch.cuda.synchronize()
+    rng = np.random.Generator(np.random.PCG64(seed))
+    ns = np.sort(rng.choice(N, 256, replace=False))
+    rows = np.arange(M) if M <= 16 else np.sort(rng.choice(M, 4, replace=False))
+    oqw, osw, _ = oracle.quantize_rows(synth.bits(w.cpu())[ns], oracle.FP16)
+    assert np.array_equal(host(qw)[ns], oqw) and np.array_equal(host(sw)[ns], osw)
+    oqa, osa, _ = oracle.quantize_rows(synth.bits(x.cpu()), oracle.BF16)
+    assert np.array_equal(host(q), oqa) and np.array_equal(host(sa), osa)
+    ms = np.repeat(np.arange(rows.size), ns.size)
+    nn = np.tile(np.arange(ns.size), rows.size)
+    ref, ab = oracle.gemm_fp8_rowwise_ref(oqa[rows], osa[rows], oqw, osw, ms, nn)
+    out = oracle.bf16_decode(host(y)[rows][:, ns]).astype(np.float64).ravel()
+    assert_within(out, ref, ab, f"rowwise M={M} {K}->{N}", "bf16")
