@@ -81,14 +81,16 @@ enum : int {
 // s_w[n]) with a scale per activation row (token) and per weight row (output
 // channel).  The fused prologue then reduces amax per activation row.
 //
-// At most WPC 1024-thread workgroups per CU: the activation prologue (copy or
-// quantization into LDS) is paid once per workgroup and spread over 16 waves.
+// At most WPC workgroups of NT threads (W = NT / 64 waves) per CU: the
+// activation prologue (copy or quantization into LDS) is paid once per
+// workgroup and spread over its waves.  NT is 1024, or 512 where each wave
+// would otherwise stream at most two batches (see launch_rowk).
 // Each workgroup takes one contiguous span of weight rows, so that at any
 // moment it streams one compact window of the weight matrix: measured on
 // MI355X, block-contiguous streaming with non-temporal loads sustains about
 // 7.1 TB/s where grid-strided streaming stays near 6 TB/s.  The K range of a
 // row is cut into S = 2^ls equal segments (a multiple of 128 bytes each), so
-// that a span holds S units per row; the 16 waves take consecutive units in
+// that a span holds S units per row; the W waves take consecutive units in
 // turn, which keeps wave w on segment w % S.  A wave streams its segment in
 // batches of U 1 KiB chunks; the 4 waves per SIMD overlap each other's loads
 // and arithmetic.  With S = 1 a wave finishes a row itself; with S > 1 the
@@ -103,8 +105,8 @@ enum : int {
 // soon as the activation arrives, without a block-wide amax first; each
 // workgroup counts itself in state[3] after its prologue, and the one that
 // arrives last reduces the amax at its end and publishes the call.
-template <int WFMT, int OUTF, int AS, int MR, int U, int CP, int WPC, int XV, bool DS = false>
-__global__ __launch_bounds__(kWgThreads) __attribute__((amdgpu_waves_per_eu(4 * WPC)))
+template <int NT, int WFMT, int OUTF, int AS, int MR, int U, int CP, int WPC, int XV, bool DS = false>
+__global__ __launch_bounds__(NT) __attribute__((amdgpu_waves_per_eu(NT / 256 * WPC)))
 void rowk_f8_kernel(
     const void* __restrict__ act, const float* __restrict__ sa_in,
     const uint8_t* __restrict__ qw, const float* __restrict__ sw,
@@ -116,7 +118,7 @@ void rowk_f8_kernel(
     static_assert(!DS || FUSED, "delayed scaling belongs to the fused prologue");
     constexpr bool IN_LDS = AS != AS_GLOBAL;
     constexpr int DT = AS == AS_BF16 ? DT_BF16 : DT_FP16;
-    constexpr int W = kWgThreads / 64;
+    constexpr int W = NT / 64;
     extern __shared__ __attribute__((aligned(16))) uint8_t codes_lds[];   // IN_LDS: MR*K codes
     __shared__ float red[MR][W];
     __shared__ float part[kPartMax];   // S > 1: [m][row of the span][segment]
@@ -167,14 +169,14 @@ void rowk_f8_kernel(
         const rsrc_t rx = make_rsrc(act, (uint32_t)(MR * K * 2));
 #pragma unroll
         for (int i = 0; i < VPT; ++i) {
-            const int v = tid + i * kWgThreads;
+            const int v = tid + i * NT;
             xr[i] = buf_load16(rx, v < nunit ? (uint32_t)(v * 16) : kOOB);
         }
     } else if constexpr (AS == AS_COPY) {
         const rsrc_t rc = make_rsrc(act, (uint32_t)(MR * K));
 #pragma unroll
         for (int i = 0; i < CPT; ++i) {
-            const int v = tid + i * kWgThreads;
+            const int v = tid + i * NT;
             cr[i] = buf_load16(rc, v < ncopy ? (uint32_t)(v * 16) : kOOB);
         }
     }
@@ -196,7 +198,7 @@ void rowk_f8_kernel(
         v2i* qg = reinterpret_cast<v2i*>(q_out);
 #pragma unroll
         for (int i = 0; i < VPT; ++i) {
-            const int v = tid + i * kWgThreads;
+            const int v = tid + i * NT;
             xmax = fmaxf(xmax, vec_absmax<DT>(xr[i]));
             if (v < nunit) {
                 const v2i c = vec_quantize<DT>(xr[i], d);
@@ -222,7 +224,7 @@ void rowk_f8_kernel(
 #pragma unroll
         for (int i = 0; i < VPT; ++i) {
             const float a = vec_absmax<DT>(xr[i]);
-            if (MR == 1 || tid + i * kWgThreads < nunit / MR) mx[0] = fmaxf(mx[0], a);
+            if (MR == 1 || tid + i * NT < nunit / MR) mx[0] = fmaxf(mx[0], a);
             else mx[MR - 1] = fmaxf(mx[MR - 1], a);
         }
 #pragma unroll
@@ -251,7 +253,7 @@ void rowk_f8_kernel(
         v2i* qg = reinterpret_cast<v2i*>(q_out);
 #pragma unroll
         for (int i = 0; i < VPT; ++i) {
-            const int v = tid + i * kWgThreads;
+            const int v = tid + i * NT;
             if (v < nunit) {
                 const v2i c = vec_quantize<DT>(xr[i], (MR == 1 || v < nunit / MR) ? d0 : d1);
                 cl[v] = c;
@@ -270,7 +272,7 @@ void rowk_f8_kernel(
             v4i* dst = reinterpret_cast<v4i*>(codes_lds);
 #pragma unroll
             for (int i = 0; i < CPT; ++i) {
-                const int v = tid + i * kWgThreads;
+                const int v = tid + i * NT;
                 if (v < ncopy) dst[v] = cr[i];
             }
             lds_barrier();
@@ -333,7 +335,7 @@ void rowk_f8_kernel(
     }
     if (S > 1) {
         lds_barrier();
-        for (int t = tid; t < MR * nrows; t += kWgThreads) {
+        for (int t = tid; t < MR * nrows; t += NT) {
             float v = 0.0f;
             for (int j = 0; j < S; ++j) v += part[t * S + j];
             const int m = t / nrows, lr = t - m * nrows;
@@ -349,7 +351,7 @@ void rowk_f8_kernel(
 #pragma unroll
             for (int i = 1; i < W; ++i) a = fmaxf(a, red[0][i]);
             __syncthreads();                           // red is reused below
-            delayed_publish<kWgThreads>(a, history, hist_len, state, &red[0][0]);
+            delayed_publish<NT>(a, history, hist_len, state, &red[0][0]);
             if (tid == 0) amax_out[0] = a;
         }
     }
@@ -438,13 +440,18 @@ int rowk_grid(int N) { return (int)(((int64_t)N + kRows * (kThreads / 64) - 1) /
 // S = 2, while QKV (24 rows of 4096: 4 -> 3 batches) and O (8 rows of 4096:
 // 2 -> 1 batch) lose about 4%, and S = 4 at 10-20 rows of 5120..8192 (Qwen-32B)
 // loses although it shortens the longest wave a little.
-int rowk_split_shift(int64_t rows_per_wg, int K, int MR, int U)
+// Batches of U KiB that the longest wave of a workgroup of W waves streams
+// when each row's K range is cut into 2^ls segments.
+int64_t rowk_wave_batches(int64_t rows_per_wg, int K, int U, int ls, int W)
 {
-    auto cost = [&](int ls) {
-        const int64_t units = rows_per_wg << ls;
-        const int64_t kseg = ((((int64_t)K + (1 << ls) - 1) >> ls) + 127) & ~(int64_t)127;
-        return ((units + 15) / 16) * ((kseg + 1024 * U - 1) / (1024 * U));
-    };
+    const int64_t units = rows_per_wg << ls;
+    const int64_t kseg = ((((int64_t)K + (1 << ls) - 1) >> ls) + 127) & ~(int64_t)127;
+    return ((units + W - 1) / W) * ((kseg + 1024 * U - 1) / (1024 * U));
+}
+
+int rowk_split_shift(int64_t rows_per_wg, int K, int MR, int U, int W)
+{
+    auto cost = [&](int ls) { return rowk_wave_batches(rows_per_wg, K, U, ls, W); };
     int best = 0;
     if (cost(0) < 4) return best;
     for (int ls = 1; ls <= 4; ++ls)
@@ -460,21 +467,44 @@ void launch_rowk(const void* act, const float* sa_in, const uint8_t* qw, const f
 {
     using C = RowkCfg<MR>;
     const size_t lds = AS != AS_GLOBAL ? (size_t)MR * K : 0;
-    const int grid = min(N, kCUs * C::WPC);
-    const int rpw = (int)(((int64_t)N + grid - 1) / grid);
-    const int ls = rowk_split_shift(rpw, K, MR, C::U);
-    const int kseg = (int)(((((int64_t)K + (1 << ls) - 1) >> ls) + 127) & ~(int64_t)127);
     // 16-byte activation vectors per thread: MR*K/8 bf16/fp16 vectors for the
     // fused prologue, MR*K/16 code vectors for AS_COPY (none for AS_GLOBAL)
     const int64_t vecs = AS == AS_GLOBAL ? 0 : (int64_t)MR * K / (AS == AS_COPY ? 16 : 8);
-    auto go = [&](auto xv) {
-        rowk_f8_kernel<WFMT, OUTF, AS, MR, C::U, CP_NT, C::WPC, decltype(xv)::value, DS>
-            <<<grid, kWgThreads, lds, st>>>(act, sa_in, qw, sw, y, q, sa_out, amax, N, K, rpw, ls,
-                                             kseg, rowscale, history, hist_len, state);
+    auto go = [&](auto nt, auto wpc) {
+        constexpr int NT = decltype(nt)::value, WPC = decltype(wpc)::value;
+        const int grid = min(N, kCUs * WPC);
+        const int rpw = (int)(((int64_t)N + grid - 1) / grid);
+        const int ls = rowk_split_shift(rpw, K, MR, C::U, NT / 64);
+        const int kseg = (int)(((((int64_t)K + (1 << ls) - 1) >> ls) + 127) & ~(int64_t)127);
+        auto launch = [&](auto xv) {
+            rowk_f8_kernel<NT, WFMT, OUTF, AS, MR, C::U, CP_NT, WPC, decltype(xv)::value, DS>
+                <<<grid, NT, lds, st>>>(act, sa_in, qw, sw, y, q, sa_out, amax, N, K, rpw, ls, kseg,
+                                        rowscale, history, hist_len, state);
+        };
+        if (vecs <= NT) launch(std::integral_constant<int, 1>{});
+        else if (vecs <= 2 * NT) launch(std::integral_constant<int, 2>{});
+        else launch(std::integral_constant<int, 4>{});
     };
-    if (vecs <= kWgThreads) go(std::integral_constant<int, 1>{});
-    else if (vecs <= 2 * kWgThreads) go(std::integral_constant<int, 2>{});
-    else go(std::integral_constant<int, 4>{});
+    // Where 1024-thread workgroups would leave each wave at most two weight
+    // batches (the Llama-7B O projection: 8 rows of 4 KiB per workgroup, one
+    // row each for 8 of the 16 waves), the activation prologue dominates;
+    // 512-thread workgroups (2 per CU) halve the waves that meet at its
+    // barriers and measured 6.96 against 7.63 us there on MI355X, while the
+    // shapes with 3 or more batches per wave were slower with them.
+    // The choice depends on N and K only, never on the activation source, so
+    // fp8_linear and fp8_quantize_act + fp8_gemm split rows alike and stay
+    // bit-identical; K is capped where the fused prologue (8 bf16 values per
+    // vector, at most 4 vectors per thread) still fits 512 threads.
+    if constexpr (MR == 1) {
+        const int grid = min(N, kCUs * C::WPC);
+        const int64_t rpw = ((int64_t)N + grid - 1) / grid;
+        const int ls = rowk_split_shift(rpw, K, MR, C::U, kWgThreads / 64);
+        if (K <= 4 * 512 * 8 && rowk_wave_batches(rpw, K, C::U, ls, kWgThreads / 64) <= 2) {
+            go(std::integral_constant<int, 512>{}, std::integral_constant<int, 2>{});
+            return;
+        }
+    }
+    go(std::integral_constant<int, kWgThreads>{}, std::integral_constant<int, C::WPC>{});
 }
 
 // Unfused FP8 weights: codes staged in LDS when they fit, else read from L2.
