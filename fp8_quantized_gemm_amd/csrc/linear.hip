@@ -470,14 +470,14 @@ void launch_rowk(const void* act, const float* sa_in, const uint8_t* qw, const f
     // 16-byte activation vectors per thread: MR*K/8 bf16/fp16 vectors for the
     // fused prologue, MR*K/16 code vectors for AS_COPY (none for AS_GLOBAL)
     const int64_t vecs = AS == AS_GLOBAL ? 0 : (int64_t)MR * K / (AS == AS_COPY ? 16 : 8);
-    auto go = [&](auto nt, auto wpc) {
-        constexpr int NT = decltype(nt)::value, WPC = decltype(wpc)::value;
+    auto go = [&](auto nt, auto wpc, auto u) {
+        constexpr int NT = decltype(nt)::value, WPC = decltype(wpc)::value, U = decltype(u)::value;
         const int grid = min(N, kCUs * WPC);
         const int rpw = (int)(((int64_t)N + grid - 1) / grid);
-        const int ls = rowk_split_shift(rpw, K, MR, C::U, NT / 64);
+        const int ls = rowk_split_shift(rpw, K, MR, U, NT / 64);
         const int kseg = (int)(((((int64_t)K + (1 << ls) - 1) >> ls) + 127) & ~(int64_t)127);
         auto launch = [&](auto xv) {
-            rowk_f8_kernel<NT, WFMT, OUTF, AS, MR, C::U, CP_NT, WPC, decltype(xv)::value, DS>
+            rowk_f8_kernel<NT, WFMT, OUTF, AS, MR, U, CP_NT, WPC, decltype(xv)::value, DS>
                 <<<grid, NT, lds, st>>>(act, sa_in, qw, sw, y, q, sa_out, amax, N, K, rpw, ls, kseg,
                                         rowscale, history, hist_len, state);
         };
@@ -485,26 +485,38 @@ void launch_rowk(const void* act, const float* sa_in, const uint8_t* qw, const f
         else if (vecs <= 2 * NT) launch(std::integral_constant<int, 2>{});
         else launch(std::integral_constant<int, 4>{});
     };
-    // Where 1024-thread workgroups would leave each wave at most two weight
-    // batches (the Llama-7B O projection: 8 rows of 4 KiB per workgroup, one
-    // row each for 8 of the 16 waves), the activation prologue dominates;
-    // 512-thread workgroups (2 per CU) halve the waves that meet at its
-    // barriers and measured 6.96 against 7.63 us there on MI355X, while the
-    // shapes with 3 or more batches per wave were slower with them.
+    // Launch shape at M = 1, from measurements on MI355X (Llama-7B and
+    // Qwen-32B decode shapes, weights cold):
+    // - rows of 4 or 8 KiB (whole 4 KiB batches) and at most 48 rows per
+    //   workgroup: 512 threads streaming 4 KiB batches (QKV 11.6 -> 11.0 us,
+    //   O 6.9 -> 6.8, gate+up 17.9 -> 17.2, Qwen-32B O 12.3 -> 10.7); rows
+    //   that end in a partial batch (K = 5120, 11008) or many rows per
+    //   workgroup (Qwen-32B gate+up, 100) were slower that way;
+    // - else, where 1024 threads would leave each wave at most two 2 KiB
+    //   batches: 512 threads, which halve the waves that meet at the
+    //   activation prologue's barriers;
+    // - else 1024 threads with 2 KiB batches.
     // The choice depends on N and K only, never on the activation source, so
     // fp8_linear and fp8_quantize_act + fp8_gemm split rows alike and stay
-    // bit-identical; K is capped where the fused prologue (8 bf16 values per
-    // vector, at most 4 vectors per thread) still fits 512 threads.
+    // bit-identical; K stays where the fused prologue (8 bf16 values per
+    // vector, at most 4 vectors per thread) fits 512 threads.
+    using I512 = std::integral_constant<int, 512>;
+    using I2 = std::integral_constant<int, 2>;
     if constexpr (MR == 1) {
         const int grid = min(N, kCUs * C::WPC);
         const int64_t rpw = ((int64_t)N + grid - 1) / grid;
+        if ((K == 4096 || K == 8192) && rpw <= 48) {
+            go(I512{}, I2{}, std::integral_constant<int, 4>{});
+            return;
+        }
         const int ls = rowk_split_shift(rpw, K, MR, C::U, kWgThreads / 64);
         if (K <= 4 * 512 * 8 && rowk_wave_batches(rpw, K, C::U, ls, kWgThreads / 64) <= 2) {
-            go(std::integral_constant<int, 512>{}, std::integral_constant<int, 2>{});
+            go(I512{}, I2{}, I2{});
             return;
         }
     }
-    go(std::integral_constant<int, kWgThreads>{}, std::integral_constant<int, C::WPC>{});
+    go(std::integral_constant<int, kWgThreads>{}, std::integral_constant<int, C::WPC>{},
+       std::integral_constant<int, C::U>{});
 }
 
 // Unfused FP8 weights: codes staged in LDS when they fit, else read from L2.
