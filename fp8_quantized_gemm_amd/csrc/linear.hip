@@ -83,8 +83,8 @@ enum : int {
 //
 // At most WPC workgroups of NT threads (W = NT / 64 waves) per CU: the
 // activation prologue (copy or quantization into LDS) is paid once per
-// workgroup and spread over its waves.  NT is 1024, or 512 where each wave
-// would otherwise stream at most two batches (see launch_rowk).
+// workgroup and spread over its waves.  NT is 1024 or 512 and the batch U is
+// 2, 3 or 4 KiB, chosen per call by launch_rowk.
 // Each workgroup takes one contiguous span of weight rows, so that at any
 // moment it streams one compact window of the weight matrix: measured on
 // MI355X, block-contiguous streaming with non-temporal loads sustains about
@@ -485,32 +485,40 @@ void launch_rowk(const void* act, const float* sa_in, const uint8_t* qw, const f
         else if (vecs <= 2 * NT) launch(std::integral_constant<int, 2>{});
         else launch(std::integral_constant<int, 4>{});
     };
-    // Launch shape at M = 1, from measurements on MI355X (Llama-7B and
-    // Qwen-32B decode shapes, weights cold):
-    // - rows of 4 or 8 KiB (whole 4 KiB batches) and at most 48 rows per
-    //   workgroup: 512 threads streaming 4 KiB batches (QKV 11.6 -> 11.0 us,
-    //   O 6.9 -> 6.8, gate+up 17.9 -> 17.2, Qwen-32B O 12.3 -> 10.7); rows
-    //   that end in a partial batch (K = 5120, 11008) or many rows per
-    //   workgroup (Qwen-32B gate+up, 100) were slower that way;
-    // - else, where 1024 threads would leave each wave at most two 2 KiB
-    //   batches: 512 threads, which halve the waves that meet at the
-    //   activation prologue's barriers;
-    // - else 1024 threads with 2 KiB batches.
-    // The choice depends on N and K only, never on the activation source, so
-    // fp8_linear and fp8_quantize_act + fp8_gemm split rows alike and stay
-    // bit-identical; K stays where the fused prologue (8 bf16 values per
-    // vector, at most 4 vectors per thread) fits 512 threads.
+    // Launch shape at M = 1 (measured on MI355X on 16 decode shapes, K = 2048
+    // .. 12288, 4 .. 100 rows per workgroup, weights cold).  The reference is
+    // 1024 threads streaming 2 KiB batches.  Rows of 3 .. 16 whole KiB instead
+    // take 512 threads streaming 3 or 4 KiB batches (the size that leaves less
+    // of a row's last batch empty; 4 on a tie) whenever the longest wave then
+    // streams no more batches than with the reference: Llama-7B QKV 11.9 ->
+    // 11.4 us, O 7.4 -> 6.6, gate+up 17.5 -> 16.9, Qwen-32B QKV 14.2 -> 13.2,
+    // O 12.3 -> 10.7.  Where it would stream more (Qwen-32B gate+up: 100 rows
+    // per workgroup), or rows end in a part of a KiB (down, K = 11008), or
+    // are shorter than 3 KiB, the larger batches measured slower.  Otherwise,
+    // where the reference leaves each wave at most two batches, 512 threads
+    // with 2 KiB batches halve the waves that meet at the activation
+    // prologue's barriers.  The choice depends on N and K only, never on the
+    // activation source, so fp8_linear and fp8_quantize_act + fp8_gemm split
+    // rows alike and stay bit-identical; K stays where the fused prologue (8
+    // bf16 values per vector, at most 4 vectors per thread) fits 512 threads.
     using I512 = std::integral_constant<int, 512>;
     using I2 = std::integral_constant<int, 2>;
     if constexpr (MR == 1) {
+        constexpr int W16 = kWgThreads / 64, W8 = 512 / 64;
         const int grid = min(N, kCUs * C::WPC);
         const int64_t rpw = ((int64_t)N + grid - 1) / grid;
-        if ((K == 4096 || K == 8192) && rpw <= 48) {
-            go(I512{}, I2{}, std::integral_constant<int, 4>{});
-            return;
+        const int64_t ref = rowk_wave_batches(rpw, K, C::U, rowk_split_shift(rpw, K, MR, C::U, W16),
+                                              W16);
+        if (K % 1024 == 0 && K >= 3 * 1024 && K <= 4 * 512 * 8) {
+            const int kb = K / 1024;
+            const int u = ((kb + 2) / 3 * 3 - kb) < ((kb + 3) / 4 * 4 - kb) ? 3 : 4;
+            if (rowk_wave_batches(rpw, K, u, rowk_split_shift(rpw, K, MR, u, W8), W8) <= ref) {
+                if (u == 3) go(I512{}, I2{}, std::integral_constant<int, 3>{});
+                else go(I512{}, I2{}, std::integral_constant<int, 4>{});
+                return;
+            }
         }
-        const int ls = rowk_split_shift(rpw, K, MR, C::U, kWgThreads / 64);
-        if (K <= 4 * 512 * 8 && rowk_wave_batches(rpw, K, C::U, ls, kWgThreads / 64) <= 2) {
+        if (K <= 4 * 512 * 8 && ref <= 2) {
             go(I512{}, I2{}, I2{});
             return;
         }

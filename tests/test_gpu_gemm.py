@@ -209,7 +209,8 @@ def test_deterministic_and_stream_order():
 @pytest.mark.parametrize("dtype", ["bf16", "fp16"])
 @pytest.mark.parametrize("M,N,K", [(1, 4096, 4096), (2, 300, 11008), (1, 37, 16), (1, 64, 32768),
                                    (1, 64, 16384), (1, 64, 16400), (1, 512, 2048),
-                                   (1, 5120, 8192), (1, 24576, 4096), (1, 25088, 4096),
+                                   (1, 5120, 8192), (1, 24576, 4096), (1, 25088, 4096), (1, 10240, 5120),
+                                   (1, 5120, 3072), (1, 40960, 5120), (1, 300, 12288),
                                    (2, 64, 16384), (2, 64, 32768),
                                    (1, 100, 65536), (2, 50, 33792), (3, 200, 1024), (16, 64, 4096),
                                    (40, 96, 512), (64, 256, 4096), (3, 16, 81920),

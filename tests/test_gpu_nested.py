@@ -177,7 +177,8 @@ def test_fp8_mode_large_grid_sampled():
 
 @pytest.mark.parametrize("M,N,K", [(1, 4096, 4096), (2, 300, 11008), (1, 37, 16), (1, 64, 32768),
                                    (1, 64, 16384), (1, 64, 16400), (1, 512, 2048), (3, 16, 81920),
-                                   (1, 5120, 8192), (1, 24576, 4096), (1, 25088, 4096), (64, 256, 4096), (256, 1000, 4112),
+                                   (1, 5120, 8192), (1, 24576, 4096), (1, 25088, 4096), (1, 10240, 5120),
+                                   (1, 5120, 3072), (1, 40960, 5120), (64, 256, 4096), (256, 1000, 4112),
                                    (4, 1000, 4096), (16, 300, 2048), (3, 50, 10912)])
 def test_fp8_mode_linear_matches_quantize_then_gemm(M, N, K):
     """nested_linear_fp8 (one fused kernel for M <= 2 with M*K <= 32768, the
