@@ -14,8 +14,11 @@ using namespace fp8q;
 namespace {
 
 constexpr int64_t kMaxDim = 0x7fffffff;
-// K bound: a 128-row tile of fp16 activations (128 * K * 2 bytes) must stay
-// addressable by the kernels' 31-bit buffer offsets.
+// K bound: the kernels address a tile's rows through 32-bit buffer
+// resources with byte offsets below 2^31.  The tallest tile, 256 rows of fp16
+// activations in the NestedFP FP16 kernel, spans 256 * K * 2 = 2^31 bytes at
+// K = 2^22 (the resource size is computed in 64 bits and still fits 32), and
+// its last row starts at 255 * K * 2 < 2^31.
 constexpr int64_t kMaxK = (int64_t)1 << 22;
 constexpr int kDecodeMaxM = 16;
 
@@ -111,9 +114,15 @@ fp8q_status linear_common(const char* where, const void* x, int dtype, const uin
         return finish(where, e);
     }
     // y is written only by the GEMM, so until then it can hold the
-    // quantizer's per-workgroup partial maxima (unless it overlaps x)
-    const uintptr_t xb = reinterpret_cast<uintptr_t>(x), yb = reinterpret_cast<uintptr_t>(y);
-    const bool y_free = yb + (uintptr_t)(M * N * 2) <= xb || xb + (uintptr_t)(M * K * 2) <= yb;
+    // quantizer's per-workgroup partial maxima, unless it overlaps anything
+    // the quantizer reads or writes (x, q, scale, amax): then the quantizer
+    // folds its maxima with atomics instead
+    const uintptr_t yb = reinterpret_cast<uintptr_t>(y), ye = yb + (uintptr_t)(M * N * 2);
+    auto apart = [&](const void* p, int64_t bytes) {
+        const uintptr_t b = reinterpret_cast<uintptr_t>(p);
+        return ye <= b || b + (uintptr_t)bytes <= yb;
+    };
+    const bool y_free = apart(x, M * K * 2) && apart(q, M * K) && apart(scale, 4) && apart(amax, 4);
     hipError_t e = launch_quantize_scratch(x, dtype, M * K, q, scale, amax,
                                            y_free ? reinterpret_cast<float*>(y) : nullptr,
                                            M * N / 2, st);

@@ -99,6 +99,12 @@ __device__ __forceinline__ uint32_t e4m3_pack4(float a, float b, float c, float 
 // 2^-80 <= s <= 2^120 and every quotient large enough to give a nonzero code.
 // Scales outside that range use the IEEE division.  An exact quotient
 // (e == 0, which includes x = -0) returns q0, keeping the sign of zero.
+//
+// Overflow: where |q0| > 896 the true quotient is beyond 448 as well (q0 is
+// within two ulps of it), so both saturate to the same code and q0 is
+// returned as it is.  The correction step must not run there: with x*r
+// rounded to +-inf (an input spike under a small delayed scale, or an
+// infinite input) the residual is -+inf and inf - inf would give NaN.
 struct Quotient {
     float s, r;
     bool fast;
@@ -111,7 +117,7 @@ struct Quotient {
     {
         const float q0 = x * r;
         const float e = __builtin_fmaf(-q0, s, x);
-        return e == 0.0f ? q0 : __builtin_fmaf(e, r, q0);
+        return (e == 0.0f || fabsf(q0) > 896.0f) ? q0 : __builtin_fmaf(e, r, q0);
     }
 };
 

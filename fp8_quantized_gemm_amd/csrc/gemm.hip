@@ -339,9 +339,11 @@ void gemm_n16_kernel(const uint16_t* __restrict__ a, const uint8_t* __restrict__
     const int m0 = (bid % tiles_m) * BM;
     const int n0 = (bid / tiles_m) * BN;
     const int nrows = min(BN, N - n0);
-    const rsrc_t ra = make_rsrc(a + (size_t)m0 * K, (uint32_t)(min(BM, M - m0) * K * 2));
-    const rsrc_t rh = make_rsrc(hi + (size_t)n0 * K, (uint32_t)(nrows * K));
-    const rsrc_t rl = make_rsrc(lo + (size_t)n0 * K, (uint32_t)(nrows * K));
+    // byte sizes in 64 bits: 256 fp16 rows at the largest K (2^22) span 2^31
+    // bytes, which a buffer resource still holds (num_records is 32 bits)
+    const rsrc_t ra = make_rsrc(a + (size_t)m0 * K, (uint32_t)((int64_t)min(BM, M - m0) * K * 2));
+    const rsrc_t rh = make_rsrc(hi + (size_t)n0 * K, (uint32_t)((int64_t)nrows * K));
+    const rsrc_t rl = make_rsrc(lo + (size_t)n0 * K, (uint32_t)((int64_t)nrows * K));
 
     const int dua = (lane & 7) ^ (lane >> 3);         // activation unit landing in slot l
     const int duw = (lane & 3) ^ ((lane >> 3) & 3);   // plane unit landing in slot l

@@ -120,7 +120,8 @@ FP8Q_API fp8q_status fp8_gemm(const uint8_t* qa, const float* sa, const uint8_t*
  *   one kernel (each workgroup quantizes the activation in LDS); otherwise it
  *   launches the quantizer and then the GEMM; while the quantizer runs, y
  *   (not yet written) may hold its per-workgroup partial maxima, unless y
- *   overlaps x.
+ *   overlaps x, q, *scale or *amax (then the quantizer uses no scratch).
+ *   Overlapping y with qw or sw is not supported.
  */
 FP8Q_API fp8q_status fp8_linear(const void* x, int dtype, const uint8_t* qw, const float* sw,
                        uint16_t* y, uint8_t* q, float* scale, float* amax, int64_t M,

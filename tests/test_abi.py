@@ -201,3 +201,14 @@ def test_binding_raises_on_cpu_tensors():
 def test_error_type_carries_status():
     e = fp8q.Fp8qError("fp8_gemm", ERR_SHAPE)
     assert e.status == ERR_SHAPE and "size out of range" in str(e)
+
+
+def test_package_exports_every_binding():
+    """Every entry point of the binding is reachable from the package itself."""
+    import fp8_quantized_gemm_amd as pkg
+
+    public = {n for n in dir(fp8q) if not n.startswith("_") and callable(getattr(fp8q, n))
+              and getattr(getattr(fp8q, n), "__module__", "") == fp8q.__name__}
+    assert public <= set(pkg.__all__), sorted(public - set(pkg.__all__))
+    for name in pkg.__all__:
+        assert getattr(pkg, name) is getattr(fp8q, name)

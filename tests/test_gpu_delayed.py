@@ -166,3 +166,77 @@ def test_full_size_llama_shapes_sequence(M, K, N):
     ref, ab = oracle.gemm_fp8_ref(want_q.reshape(M, K)[rows], want_s, oqw[ns], osw, ms, nn)
     out = oracle.bf16_decode(host(y)[rows][:, ns]).astype(np.float64).ravel()
     assert_within(out, ref, ab, f"delayed M={M} {K}->{N}", "bf16")
+
+
+def _spike_sequence(M, K, dtype, seed):
+    """Calls that drive x / s beyond the binary32 range under a small delayed
+    scale: the history first holds an amax of exactly 1.0 (scale 1/448), then
+    inputs carry spikes whose quotient x * (1/s) overflows (bf16: 1e36,
+    -3e38, a lone 3e38 among N(0,1) values; both dtypes: +-inf; fp16 also its
+    largest finite value 65504), with calls of amax 1.0 in between so that
+    the scale drops back to 1/448 before each spike (history length 1).  The
+    infinite spike comes last, so no call quantizes with an infinite scale
+    except the oracle-checked state it leaves."""
+    td = torch.bfloat16 if dtype == "bf16" else torch.float16
+    rng = np.random.Generator(np.random.PCG64(seed))
+
+    def unit():                                  # N(0,1) clipped, amax exactly 1.0
+        v = np.clip(rng.standard_normal((M, K)).astype(np.float32) * 0.3, -0.99, 0.99)
+        v.flat[rng.integers(M * K)] = 1.0
+        return v
+
+    def spiked(vals):
+        v = rng.standard_normal((M, K)).astype(np.float32)
+        idx = rng.choice(M * K, len(vals), replace=False)
+        for i, s in zip(idx, vals):
+            v.flat[i] = s
+        return v
+
+    if dtype == "bf16":
+        spikes = [[1e36, -1e36, 5e37], [-3e38], [3e38], [np.inf, -np.inf, 1e36]]
+    else:
+        spikes = [[65504.0, -65504.0], [np.inf], [-np.inf, 65504.0]]
+    seq = [unit()]
+    for sp in spikes:
+        seq += [spiked(sp), unit()]
+    seq.pop()                                    # end on the infinite spike
+    return [torch.from_numpy(v).to(td) for v in seq]
+
+
+@pytest.mark.parametrize("dtype", ["bf16", "fp16"])
+@pytest.mark.parametrize("path,M,K,N", [("one workgroup", 1, 4096, 0),
+                                        ("grid-stride", 64, 4096, 0),
+                                        ("fused decode", 1, 4096, 512),
+                                        ("fused decode", 2, 11008, 300),
+                                        ("two-launch linear", 24, 4096, 300)])
+def test_delayed_overflowing_quotients_saturate(path, M, K, N, dtype):
+    """Codes of spikes whose quotient overflows binary32 saturate to +-448
+    (0x7E / 0xFE) as the oracle's IEEE quotient does, never the NaN code; the
+    scale, amax, ring and state follow the oracle call by call, and the
+    linear's output equals the GEMM on the same codes."""
+    xs = _spike_sequence(M, K, dtype, seed=synth.seed_for("ds-spike", path, M, K, dtype))
+    code = oracle.BF16 if dtype == "bf16" else oracle.FP16
+    od = oracle.DelayedScaling(1)
+    ds = fp8q.DelayedScaling(1, device=DEV)
+    if N:
+        w = synth.normal((N, K), 0.02, "fp16", seed=synth.seed_for("ds-spike-w", N, K), device=DEV)
+        qw, sw, _ = fp8q.fp8_quantize_act(w)
+    saturated = 0
+    for t, x in enumerate(xs):
+        want_q, want_s, want_a = od.quantize(synth.bits(x).ravel(), code)
+        say("delayed spike", path, dtype, M, K, N, "call", t)
+        if N:
+            y, q, s, a = fp8q.fp8_linear_delayed(x.to(DEV), qw, sw, ds)
+        else:
+            q, s, a = fp8q.fp8_quantize_act_delayed(x.to(DEV), ds)
+        got = host(q).ravel()
+        assert not np.any((got & 0x7F) == 0x7F), f"call {t}: NaN code"
+        assert np.array_equal(got, want_q), f"call {t}: codes"
+        assert host(s)[0] == np.float32(want_s), f"call {t}: scale"
+        assert host(a)[0] == np.float32(want_a), f"call {t}: amax"
+        saturated += int(np.count_nonzero((want_q & 0x7F) == 0x7E))
+        if N:
+            y2 = fp8q.fp8_gemm(q, s, qw, sw)
+            assert torch.equal(y.view(torch.int16), y2.view(torch.int16)), f"call {t}: y"
+        _check_state(ds, od, f"{path} call {t}")
+    assert saturated > 0
