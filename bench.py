@@ -43,7 +43,10 @@ HBM_PEAK_GBS = 8000.0         # MI355X HBM3E, GB/s
 FP8_PEAK_TFLOPS = 5000.0      # dense FP8 MFMA
 FP16_PEAK_TFLOPS = 2500.0     # dense FP16 MFMA
 LAYERS = 32
+QWEN_LAYERS = 64
+CFG1_COPIES = 64              # 64 x 16 MiB of weights: beyond the 256 MB last-level cache
 METRIC = "FP8 linear: HBM GB/s @M=1 and TFLOP/s @M=512, % of MI355X peak"
+PARTS = ("cfg1", "decode", "prefill", "delayed", "qwen", "rowwise", "kv", "nested")
 
 
 def parse():
@@ -61,6 +64,11 @@ def parse():
     p.add_argument("--only-prefill", action="store_true",
                    help="run only the prefill figures (M = 512, 2048) and print them: the "
                         "command that the prefill GEMM's rocprofv3 summaries are taken on")
+    p.add_argument("--only", default="", metavar="PARTS",
+                   help="run only these secondary figures (comma-separated: " +
+                        ", ".join(PARTS) + ") and print them as one JSON line, without the "
+                        "headline step: the commands the per-kernel rocprofv3 summaries "
+                        "are taken on")
     p.add_argument("--copy-calibration-mib", type=int, default=0, metavar="MIB",
                    help="instead of the benchmark, run 5 launches of a plain elementwise "
                         "copy (read MIB MiB, write MIB MiB) so that HBM byte counters "
@@ -282,12 +290,45 @@ def prefill_figures(torch, fp8q, mm, graph=True, call=linear_call):
             "ms_per_step": round(dt * 1e3, 3)}
 
 
-def secondary(torch, fp8q, synth, model1, dev,
-              parts=("decode", "prefill", "delayed", "qwen", "rowwise", "kv", "nested"),
-              graph=True):
-    """Prefill, M = 4/8 decode, delayed scaling, Qwen-32B, per-token/per-channel
-    and NestedFP figures (a few steps each)."""
+def single_linear_figure(torch, fp8q, synth, dev, graph=True):
+    """The single 4096 -> 4096 linear at M = 1 (fp16 N(0, 0.02) weights
+    quantized per tensor, bf16 N(0, 1) activation quantized per call):
+    one fp8_linear call on each of CFG1_COPIES distinct weight copies per step,
+    so every call reads its 16 MiB of codes from HBM rather than from the
+    256 MB last-level cache."""
+    K = N = 4096
+    mm = Model.__new__(Model)
+    mm.M = 1
+    mm.linears = []
+    for c in range(CFG1_COPIES):
+        w = synth.normal((N, K), 0.02, "fp16", seed=synth.seed_for("cfg1-w", c), device=dev)
+        qw, sw, _ = fp8q.fp8_quantize_act(w)
+        del w
+        mm.linears.append(dict(layer=c, name="single", K=K, N=N, qw=qw, sw=sw, rowwise=False,
+                               x=synth.activation(1, K, seed=synth.seed_for("cfg1-x", c),
+                                                  device=dev),
+                               q=torch.empty((1, K), dtype=torch.uint8, device=dev),
+                               sa=torch.empty(1, dtype=torch.float32, device=dev),
+                               amax=torch.empty(1, dtype=torch.float32, device=dev),
+                               y=torch.empty((1, N), dtype=torch.bfloat16, device=dev)))
+    torch.cuda.synchronize()
+    dt, dev_dt = time_steps(torch, fp8q, mm, steps=10, warmup=3, graph=graph)
+    byts = sum(mm.gemm_bytes(L) + mm.quant_bytes(L) for L in mm.linears)
+    per_launch = dev_dt / len(mm.linears)
+    return {"GB_per_s": round(byts / dt / 1e9, 1),
+            "frac_hbm": round(byts / dt / 1e9 / HBM_PEAK_GBS, 4),
+            "us_per_linear": round(per_launch * 1e6, 3),
+            "algorithmic_bytes_per_linear": byts // len(mm.linears),
+            "weight_copies": CFG1_COPIES}
+
+
+def secondary(torch, fp8q, synth, model1, dev, parts=PARTS, graph=True):
+    """The single-linear, prefill, M = 4/8 decode, delayed scaling, Qwen-32B,
+    per-token/per-channel, KV-cache and NestedFP figures (a few steps each)."""
     out = {}
+    if "cfg1" in parts:
+        out["single_4096x4096_m1"] = single_linear_figure(torch, fp8q, synth, dev, graph)
+        progress("single linear done")
     # decode at M = 4, 8 on the same weights (activations re-drawn)
     for M in ((4, 8) if "decode" in parts else ()):
         out[f"decode_m{M}"] = decode_figures(torch, fp8q, with_activations(torch, synth, model1, M,
@@ -311,17 +352,19 @@ def secondary(torch, fp8q, synth, model1, dev,
         del mm
         for L in model1.linears:
             del L["ds"]
-    # Qwen-32B linears (weights N(0, 0.015)) on 8 of the 64 layers: 3.9 GB of
-    # E4M3 weights, still cold in HBM on every step; decode M = 1, 16, prefill
-    # M = 1024
+    # Qwen-32B linears (weights N(0, 0.015)) on all 64 layers: 31.2 GB of E4M3
+    # weights, cold in HBM on every step; decode M = 1, 16, prefill M = 1024
     if "qwen" in parts:
-        mq = Model(torch, fp8q, synth, M=1, dev=dev, spec=synth.QWEN32B_LINEARS, layers=8,
-                   sigma=0.015, tag="wq")
-        out["qwen32b_decode_m1"] = dict(decode_figures(torch, fp8q, mq, graph), layers=8)
+        mq = Model(torch, fp8q, synth, M=1, dev=dev, spec=synth.QWEN32B_LINEARS,
+                   layers=QWEN_LAYERS, sigma=0.015, tag="wq")
+        progress("qwen-32b model built")
+        out["qwen32b_decode_m1"] = dict(decode_figures(torch, fp8q, mq, graph), layers=QWEN_LAYERS)
         out["qwen32b_decode_m16"] = dict(decode_figures(
-            torch, fp8q, with_activations(torch, synth, mq, 16, dev, "xq"), graph), layers=8)
+            torch, fp8q, with_activations(torch, synth, mq, 16, dev, "xq"), graph),
+            layers=QWEN_LAYERS)
         out["qwen32b_prefill_m1024"] = dict(prefill_figures(
-            torch, fp8q, with_activations(torch, synth, mq, 1024, dev, "xqp"), graph), layers=8)
+            torch, fp8q, with_activations(torch, synth, mq, 1024, dev, "xqp"), graph),
+            layers=QWEN_LAYERS)
         progress("qwen-32b done")
         del mq
     # per-token activation and per-channel weight scales (fp8_linear_rowwise)
@@ -357,10 +400,11 @@ def secondary(torch, fp8q, synth, model1, dev,
         del blocks, outs
     if "nested" not in parts:
         return out
-    # NestedFP at M = 1 and 256 on 8 layers of fp16 weights (hi/lo planes)
+    # NestedFP at M = 1 and 256 on all 32 layers of fp16 weights (hi/lo planes:
+    # 12.95 GB, and as much again for the E4M3 upper-byte split)
     nested = []
     nested4 = []                       # planes of the E4M3 upper-byte split
-    for layer in range(8):
+    for layer in range(LAYERS):
         for name, K, N in synth.LLAMA7B_LINEARS:
             w = synth.normal((N, K), 0.02, "fp16", seed=synth.seed_for("w", layer, name), device=dev)
             hi, lo = fp8q.nested_split(w)
@@ -400,10 +444,12 @@ def secondary(torch, fp8q, synth, model1, dev,
             if mode.startswith("fp8"):
                 byts = sum(N * K + M * K + 2 * M * N + 3 * M * K for K, N, _, _ in nested)
             fl = sum(2 * M * N * K for K, N, _, _ in nested)
+            peak = FP16_PEAK_TFLOPS if mode.startswith("fp16") else FP8_PEAK_TFLOPS
             out[f"nested_{mode}_m{M}"] = {"GB_per_s": round(byts / dt / 1e9, 1),
                                           "frac_hbm": round(byts / dt / 1e9 / HBM_PEAK_GBS, 4),
                                           "TFLOP_per_s": round(fl / dt / 1e12, 2),
-                                          "layers": 8}
+                                          "frac_mfma": round(fl / dt / 1e12 / peak, 4),
+                                          "layers": LAYERS}
             progress(f"nested {mode} M={M} done")
     return out
 
@@ -445,9 +491,14 @@ def main():
     torch.cuda.set_device(0)
     model = Model(torch, fp8q, synth, M=1, dev=dev)
     progress("decode model built (128 E4M3 weight matrices)")
-    if args.only_prefill:
-        print(json.dumps({"prefill": secondary(torch, fp8q, synth, model, dev, parts=("prefill",),
-                                               graph=not args.eager)}), flush=True)
+    if args.only_prefill or args.only:
+        parts = ("prefill",) if args.only_prefill else tuple(args.only.split(","))
+        bad = [p for p in parts if p not in PARTS]
+        if bad:
+            print(f"unknown parts {bad}; choose from {PARTS}", file=sys.stderr)
+            sys.exit(2)
+        print(json.dumps({"secondary": secondary(torch, fp8q, synth, model, dev, parts=parts,
+                                                 graph=not args.eager)}), flush=True)
         return
     graph = not args.eager
     dt, dev_step = time_steps(torch, fp8q, model, args.steps, args.warmup, graph=graph)

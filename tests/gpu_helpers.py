@@ -52,3 +52,17 @@ def assert_within(out_vals: np.ndarray, ref: np.ndarray, ab: np.ndarray, what: s
         raise AssertionError(
             f"{what}: {bad.size}/{ok.size} outside tolerance; first at flat index {i}: "
             f"out={out_vals[i]!r} ref={ref[i]!r} absref={ab[i]!r}")
+
+
+def dense_sample(M, N, rng, rows=32, cols=32):
+    """Output positions checked against the oracle at full size: every element
+    when M <= 16; otherwise `rows` seeded rows across all N plus `cols` seeded
+    columns across all M.  Returns (ms, ns) flat index arrays."""
+    if M <= 16:
+        mm, nn = np.meshgrid(np.arange(M), np.arange(N), indexing="ij")
+        return mm.ravel(), nn.ravel()
+    r = np.sort(rng.choice(M, min(rows, M), replace=False))
+    c = np.sort(rng.choice(N, min(cols, N), replace=False))
+    ms = np.concatenate([np.repeat(r, N), np.tile(np.arange(M), c.size)])
+    ns = np.concatenate([np.tile(np.arange(N), r.size), np.repeat(c, M)])
+    return ms, ns

@@ -11,7 +11,7 @@ import torch
 
 import oracle
 from fp8_quantized_gemm_amd import fp8q, synth
-from gpu_helpers import DEV, assert_within, host, say, scalar_dev, to_dev_u8
+from gpu_helpers import DEV, assert_within, dense_sample, host, say, scalar_dev, to_dev_u8
 
 pytestmark = pytest.mark.gpu
 
@@ -154,17 +154,17 @@ LAYER_SHAPES = [(K, N) for _, K, N in synth.LLAMA7B_LINEARS] + \
                [(K, N) for _, K, N in synth.QWEN32B_LINEARS]
 
 
-@pytest.mark.parametrize("M", [1, 8, 16, 512, 1024, 2048])
+@pytest.mark.parametrize("M", [1, 4, 8, 16, 512, 1024, 2048])
 @pytest.mark.parametrize("K,N", LAYER_SHAPES)
-def test_full_size_layers_sampled(M, K, N):
-    """Full Llama-7B / Qwen-32B linear shapes, GPU quantization + GEMM: codes of
-    the sampled rows bit-exact, outputs within tolerance on a seeded sample
-    (whole rows for M <= 16, 2 rows + 2 columns + 256 pairs otherwise)."""
+def test_full_size_layers_dense(M, K, N):
+    """Full Llama-7B / Qwen-32B linear shapes, GPU quantization + GEMM: the
+    activation codes, scales and every weight code bit-exact; outputs within
+    tolerance of the fp64 checker on every element for M <= 16, and on 32
+    seeded rows x all N plus 32 seeded columns x all M otherwise."""
     sigma = 0.015 if (K, N) in [(k, n) for _, k, n in synth.QWEN32B_LINEARS] else 0.02
     seed = synth.seed_for("layer", M, K, N)
     x, w, qa, sa, qw, sw, y = _gpu_pipeline(M, N, K, seed, outliers=M > 16, sigma=sigma)
     rng = np.random.Generator(np.random.PCG64(seed))
-    # oracle quantization of W: full amax, codes of the sampled rows only
     wb = synth.bits(w)
     s_w = oracle.scale_from_amax(oracle.amax(wb.ravel(), oracle.FP16))
     xb = synth.bits(x)
@@ -172,24 +172,12 @@ def test_full_size_layers_sampled(M, K, N):
     assert np.float32(host(sa)[0]) == np.float32(osa)
     assert np.float32(host(sw)[0]) == np.float32(s_w)
     assert np.array_equal(host(qa).ravel(), oqa)
-    if M <= 16:
-        ns = np.sort(rng.choice(N, size=min(N, 512), replace=False))
-        ms_all = np.repeat(np.arange(M), ns.size)
-        ns_all = np.tile(np.arange(ns.size), M)
-    else:
-        rows = rng.choice(M, 2, replace=False)
-        cols = rng.choice(N, 2, replace=False)
-        ns = np.unique(np.concatenate([cols, rng.choice(N, 254, replace=False)]))
-        pm = np.concatenate([np.repeat(rows, ns.size), np.arange(M), np.arange(M)])
-        pn_glob = np.concatenate([np.tile(ns, rows.size), np.full(M, cols[0]), np.full(M, cols[1])])
-        pos = {n: i for i, n in enumerate(ns)}
-        ms_all = pm
-        ns_all = np.array([pos[n] for n in pn_glob])
-    wq_rows = oracle.quantize_with_scale(wb[ns].ravel(), oracle.FP16, s_w).reshape(ns.size, K)
-    assert np.array_equal(host(qw)[ns], wq_rows), "weight codes differ"
-    ref, ab = oracle.gemm_fp8_ref(oqa.reshape(M, K), osa, wq_rows, s_w, ms_all, ns_all)
-    yb = host(y)
-    out = oracle.bf16_decode(yb[ms_all, ns[ns_all]]).astype(np.float64)
+    oqw = oracle.quantize_with_scale(wb.ravel(), oracle.FP16, s_w).reshape(N, K)
+    assert np.array_equal(host(qw), oqw), "weight codes differ"
+    del wb
+    ms, ns = dense_sample(M, N, rng)
+    ref, ab = oracle.gemm_fp8_ref(oqa.reshape(M, K), osa, oqw, s_w, ms, ns)
+    out = oracle.bf16_decode(host(y)[ms, ns]).astype(np.float64)
     assert_within(out, ref, ab, f"M={M} {K}->{N}", "bf16")
 
 
@@ -239,8 +227,7 @@ def test_linear_matches_quantize_then_gemm(M, N, K, dtype):
     oq, os_, oa = oracle.quantize(synth.bits(x).ravel(), code)
     assert np.array_equal(host(q).ravel(), oq)
     assert float(host(s)[0]) == os_ and float(host(a)[0]) == oa
-    ms = np.repeat(np.arange(M), min(N, 64))
-    ns = np.tile(np.arange(min(N, 64)), M)
+    ms, ns = dense_sample(M, N, np.random.Generator(np.random.PCG64(seed)))
     ref, ab = oracle.gemm_fp8_ref(oq.reshape(M, K), os_, oqw.reshape(N, K), osw, ms, ns)
     out = oracle.bf16_decode(host(y)[ms, ns]).astype(np.float64)
     assert_within(out, ref, ab, f"linear {M}x{N}x{K}", "bf16")

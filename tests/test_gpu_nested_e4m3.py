@@ -18,7 +18,7 @@ import torch
 
 import oracle
 from fp8_quantized_gemm_amd import fp8q, synth
-from gpu_helpers import DEV, assert_within, host, say, scalar_dev, to_dev_u8
+from gpu_helpers import DEV, assert_within, dense_sample, host, say, scalar_dev, to_dev_u8
 
 pytestmark = pytest.mark.gpu
 
@@ -116,11 +116,13 @@ def test_linear_fp8_e4m3_matches_quantize_then_gemm(M, N, K):
 
 @pytest.mark.parametrize("M", [1, 256])
 @pytest.mark.parametrize("K,N", [(K, N) for _, K, N in synth.LLAMA7B_LINEARS])
-def test_full_size_llama_shapes_sampled(M, K, N):
+def test_full_size_llama_shapes_dense(M, K, N):
     """Both modes on the Llama-7B linear shapes as the benchmark runs them (GPU
     split; FP8 mode through nested_linear_fp8_e4m3, which quantizes the fp16
-    activation itself): the split of 256 sampled weight rows bit-exact, the
-    sampled outputs within tolerance of the oracle, the codes bit-exact."""
+    activation itself): the split of every weight row and the activation codes
+    bit-exact; outputs within tolerance of the oracle on every element at
+    M = 1, on 32 seeded rows x all N plus 32 seeded columns x all M at
+    M = 256."""
     seed = synth.seed_for("nested-e4m3-full", M, K, N)
     a = synth.activation(M, K, seed=seed, dtype="fp16", device=DEV)
     w = synth.normal((N, K), 0.02, "fp16", seed=seed + 1, device=DEV)
@@ -131,21 +133,17 @@ def test_full_size_llama_shapes_sampled(M, K, N):
     torch.cuda.synchronize()
     assert int(bad.item()) == 0
     rng = np.random.Generator(np.random.PCG64(seed))
-    ns = np.sort(rng.choice(N, 256, replace=False))
-    rows = np.arange(M) if M <= 16 else np.sort(rng.choice(M, 4, replace=False))
-    wb = synth.bits(w.cpu())[ns]
+    wb = synth.bits(w.cpu())
     ohi, olo, _ = oracle.nested_split_e4m3(wb)
-    assert np.array_equal(host(hi)[ns], ohi) and np.array_equal(host(lo)[ns], olo)
+    assert np.array_equal(host(hi), ohi) and np.array_equal(host(lo), olo)
     ab16 = synth.bits(a.cpu())
-    ms = np.repeat(np.arange(rows.size), ns.size)
-    nn = np.tile(np.arange(ns.size), rows.size)
+    ms, ns = dense_sample(M, N, rng)
     phi, plo = oracle.nested_split(wb)              # the same words, plain planes
-    ref, ab = oracle.nested_fp16_ref(ab16[rows], phi, plo, ms, nn)
-    out = oracle.f16_decode(host(y16)[rows][:, ns]).ravel()
+    ref, ab = oracle.nested_fp16_ref(ab16, phi, plo, ms, ns)
+    out = oracle.f16_decode(host(y16)[ms, ns]).astype(np.float64)
     assert_within(out, ref, ab, f"fp16 e4m3 M={M} {K}->{N}", "fp16")
     oqa, osa, _ = oracle.quantize(ab16.ravel(), oracle.FP16)
     assert np.array_equal(host(qa).ravel(), oqa) and host(sa)[0] == np.float32(osa)
-    ref8, ab8 = oracle.gemm_fp8_ref(oqa.reshape(M, K)[rows], osa, ohi, oracle.NESTED_E4M3_SCALE,
-                                    ms, nn)
-    out8 = oracle.f16_decode(host(y8)[rows][:, ns]).ravel()
+    ref8, ab8 = oracle.gemm_fp8_ref(oqa.reshape(M, K), osa, ohi, oracle.NESTED_E4M3_SCALE, ms, ns)
+    out8 = oracle.f16_decode(host(y8)[ms, ns]).astype(np.float64)
     assert_within(out8, ref8, ab8, f"fp8 e4m3 M={M} {K}->{N}", "fp16")

@@ -19,7 +19,7 @@ import torch
 
 import oracle
 from fp8_quantized_gemm_amd import fp8q, synth
-from gpu_helpers import DEV, assert_within, host, say, to_dev_u8
+from gpu_helpers import DEV, assert_within, dense_sample, host, say, to_dev_u8
 
 pytestmark = pytest.mark.gpu
 
@@ -204,12 +204,13 @@ def test_linear_rowwise_graph_replays():
 
 @pytest.mark.parametrize("M", [1, 512])
 @pytest.mark.parametrize("K,N", [(K, N) for _, K, N in synth.LLAMA7B_LINEARS])
-def test_full_size_llama_shapes_sampled(M, K, N):
+def test_full_size_llama_shapes_dense(M, K, N):
     """fp8_linear_rowwise on the Llama-7B linear shapes as the benchmark calls
     it (weights quantized per channel on the GPU, activations per token with
-    outlier channels): per-channel codes and scales of 256 sampled weight rows
-    and all activation codes and scales bit-exact; sampled outputs within
-    tolerance of the oracle."""
+    outlier channels): every per-channel weight code and scale and every
+    activation code and scale bit-exact; outputs within tolerance of the
+    oracle on every element at M = 1, on 32 seeded rows x all N plus 32
+    seeded columns x all M at M = 512."""
     seed = synth.seed_for("rowwise-full", M, K, N)
     x = synth.activation(M, K, seed=seed, outliers=True, device=DEV)
     w = synth.normal((N, K), 0.02, "fp16", seed=seed + 1, device=DEV)
@@ -218,14 +219,11 @@ def test_full_size_llama_shapes_sampled(M, K, N):
     y, q, sa, _ = fp8q.fp8_linear_rowwise(x, qw, sw)
     torch.cuda.synchronize()
     rng = np.random.Generator(np.random.PCG64(seed))
-    ns = np.sort(rng.choice(N, 256, replace=False))
-    rows = np.arange(M) if M <= 16 else np.sort(rng.choice(M, 4, replace=False))
-    oqw, osw, _ = oracle.quantize_rows(synth.bits(w.cpu())[ns], oracle.FP16)
-    assert np.array_equal(host(qw)[ns], oqw) and np.array_equal(host(sw)[ns], osw)
+    oqw, osw, _ = oracle.quantize_rows(synth.bits(w.cpu()), oracle.FP16)
+    assert np.array_equal(host(qw), oqw) and np.array_equal(host(sw), osw)
     oqa, osa, _ = oracle.quantize_rows(synth.bits(x.cpu()), oracle.BF16)
     assert np.array_equal(host(q), oqa) and np.array_equal(host(sa), osa)
-    ms = np.repeat(np.arange(rows.size), ns.size)
-    nn = np.tile(np.arange(ns.size), rows.size)
-    ref, ab = oracle.gemm_fp8_rowwise_ref(oqa[rows], osa[rows], oqw, osw, ms, nn)
-    out = oracle.bf16_decode(host(y)[rows][:, ns]).astype(np.float64).ravel()
+    ms, ns = dense_sample(M, N, rng)
+    ref, ab = oracle.gemm_fp8_rowwise_ref(oqa, osa, oqw, osw, ms, ns)
+    out = oracle.bf16_decode(host(y)[ms, ns]).astype(np.float64)
     assert_within(out, ref, ab, f"rowwise M={M} {K}->{N}", "bf16")
