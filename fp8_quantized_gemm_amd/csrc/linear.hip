@@ -1,27 +1,28 @@
-// Decode path for M <= 2 activation rows: row-contiguous weight streaming on
-// the VALU, and the fused decode linear (dynamic activation quantization +
-// FP8 GEMM in one launch).
+// Decode path for M <= 2 activation rows: row-contiguous weight streaming,
+// and the fused decode linear (dynamic activation quantization + FP8 GEMM in
+// one launch).
 //
 // The weight matrix is read once and dominates the bytes (page "7B参数模型在
 // 消费级GPU上的极限" §1: memory bandwidth is the first bottleneck of token
 // generation), so the access pattern is chosen for HBM: each wave streams
 // its weight rows with every lane reading 16 consecutive bytes, i.e. 1 KiB
 // of one row per load instruction, rather than the 16-rows-by-64-bytes
-// pattern the MFMA operand layout would impose.  With at most two activation
-// rows the arithmetic runs on the VALU in fp16 pairs: the activation values
-// sit in LDS as fp16 (every E4M3 value is exact in fp16), each pair of weight
-// codes becomes an fp16 pair with one conversion, and v_dot2_f32_f16 adds two
-// exact products into an fp32 accumulator, 16 VALU instructions per 16 weight
-// bytes and row (decoding both operands to fp32 and multiplying and adding
-// in fp32 took 48, which held the stream back: the Llama-7B decode step ran
-// 7% faster in fp16 pairs, measured on MI355X).  Each wave finishes its dot
+// pattern the MFMA operand layout would impose.  The products still run on
+// the matrix cores: with at most two activation rows an MFMA is computed on
+// its diagonal (each lane pairs its own weight bytes with the activation
+// codes of the same positions, see the main loop), one 16x16x128 FP8 MFMA
+// per 2 KiB of weights and activation row, so the VALU does no per-element
+// work.  (Measured on MI355X, Llama-7B decode step: decoding both operands to
+// fp32 and multiplying on the VALU, 48 instructions per 16 weight bytes,
+// held the stream back; fp16 pairs with v_dot2_f32_f16, 16 instructions,
+// were 7% faster; the MFMA diagonal another 2%.)  Each wave finishes its dot
 // products with a 64-lane sum.
 //
 // The fused variant quantizes the bf16/fp16 activation itself: every
 // workgroup reduces amax over the whole activation (L2-resident), computes
 // s = amax/448 and the E4M3 codes with the same device routines as
-// fp8_quantize_act, keeps their values in LDS, and workgroup 0 also writes
-// the codes, scale and amax to memory.  The activation loads and then the first
+// fp8_quantize_act, keeps the codes in LDS, and workgroup 0 also writes the
+// codes, scale and amax to memory.  The activation loads and then the first
 // batch of weight loads are issued before this prologue, so the prologue
 // waits only for the activation and HBM is busy while it runs.  The FP8 GEMM is the one
 // of page "C++与FP8量化" §3.3; the quantization follows the page on a 7B
@@ -49,40 +50,16 @@ constexpr int kPartMax = 1024;    // per-workgroup partial sums of the split-K d
 
 typedef _Float16 h2 __attribute__((ext_vector_type(2)));
 
-// Four FP8 codes (one dword, code i in byte i) -> two dwords of packed fp16
-// pairs (codes 0,1, then 2,3).  Every E4M3 and E5M2 value is exact in fp16
-// (E4M3 subnormals are fp16 normals; an E5M2 code b is the fp16 word b << 8,
-// its subnormals fp16 subnormals, which the fp16 dot product keeps), so the
-// products formed from these pairs are the exact products of the codes.
-template <int FMT>
-__device__ __forceinline__ v2i fp8x4_to_f16(int c)
+__device__ __forceinline__ v8i cat8(const v4i& lo, const v4i& hi)
 {
-    if constexpr (mfma_format(FMT) == 0) {
-        const h2 lo = __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(c, 1.0f, false);
-        const h2 hi = __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(c, 1.0f, true);
-        return v2i{__builtin_bit_cast(int, lo), __builtin_bit_cast(int, hi)};
-    } else {
-        return v2i{(int)__builtin_amdgcn_perm(0u, (uint32_t)c, 0x010c000cu),
-                   (int)__builtin_amdgcn_perm(0u, (uint32_t)c, 0x030c020cu)};
-    }
-}
-// 16 codes -> 8 dwords of fp16 pairs
-template <int FMT>
-__device__ __forceinline__ void fp8x16_to_f16(const v4i& v, int (&h)[8])
-{
-#pragma unroll
-    for (int d = 0; d < 4; ++d) {
-        const v2i p = fp8x4_to_f16<FMT>(v[d]);
-        h[2 * d] = p[0];
-        h[2 * d + 1] = p[1];
-    }
+    return v8i{lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
 }
 
 // ---------------------------------------------------------------- FP8 / BF8 weights
 // Activation source of the FP8 kernel.
 enum : int {
-    AS_GLOBAL = 0,   // E4M3 codes read from memory (L2) and converted in the main loop
-    AS_COPY = 1,     // E4M3 codes converted into LDS (as fp16) once per workgroup
+    AS_GLOBAL = 0,   // E4M3 codes read from memory (L2) in the main loop
+    AS_COPY = 1,     // E4M3 codes copied into LDS once per workgroup
     AS_BF16 = 2,     // bf16 activation quantized into LDS once per workgroup (fused)
     AS_FP16 = 3,     // fp16 activation quantized into LDS once per workgroup (fused)
 };
@@ -131,8 +108,7 @@ void rowk_f8_kernel(
     constexpr bool IN_LDS = AS != AS_GLOBAL;
     constexpr int DT = AS == AS_BF16 ? DT_BF16 : DT_FP16;
     constexpr int W = NT / 64;
-    // IN_LDS: the MR*K activation values, as fp16 (2 bytes each)
-    extern __shared__ __attribute__((aligned(16))) uint8_t act_lds[];
+    extern __shared__ __attribute__((aligned(16))) uint8_t codes_lds[];   // IN_LDS: MR*K codes
     __shared__ float red[MR][W];
     __shared__ float part[kPartMax];   // S > 1: [m][row of the span][segment]
 
@@ -217,7 +193,7 @@ void rowk_f8_kernel(
 #pragma unroll
         for (int m = 0; m < MR; ++m) s_a[m] = sd;
         const Quotient d(sd);
-        v4i* hl = reinterpret_cast<v4i*>(act_lds);
+        v2i* cl = reinterpret_cast<v2i*>(codes_lds);
         v2i* qg = reinterpret_cast<v2i*>(q_out);
 #pragma unroll
         for (int i = 0; i < VPT; ++i) {
@@ -225,8 +201,7 @@ void rowk_f8_kernel(
             xmax = fmaxf(xmax, vec_absmax<DT>(xr[i]));
             if (v < nunit) {
                 const v2i c = vec_quantize<DT>(xr[i], d);
-                const v2i f0 = fp8x4_to_f16<WF_E4M3>(c[0]), f1 = fp8x4_to_f16<WF_E4M3>(c[1]);
-                hl[v] = v4i{f0[0], f0[1], f1[0], f1[1]};
+                cl[v] = c;
                 if (blockIdx.x == 0) qg[v] = c;
             }
         }
@@ -273,15 +248,14 @@ void rowk_f8_kernel(
 #pragma unroll
         for (int m = 0; m < MR; ++m) s_a[m] = scale_from_amax(amax[m]);
         const Quotient d0(s_a[0]), d1(s_a[MR - 1]);
-        v4i* hl = reinterpret_cast<v4i*>(act_lds);
+        v2i* cl = reinterpret_cast<v2i*>(codes_lds);
         v2i* qg = reinterpret_cast<v2i*>(q_out);
 #pragma unroll
         for (int i = 0; i < VPT; ++i) {
             const int v = tid + i * NT;
             if (v < nunit) {
                 const v2i c = vec_quantize<DT>(xr[i], (MR == 1 || v < nunit / MR) ? d0 : d1);
-                const v2i f0 = fp8x4_to_f16<WF_E4M3>(c[0]), f1 = fp8x4_to_f16<WF_E4M3>(c[1]);
-                hl[v] = v4i{f0[0], f0[1], f1[0], f1[1]};
+                cl[v] = c;
                 if (blockIdx.x == 0) qg[v] = c;
             }
         }
@@ -294,16 +268,11 @@ void rowk_f8_kernel(
 #pragma unroll
         for (int m = 0; m < MR; ++m) s_a[m] = sa_in[rowscale ? m : 0];
         if constexpr (AS == AS_COPY) {
-            v4i* dst = reinterpret_cast<v4i*>(act_lds);
+            v4i* dst = reinterpret_cast<v4i*>(codes_lds);
 #pragma unroll
             for (int i = 0; i < CPT; ++i) {
                 const int v = tid + i * NT;
-                if (v < ncopy) {
-                    int h[8];
-                    fp8x16_to_f16<WF_E4M3>(cr[i], h);
-                    dst[2 * v] = v4i{h[0], h[1], h[2], h[3]};
-                    dst[2 * v + 1] = v4i{h[4], h[5], h[6], h[7]};
-                }
+                if (v < ncopy) dst[v] = cr[i];
             }
             lds_barrier();
         }
@@ -315,16 +284,21 @@ void rowk_f8_kernel(
     };
     const rsrc_t ra = make_rsrc(act, (uint32_t)(MR * K));
 
+    constexpr int WMF = mfma_format(WFMT);   // MFMA format selector of the weight operand
+    // lanes holding the diagonal of the 16x16 MFMA result: lane l holds
+    // D[4 (l/16) + e][l % 16], e = 0..3, so D[i][i] sits in lane l with
+    // e = l % 16 - 4 (l/16) in [0, 4)
+    const int dg = (lane & 15) - 4 * (lane >> 4);
     for (int u = u0; u < nunits; u += W) {
         const int lr = u >> ls;
         const int64_t row = rbeg + lr;
-        float acc[MR];
+        v4f acc[MR];
 #pragma unroll
-        for (int m = 0; m < MR; ++m) acc[m] = 0.0f;
+        for (int m = 0; m < MR; ++m) acc[m] = v4f{0.f, 0.f, 0.f, 0.f};
         for (int kbi = 0; kbi < nkb; ++kbi) {
             const int kb = klo + kbi * 1024 * U;
             if (kbi > 0) load_w(row, kb, true);   // (the first batch is already in flight)
-            int a[MR][U][8];                     // activation values as fp16 pairs
+            v4i a[MR][U];
 #pragma unroll
             for (int uu = 0; uu < U; ++uu) {
                 const int k = kb + uu * 1024 + lane * 16;
@@ -332,35 +306,43 @@ void rowk_f8_kernel(
 #pragma unroll
                 for (int m = 0; m < MR; ++m) {
                     if constexpr (IN_LDS) {
-                        const uint8_t* src = act_lds + 2 * (m * K + (in ? k : 0));
-                        const v4i v0 = *reinterpret_cast<const v4i*>(src);
-                        const v4i v1 = *reinterpret_cast<const v4i*>(src + 16);
-#pragma unroll
-                        for (int j = 0; j < 4; ++j) {
-                            a[m][uu][j] = in ? v0[j] : 0;
-                            a[m][uu][4 + j] = in ? v1[j] : 0;
-                        }
+                        const v4i v = *reinterpret_cast<const v4i*>(codes_lds + m * K + (in ? k : 0));
+                        a[m][uu] = in ? v : v4i{0, 0, 0, 0};
                     } else {
-                        fp8x16_to_f16<WF_E4M3>(buf_load16(ra, in ? (uint32_t)(m * K + k) : kOOB),
-                                               a[m][uu]);
+                        a[m][uu] = buf_load16(ra, in ? (uint32_t)(m * K + k) : kOOB);
                     }
                 }
             }
+            // One MFMA per pair of 1 KiB chunks: lane l supplies the 32 weight
+            // bytes it loaded (row positions kb + uu KiB + 16 l, 16 each) as
+            // its A operand and the activation codes of the same positions as
+            // its B operand.  A lane's A and B bytes meet in the same products,
+            // so D[i][j] sums W at the positions of lanes {i + 16 g} times x at
+            // those of lanes {j + 16 g}, and the diagonal D[i][i], i = 0..15,
+            // holds the dot product over the 64 lanes' positions in 16 parts.
+            // The weights stay in the streaming layout (1 KiB of one row per
+            // load instruction) and nothing is decoded on the VALU.
 #pragma unroll
-            for (int uu = 0; uu < U; ++uu) {
-                int wh[8];
-                fp8x16_to_f16<WFMT>(w[uu], wh);
+            for (int uu = 0; uu < U; uu += 2) {
+                // an odd last chunk pairs with zeros, which the compiler must
+                // not see as constants (its combiner fails on a scaled MFMA
+                // whose operand is partly known)
+                v4i z = {0, 0, 0, 0};
+                asm volatile("" : "+v"(z));
+                const v8i wv = uu + 1 < U ? cat8(w[uu], w[uu + 1]) : cat8(w[uu], z);
 #pragma unroll
-                for (int m = 0; m < MR; ++m)
-#pragma unroll
-                    for (int j = 0; j < 8; ++j)
-                        acc[m] = __builtin_amdgcn_fdot2(__builtin_bit_cast(h2, a[m][uu][j]),
-                                                        __builtin_bit_cast(h2, wh[j]), acc[m], false);
+                for (int m = 0; m < MR; ++m) {
+                    const v8i av = uu + 1 < U ? cat8(a[m][uu], a[m][uu + 1]) : cat8(a[m][uu], z);
+                    acc[m] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(wv, av, acc[m], WMF, 0,
+                                                                              0, 0, 0, 0);
+                }
             }
         }
 #pragma unroll
         for (int m = 0; m < MR; ++m) {
-            const float v = wave_sum(acc[m]);
+            const float dv = dg == 0 ? acc[m][0] : dg == 1 ? acc[m][1] : dg == 2 ? acc[m][2]
+                           : dg == 3 ? acc[m][3] : 0.0f;
+            const float v = wave_sum(dv);
             if (lane == 0) {
                 if (S == 1) y[(size_t)m * N + row] = (uint16_t)f32_to_out_bits<OUTF>(v * out_scale(m, row));
                 else part[(m * nrows + lr) * S + seg] = v;
@@ -502,7 +484,7 @@ void launch_rowk(const void* act, const float* sa_in, const uint8_t* qw, const f
                  uint32_t* state = nullptr)
 {
     using C = RowkCfg<MR>;
-    const size_t lds = AS != AS_GLOBAL ? (size_t)MR * K * 2 : 0;
+    const size_t lds = AS != AS_GLOBAL ? (size_t)MR * K : 0;
     // 16-byte activation vectors per thread: MR*K/8 bf16/fp16 vectors for the
     // fused prologue, MR*K/16 code vectors for AS_COPY (none for AS_GLOBAL)
     const int64_t vecs = AS == AS_GLOBAL ? 0 : (int64_t)MR * K / (AS == AS_COPY ? 16 : 8);
