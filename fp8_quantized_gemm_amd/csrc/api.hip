@@ -6,6 +6,9 @@
 #include <cstdio>
 #include <cstring>
 
+#include <initializer_list>
+#include <utility>
+
 #include "common.hpp"
 #include "fp8q.h"
 
@@ -98,31 +101,42 @@ hipError_t dispatch_fp8(const uint8_t* qa, const float* sa, const uint8_t* qw, c
         if (s_ != FP8Q_OK) return s_;      \
     } while (0)
 
+// True when the n bytes at y share none with the ranges given as (pointer,
+// byte count) pairs.
+bool apart_from(const void* y, int64_t n, std::initializer_list<std::pair<const void*, int64_t>> ranges)
+{
+    const uintptr_t yb = reinterpret_cast<uintptr_t>(y), ye = yb + (uintptr_t)n;
+    for (const auto& rg : ranges) {
+        const uintptr_t b = reinterpret_cast<uintptr_t>(rg.first);
+        if (!(ye <= b || b + (uintptr_t)rg.second <= yb)) return false;
+    }
+    return true;
+}
+
 // quantize + GEMM of fp8_linear / nested_linear_fp8 (pointers already checked)
 fp8q_status linear_common(const char* where, const void* x, int dtype, const uint8_t* qw,
                           const float* sw, uint16_t* y, uint8_t* q, float* scale, float* amax,
                           int64_t M, int64_t N, int64_t K, int wfmt, int outf, int rowscale,
                           hipStream_t st)
 {
-    if (M <= kRowkMaxM && M * K <= kFusedMaxMK)
+    // The one-launch paths read x and store q, *scale and *amax while other
+    // workgroups already store y, and the two-launch path lends y to the
+    // quantizer as scratch: all of them need y apart from those four.  With
+    // an overlap the quantizer runs without scratch and the GEMM follows it.
+    const int64_t sbytes = rowscale ? 4 * M : 4;
+    const bool y_free = apart_from(y, M * N * 2, {{x, M * K * 2}, {q, M * K}, {scale, sbytes}, {amax, sbytes}});
+    if (y_free && M <= kRowkMaxM && M * K <= kFusedMaxMK)
         return finish(where, launch_linear_fused(x, dtype, qw, sw, y, q, scale, amax, (int)M,
                                                  (int)N, (int)K, wfmt, outf, rowscale, st));
+    if (y_free && !rowscale && M > kRowkMaxM && linear_gemv_fused_pays(M, N, K))
+        return finish(where, launch_linear_gemv_fused(x, dtype, qw, sw, y, q, scale, amax, (int)M,
+                                                      (int)N, (int)K, wfmt, outf, st));
     if (rowscale) {
         hipError_t e = launch_quantize_rows(x, dtype, M, K, q, scale, amax, st);
         if (e == hipSuccess)
             e = dispatch_fp8(q, scale, qw, sw, y, (int)M, (int)N, (int)K, wfmt, outf, 1, st);
         return finish(where, e);
     }
-    // y is written only by the GEMM, so until then it can hold the
-    // quantizer's per-workgroup partial maxima, unless it overlaps anything
-    // the quantizer reads or writes (x, q, scale, amax): then the quantizer
-    // folds its maxima with atomics instead
-    const uintptr_t yb = reinterpret_cast<uintptr_t>(y), ye = yb + (uintptr_t)(M * N * 2);
-    auto apart = [&](const void* p, int64_t bytes) {
-        const uintptr_t b = reinterpret_cast<uintptr_t>(p);
-        return ye <= b || b + (uintptr_t)bytes <= yb;
-    };
-    const bool y_free = apart(x, M * K * 2) && apart(q, M * K) && apart(scale, 4) && apart(amax, 4);
     hipError_t e = launch_quantize_scratch(x, dtype, M * K, q, scale, amax,
                                            y_free ? reinterpret_cast<float*>(y) : nullptr,
                                            M * N / 2, st);
@@ -243,7 +257,11 @@ fp8q_status fp8_linear_delayed(const void* x, int dtype, const uint8_t* qw, cons
         return FP8Q_ERR_ALIGN;
     FP8Q_TRY(check_device());
     hipStream_t st = (hipStream_t)stream;
-    if (M <= kRowkMaxM && M * K <= kFusedMaxMK)
+    // the fused kernel also reads and advances history and state while
+    // other workgroups store y
+    if (M <= kRowkMaxM && M * K <= kFusedMaxMK &&
+        apart_from(y, M * N * 2, {{x, M * K * 2}, {q, M * K}, {scale, 4}, {amax, 4},
+                                  {history, history_len * 4}, {state, 16}}))
         return finish("fp8_linear_delayed",
                       launch_linear_fused_delayed(x, dtype, qw, sw, y, q, scale, amax, history,
                                                   history_len, state, (int)M, (int)N, (int)K, st));

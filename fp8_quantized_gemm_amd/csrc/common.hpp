@@ -6,6 +6,8 @@
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
+#include <atomic>
+
 namespace fp8q {
 
 typedef int v2i __attribute__((ext_vector_type(2)));
@@ -410,6 +412,23 @@ hipError_t launch_quantize_delayed(const void* x, int dtype, int64_t n, uint8_t*
                                    float* amax, float* history, int64_t L, uint32_t* state,
                                    hipStream_t stream);
 
+// ---------------------------------------------------------------- launch helpers
+// Raises a kernel's dynamic LDS limit to `lds` bytes once per device (the
+// attribute is set for the current device).  `done` holds one bit per device
+// id below 64; two threads racing on a first call both set it, which is
+// harmless; devices 64 and up set it on every call.
+inline hipError_t set_lds_limit_once(const void* kern, size_t lds, std::atomic<uint64_t>& done)
+{
+    int dev = 0;
+    hipError_t e = hipGetDevice(&dev);
+    if (e != hipSuccess) return e;
+    const uint64_t bit = (dev >= 0 && dev < 64) ? (uint64_t)1 << dev : 0;
+    if (bit != 0 && (done.load(std::memory_order_acquire) & bit) != 0) return hipSuccess;
+    e = hipFuncSetAttribute(kern, hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
+    if (e == hipSuccess && bit != 0) done.fetch_or(bit, std::memory_order_release);
+    return e;
+}
+
 // Row-contiguous decode path for M <= kRowkMaxM (see linear.hip).
 constexpr int kRowkMaxM = 2;
 // Largest M*K the fused decode linear quantizes in LDS.
@@ -437,6 +456,14 @@ hipError_t launch_e4m3_encode_f32(const float* v, uint8_t* q, int64_t n, hipStre
 hipError_t launch_gemv_fp8(const uint8_t* qa, const float* sa, const uint8_t* qw,
                            const float* sw, uint16_t* y, int M, int N, int K, int wfmt,
                            int outf, int rowscale, hipStream_t stream);
+// fp8_linear in one launch for 3 <= M <= 16 (see gemv.hip): quantizer and
+// GEMV fused, per-tensor scales only; M * K at most kFusedGemvMaxMK, taken
+// where linear_gemv_fused_pays says so.
+constexpr int64_t kFusedGemvMaxMK = 65536;
+bool linear_gemv_fused_pays(int64_t M, int64_t N, int64_t K);
+hipError_t launch_linear_gemv_fused(const void* x, int dtype, const uint8_t* qw, const float* sw,
+                                    uint16_t* y, uint8_t* q, float* scale, float* amax, int M,
+                                    int N, int K, int wfmt, int outf, hipStream_t stream);
 hipError_t launch_tile_fp8(const uint8_t* qa, const float* sa, const uint8_t* qw,
                            const float* sw, uint16_t* y, int M, int N, int K, int wfmt,
                            int outf, int rowscale, hipStream_t stream);

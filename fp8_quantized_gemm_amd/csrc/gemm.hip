@@ -66,23 +66,6 @@ __device__ __forceinline__ void store_tile(uint16_t* __restrict__ y, const v4f (
     }
 }
 
-// ---------------------------------------------------------------- shared pieces
-// Raises a kernel's dynamic LDS limit to `lds` bytes once per device (the
-// attribute is set for the current device).  `done` holds one bit per device
-// id below 64; two threads racing on a first call both set it, which is
-// harmless; devices 64 and up set it on every call.
-inline hipError_t set_lds_limit_once(const void* kern, size_t lds, std::atomic<uint64_t>& done)
-{
-    int dev = 0;
-    hipError_t e = hipGetDevice(&dev);
-    if (e != hipSuccess) return e;
-    const uint64_t bit = (dev >= 0 && dev < 64) ? (uint64_t)1 << dev : 0;
-    if (bit != 0 && (done.load(std::memory_order_acquire) & bit) != 0) return hipSuccess;
-    e = hipFuncSetAttribute(kern, hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
-    if (e == hipSuccess && bit != 0) done.fetch_or(bit, std::memory_order_release);
-    return e;
-}
-
 // The compiler does not order LDS reads after asynchronous direct-to-LDS
 // loads, so a kernel that uses them waits explicitly (s_waitcnt vmcnt) for
 // its own loads and then synchronizes the workgroup before reading.

@@ -20,6 +20,8 @@
 // [64+16g, 64+16g+16) of each 128-byte K block, so every load instruction of
 // a wave reads 64 contiguous bytes of each of 16 rows.  The result lane l
 // holds D[4g + i][l % 16], i = 0..3.
+#include <algorithm>
+
 #include "common.hpp"
 
 namespace fp8q {
@@ -106,6 +108,181 @@ __global__ __launch_bounds__(WAVES * 64) void gemv_f8_kernel(
     }
 }
 
+// ---------------------------------------------------------------- quantize + FP8 GEMV, one launch
+// The whole linear layer (dynamic per-tensor activation quantization, then
+// the GEMM) for 3 <= M <= 16 and M*K <= kFusedGemvMaxMK, on a grid of at
+// most two workgroups per CU that loop over the 16-row weight tiles t =
+// blockIdx.x, blockIdx.x + gridDim.x, ...  Each workgroup first reads all of
+// x (from L2 after the first
+// ones), reduces its amax and quantizes it into LDS with the standalone
+// quantizer's scale and rounding, so its codes are bit-identical; workgroup 0
+// also stores q, *scale and *amax.  That prologue runs once per workgroup,
+// not once per tile.  The weights stream as in gemv_f8_kernel, with the
+// activation fragments read from LDS.
+//
+// Thread t handles vectors t, t + NT, ... (XV of them at most) of the
+// row-major activation, 8 elements each (K % 16 == 0: a vector never
+// straddles two rows).  Up to four vectors stay in registers from the amax
+// to the quantization; with eight, x is read a second time (L2 hits) to
+// quantize.  Loads return in order, so with one or two vectors the first
+// batch of weight loads is issued right after the activation loads and is
+// in flight during the prologue; with more it follows the prologue (beside
+// the vectors it would not fit in 64 VGPRs, which keeps two workgroups per
+// CU).  Each next tile's first batch is issued before the current tile's
+// epilogue.
+//
+// LDS (at most 80 KiB): the codes, row m at m * K, its 16-byte unit c at
+// unit c ^ (m & 15) within each complete group of 16 units (so the 16 rows
+// of a fragment read fall on different banks); then the wave partials of the
+// epilogue, whose first WAVES floats hold the per-wave maxima of the prologue.
+__device__ __forceinline__ int code_unit(int m, int c, int units)
+{
+    return (c | 15) < units ? c ^ (m & 15) : c;
+}
+
+template <int DT, int WFMT, int OUTF, int WAVES, int U, int XV>
+__global__ __launch_bounds__(WAVES * 64) __attribute__((amdgpu_waves_per_eu(8, 8)))
+void gemv_f8_fused_kernel(
+    const uint16_t* __restrict__ x, const uint8_t* __restrict__ qw, const float* __restrict__ sw,
+    uint16_t* __restrict__ y, uint8_t* __restrict__ q, float* __restrict__ scale,
+    float* __restrict__ amax_out, int M, int N, int K)
+{
+    constexpr int NT = WAVES * 64;
+    constexpr bool kHold = XV <= 4;            // vectors kept from amax to quantization
+    constexpr bool kEarlyW = XV <= 2;          // first weight batch ahead of the prologue
+    extern __shared__ __attribute__((aligned(16))) uint8_t lds[];
+    float(*red)[16][16] = reinterpret_cast<float(*)[16][16]>(lds + M * K);
+    float* const wmax = &red[0][0][0];
+
+    const int tid = threadIdx.x;
+    const int lane = tid & 63;
+    const int wave = tid >> 6;
+    const int r = lane & 15;
+    const int g = lane >> 4;
+    const int tiles = (N + 15) >> 4;
+    const int units = K >> 4;
+
+    const int nvec = (M * K) >> 3;
+    const v4i* xv = reinterpret_cast<const v4i*>(x);
+    auto load_x = [&](v4i (&v)[XV]) {
+#pragma unroll
+        for (int j = 0; j < XV; ++j) {
+            const int i = tid + j * NT;
+            v[j] = i < nvec ? xv[i] : v4i{0, 0, 0, 0};
+        }
+    };
+
+    // weight loads: batch of blocks kb0, kb0 + WAVES, ... of the current tile
+    const uint32_t row_off = (uint32_t)(r * K);   // past the resource for padded rows
+    const int nblk = (K + 127) >> 7;
+    v4i w0[U], w1[U];
+    auto load_w = [&](const rsrc_t& rw, int kb0) {
+#pragma unroll
+        for (int u = 0; u < U; ++u) {
+            const int k0 = (kb0 + u * WAVES) * 128 + g * 16;
+            const int k1 = k0 + 64;
+            w0[u] = buf_load16(rw, k0 < K ? row_off + k0 : kOOB);
+            w1[u] = buf_load16(rw, k1 < K ? row_off + k1 : kOOB);
+        }
+    };
+    auto tile_rsrc = [&](int t) {
+        const int n0 = t * 16;
+        return make_rsrc(qw + (size_t)n0 * K, (uint32_t)(min(16, N - n0) * K));
+    };
+
+    // amax of the whole activation
+    v4i v[XV];
+    load_x(v);
+    __builtin_amdgcn_sched_barrier(0);
+    rsrc_t rw = tile_rsrc(blockIdx.x);
+    if constexpr (kEarlyW) load_w(rw, wave);
+    __builtin_amdgcn_sched_barrier(0);
+    float m = 0.0f;
+#pragma unroll
+    for (int j = 0; j < XV; ++j) m = fmaxf(m, vec_absmax<DT>(v[j]));
+    m = wave_max(m);
+    if (lane == 0) wmax[wave] = m;
+    lds_barrier();
+    float a = wmax[0];
+#pragma unroll
+    for (int w = 1; w < WAVES; ++w) a = fmaxf(a, wmax[w]);
+    const float s = scale_from_amax(a);
+    const Quotient d(s);
+
+    // codes into LDS (and q from workgroup 0)
+    if constexpr (!kHold) load_x(v);
+    const int kv = K >> 3;
+    v2i* const qv = reinterpret_cast<v2i*>(q);
+#pragma unroll
+    for (int j = 0; j < XV; ++j) {
+        const int i = tid + j * NT;
+        if (i < nvec) {
+            const v2i c = vec_quantize<DT>(v[j], d);
+            const int row = i / kv;
+            const int col8 = i - row * kv;     // 8-byte half col8 & 1 of unit col8 >> 1
+            *reinterpret_cast<v2i*>(lds + row * K + code_unit(row, col8 >> 1, units) * 16 +
+                                    (col8 & 1) * 8) = c;
+            if (blockIdx.x == 0) qv[i] = c;
+        }
+        // one vector at a time: interleaving them would need more than 64 VGPRs
+        __builtin_amdgcn_sched_barrier(0);
+    }
+    if (blockIdx.x == 0 && tid == 0) {
+        *scale = s;
+        *amax_out = a;
+    }
+    if constexpr (!kEarlyW) load_w(rw, wave);
+    lds_barrier();
+
+    // activation row r of this lane (rows past M read as zero)
+    const bool arow = r < M;
+    const uint8_t* const ar = lds + (arow ? r : 0) * K;
+    auto afrag = [&](int k) {
+        const int c = k < K ? k >> 4 : 0;
+        const v4i cv = *reinterpret_cast<const v4i*>(ar + code_unit(r, c, units) * 16);
+        return (arow && k < K) ? cv : v4i{0, 0, 0, 0};
+    };
+    const float sc = s * ((sw != nullptr) ? *sw : implied_wscale(WFMT));
+
+    for (int t = blockIdx.x; t < tiles; t += gridDim.x) {
+        v4f acc = {0.f, 0.f, 0.f, 0.f};
+        for (int kb0 = wave;;) {
+            __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+            for (int u = 0; u < U; ++u) {
+                const int k0 = (kb0 + u * WAVES) * 128 + g * 16;
+                acc = mfma_f8<WFMT>(cat(afrag(k0), afrag(k0 + 64)), cat(w0[u], w1[u]), acc);
+            }
+            kb0 += WAVES * U;
+            if (kb0 >= nblk) break;
+            // the next batch reuses the registers of this one
+            __builtin_amdgcn_sched_barrier(0);
+            load_w(rw, kb0);
+        }
+#pragma unroll
+        for (int i = 0; i < 4; ++i) red[wave][4 * g + i][r] = acc[i];
+        __builtin_amdgcn_sched_barrier(0);
+        // the next tile's first batch goes out before this tile's epilogue
+        const int tn = t + (int)gridDim.x;
+        if (tn < tiles) {
+            rw = tile_rsrc(tn);
+            load_w(rw, wave);
+        }
+        lds_barrier();
+        const int n0 = t * 16;
+        const int rows = min(16, N - n0);
+        for (int e = tid; e < M * 16; e += NT) {
+            const int mm = e >> 4, c = e & 15;
+            if (c >= rows) continue;
+            float vsum = red[0][mm][c];
+#pragma unroll
+            for (int w = 1; w < WAVES; ++w) vsum += red[w][mm][c];
+            y[(size_t)mm * N + n0 + c] = (uint16_t)f32_to_out_bits<OUTF>(vsum * sc);
+        }
+        lds_barrier();                         // red is free for the next tile
+    }
+}
+
 // ---------------------------------------------------------------- NestedFP FP16 GEMV
 // y[m, n] = fp16( sum_k a[m,k] * fp16((hi[n,k] << 8) | lo[n,k]) ).
 // A K block is 64 elements: lane group g takes elements [16g, 16g+16) (16
@@ -184,6 +361,19 @@ __global__ __launch_bounds__(WAVES * 64) void gemv_nested16_kernel(
 // projections); the NestedFP FP16 GEMV keeps 4 waves of 4 blocks.
 constexpr int kGemvWaves = 16;
 constexpr int kGemvUnroll = 2;
+// workgroups of the one-launch linear: two per CU of an MI355X at most, the
+// 16-row tiles spread evenly over them
+constexpr int kGemvSlots = 2 * 256;
+inline int64_t gemv_tiles_per_workgroup(int64_t N)
+{
+    const int64_t tiles = (N + 15) / 16;
+    return (tiles + kGemvSlots - 1) / kGemvSlots;
+}
+inline int64_t gemv_grid(int64_t N)
+{
+    const int64_t per = gemv_tiles_per_workgroup(N);
+    return ((N + 15) / 16 + per - 1) / per;
+}
 constexpr int kNestedWaves = 4;
 constexpr int kNestedUnroll = 4;
 
@@ -206,6 +396,70 @@ hipError_t launch_gemv_fp8(const uint8_t* qa, const float* sa, const uint8_t* qw
     else
         return hipErrorInvalidValue;
     return hipGetLastError();
+}
+
+namespace {
+
+template <int DT, int WFMT, int OUTF, int XV>
+hipError_t launch_gemv_fused_xv(const void* x, const uint8_t* qw, const float* sw, uint16_t* y,
+                                uint8_t* q, float* scale, float* amax, int M, int N, int K,
+                                hipStream_t stream)
+{
+    auto kern = gemv_f8_fused_kernel<DT, WFMT, OUTF, kGemvWaves, kGemvUnroll, XV>;
+    constexpr size_t kRed = (size_t)kGemvWaves * 16 * 16 * 4;
+    static_assert(kFusedGemvMaxMK + kRed <= 80 * 1024, "two workgroups per CU");
+    const size_t lds = (size_t)M * K + kRed;
+    static std::atomic<uint64_t> attr_devices{0};
+    if (const hipError_t e = set_lds_limit_once(reinterpret_cast<const void*>(kern),
+                                                (size_t)kFusedGemvMaxMK + kRed, attr_devices);
+        e != hipSuccess)
+        return e;
+    kern<<<(unsigned)gemv_grid(N), kGemvWaves * 64, lds, stream>>>(static_cast<const uint16_t*>(x), qw,
+                                                                   sw, y, q, scale, amax, M, N, K);
+    return hipGetLastError();
+}
+
+template <int DT, int WFMT, int OUTF>
+hipError_t launch_gemv_fused_fmt(const void* x, const uint8_t* qw, const float* sw, uint16_t* y,
+                                 uint8_t* q, float* scale, float* amax, int M, int N, int K,
+                                 hipStream_t stream)
+{
+    // vectors of 8 elements per thread
+    const int per = (int)(((int64_t)M * K / 8 + kGemvWaves * 64 - 1) / (kGemvWaves * 64));
+    if (per <= 1) return launch_gemv_fused_xv<DT, WFMT, OUTF, 1>(x, qw, sw, y, q, scale, amax, M, N, K, stream);
+    if (per <= 2) return launch_gemv_fused_xv<DT, WFMT, OUTF, 2>(x, qw, sw, y, q, scale, amax, M, N, K, stream);
+    if (per <= 4) return launch_gemv_fused_xv<DT, WFMT, OUTF, 4>(x, qw, sw, y, q, scale, amax, M, N, K, stream);
+    return launch_gemv_fused_xv<DT, WFMT, OUTF, 8>(x, qw, sw, y, q, scale, amax, M, N, K, stream);
+}
+
+}  // namespace
+
+bool linear_gemv_fused_pays(int64_t M, int64_t N, int64_t K)
+{
+    // Measured on the Llama-7B decode linears at M = 4, 8, 16: with up to four
+    // activation vectors per thread the one launch beats quantizer + GEMV on
+    // every shape; with eight (x read twice, the first weight batch after the
+    // prologue) only where a workgroup covers three or more tiles.
+    if (M < 3 || M > 16 || (K & 15) != 0) return false;
+    if (M * K <= 4 * 8 * kGemvWaves * 64) return true;
+    return M * K <= kFusedGemvMaxMK && gemv_tiles_per_workgroup(N) >= 3;
+}
+
+hipError_t launch_linear_gemv_fused(const void* x, int dtype, const uint8_t* qw, const float* sw,
+                                    uint16_t* y, uint8_t* q, float* scale, float* amax, int M,
+                                    int N, int K, int wfmt, int outf, hipStream_t stream)
+{
+    static_assert(kFusedGemvMaxMK / 8 <= 8 * kGemvWaves * 64, "XV = 8 covers the largest activation");
+    if (M < 1 || M > 16 || (int64_t)M * K > kFusedGemvMaxMK || (K & 15) != 0) return hipErrorInvalidValue;
+    if (wfmt == WF_E4M3 && outf == OUT_BF16 && dtype == DT_BF16)
+        return launch_gemv_fused_fmt<DT_BF16, WF_E4M3, OUT_BF16>(x, qw, sw, y, q, scale, amax, M, N, K, stream);
+    if (wfmt == WF_E4M3 && outf == OUT_BF16 && dtype == DT_FP16)
+        return launch_gemv_fused_fmt<DT_FP16, WF_E4M3, OUT_BF16>(x, qw, sw, y, q, scale, amax, M, N, K, stream);
+    if (wfmt == WF_E5M2 && outf == OUT_FP16 && dtype == DT_FP16)
+        return launch_gemv_fused_fmt<DT_FP16, WF_E5M2, OUT_FP16>(x, qw, sw, y, q, scale, amax, M, N, K, stream);
+    if (wfmt == WF_E4M3_SC8 && outf == OUT_FP16 && dtype == DT_FP16)
+        return launch_gemv_fused_fmt<DT_FP16, WF_E4M3_SC8, OUT_FP16>(x, qw, sw, y, q, scale, amax, M, N, K, stream);
+    return hipErrorInvalidValue;
 }
 
 hipError_t launch_gemv_nested16(const uint16_t* a, const uint8_t* hi, const uint8_t* lo,

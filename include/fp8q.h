@@ -116,12 +116,15 @@ FP8Q_API fp8q_status fp8_gemm(const uint8_t* qa, const float* sa, const uint8_t*
  *   qw[N,K], *sw in: E4M3 weight codes and scale
  *   y[M,N]   out: bf16 bit patterns
  *   q[M,K], *scale, *amax out: the activation codes, scale and amax
- *   Size rules as fp8_gemm.  For M <= 2 and M*K <= 32768 the whole layer is
- *   one kernel (each workgroup quantizes the activation in LDS); otherwise it
- *   launches the quantizer and then the GEMM; while the quantizer runs, y
- *   (not yet written) may hold its per-workgroup partial maxima, unless y
- *   overlaps x, q, *scale or *amax (then the quantizer uses no scratch).
- *   Overlapping y with qw or sw is not supported.
+ *   Size rules as fp8_gemm.  For M <= 16 with M*K <= 32768, and for
+ *   3 <= M <= 16 with M*K <= 65536 and N > 16384, the whole layer is one
+ *   kernel (each workgroup quantizes the activation in LDS);
+ *   otherwise it launches the quantizer and then the GEMM, and while the
+ *   quantizer runs y (not yet written) may hold its per-workgroup partial
+ *   maxima.  y may overlap x, q,
+ *   *scale or *amax (e.g. in place over x): then the layer always takes the
+ *   two launches and the quantizer uses no scratch.  Overlapping y with qw
+ *   or sw is not supported.
  */
 FP8Q_API fp8q_status fp8_linear(const void* x, int dtype, const uint8_t* qw, const float* sw,
                        uint16_t* y, uint8_t* q, float* scale, float* amax, int64_t M,
@@ -168,7 +171,8 @@ FP8Q_API fp8q_status fp8_gemm_rowwise(const uint8_t* qa, const float* sa, const 
  *   y[M,N]    out: bf16 bit patterns
  *   q[M,K], sa[M], amax[M] out: activation codes, per-token scales and amax
  *   Size rules as fp8_gemm.  For M <= 2 and M*K <= 32768 one kernel (each
- *   workgroup quantizes both rows in LDS); otherwise two launches.
+ *   workgroup quantizes both rows in LDS) unless y overlaps x, q, sa or
+ *   amax; otherwise two launches.
  */
 FP8Q_API fp8q_status fp8_linear_rowwise(const void* x, int dtype, const uint8_t* qw,
                                         const float* sw, uint16_t* y, uint8_t* q, float* sa,
@@ -229,7 +233,8 @@ FP8Q_API fp8q_status fp8_quantize_act_delayed(const void* x, int dtype, int64_t 
  *   activation is quantized as fp8_quantize_act_delayed does, then multiplied
  *   with fp8_gemm; bit-identical to the two calls in sequence.  For M <= 2
  *   and M*K <= 32768 one kernel, whose quantization needs no reduction over
- *   the activation first.  Size rules as fp8_gemm.
+ *   the activation first, unless y overlaps x, q, *scale, *amax, history or
+ *   state (then two launches).  Size rules as fp8_gemm.
  */
 FP8Q_API fp8q_status fp8_linear_delayed(const void* x, int dtype, const uint8_t* qw,
                                         const float* sw, uint16_t* y, uint8_t* q, float* scale,
@@ -288,9 +293,12 @@ FP8Q_API fp8q_status nested_gemm_fp8(const uint8_t* qa, const float* sa, const u
  *   hi[N,K]  in : hi byte plane of the fp16 weights, read as E5M2
  *   y[M,N]   out: fp16 bit patterns
  *   q[M,K], *scale, *amax out: the activation codes, scale and amax
- *   Size rules as fp8_gemm.  As for fp8_linear, M <= 2 with M*K <= 32768 is
- *   one kernel; otherwise the quantizer runs first and may keep its
- *   per-workgroup partial maxima in y (not yet written) unless y overlaps a.
+ *   Size rules as fp8_gemm.  One kernel for the same sizes as fp8_linear
+ *   (M <= 16 with M*K <= 32768, or 3 <= M <= 16 with M*K <= 65536 and
+ *   N > 16384); otherwise the
+ *   quantizer runs first and may keep its per-workgroup partial maxima in y
+ *   (not yet written); y overlapping a, q, *scale or *amax takes the two
+ *   launches without that scratch.
  */
 FP8Q_API fp8q_status nested_linear_fp8(const uint16_t* a, const uint8_t* hi, uint16_t* y,
                               uint8_t* q, float* scale, float* amax, int64_t M, int64_t N,

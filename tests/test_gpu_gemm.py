@@ -203,12 +203,19 @@ def test_deterministic_and_stream_order():
                                    (1, 100, 65536), (2, 50, 33792), (3, 200, 1024), (16, 64, 4096),
                                    (40, 96, 512), (64, 256, 4096), (3, 16, 81920),
                                    (4, 4096, 4096), (8, 1000, 4096), (16, 300, 2048),
-                                   (5, 37, 6544), (3, 12300, 10912)])
+                                   (5, 37, 6544), (3, 12300, 10912), (16, 4096, 4096),
+                                   (7, 333, 9360), (3, 64, 16), (12, 100, 5456), (9, 1000, 7296),
+                                   (4, 22016, 4096), (6, 20007, 5456), (16, 20007, 4096),
+                                   (12, 16401, 5456)])
 def test_linear_matches_quantize_then_gemm(M, N, K, dtype):
-    """fp8_linear (fused for M <= 2, M*K <= 32768) returns the codes, scale and
+    """fp8_linear (one launch for M <= 16 with M*K <= 32768 and for
+    3 <= M <= 16 with M*K <= 65536 and N > 16384: the row kernel for M <= 2,
+    else the quantizing GEMV with 1, 2, 4 or 8 activation vectors per thread,
+    ragged K blocks and up to three 16-row tiles per workgroup; 16x4096x4096,
+    7x333x9360, 12x100x5456 and 9x1000x7296 are past it) returns the codes, scale and
     amax of fp8_quantize_act bit-exactly and the same y as fp8_gemm on them;
-    both agree with the oracle.  Above 32768 elements fp8_linear keeps its
-    amax partials in y when y holds enough floats (64x256x4096) and falls
+    both agree with the oracle.  Past the one-launch sizes fp8_linear keeps
+    its amax partials in y when y holds enough floats (64x256x4096) and falls
     back to the atomic path when it does not (3x16x81920)."""
     seed = synth.seed_for("linear", M, N, K, dtype)
     x = synth.activation(M, K, seed=seed, dtype=dtype, outliers=M > 2)
@@ -231,6 +238,27 @@ def test_linear_matches_quantize_then_gemm(M, N, K, dtype):
     ref, ab = oracle.gemm_fp8_ref(oq.reshape(M, K), os_, oqw.reshape(N, K), osw, ms, ns)
     out = oracle.bf16_decode(host(y)[ms, ns]).astype(np.float64)
     assert_within(out, ref, ab, f"linear {M}x{N}x{K}", "bf16")
+
+
+@pytest.mark.parametrize("M,N,K", [(1, 512, 4096), (2, 8192, 1024), (4, 1024, 4096),
+                                   (16, 2048, 4096), (3, 64, 8192)])
+def test_linear_output_overlapping_input(M, N, K):
+    """y laid over x (in place): the one-launch kernels would store y while
+    other workgroups still read x, so fp8_linear quantizes first and runs the
+    GEMM after; y, q, scale and amax equal those of separate buffers."""
+    seed = synth.seed_for("linear-overlap", M, N, K)
+    x = synth.activation(M, K, seed=seed, outliers=M > 2)
+    w = synth.normal((N, K), 0.02, "fp16", seed=seed + 1)
+    oqw, osw, _ = oracle.quantize(synth.bits(w).ravel(), oracle.FP16)
+    qw, sw = to_dev_u8(oqw.reshape(N, K)), scalar_dev(osw)
+    say("linear overlap", M, N, K)
+    y1, q1, s1, a1 = fp8q.fp8_linear(x.to(DEV), qw, sw)
+    buf = torch.zeros(max(M * K, M * N), dtype=torch.bfloat16, device=DEV)
+    buf[:M * K].copy_(x.reshape(-1).to(DEV))
+    y2, q2, s2, a2 = fp8q.fp8_linear(buf[:M * K].view(M, K), qw, sw, buf[:M * N].view(M, N))
+    torch.cuda.synchronize()
+    assert torch.equal(q1, q2) and torch.equal(s1, s2) and torch.equal(a1, a2)
+    assert torch.equal(y1, y2)
 
 
 # ------------------------------------------------------------------ big-tile path
