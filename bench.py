@@ -332,7 +332,7 @@ def secondary(torch, fp8q, synth, model1, dev, parts=PARTS, graph=True):
     # decode at M = 4, 8 on the same weights (activations re-drawn)
     for M in ((4, 8) if "decode" in parts else ()):
         out[f"decode_m{M}"] = decode_figures(torch, fp8q, with_activations(torch, synth, model1, M,
-                                                                           dev, "x"))
+                                                                           dev, "x"), graph)
         progress(f"decode M={M} done")
     # prefill M = 512, 2048 (activations with 0.1% outlier channels x50)
     for M in ((512, 2048) if "prefill" in parts else ()):
