@@ -391,7 +391,7 @@ def secondary(torch, fp8q, synth, model1, dev, parts=PARTS, graph=True):
             for x, (q, s, a) in zip(blocks, outs):
                 fp8q.fp8_quantize_kv(x, q, s, a)
 
-        dt, _ = time_fn(torch, kv_step, steps=10, warmup=2)
+        dt, _ = time_fn(torch, kv_step, steps=10, warmup=2, graph=graph)
         byts = 3 * sum(x.numel() for x in blocks)
         out["kv_quantize_16x4096x32x128"] = {"GB_per_s": round(byts / dt / 1e9, 1),
                                              "frac_hbm": round(byts / dt / 1e9 / HBM_PEAK_GBS, 4),
@@ -439,7 +439,7 @@ def secondary(torch, fp8q, synth, model1, dev, parts=PARTS, graph=True):
 
         for mode, fn, wbytes in (("fp16", step16, 2), ("fp8", step8, 1),
                                  ("fp16_e4m3split", step16e, 2), ("fp8_e4m3split", step8e, 1)):
-            dt, _ = time_fn(torch, fn, steps=5, warmup=2)
+            dt, _ = time_fn(torch, fn, steps=5, warmup=2, graph=graph)
             byts = sum(wbytes * N * K + 2 * M * K + 2 * M * N for K, N, _, _ in nested)
             if mode.startswith("fp8"):
                 byts = sum(N * K + M * K + 2 * M * N + 3 * M * K for K, N, _, _ in nested)
