@@ -3,8 +3,10 @@ every replay must reproduce the eager results bit-exactly.  Between replays
 the outputs are overwritten eagerly and the device is synchronized, so a
 replay that skipped or reordered work, or a captured memory operation that
 misbehaves on later replays, shows up as a mismatch.  Covers each launch
-pattern of the path: the fused decode linear (M = 1), quantizer + MFMA GEMV
-(M = 4), the two-launch partial-maxima quantizer + tile GEMM (M = 512), the
+pattern of the path: the fused decode linear (M = 1), the one-launch
+quantizing GEMV (M = 4, 8, 16, with one to three tiles per workgroup), the
+partial-maxima quantizer + MFMA GEMV (M = 4 on the down projection) and
++ tile GEMM (M = 512), the
 stand-alone quantizer's atomic path (its amax is cleared by a kernel, not a
 memset), and both NestedFP modes."""
 import pytest
@@ -54,6 +56,7 @@ def _check_graph(calls, outs):
 
 
 @pytest.mark.parametrize("M,K,N", [(1, 4096, 4096), (4, 4096, 12288), (4, 11008, 4096),
+                                   (8, 4096, 4096), (16, 4096, 22016),
                                    (512, 4096, 12288), (512, 11008, 4096)])
 def test_fp8_linear_graph_replays(M, K, N):
     _, qw, sw = _weights(N, K, seed=synth.seed_for("graph-w", M, K, N))

@@ -228,6 +228,55 @@ def test_fp16_mode_tile_shapes_ragged_sampled(M, N, K):
     assert_within(out, ref, ab, f"fp16 mode {M}x{N}x{K}", "fp16")
 
 
+def test_largest_k_fp16_mode_256_row_tiles():
+    """NestedFP FP16 mode at K = 2^22 on the 256x256 tile (M = 2048, N = 8192
+    pick it): an activation tile of 256 rows spans 256 * 8 MiB = 2^31 bytes,
+    the most a buffer resource of the kernel holds, and its last row starts
+    at 255 * 2^23 bytes.  Activations and weights take the values 0, +1 and -1
+    (fp16 words 0x0000, 0x3C00, 0xBC00: hi plane 0x00 / 0x3C / 0xBC, lo plane
+    zero), so every partial sum is an integer far below 2^24, exact in fp32 in
+    any order: 16 x 16 sampled outputs, rows and columns on both sides of tile
+    borders, equal the oracle's exact sums rounded to fp16 bit for bit.  About
+    86 GB of device memory, built on the device in chunks."""
+    M, N, K = 2048, 8192, 1 << 22
+    gen = torch.Generator(device=DEV)
+    gen.manual_seed(synth.seed_for("nested-kmax-256", M, N, K))
+    say("fp16 mode largest K, 256-row tiles", M, N, K)
+    hi = torch.empty((N, K), dtype=torch.uint8, device=DEV)
+    lo = torch.zeros((N, K), dtype=torch.uint8, device=DEV)
+    a = torch.empty((M, K), dtype=torch.float16, device=DEV)
+    for dst, rows, as_bytes in ((hi, N, True), (a, M, False)):
+        for r0 in range(0, rows, 256):
+            t = torch.randint(0, 3, (min(256, rows - r0), K), generator=gen, device=DEV,
+                              dtype=torch.uint8)
+            one, neg = t == 1, t == 2
+            if as_bytes:
+                dst[r0:r0 + t.shape[0]] = one.to(torch.uint8) * 0x3C + neg.to(torch.uint8) * 0xBC
+            else:
+                dst[r0:r0 + t.shape[0]] = one.to(torch.float16) - neg.to(torch.float16)
+            del t, one, neg
+    y = fp8q.nested_gemm_fp16(a, hi, lo)
+    torch.cuda.synchronize()
+    rng = np.random.Generator(np.random.PCG64(K + 7))
+    ms = np.unique(np.concatenate([[0, 255, 256, 1023, 1024, M - 1], rng.integers(0, M, 10)]))
+    ns = np.unique(np.concatenate([[0, 255, 256, 4096, N - 1], rng.integers(0, N, 11)]))
+    mi = torch.from_numpy(ms).to(DEV)
+    ni = torch.from_numpy(ns).to(DEV)
+    a_rows = synth.bits(a.index_select(0, mi).cpu())
+    hi_rows = hi.index_select(0, ni).cpu().numpy()
+    lo_rows = lo.index_select(0, ni).cpu().numpy()
+    yb = host(y)
+    del a, hi, lo, y
+    torch.cuda.empty_cache()
+    pm = np.repeat(np.arange(ms.size), ns.size)
+    pn = np.tile(np.arange(ns.size), ms.size)
+    ref, _ = oracle.nested_fp16_ref(a_rows, hi_rows, lo_rows, pm, pn)
+    assert np.all(ref == np.round(ref)) and np.all(np.abs(ref) < 2 ** 24)
+    want = ref.astype(np.float16).view(np.uint16)
+    got = yb[ms[pm], ns[pn]]
+    assert np.array_equal(got, want), f"{int(np.sum(got != want))} of {got.size} outputs differ"
+
+
 def test_largest_k_fp16_mode_sampled():
     """NestedFP FP16 mode at K = 2^22 (activation rows of 8 MiB, tile path):
     sampled outputs within tolerance of the fp64 checker."""
