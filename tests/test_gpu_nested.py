@@ -178,10 +178,13 @@ def test_fp8_mode_large_grid_sampled():
                                    (1, 64, 16384), (1, 64, 16400), (1, 512, 2048), (3, 16, 81920),
                                    (1, 5120, 8192), (1, 24576, 4096), (1, 25088, 4096), (1, 10240, 5120),
                                    (1, 5120, 3072), (1, 40960, 5120), (64, 256, 4096), (256, 1000, 4112),
-                                   (4, 1000, 4096), (16, 300, 2048), (3, 50, 10912)])
+                                   (4, 1000, 4096), (16, 300, 2048), (3, 50, 10912),
+                                   (16, 16400, 4096)])
 def test_fp8_mode_linear_matches_quantize_then_gemm(M, N, K):
-    """nested_linear_fp8 (one fused kernel for M <= 2 with M*K <= 32768, the
-    two-launch quantizer with partial maxima in y otherwise) writes the same
+    """nested_linear_fp8 (one launch for M <= 2 with M*K <= 32768 and for
+    3 <= M <= 16 with M*K <= 32768, or up to 65536 with N > 16384 (16x16400x4096,
+    the activation read twice); the two-launch quantizer with partial maxima in
+    y otherwise) writes the same
     codes, scale, amax and output bits as fp8_quantize_act followed by
     nested_gemm_fp8; codes equal the oracle's, sampled outputs within the
     GEMM tolerance."""

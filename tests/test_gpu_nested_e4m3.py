@@ -101,7 +101,8 @@ def test_fp8_mode_random_within_tolerance(M, N, K):
     assert_within(out, ref, ab, f"fp8 e4m3 {M}x{N}x{K}", "fp16")
 
 
-@pytest.mark.parametrize("M,N,K", [(1, 4096, 4096), (2, 300, 11008), (5, 1000, 4096), (300, 129, 272)])
+@pytest.mark.parametrize("M,N,K", [(1, 4096, 4096), (2, 300, 11008), (5, 1000, 4096), (300, 129, 272),
+                                   (12, 16401, 5456)])
 def test_linear_fp8_e4m3_matches_quantize_then_gemm(M, N, K):
     w = synth.normal((N, K), 0.02, "fp16", seed=synth.seed_for("e4l", M, N, K), device=DEV)
     a = synth.activation(M, K, seed=synth.seed_for("e4la", M, N, K), dtype="fp16", device=DEV)
