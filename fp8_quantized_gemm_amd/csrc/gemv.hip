@@ -113,12 +113,11 @@ __global__ __launch_bounds__(WAVES * 64) void gemv_f8_kernel(
 // the GEMM) for 3 <= M <= 16 and M*K <= kFusedGemvMaxMK, on a grid of at
 // most two workgroups per CU that loop over the 16-row weight tiles t =
 // blockIdx.x, blockIdx.x + gridDim.x, ...  Each workgroup first reads all of
-// x (from L2 after the first
-// ones), reduces its amax and quantizes it into LDS with the standalone
-// quantizer's scale and rounding, so its codes are bit-identical; workgroup 0
-// also stores q, *scale and *amax.  That prologue runs once per workgroup,
-// not once per tile.  The weights stream as in gemv_f8_kernel, with the
-// activation fragments read from LDS.
+// x (from L2 after the first ones), reduces its amax and quantizes it into
+// LDS with the standalone quantizer's scale and rounding, so its codes are
+// bit-identical; workgroup 0 also stores q, *scale and *amax.  That prologue
+// runs once per workgroup, not once per tile.  The weights stream as in
+// gemv_f8_kernel, with the activation fragments read from LDS.
 //
 // Thread t handles vectors t, t + NT, ... (XV of them at most) of the
 // row-major activation, 8 elements each (K % 16 == 0: a vector never
