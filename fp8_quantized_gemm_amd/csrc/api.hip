@@ -102,8 +102,9 @@ hipError_t dispatch_fp8(const uint8_t* qa, const float* sa, const uint8_t* qw, c
     } while (0)
 
 // True when the n bytes at y share none with the ranges given as (pointer,
-// byte count) pairs.
-bool apart_from(const void* y, int64_t n, std::initializer_list<std::pair<const void*, int64_t>> ranges)
+// byte count) pairs.  Sizes are products of validated dimensions taken in
+// unsigned arithmetic (M * N * 2 can pass 2^63 at the largest M and N).
+bool apart_from(const void* y, uint64_t n, std::initializer_list<std::pair<const void*, uint64_t>> ranges)
 {
     const uintptr_t yb = reinterpret_cast<uintptr_t>(y), ye = yb + (uintptr_t)n;
     for (const auto& rg : ranges) {
@@ -123,8 +124,9 @@ fp8q_status linear_common(const char* where, const void* x, int dtype, const uin
     // workgroups already store y, and the two-launch path lends y to the
     // quantizer as scratch: all of them need y apart from those four.  With
     // an overlap the quantizer runs without scratch and the GEMM follows it.
-    const int64_t sbytes = rowscale ? 4 * M : 4;
-    const bool y_free = apart_from(y, M * N * 2, {{x, M * K * 2}, {q, M * K}, {scale, sbytes}, {amax, sbytes}});
+    const uint64_t um = (uint64_t)M, un = (uint64_t)N, uk = (uint64_t)K;
+    const uint64_t sbytes = rowscale ? 4 * um : 4;
+    const bool y_free = apart_from(y, um * un * 2, {{x, um * uk * 2}, {q, um * uk}, {scale, sbytes}, {amax, sbytes}});
     if (y_free && M <= kRowkMaxM && M * K <= kFusedMaxMK)
         return finish(where, launch_linear_fused(x, dtype, qw, sw, y, q, scale, amax, (int)M,
                                                  (int)N, (int)K, wfmt, outf, rowscale, st));
@@ -260,8 +262,9 @@ fp8q_status fp8_linear_delayed(const void* x, int dtype, const uint8_t* qw, cons
     // the fused kernel also reads and advances history and state while
     // other workgroups store y
     if (M <= kRowkMaxM && M * K <= kFusedMaxMK &&
-        apart_from(y, M * N * 2, {{x, M * K * 2}, {q, M * K}, {scale, 4}, {amax, 4},
-                                  {history, history_len * 4}, {state, 16}}))
+        apart_from(y, (uint64_t)M * (uint64_t)N * 2,
+                   {{x, (uint64_t)(M * K * 2)}, {q, (uint64_t)(M * K)}, {scale, 4}, {amax, 4},
+                    {history, (uint64_t)history_len * 4}, {state, 16}}))
         return finish("fp8_linear_delayed",
                       launch_linear_fused_delayed(x, dtype, qw, sw, y, q, scale, amax, history,
                                                   history_len, state, (int)M, (int)N, (int)K, st));
