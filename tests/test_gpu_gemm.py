@@ -240,6 +240,33 @@ def test_linear_matches_quantize_then_gemm(M, N, K, dtype):
     assert_within(out, ref, ab, f"linear {M}x{N}x{K}", "bf16")
 
 
+@pytest.mark.parametrize("M,N,K", [(1, 1, 16), (2, 17, 4096), (3, 1, 16), (4, 17, 4096),
+                                   (16, 33, 2048), (8, 16400, 8192), (40, 96, 512)])
+@pytest.mark.parametrize("dtype", ["bf16", "fp16"])
+def test_linear_zero_activation(M, N, K, dtype):
+    """An all-zero (and all negative-zero) activation on every launch pattern
+    of fp8_linear (row kernel, one-launch GEMV with one or several tiles per
+    workgroup, tile GEMM, single and ragged output columns): amax 0, scale 1,
+    every code the encoding of the input's signed zero, every output +0, as
+    the oracle gives."""
+    seed = synth.seed_for("linear-zero", M, N, K, dtype)
+    w = synth.normal((N, K), 0.02, "fp16", seed=seed)
+    oqw, osw, _ = oracle.quantize(synth.bits(w).ravel(), oracle.FP16)
+    qw, sw = to_dev_u8(oqw.reshape(N, K)), scalar_dev(osw)
+    tdt = torch.bfloat16 if dtype == "bf16" else torch.float16
+    code = oracle.BF16 if dtype == "bf16" else oracle.FP16
+    for neg in (False, True):
+        x = torch.zeros((M, K), dtype=tdt)
+        if neg:
+            x = -x
+        say("linear zero", M, N, K, dtype, "neg" if neg else "pos")
+        y, q, s, a = fp8q.fp8_linear(x.to(DEV), qw, sw)
+        oq, os_, oa = oracle.quantize(synth.bits(x).ravel(), code)
+        assert float(host(s)[0]) == os_ == 1.0 and float(host(a)[0]) == oa == 0.0
+        assert np.array_equal(host(q).ravel(), oq)
+        assert np.all(host(y) == 0), "outputs must be +0"
+
+
 @pytest.mark.parametrize("M,N,K", [(1, 512, 4096), (2, 8192, 1024), (4, 1024, 4096),
                                    (16, 2048, 4096), (3, 64, 8192)])
 def test_linear_output_overlapping_input(M, N, K):
