@@ -314,10 +314,12 @@ def test_big_tile_identity_returns_every_weight(MK, N):
 
 @pytest.mark.parametrize("M,N,K", [(4096, 4096, 80), (4100, 12300, 48), (2000, 12000, 80),
                                    (2040, 4090, 48), (510, 8190, 80), (200, 22000, 48),
-                                   (639, 5370, 80), (500, 4000, 48), (60, 5000, 80)])
+                                   (639, 5370, 80), (500, 4000, 48), (60, 5000, 80),
+                                   (500, 4000, 272), (512, 4096, 400)])
 def test_big_tile_small_integers_bit_exact(M, N, K):
-    """Small integers through every tile kernel; K = 80 and 48 leave a
-    partial K step (out-of-range units read as zero)."""
+    """Small integers through every tile kernel; K = 80, 48, 272 and 400
+    leave a partial K step (out-of-range units read as zero).  500 x 4000 and
+    512 x 4096 take the 128x64 tile, here over 1, 3 and 4 K steps."""
     rng = np.random.Generator(np.random.PCG64(K + N))
     qa, qw = _small_int(rng, M, N, K)
     say("big small int", M, N, K, "tiles256", _big_tiles(M, N))
