@@ -101,17 +101,49 @@ hipError_t dispatch_fp8(const uint8_t* qa, const float* sa, const uint8_t* qw, c
         if (s_ != FP8Q_OK) return s_;      \
     } while (0)
 
-// True when the n bytes at y share none with the ranges given as (pointer,
-// byte count) pairs.  Sizes are products of validated dimensions taken in
-// unsigned arithmetic (M * N * 2 can pass 2^63 at the largest M and N).
-bool apart_from(const void* y, uint64_t n, std::initializer_list<std::pair<const void*, uint64_t>> ranges)
+// A buffer of a call: base pointer and byte count.  Byte counts are products
+// of validated dimensions taken in unsigned arithmetic (M * N * 2 can pass
+// 2^63 at the largest M and N).
+struct Buf {
+    const void* p;
+    uint64_t n;
+};
+
+bool overlap(const Buf& a, const Buf& b)
 {
-    const uintptr_t yb = reinterpret_cast<uintptr_t>(y), ye = yb + (uintptr_t)n;
-    for (const auto& rg : ranges) {
-        const uintptr_t b = reinterpret_cast<uintptr_t>(rg.first);
-        if (!(ye <= b || b + (uintptr_t)rg.second <= yb)) return false;
+    if (a.n == 0 || b.n == 0) return false;
+    const uintptr_t ab = reinterpret_cast<uintptr_t>(a.p), bb = reinterpret_cast<uintptr_t>(b.p);
+    return ab < bb + (uintptr_t)b.n && bb < ab + (uintptr_t)a.n;
+}
+
+// FP8Q_ERR_OVERLAP when an output shares a byte with another output or with
+// one of the inputs (other workgroups would still read or write those bytes).
+fp8q_status check_apart(std::initializer_list<Buf> outs, std::initializer_list<Buf> ins)
+{
+    for (auto o = outs.begin(); o != outs.end(); ++o) {
+        for (auto o2 = o + 1; o2 != outs.end(); ++o2)
+            if (overlap(*o, *o2)) return FP8Q_ERR_OVERLAP;
+        for (const Buf& i : ins)
+            if (overlap(*o, i)) return FP8Q_ERR_OVERLAP;
     }
-    return true;
+    return FP8Q_OK;
+}
+
+uint64_t u64(int64_t v) { return (uint64_t)v; }
+
+// The buffers of a linear layer (fp8_linear and its variants): outputs q,
+// scale, amax apart from everything; y apart from those and from the weights,
+// but allowed over the activation x (in place).  sbytes: bytes of scale and
+// amax.
+fp8q_status check_linear_apart(const void* x, int64_t xelem, const void* qw, const void* sw,
+                               uint64_t swbytes, const void* y, const void* q, const void* scale,
+                               const void* amax, uint64_t sbytes, int64_t M, int64_t N, int64_t K)
+{
+    const Buf bx{x, u64(M) * u64(K) * u64(xelem)}, bq{q, u64(M) * u64(K)},
+        bw{qw, u64(N) * u64(K)}, bsw{sw, sw ? swbytes : 0}, by{y, u64(M) * u64(N) * 2},
+        bs{scale, sbytes}, ba{amax, sbytes};
+    FP8Q_TRY(check_apart({bq, bs, ba}, {bx, bw, bsw, by}));
+    return check_apart({by}, {bw, bsw});
 }
 
 // quantize + GEMM of fp8_linear / nested_linear_fp8 (pointers already checked)
@@ -120,13 +152,12 @@ fp8q_status linear_common(const char* where, const void* x, int dtype, const uin
                           int64_t M, int64_t N, int64_t K, int wfmt, int outf, int rowscale,
                           hipStream_t st)
 {
-    // The one-launch paths read x and store q, *scale and *amax while other
-    // workgroups already store y, and the two-launch path lends y to the
-    // quantizer as scratch: all of them need y apart from those four.  With
-    // an overlap the quantizer runs without scratch and the GEMM follows it.
-    const uint64_t um = (uint64_t)M, un = (uint64_t)N, uk = (uint64_t)K;
-    const uint64_t sbytes = rowscale ? 4 * um : 4;
-    const bool y_free = apart_from(y, um * un * 2, {{x, um * uk * 2}, {q, um * uk}, {scale, sbytes}, {amax, sbytes}});
+    // The caller has checked that q, *scale and *amax share no byte with any
+    // other buffer and y none with them or the weights.  y may lie over x:
+    // the one-launch paths read x while other workgroups already store y,
+    // and the two-launch path lends y to the quantizer as scratch, so with
+    // that overlap the quantizer runs without scratch and the GEMM follows.
+    const bool y_free = !overlap({y, u64(M) * u64(N) * 2}, {x, u64(M) * u64(K) * 2});
     if (y_free && M <= kRowkMaxM && M * K <= kFusedMaxMK)
         return finish(where, launch_linear_fused(x, dtype, qw, sw, y, q, scale, amax, (int)M,
                                                  (int)N, (int)K, wfmt, outf, rowscale, st));
@@ -163,6 +194,7 @@ const char* fp8q_status_str(int status)
     case FP8Q_ERR_DTYPE: return "unknown dtype";
     case FP8Q_ERR_LAUNCH: return "HIP call or kernel launch failed";
     case FP8Q_ERR_DEVICE: return "current device is not gfx950";
+    case FP8Q_ERR_OVERLAP: return "an output buffer overlaps another buffer of the call";
     default: return "unknown status";
     }
 }
@@ -176,6 +208,7 @@ fp8q_status fp8_quantize_act(const void* x, int dtype, int64_t n, uint8_t* q, fl
     if (dtype != FP8Q_BF16 && dtype != FP8Q_FP16) return FP8Q_ERR_DTYPE;
     if (n < 1 || n > ((int64_t)1 << 40)) return FP8Q_ERR_SHAPE;
     if (!aligned16(x) || !aligned16(q) || !aligned4(scale) || !aligned4(amax)) return FP8Q_ERR_ALIGN;
+    FP8Q_TRY(check_apart({{q, u64(n)}, {scale, 4}, {amax, 4}}, {{x, u64(n) * 2}}));
     FP8Q_TRY(check_device());
     return finish("fp8_quantize_act",
                   launch_quantize(x, dtype, n, q, scale, amax, (hipStream_t)stream));
@@ -188,6 +221,8 @@ fp8q_status fp8_gemm(const uint8_t* qa, const float* sa, const uint8_t* qw, cons
     FP8Q_TRY(check_gemm_sizes(M, N, K));
     if (!aligned16(qa) || !aligned16(qw) || !aligned16(y) || !aligned4(sa) || !aligned4(sw))
         return FP8Q_ERR_ALIGN;
+    FP8Q_TRY(check_apart({{y, u64(M) * u64(N) * 2}},
+                         {{qa, u64(M) * u64(K)}, {sa, 4}, {qw, u64(N) * u64(K)}, {sw, 4}}));
     FP8Q_TRY(check_device());
     return finish("fp8_gemm", dispatch_fp8(qa, sa, qw, sw, y, (int)M, (int)N, (int)K, WF_E4M3,
                                            OUT_BF16, 0, (hipStream_t)stream));
@@ -203,6 +238,7 @@ fp8q_status fp8_linear(const void* x, int dtype, const uint8_t* qw, const float*
     if (!aligned16(x) || !aligned16(qw) || !aligned16(y) || !aligned16(q) || !aligned4(sw) ||
         !aligned4(scale) || !aligned4(amax))
         return FP8Q_ERR_ALIGN;
+    FP8Q_TRY(check_linear_apart(x, 2, qw, sw, 4, y, q, scale, amax, 4, M, N, K));
     FP8Q_TRY(check_device());
     return linear_common("fp8_linear", x, dtype, qw, sw, y, q, scale, amax, M, N, K, WF_E4M3,
                          OUT_BF16, 0, (hipStream_t)stream);
@@ -219,6 +255,8 @@ fp8q_status fp8_quantize_kv(const void* x, int dtype, int64_t tokens, int64_t he
         tokens > ((int64_t)1 << 40) / (heads * head_dim))
         return FP8Q_ERR_SHAPE;
     if (!aligned16(x) || !aligned16(q) || !aligned4(scale) || !aligned4(amax)) return FP8Q_ERR_ALIGN;
+    const uint64_t nkv = u64(tokens) * u64(heads) * u64(head_dim);
+    FP8Q_TRY(check_apart({{q, nkv}, {scale, 4 * u64(heads)}, {amax, 4 * u64(heads)}}, {{x, 2 * nkv}}));
     FP8Q_TRY(check_device());
     return finish("fp8_quantize_kv", launch_quantize_kv(x, dtype, tokens, heads, head_dim, q, scale,
                                                         amax, (hipStream_t)stream));
@@ -238,6 +276,9 @@ fp8q_status fp8_quantize_act_delayed(const void* x, int dtype, int64_t n, uint8_
     if (!aligned16(x) || !aligned16(q) || !aligned4(scale) || !aligned4(amax) ||
         !aligned4(history) || !aligned16(state))
         return FP8Q_ERR_ALIGN;
+    FP8Q_TRY(check_apart({{q, u64(n)}, {scale, 4}, {amax, 4}, {history, 4 * u64(history_len)},
+                          {state, 16}},
+                         {{x, u64(n) * 2}}));
     FP8Q_TRY(check_device());
     return finish("fp8_quantize_act_delayed",
                   launch_quantize_delayed(x, dtype, n, q, scale, amax, history, history_len, state,
@@ -257,14 +298,18 @@ fp8q_status fp8_linear_delayed(const void* x, int dtype, const uint8_t* qw, cons
     if (!aligned16(x) || !aligned16(qw) || !aligned16(y) || !aligned16(q) || !aligned4(sw) ||
         !aligned4(scale) || !aligned4(amax) || !aligned4(history) || !aligned16(state))
         return FP8Q_ERR_ALIGN;
+    FP8Q_TRY(check_linear_apart(x, 2, qw, sw, 4, y, q, scale, amax, 4, M, N, K));
+    {
+        const Buf bh{history, 4 * u64(history_len)}, bst{state, 16};
+        FP8Q_TRY(check_apart({bh, bst}, {{x, u64(M) * u64(K) * 2}, {qw, u64(N) * u64(K)}, {sw, 4},
+                                         {y, u64(M) * u64(N) * 2}, {q, u64(M) * u64(K)},
+                                         {scale, 4}, {amax, 4}}));
+    }
     FP8Q_TRY(check_device());
     hipStream_t st = (hipStream_t)stream;
-    // the fused kernel also reads and advances history and state while
-    // other workgroups store y
+    // the fused kernel reads x while other workgroups store y
     if (M <= kRowkMaxM && M * K <= kFusedMaxMK &&
-        apart_from(y, (uint64_t)M * (uint64_t)N * 2,
-                   {{x, (uint64_t)(M * K * 2)}, {q, (uint64_t)(M * K)}, {scale, 4}, {amax, 4},
-                    {history, (uint64_t)history_len * 4}, {state, 16}}))
+        !overlap({y, u64(M) * u64(N) * 2}, {x, u64(M) * u64(K) * 2}))
         return finish("fp8_linear_delayed",
                       launch_linear_fused_delayed(x, dtype, qw, sw, y, q, scale, amax, history,
                                                   history_len, state, (int)M, (int)N, (int)K, st));
@@ -283,6 +328,8 @@ fp8q_status fp8_quantize_rows(const void* x, int dtype, int64_t rows, int64_t co
     if (rows < 1 || rows > kMaxDim || cols < 16 || (cols % 16) != 0 || cols > kMaxK)
         return FP8Q_ERR_SHAPE;
     if (!aligned16(x) || !aligned16(q) || !aligned4(scale) || !aligned4(amax)) return FP8Q_ERR_ALIGN;
+    FP8Q_TRY(check_apart({{q, u64(rows) * u64(cols)}, {scale, 4 * u64(rows)}, {amax, 4 * u64(rows)}},
+                         {{x, u64(rows) * u64(cols) * 2}}));
     FP8Q_TRY(check_device());
     return finish("fp8_quantize_rows",
                   launch_quantize_rows(x, dtype, rows, cols, q, scale, amax, (hipStream_t)stream));
@@ -296,6 +343,8 @@ fp8q_status fp8_gemm_rowwise(const uint8_t* qa, const float* sa, const uint8_t* 
     FP8Q_TRY(check_gemm_sizes(M, N, K));
     if (!aligned16(qa) || !aligned16(qw) || !aligned16(y) || !aligned4(sa) || !aligned4(sw))
         return FP8Q_ERR_ALIGN;
+    FP8Q_TRY(check_apart({{y, u64(M) * u64(N) * 2}}, {{qa, u64(M) * u64(K)}, {sa, 4 * u64(M)},
+                                                      {qw, u64(N) * u64(K)}, {sw, 4 * u64(N)}}));
     FP8Q_TRY(check_device());
     return finish("fp8_gemm_rowwise", dispatch_fp8(qa, sa, qw, sw, y, (int)M, (int)N, (int)K,
                                                    WF_E4M3, OUT_BF16, 1, (hipStream_t)stream));
@@ -311,6 +360,7 @@ fp8q_status fp8_linear_rowwise(const void* x, int dtype, const uint8_t* qw, cons
     if (!aligned16(x) || !aligned16(qw) || !aligned16(y) || !aligned16(q) || !aligned4(sw) ||
         !aligned4(sa) || !aligned4(amax))
         return FP8Q_ERR_ALIGN;
+    FP8Q_TRY(check_linear_apart(x, 2, qw, sw, 4 * u64(N), y, q, sa, amax, 4 * u64(M), M, N, K));
     FP8Q_TRY(check_device());
     return linear_common("fp8_linear_rowwise", x, dtype, qw, sw, y, q, sa, amax, M, N, K, WF_E4M3,
                          OUT_BF16, 1, (hipStream_t)stream);
@@ -325,6 +375,7 @@ fp8q_status nested_linear_fp8(const uint16_t* a, const uint8_t* hi, uint16_t* y,
     if (!aligned16(a) || !aligned16(hi) || !aligned16(y) || !aligned16(q) || !aligned4(scale) ||
         !aligned4(amax))
         return FP8Q_ERR_ALIGN;
+    FP8Q_TRY(check_linear_apart(a, 2, hi, nullptr, 0, y, q, scale, amax, 4, M, N, K));
     FP8Q_TRY(check_device());
     return linear_common("nested_linear_fp8", a, FP8Q_FP16, hi, nullptr, y, q, scale, amax, M, N,
                          K, WF_E5M2, OUT_FP16, 0, (hipStream_t)stream);
@@ -336,6 +387,7 @@ fp8q_status nested_split(const uint16_t* w, uint8_t* hi, uint8_t* lo, int64_t n,
     if (!w || !hi || !lo) return FP8Q_ERR_NULL;
     if (n < 1 || n > ((int64_t)1 << 40)) return FP8Q_ERR_SHAPE;
     if (!aligned16(w) || !aligned16(hi) || !aligned16(lo)) return FP8Q_ERR_ALIGN;
+    FP8Q_TRY(check_apart({{hi, u64(n)}, {lo, u64(n)}}, {{w, 2 * u64(n)}}));
     FP8Q_TRY(check_device());
     return finish("nested_split", launch_nested_split(w, hi, lo, n, SP_PLAIN, nullptr,
                                                       (hipStream_t)stream));
@@ -347,6 +399,7 @@ fp8q_status nested_rebuild_fp16(const uint8_t* hi, const uint8_t* lo, uint16_t* 
     if (!w || !hi || !lo) return FP8Q_ERR_NULL;
     if (n < 1 || n > ((int64_t)1 << 40)) return FP8Q_ERR_SHAPE;
     if (!aligned16(w) || !aligned16(hi) || !aligned16(lo)) return FP8Q_ERR_ALIGN;
+    FP8Q_TRY(check_apart({{w, 2 * u64(n)}}, {{hi, u64(n)}, {lo, u64(n)}}));
     FP8Q_TRY(check_device());
     return finish("nested_rebuild_fp16",
                   launch_nested_rebuild(hi, lo, w, n, SP_PLAIN, (hipStream_t)stream));
@@ -369,6 +422,8 @@ fp8q_status nested_gemm_fp16(const uint16_t* a, const uint8_t* hi, const uint8_t
     if (!a || !hi || !lo || !y) return FP8Q_ERR_NULL;
     FP8Q_TRY(check_gemm_sizes(M, N, K));
     if (!aligned16(a) || !aligned16(hi) || !aligned16(lo) || !aligned16(y)) return FP8Q_ERR_ALIGN;
+    FP8Q_TRY(check_apart({{y, u64(M) * u64(N) * 2}},
+                         {{a, u64(M) * u64(K) * 2}, {hi, u64(N) * u64(K)}, {lo, u64(N) * u64(K)}}));
     FP8Q_TRY(check_device());
     return finish("nested_gemm_fp16",
                   dispatch_nested16(a, hi, lo, y, M, N, K, SP_PLAIN, (hipStream_t)stream));
@@ -380,6 +435,8 @@ fp8q_status nested_gemm_fp8(const uint8_t* qa, const float* sa, const uint8_t* h
     if (!qa || !sa || !hi || !y) return FP8Q_ERR_NULL;
     FP8Q_TRY(check_gemm_sizes(M, N, K));
     if (!aligned16(qa) || !aligned16(hi) || !aligned16(y) || !aligned4(sa)) return FP8Q_ERR_ALIGN;
+    FP8Q_TRY(check_apart({{y, u64(M) * u64(N) * 2}},
+                         {{qa, u64(M) * u64(K)}, {sa, 4}, {hi, u64(N) * u64(K)}}));
     FP8Q_TRY(check_device());
     return finish("nested_gemm_fp8", dispatch_fp8(qa, sa, hi, nullptr, y, (int)M, (int)N, (int)K,
                                                   WF_E5M2, OUT_FP16, 0, (hipStream_t)stream));
@@ -393,6 +450,8 @@ fp8q_status nested_split_e4m3(const uint16_t* w, uint8_t* hi, uint8_t* lo, int64
     if (!aligned16(w) || !aligned16(hi) || !aligned16(lo) ||
         (out_of_range != nullptr && (reinterpret_cast<uintptr_t>(out_of_range) & 7u) != 0))
         return FP8Q_ERR_ALIGN;
+    FP8Q_TRY(check_apart({{hi, u64(n)}, {lo, u64(n)}, {out_of_range, out_of_range ? 8u : 0u}},
+                         {{w, 2 * u64(n)}}));
     FP8Q_TRY(check_device());
     return finish("nested_split_e4m3",
                   launch_nested_split(w, hi, lo, n, SP_E4M3,
@@ -406,6 +465,7 @@ fp8q_status nested_rebuild_e4m3(const uint8_t* hi, const uint8_t* lo, uint16_t* 
     if (!w || !hi || !lo) return FP8Q_ERR_NULL;
     if (n < 1 || n > ((int64_t)1 << 40)) return FP8Q_ERR_SHAPE;
     if (!aligned16(w) || !aligned16(hi) || !aligned16(lo)) return FP8Q_ERR_ALIGN;
+    FP8Q_TRY(check_apart({{w, 2 * u64(n)}}, {{hi, u64(n)}, {lo, u64(n)}}));
     FP8Q_TRY(check_device());
     return finish("nested_rebuild_e4m3",
                   launch_nested_rebuild(hi, lo, w, n, SP_E4M3, (hipStream_t)stream));
@@ -417,6 +477,8 @@ fp8q_status nested_gemm_fp16_e4m3(const uint16_t* a, const uint8_t* hi, const ui
     if (!a || !hi || !lo || !y) return FP8Q_ERR_NULL;
     FP8Q_TRY(check_gemm_sizes(M, N, K));
     if (!aligned16(a) || !aligned16(hi) || !aligned16(lo) || !aligned16(y)) return FP8Q_ERR_ALIGN;
+    FP8Q_TRY(check_apart({{y, u64(M) * u64(N) * 2}},
+                         {{a, u64(M) * u64(K) * 2}, {hi, u64(N) * u64(K)}, {lo, u64(N) * u64(K)}}));
     FP8Q_TRY(check_device());
     return finish("nested_gemm_fp16_e4m3",
                   dispatch_nested16(a, hi, lo, y, M, N, K, SP_E4M3, (hipStream_t)stream));
@@ -428,6 +490,8 @@ fp8q_status nested_gemm_fp8_e4m3(const uint8_t* qa, const float* sa, const uint8
     if (!qa || !sa || !hi || !y) return FP8Q_ERR_NULL;
     FP8Q_TRY(check_gemm_sizes(M, N, K));
     if (!aligned16(qa) || !aligned16(hi) || !aligned16(y) || !aligned4(sa)) return FP8Q_ERR_ALIGN;
+    FP8Q_TRY(check_apart({{y, u64(M) * u64(N) * 2}},
+                         {{qa, u64(M) * u64(K)}, {sa, 4}, {hi, u64(N) * u64(K)}}));
     FP8Q_TRY(check_device());
     return finish("nested_gemm_fp8_e4m3",
                   dispatch_fp8(qa, sa, hi, nullptr, y, (int)M, (int)N, (int)K, WF_E4M3_SC8,
@@ -443,6 +507,7 @@ fp8q_status nested_linear_fp8_e4m3(const uint16_t* a, const uint8_t* hi, uint16_
     if (!aligned16(a) || !aligned16(hi) || !aligned16(y) || !aligned16(q) || !aligned4(scale) ||
         !aligned4(amax))
         return FP8Q_ERR_ALIGN;
+    FP8Q_TRY(check_linear_apart(a, 2, hi, nullptr, 0, y, q, scale, amax, 4, M, N, K));
     FP8Q_TRY(check_device());
     return linear_common("nested_linear_fp8_e4m3", a, FP8Q_FP16, hi, nullptr, y, q, scale, amax, M,
                          N, K, WF_E4M3_SC8, OUT_FP16, 0, (hipStream_t)stream);
@@ -453,6 +518,7 @@ fp8q_status fp8q_e4m3_encode_f32(const float* v, uint8_t* q, int64_t n, fp8q_str
     if (!v || !q) return FP8Q_ERR_NULL;
     if (n < 1 || n > ((int64_t)1 << 40)) return FP8Q_ERR_SHAPE;
     if (!aligned16(v) || !aligned16(q)) return FP8Q_ERR_ALIGN;
+    FP8Q_TRY(check_apart({{q, u64(n)}}, {{v, 4 * u64(n)}}));
     FP8Q_TRY(check_device());
     return finish("fp8q_e4m3_encode_f32", launch_e4m3_encode_f32(v, q, n, (hipStream_t)stream));
 }

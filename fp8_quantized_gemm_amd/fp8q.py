@@ -58,7 +58,7 @@ for _name, (_res, _args) in _SIGS.items():
     _fn.restype = _res
     _fn.argtypes = _args
 
-ABI_VERSION = 1
+ABI_VERSION = 2
 if lib.fp8q_abi_version() != ABI_VERSION:
     raise ImportError(f"libfp8q ABI {lib.fp8q_abi_version()} != binding ABI {ABI_VERSION}")
 

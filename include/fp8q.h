@@ -26,6 +26,12 @@
  *    amax stay on the device.
  *  - Arguments are validated on the host before any HIP call; on a validation
  *    error nothing is launched.  Base pointers must be 16-byte aligned.
+ *  - No output buffer may share a byte with another buffer of the same call,
+ *    input or output (FP8Q_ERR_OVERLAP): other workgroups still read and
+ *    write those bytes.  Inputs may share memory with each other.  The one
+ *    exception is the y of the linear calls (fp8_linear, fp8_linear_rowwise,
+ *    fp8_linear_delayed, nested_linear_fp8, nested_linear_fp8_e4m3), which
+ *    may lie over their activation input (in place).
  *    A failed launch returns FP8Q_ERR_LAUNCH; faults inside a kernel surface
  *    at the caller's next synchronization, as for any HIP work.
  *  - Calls on different streams are independent (no shared mutable state).
@@ -39,7 +45,7 @@
 extern "C" {
 #endif
 
-#define FP8Q_ABI_VERSION 1
+#define FP8Q_ABI_VERSION 2
 
 typedef enum {
     FP8Q_OK = 0,
@@ -48,7 +54,8 @@ typedef enum {
     FP8Q_ERR_ALIGN = 3,   /* a base pointer is not 16-byte aligned             */
     FP8Q_ERR_DTYPE = 4,   /* unknown input dtype                               */
     FP8Q_ERR_LAUNCH = 5,  /* a HIP call or kernel launch failed                */
-    FP8Q_ERR_DEVICE = 6   /* the current device is not a gfx950 GPU            */
+    FP8Q_ERR_DEVICE = 6,  /* the current device is not a gfx950 GPU            */
+    FP8Q_ERR_OVERLAP = 7  /* an output overlaps another buffer of the call     */
 } fp8q_status;
 
 typedef enum { FP8Q_BF16 = 0, FP8Q_FP16 = 1 } fp8q_dtype;
@@ -121,10 +128,9 @@ FP8Q_API fp8q_status fp8_gemm(const uint8_t* qa, const float* sa, const uint8_t*
  *   kernel (each workgroup quantizes the activation in LDS);
  *   otherwise it launches the quantizer and then the GEMM, and while the
  *   quantizer runs y (not yet written) may hold its per-workgroup partial
- *   maxima.  y may overlap x, q,
- *   *scale or *amax (e.g. in place over x): then the layer always takes the
- *   two launches and the quantizer uses no scratch.  Overlapping y with qw
- *   or sw is not supported.
+ *   maxima.  y may lie over x (in place): then the layer always takes the
+ *   two launches and the quantizer uses no scratch.  Every other overlap of
+ *   an output returns FP8Q_ERR_OVERLAP.
  */
 FP8Q_API fp8q_status fp8_linear(const void* x, int dtype, const uint8_t* qw, const float* sw,
                        uint16_t* y, uint8_t* q, float* scale, float* amax, int64_t M,
@@ -171,8 +177,8 @@ FP8Q_API fp8q_status fp8_gemm_rowwise(const uint8_t* qa, const float* sa, const 
  *   y[M,N]    out: bf16 bit patterns
  *   q[M,K], sa[M], amax[M] out: activation codes, per-token scales and amax
  *   Size rules as fp8_gemm.  For M <= 2 and M*K <= 32768 one kernel (each
- *   workgroup quantizes both rows in LDS) unless y overlaps x, q, sa or
- *   amax; otherwise two launches.
+ *   workgroup quantizes both rows in LDS) unless y lies over x; otherwise
+ *   two launches.
  */
 FP8Q_API fp8q_status fp8_linear_rowwise(const void* x, int dtype, const uint8_t* qw,
                                         const float* sw, uint16_t* y, uint8_t* q, float* sa,
@@ -233,8 +239,9 @@ FP8Q_API fp8q_status fp8_quantize_act_delayed(const void* x, int dtype, int64_t 
  *   activation is quantized as fp8_quantize_act_delayed does, then multiplied
  *   with fp8_gemm; bit-identical to the two calls in sequence.  For M <= 2
  *   and M*K <= 32768 one kernel, whose quantization needs no reduction over
- *   the activation first, unless y overlaps x, q, *scale, *amax, history or
- *   state (then two launches).  Size rules as fp8_gemm.
+ *   the activation first, unless y lies over x (then two launches).  history
+ *   and state, like the outputs, may share no byte with another buffer of
+ *   the call.  Size rules as fp8_gemm.
  */
 FP8Q_API fp8q_status fp8_linear_delayed(const void* x, int dtype, const uint8_t* qw,
                                         const float* sw, uint16_t* y, uint8_t* q, float* scale,
@@ -297,8 +304,8 @@ FP8Q_API fp8q_status nested_gemm_fp8(const uint8_t* qa, const float* sa, const u
  *   (M <= 16 with M*K <= 32768, or 3 <= M <= 16 with M*K <= 65536 and
  *   N > 16384); otherwise the
  *   quantizer runs first and may keep its per-workgroup partial maxima in y
- *   (not yet written); y overlapping a, q, *scale or *amax takes the two
- *   launches without that scratch.
+ *   (not yet written); y lying over a (in place) takes the two launches
+ *   without that scratch.
  */
 FP8Q_API fp8q_status nested_linear_fp8(const uint16_t* a, const uint8_t* hi, uint16_t* y,
                               uint8_t* q, float* scale, float* amax, int64_t M, int64_t N,

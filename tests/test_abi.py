@@ -13,6 +13,7 @@ ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
 HEADER = os.path.join(ROOT, "include", "fp8q.h")
 
 OK, ERR_NULL, ERR_SHAPE, ERR_ALIGN, ERR_DTYPE = 0, 1, 2, 3, 4
+ERR_OVERLAP = 7
 
 P16 = ctypes.c_void_p(0x1000)      # aligned, never dereferenced: validation fails first
 P17 = ctypes.c_void_p(0x1001)
@@ -49,8 +50,8 @@ def test_no_internal_symbols_exported():
 
 
 def test_version_and_status_strings():
-    assert fp8q.lib.fp8q_abi_version() == 1
-    for s in range(7):
+    assert fp8q.lib.fp8q_abi_version() == 2
+    for s in range(8):
         assert fp8q.lib.fp8q_status_str(s)
     assert fp8q.lib.fp8q_status_str(99) == b"unknown status"
 
@@ -188,6 +189,71 @@ GEMM_SIG = [P16, P16, P16, P16, P16]
 ])
 def test_validation_before_any_hip_call(fn, args, status):
     assert getattr(fp8q.lib, fn)(*args) == status
+
+
+# Distinct, aligned, never dereferenced base addresses 64 KiB apart.
+def _at(region, offset=0):
+    return ctypes.c_void_p(0x100000 + region * 0x10000 + offset)
+
+
+A, B, C, D, E, F, G, H = (_at(i) for i in range(8))
+
+
+@pytest.mark.parametrize("fn,args", [
+    # fp8_quantize_act(x, dtype, n, q, scale, amax): q inside x, scale inside q, scale == amax
+    ("fp8_quantize_act", [A, 0, 64, _at(0, 64), C, D, NULL]),
+    ("fp8_quantize_act", [A, 0, 64, B, _at(1, 16), D, NULL]),
+    ("fp8_quantize_act", [A, 0, 64, B, C, C, NULL]),
+    ("fp8_quantize_act", [A, 1, 64, B, _at(0, 124), D, NULL]),
+    # fp8_gemm(qa, sa, qw, sw, y, M, N, K): y over qa, over sw, over the last weight row
+    ("fp8_gemm", [A, B, C, D, A, 1, 1, 16, NULL]),
+    ("fp8_gemm", [A, B, C, D, D, 1, 1, 16, NULL]),
+    ("fp8_gemm", [A, B, C, D, _at(2, 16 * 16), 2, 17, 16, NULL]),
+    # fp8_linear(x, dtype, qw, sw, y, q, scale, amax, M, N, K): y == q, q over x,
+    # y over the weights, amax == scale
+    ("fp8_linear", [A, 0, C, D, B, B, E, F, 1, 1, 16, NULL]),
+    ("fp8_linear", [A, 0, C, D, B, A, E, F, 1, 1, 16, NULL]),
+    ("fp8_linear", [A, 0, C, D, C, G, E, F, 1, 1, 16, NULL]),
+    ("fp8_linear", [A, 0, C, D, B, G, E, E, 1, 1, 16, NULL]),
+    # fp8_quantize_kv(x, dtype, T, H, D, q, scale, amax): q over x, amax inside scale
+    ("fp8_quantize_kv", [A, 0, 4, 2, 8, _at(0, 32), C, D, NULL]),
+    ("fp8_quantize_kv", [A, 0, 4, 2, 8, B, C, _at(2, 4), NULL]),
+    # fp8_quantize_act_delayed(x, dtype, n, q, scale, amax, history, L, state):
+    # history over q, state == scale
+    ("fp8_quantize_act_delayed", [A, 0, 64, B, C, D, _at(1, 32), 4, E, NULL]),
+    ("fp8_quantize_act_delayed", [A, 0, 64, B, E, D, F, 4, E, NULL]),
+    # fp8_linear_delayed(x, dtype, qw, sw, y, q, scale, amax, history, L, state, M, N, K):
+    # history over y, state over x
+    ("fp8_linear_delayed", [A, 0, C, D, B, E, F, G, B, 4, H, 1, 1, 16, NULL]),
+    ("fp8_linear_delayed", [A, 0, C, D, B, E, F, G, H, 4, A, 1, 1, 16, NULL]),
+    # fp8_quantize_rows(x, dtype, rows, cols, q, scale, amax): amax inside scale
+    ("fp8_quantize_rows", [A, 0, 2, 16, B, C, _at(2, 4), NULL]),
+    # fp8_gemm_rowwise(qa, sa, qw, sw, y, M, N, K): y over sw[N]
+    ("fp8_gemm_rowwise", [A, B, C, D, _at(3, 32), 1, 16, 16, NULL]),
+    # fp8_linear_rowwise(x, dtype, qw, sw, y, q, sa, amax, M, N, K): amax inside sa[M]
+    ("fp8_linear_rowwise", [A, 0, C, D, B, E, F, _at(5, 4), 2, 1, 16, NULL]),
+    # nested_split(w, hi, lo, n) / nested_rebuild_fp16(hi, lo, w, n)
+    ("nested_split", [A, _at(0, 64), C, 64, NULL]),
+    ("nested_split", [A, B, B, 64, NULL]),
+    ("nested_rebuild_fp16", [A, B, _at(1, 48), 64, NULL]),
+    ("nested_split_e4m3", [A, B, C, 64, _at(1, 8), NULL]),
+    ("nested_rebuild_e4m3", [A, B, A, 64, NULL]),
+    # nested_gemm_fp16(a, hi, lo, y, M, N, K) / nested_gemm_fp8(qa, sa, hi, y, M, N, K)
+    ("nested_gemm_fp16", [A, B, C, A, 1, 1, 16, NULL]),
+    ("nested_gemm_fp16_e4m3", [A, B, C, C, 1, 1, 16, NULL]),
+    ("nested_gemm_fp8", [A, B, C, C, 1, 1, 16, NULL]),
+    ("nested_gemm_fp8_e4m3", [A, B, C, B, 1, 1, 16, NULL]),
+    # nested_linear_fp8(a, hi, y, q, scale, amax, M, N, K): q over a, y over hi
+    ("nested_linear_fp8", [A, B, C, A, E, F, 1, 1, 16, NULL]),
+    ("nested_linear_fp8_e4m3", [A, B, B, D, E, F, 1, 1, 16, NULL]),
+    # fp8q_e4m3_encode_f32(v, q, n): codes over the values
+    ("fp8q_e4m3_encode_f32", [A, _at(0, 16), 16, NULL]),
+])
+def test_overlapping_outputs_rejected_before_any_hip_call(fn, args):
+    """An output sharing bytes with another buffer of the call is refused
+    with FP8Q_ERR_OVERLAP; nothing is launched (the pointers are never
+    dereferenced)."""
+    assert getattr(fp8q.lib, fn)(*args) == ERR_OVERLAP
 
 
 def test_binding_raises_on_cpu_tensors():

@@ -288,6 +288,23 @@ def test_linear_output_overlapping_input(M, N, K):
     assert torch.equal(y1, y2)
 
 
+def test_linear_output_over_the_codes_is_refused():
+    """y sharing bytes with q: the GEMM would read codes that other workgroups
+    overwrite, so the call is refused (FP8Q_ERR_OVERLAP) and nothing runs."""
+    M, N, K = 4, 64, 256
+    x = synth.activation(M, K, seed=5).to(DEV)
+    qw = torch.zeros((N, K), dtype=torch.uint8, device=DEV)
+    sw = torch.ones(1, dtype=torch.float32, device=DEV)
+    buf = torch.zeros(max(M * K, 2 * M * N), dtype=torch.uint8, device=DEV)
+    q = buf[:M * K].view(M, K)
+    y = buf[:2 * M * N].view(torch.bfloat16).view(M, N)
+    with pytest.raises(fp8q.Fp8qError) as err:
+        fp8q.fp8_linear(x, qw, sw, y, q)
+    assert err.value.status == 7
+    torch.cuda.synchronize()
+    assert int(buf.count_nonzero()) == 0
+
+
 # ------------------------------------------------------------------ big-tile path
 # The tile shape is picked per call from the cost of its rounds of
 # workgroups: 256x256 (4096x4096, 4100x12300), 256x192 (2000x12000,
