@@ -79,12 +79,20 @@ __device__ __forceinline__ float e4m3_saturate(float v)
     return fabsf(v) > 448.0f ? copysignf(448.0f, v) : v;
 }
 
+// Four binary32 values already within [-448, 448] -> four E4M3 codes, value
+// i in byte i.
+__device__ __forceinline__ uint32_t e4m3_pack4_in_range(float a, float b, float c, float d)
+{
+    int r = __builtin_amdgcn_cvt_pk_fp8_f32(a, b, 0, false);
+    r = __builtin_amdgcn_cvt_pk_fp8_f32(c, d, r, true);
+    return (uint32_t)r;
+}
+
 // Four binary32 values -> four E4M3 codes, value i in byte i.
 __device__ __forceinline__ uint32_t e4m3_pack4(float a, float b, float c, float d)
 {
-    int r = __builtin_amdgcn_cvt_pk_fp8_f32(e4m3_saturate(a), e4m3_saturate(b), 0, false);
-    r = __builtin_amdgcn_cvt_pk_fp8_f32(e4m3_saturate(c), e4m3_saturate(d), r, true);
-    return (uint32_t)r;
+    return e4m3_pack4_in_range(e4m3_saturate(a), e4m3_saturate(b), e4m3_saturate(c),
+                               e4m3_saturate(d));
 }
 
 // ---------------------------------------------------------------- quantizer elements
@@ -99,14 +107,21 @@ __device__ __forceinline__ uint32_t e4m3_pack4(float a, float b, float c, float 
 // fp32 divisor significand (checked exhaustively against IEEE division); the
 // argument needs a finite r and an exact residual, which hold for
 // 2^-80 <= s <= 2^120 and every quotient large enough to give a nonzero code.
-// Scales outside that range use the IEEE division.  An exact quotient
-// (e == 0, which includes x = -0) returns q0, keeping the sign of zero.
+// Scales outside that range use the IEEE division.
 //
-// Overflow: where |q0| > 896 the true quotient is beyond 448 as well (q0 is
-// within two ulps of it), so both saturate to the same code and q0 is
-// returned as it is.  The correction step must not run there: with x*r
-// rounded to +-inf (an input spike under a small delayed scale, or an
-// infinite input) the residual is -+inf and inf - inf would give NaN.
+// The quantizer takes sat_div, which returns the quotient already saturated
+// to [-448, 448] in six VALU operations and no branch or select:
+//  - q0 is clamped to [-896, 896] first (a median of three).  Where that
+//    changes q0 the true quotient is beyond 448 as well (q0 is within an ulp
+//    of it) and the result saturates either way; the correction step must
+//    not start from an infinite q0 (an input spike under a small delayed
+//    scale, or an infinite input), where x - q0 s = -+inf and -+inf r +
+//    q0 would give NaN.
+//  - The result takes the sign of x: an exact zero quotient (x = -0) comes
+//    out of the correction step as +0.
+//  - The clamp to [-448, 448] is the saturation; the E4M3 converter then
+//    only rounds.  NaN inputs, outside the quantizer's contract, come out as
+//    whatever code the hardware median gives a NaN operand.
 struct Quotient {
     float s, r;
     bool fast;
@@ -115,11 +130,12 @@ struct Quotient {
         r = 1.0f / s_;
         fast = s_ >= 0x1p-80f && s_ <= 0x1p120f;
     }
-    __device__ __forceinline__ float fast_div(float x) const
+    __device__ __forceinline__ float sat_div(float x) const
     {
-        const float q0 = x * r;
+        const float q0 = __builtin_amdgcn_fmed3f(x * r, -896.0f, 896.0f);
         const float e = __builtin_fmaf(-q0, s, x);
-        return (e == 0.0f || fabsf(q0) > 896.0f) ? q0 : __builtin_fmaf(e, r, q0);
+        const float q = __builtin_copysignf(__builtin_fmaf(e, r, q0), x);
+        return __builtin_amdgcn_fmed3f(q, -448.0f, 448.0f);
     }
 };
 
@@ -149,22 +165,31 @@ __device__ __forceinline__ float vec_absmax(const v2i& v)
     return m;
 }
 
-// 2*NW input halves (NW dwords) -> 2*NW quotients x / s
+// 2*NW input halves (NW dwords) -> their E4M3 codes, four to a dword.  The
+// quotients of the fast path are saturated already; the IEEE division of the
+// other scales saturates in the converter's wrapper.
 template <int DT, int NW>
-__device__ __forceinline__ void vec_divide(const int (&w)[NW], const Quotient& d, float (&f)[2 * NW])
+__device__ __forceinline__ void vec_codes(const int (&w)[NW], const Quotient& d, int (&c)[NW / 2])
 {
+    float f[2 * NW];
     if (d.fast) {
 #pragma unroll
         for (int i = 0; i < NW; ++i) {
-            f[2 * i] = d.fast_div(half_bits_to_f32<DT>((uint32_t)w[i] & 0xffffu));
-            f[2 * i + 1] = d.fast_div(half_bits_to_f32<DT>((uint32_t)w[i] >> 16));
+            f[2 * i] = d.sat_div(half_bits_to_f32<DT>((uint32_t)w[i] & 0xffffu));
+            f[2 * i + 1] = d.sat_div(half_bits_to_f32<DT>((uint32_t)w[i] >> 16));
         }
+#pragma unroll
+        for (int i = 0; i < NW / 2; ++i)
+            c[i] = (int)e4m3_pack4_in_range(f[4 * i], f[4 * i + 1], f[4 * i + 2], f[4 * i + 3]);
     } else {
 #pragma unroll
         for (int i = 0; i < NW; ++i) {
             f[2 * i] = half_bits_to_f32<DT>((uint32_t)w[i] & 0xffffu) / d.s;
             f[2 * i + 1] = half_bits_to_f32<DT>((uint32_t)w[i] >> 16) / d.s;
         }
+#pragma unroll
+        for (int i = 0; i < NW / 2; ++i)
+            c[i] = (int)e4m3_pack4(f[4 * i], f[4 * i + 1], f[4 * i + 2], f[4 * i + 3]);
     }
 }
 
@@ -173,12 +198,9 @@ template <int DT>
 __device__ __forceinline__ v2i vec_quantize(const v4i& v, const Quotient& d)
 {
     const int w[4] = {v[0], v[1], v[2], v[3]};
-    float f[8];
-    vec_divide<DT, 4>(w, d, f);
-    v2i r;
-    r[0] = (int)e4m3_pack4(f[0], f[1], f[2], f[3]);
-    r[1] = (int)e4m3_pack4(f[4], f[5], f[6], f[7]);
-    return r;
+    int c[2];
+    vec_codes<DT, 4>(w, d, c);
+    return v2i{c[0], c[1]};
 }
 
 // 4 input halves -> 4 E4M3 codes (one dword)
@@ -186,16 +208,18 @@ template <int DT>
 __device__ __forceinline__ uint32_t vec_quantize(const v2i& v, const Quotient& d)
 {
     const int w[2] = {v[0], v[1]};
-    float f[4];
-    vec_divide<DT, 2>(w, d, f);
-    return e4m3_pack4(f[0], f[1], f[2], f[3]);
+    int c[1];
+    vec_codes<DT, 2>(w, d, c);
+    return (uint32_t)c[0];
 }
 
 template <int DT>
 __device__ __forceinline__ uint8_t scalar_quantize(uint16_t h, const Quotient& d)
 {
     const float x = half_bits_to_f32<DT>(h);
-    return (uint8_t)(e4m3_pack4(d.fast ? d.fast_div(x) : x / d.s, 0.f, 0.f, 0.f) & 0xffu);
+    const uint32_t c = d.fast ? e4m3_pack4_in_range(d.sat_div(x), 0.f, 0.f, 0.f)
+                              : e4m3_pack4(x / d.s, 0.f, 0.f, 0.f);
+    return (uint8_t)(c & 0xffu);
 }
 
 __device__ __forceinline__ float scale_from_amax(float amax)

@@ -90,6 +90,10 @@ def _stream(t: torch.Tensor):
 def _dev(t: torch.Tensor, name: str, dtype=None, shape=None):
     if not isinstance(t, torch.Tensor) or not t.is_cuda:
         raise TypeError(f"{name} must be a CUDA (HIP) tensor")
+    if t.device.index != torch.cuda.current_device():
+        # the library launches on the current device
+        raise ValueError(f"{name} is on {t.device}, the current device is "
+                         f"cuda:{torch.cuda.current_device()}")
     if dtype is not None and t.dtype != dtype:
         raise TypeError(f"{name} must be {dtype}, got {t.dtype}")
     if not t.is_contiguous():

@@ -13,18 +13,20 @@
  *        prints: <cases> <mismatches>
  *
  *   sat  the E4M3 code (OCP E4M3, round to nearest even, saturating at
- *        +-448, infinities included) of the device routine's result (the
- *        correction step skipped where |q0| > 896 or e == 0) equals the code
- *        of the IEEE quotient: every one of the 65536 bit patterns of a bf16
- *        or fp16 input (infinities and NaNs included; a NaN's sign is left
- *        out of the comparison, as no format rule fixes it) against divisors
- *        s = 2^E (1 + m 2^-23) for E in [e_lo, e_hi] and `count` significands
- *        m spread by `step`.  (Below 2^-10 every value encodes to a signed
- *        zero, so the routine may differ from the quotient there, where the
+ *        +-448, infinities included) of the device routine's result equals
+ *        the code of the IEEE quotient: every non-NaN bit pattern of a bf16
+ *        or fp16 input (infinities included; NaN inputs are outside the
+ *        quantizer's contract) against divisors s = 2^E (1 + m 2^-23) for E
+ *        in [e_lo, e_hi] and `count` significands m spread by `step`.  The
+ *        device routine: q0 = RN(x r) clamped to [-896, 896] (a median of
+ *        three), the correction step from the clamped q0, the sign of x put
+ *        on the result (which keeps -0), then a clamp to [-448, 448] before
+ *        the converter.  (Below 2^-10 every value encodes to a signed zero,
+ *        so the routine may differ from the quotient there, where the
  *        residual underflows.)  The same sweep also counts the code
- *        mismatches of the correction step applied everywhere (no overflow
- *        guard), which must be nonzero wherever the sweep reaches quotients
- *        that overflow binary32.
+ *        mismatches of the correction step from the unclamped q0, which must
+ *        be nonzero wherever the sweep reaches quotients that overflow
+ *        binary32 (x r = inf gives x - inf s = -inf, then -inf r + inf).
  *        usage: quotient_check sat <bf16|fp16> <e_lo> <e_hi> <first s significand> <count> <step>
  *        prints: <cases> <mismatches> <mismatches without the guard>
  */
@@ -76,6 +78,18 @@ static unsigned e4m3_code(float v)
         f = 0;
     }
     return sgn | (unsigned)((e + 7) << 3) | f;
+}
+
+/* v_med3_f32 on non-NaN inputs with lo <= hi */
+static float med3(float a, float lo, float hi) { return fminf(fmaxf(a, lo), hi); }
+
+/* the device routine: x / s saturated to [-448, 448], ready for the converter */
+static float device_quotient(float x, float s, float r)
+{
+    const float q0 = med3(x * r, -896.0f, 896.0f);
+    const float e = fmaf(-q0, s, x);
+    const float q = fmaf(e, r, q0);
+    return med3(copysignf(q, x), -448.0f, 448.0f);
 }
 
 static int same_code(unsigned a, unsigned b)
@@ -130,11 +144,11 @@ static int run_sat(int argc, char** argv)
             const float r = 1.0f / s;
             for (uint32_t h = 0; h < 65536; ++h) {
                 const float x = xs[h];
+                if (isnan(x)) continue;
                 const float q0 = x * r;
                 const float e = fmaf(-q0, s, x);
-                const float corrected = fmaf(e, r, q0);
-                const float dev = (e == 0.0f || fabsf(q0) > 896.0f) ? q0 : corrected;
-                const float unguarded = e == 0.0f ? q0 : corrected;
+                const float unguarded = copysignf(fmaf(e, r, q0), x);
+                const float dev = device_quotient(x, s, r);
                 const unsigned want = e4m3_code(x / s);
                 ++total;
                 if (!same_code(e4m3_code(dev), want)) ++bad;
