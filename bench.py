@@ -368,13 +368,13 @@ def secondary(torch, fp8q, synth, model1, dev, parts=PARTS, graph=True):
         progress("qwen-32b done")
         del mq
     # per-token activation and per-channel weight scales (fp8_linear_rowwise)
-    # on 8 Llama-7B layers: 1.6 GB of E4M3 weights, cold in HBM on every step
+    # on all 32 Llama-7B layers: 6.48 GB of E4M3 weights, cold in HBM on every step
     if "rowwise" in parts:
-        mr = Model(torch, fp8q, synth, M=1, dev=dev, layers=8, tag="w", rowwise=True)
-        out["rowwise_decode_m1"] = dict(decode_figures(torch, fp8q, mr, graph), layers=8)
+        mr = Model(torch, fp8q, synth, M=1, dev=dev, layers=LAYERS, tag="w", rowwise=True)
+        out["rowwise_decode_m1"] = dict(decode_figures(torch, fp8q, mr, graph), layers=LAYERS)
         out["rowwise_prefill_m512"] = dict(prefill_figures(
             torch, fp8q, with_activations(torch, synth, mr, 512, dev, "xp", outliers=True), graph),
-            layers=8)
+            layers=LAYERS)
         progress("per-token / per-channel done")
         del mr
     # FP8 KV cache: the K and V blocks of 8 layers, each 4096 tokens x 32 heads x
