@@ -361,8 +361,15 @@ __global__ __launch_bounds__(WAVES * 64) void gemv_nested16_kernel(
 constexpr int kGemvWaves = 16;
 constexpr int kGemvUnroll = 2;
 // workgroups of the one-launch linear: two per CU of an MI355X at most, the
-// 16-row tiles spread evenly over them
-constexpr int kGemvSlots = 2 * 256;
+// 16-row tiles dealt out to them in turn.  Each workgroup pays the prologue,
+// so the grid is as small as the tiles allow (`per` tiles per workgroup)
+// unless a full grid lowers the most tiles any CU streams: the dispatcher
+// gives every CU one of the first 256 workgroups and one of the rest, so with
+// 2 x 256 workgroups a CU streams at most ceil(tiles / 256) tiles (768 tiles:
+// three per CU, where 384 workgroups of two left half the CUs with four;
+// measured on the QKV projection at M = 4 / 8: 13.5 -> 12.0 / 14.8 -> 13.4 us).
+constexpr int kCUs = 256;                  // compute units of an MI355X
+constexpr int kGemvSlots = 2 * kCUs;
 inline int64_t gemv_tiles_per_workgroup(int64_t N)
 {
     const int64_t tiles = (N + 15) / 16;
@@ -370,8 +377,12 @@ inline int64_t gemv_tiles_per_workgroup(int64_t N)
 }
 inline int64_t gemv_grid(int64_t N)
 {
+    const int64_t tiles = (N + 15) / 16;
     const int64_t per = gemv_tiles_per_workgroup(N);
-    return ((N + 15) / 16 + per - 1) / per;
+    const int64_t tight = (tiles + per - 1) / per;
+    const int64_t most_tight = (tight > kCUs ? 2 : 1) * per;
+    const int64_t most_full = (tiles + kCUs - 1) / kCUs;
+    return most_full < most_tight ? std::min<int64_t>(tiles, kGemvSlots) : tight;
 }
 constexpr int kNestedWaves = 4;
 constexpr int kNestedUnroll = 4;
