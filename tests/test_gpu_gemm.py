@@ -95,8 +95,13 @@ def _small_int(rng, M, N, K):
 
 
 @pytest.mark.parametrize("M,N,K", [(1, 64, 160), (5, 1000, 4096), (16, 48, 11008),
-                                   (17, 64, 160), (100, 300, 4096), (300, 129, 1040)])
+                                   (17, 64, 160), (100, 300, 4096), (300, 129, 1040),
+                                   (16, 16401, 1040), (5, 20007, 272)])
 def test_small_integers_bit_exact(M, N, K):
+    """Exact small-integer sums on every path; 16 x 16401 and 5 x 20007 take
+    the GEMV with two 16-row tiles per workgroup: its last workgroup has a
+    one-row second tile (N = 16401) or a 7-row first tile and an empty second
+    one (N = 20007)."""
     rng = np.random.Generator(np.random.PCG64(M * 7 + N * 3 + K))
     qa, qw = _small_int(rng, M, N, K)
     say("small int", M, N, K)

@@ -73,10 +73,12 @@ def _run(qa, sa, qw, sw, guard=32):
 
 
 # M = 1, 2: row kernel (N = 4096, K = 11008 splits each row over two waves);
-# M = 3..16: GEMV; larger M: tile shapes 64x64 .. 256x256
+# M = 3..16: GEMV (N >= 16384: two 16-row tiles per workgroup, 16417 leaving
+# the last one a one-row tile and an empty one); larger M: tile shapes
+# 64x64 .. 256x256
 SHAPES = [(1, 37, 160), (1, 4096, 11008), (2, 300, 4096), (2, 16, 16384), (1, 5, 65536),
-          (3, 100, 1040), (16, 4100, 4096), (17, 64, 272), (129, 257, 4096), (512, 1000, 4096),
-          (300, 4100, 1040), (2048, 1536, 512)]
+          (3, 100, 1040), (16, 4100, 4096), (7, 16417, 272), (17, 64, 272), (129, 257, 4096),
+          (512, 1000, 4096), (300, 4100, 1040), (2048, 1536, 512)]
 
 
 @pytest.mark.parametrize("M,N,K", SHAPES)
