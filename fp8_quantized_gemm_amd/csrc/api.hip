@@ -277,7 +277,7 @@ fp8q_status fp8_quantize_act_delayed(const void* x, int dtype, int64_t n, uint8_
         !aligned4(history) || !aligned16(state))
         return FP8Q_ERR_ALIGN;
     FP8Q_TRY(check_apart({{q, u64(n)}, {scale, 4}, {amax, 4}, {history, 4 * u64(history_len)},
-                          {state, 16}},
+                          {state, 4 * u64(FP8Q_DELAYED_STATE_WORDS)}},
                          {{x, u64(n) * 2}}));
     FP8Q_TRY(check_device());
     return finish("fp8_quantize_act_delayed",
@@ -300,7 +300,8 @@ fp8q_status fp8_linear_delayed(const void* x, int dtype, const uint8_t* qw, cons
         return FP8Q_ERR_ALIGN;
     FP8Q_TRY(check_linear_apart(x, 2, qw, sw, 4, y, q, scale, amax, 4, M, N, K));
     {
-        const Buf bh{history, 4 * u64(history_len)}, bst{state, 16};
+        const Buf bh{history, 4 * u64(history_len)},
+            bst{state, 4 * u64(FP8Q_DELAYED_STATE_WORDS)};
         FP8Q_TRY(check_apart({bh, bst}, {{x, u64(M) * u64(K) * 2}, {qw, u64(N) * u64(K)}, {sw, 4},
                                          {y, u64(M) * u64(N) * 2}, {q, u64(M) * u64(K)},
                                          {scale, 4}, {amax, 4}}));

@@ -8,6 +8,8 @@
 
 #include <atomic>
 
+#include "fp8q.h"
+
 namespace fp8q {
 
 typedef int v2i __attribute__((ext_vector_type(2)));
@@ -381,32 +383,108 @@ __device__ __forceinline__ int block_sum_int(int v, int* lds)
 //   state[0]    float bits of the scale the next call uses (0: none yet -> 1)
 //   state[1]    float bits of the running max of the current call
 //   state[2]    ring position
-//   state[3]    workgroups of the current call that have arrived
-// state[1] and state[3] are back at 0 when a call ends, so the caller only
-// zero-fills state and history once.  Calls on one state must not overlap.
+//   state[3]    groups of workgroups of the current call that have arrived
+//   state[4]    float bits of max(history)
+//   state[32 (1 + j)], state[32 (1 + j) + 1], j = 0..7: arrivals and running
+//               max of group j (the workgroups blockIdx.x = j, j + 8, ...)
+// Every word but [0] and [2] is back at 0 when a call ends, so the caller
+// only zero-fills state and history once.  Calls on one state must not
+// overlap.
+constexpr int kDsLine = 32;                         // words per 128-byte line
+constexpr int kDsGroups = 8;
+constexpr int kDsStateWords = kDsLine * (1 + kDsGroups);
+static_assert(kDsStateWords == FP8Q_DELAYED_STATE_WORDS, "state layout of fp8q.h");
+
 __device__ __forceinline__ float delayed_scale(const uint32_t* state)
 {
     const float s = __uint_as_float(state[0]);
     return s > 0.0f ? s : 1.0f;
 }
 
-// Run by every thread of the one workgroup that ends a call: history[pos] =
-// amax, the next scale from the maximum of the new history, pos advanced,
-// the accumulators cleared.
-template <int NT>
-__device__ __forceinline__ void delayed_publish(float amax, float* history, int64_t L,
-                                                uint32_t* state, float* lds)
+// The arrival of a workgroup of the current call, run by its thread 0 after
+// the workgroup's last read of state[0]; with fold, m (the workgroup's
+// maximum) is folded into the call's running max state[1] first.  Returns
+// true in the workgroup that arrives last, which then ends the call
+// (delayed_publish); fences keep every fold ahead of its count, so the last
+// arrival sees all of them.  Same-address device-scope atomics serialize on
+// MI355X (about 8 ns each).  With GROUPS = 8 a workgroup counts in the
+// 128-byte line of its group (blockIdx.x % 8) and only the last of each group
+// counts in state[3], so the longest queue is ceil(G / 8) + 8 atomics instead
+// of G, at the price of a second round of dependent atomics: measured on the
+// 512 workgroups of the fused decode kernel the two levels pay, on the 64-256
+// of the grid-stride quantizer one level is faster.
+template <int GROUPS>
+__device__ __forceinline__ bool delayed_arrive(uint32_t* state, float m, bool fold)
+{
+    static_assert(GROUPS == 1 || GROUPS == kDsGroups, "one level or one line per group");
+    const uint32_t G = gridDim.x;
+    if constexpr (GROUPS == 1) {
+        if (fold) {
+            atomicMax(&state[1], __float_as_uint(m));
+            __threadfence();
+        }
+        return atomicAdd(&state[3], 1u) == G - 1;
+    } else {
+        const uint32_t j = blockIdx.x & (kDsGroups - 1);
+        uint32_t* const line = state + kDsLine * (1 + j);
+        if (fold) {
+            atomicMax(&line[1], __float_as_uint(m));
+            __threadfence();
+        }
+        const uint32_t members = (G - j + kDsGroups - 1) / kDsGroups;
+        if (atomicAdd(&line[0], 1u) != members - 1) return false;
+        __threadfence();
+        if (fold) {
+            atomicMax(&state[1], atomicMax(&line[1], 0u));
+            __threadfence();
+        }
+        const uint32_t groups = G < (uint32_t)kDsGroups ? G : (uint32_t)kDsGroups;
+        return atomicAdd(&state[3], 1u) == groups - 1;
+    }
+}
+
+// What the workgroup that ends a call needs of the state as the call found
+// it: every workgroup reads it at its start (nothing changes it before the
+// call ends), so the end of the call waits for no further load.
+struct DelayedView {
+    uint32_t pos;      // ring position
+    float evicted;     // history[pos], the entry this call replaces
+    float hmax;        // max(history) = state[4]
+};
+__device__ __forceinline__ DelayedView delayed_view(const float* history, int64_t L,
+                                                    const uint32_t* state)
 {
     const uint32_t pos = (int64_t)state[2] < L ? state[2] : 0u;   // a corrupted position stays in range
-    float m = 0.0f;
-    for (int64_t i = threadIdx.x; i < L; i += NT) m = fmaxf(m, i == pos ? amax : history[i]);
-    m = block_max<NT>(m, lds);
+    return DelayedView{pos, history[pos], __uint_as_float(state[4])};
+}
+
+// Run by every thread of the one workgroup that ends a call: history[pos] =
+// amax, the next scale from the maximum of the new history, pos advanced,
+// the accumulators cleared.  The new maximum is max(hmax, amax) unless the
+// replaced entry held the maximum and amax is smaller; only then is the
+// history scanned.
+template <int NT>
+__device__ __forceinline__ void delayed_publish(float amax, const DelayedView& v, float* history,
+                                                int64_t L, uint32_t* state, float* lds)
+{
+    float m = fmaxf(v.hmax, amax);
+    if (!(v.evicted < v.hmax || amax >= v.hmax)) {
+        m = 0.0f;
+        for (int64_t i = threadIdx.x; i < L; i += NT) m = fmaxf(m, i == v.pos ? amax : history[i]);
+        m = block_max<NT>(m, lds);
+    }
+    static_assert(NT >= kDsGroups, "one thread per group line");
+    if (threadIdx.x < kDsGroups) {
+        state[kDsLine * (1 + threadIdx.x)] = 0u;
+        state[kDsLine * (1 + threadIdx.x) + 1] = 0u;
+    }
     if (threadIdx.x == 0) {
-        history[pos] = amax;
+        history[v.pos] = amax;
         state[0] = __float_as_uint(scale_from_amax(m));
         state[1] = 0u;
-        state[2] = (int64_t)pos + 1 == L ? 0u : pos + 1;
+        state[2] = (int64_t)v.pos + 1 == L ? 0u : v.pos + 1;
         state[3] = 0u;
+        state[4] = __float_as_uint(m);
     }
 }
 

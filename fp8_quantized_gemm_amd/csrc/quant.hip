@@ -389,10 +389,11 @@ __global__ __launch_bounds__(kBigThreads) void kv_quant_tokens_kernel(
 // (delayed_scale), so every element is quantized as soon as it is loaded and
 // the amax of x is only recorded.  Small n: one workgroup, which ends the
 // call itself.  Larger n: a grid-stride pass in which every workgroup folds
-// its maximum into state[1] with an integer atomicMax on the float bits
-// (monotone for non-negative floats) and then counts itself in state[3]; the
-// workgroup that arrives last publishes the call (delayed_publish).  Nothing
-// waits for another workgroup, so the grid needs no co-residency.
+// its maximum into the call's running max with integer atomicMax on the
+// float bits (monotone for non-negative floats) and counts itself
+// (delayed_arrive); the workgroup that arrives last publishes the call
+// (delayed_publish).  Nothing waits for another workgroup, so the grid needs
+// no co-residency.
 template <int DT>
 __global__ __launch_bounds__(kSmallThreads) void quant_small_delayed_kernel(
     const uint16_t* __restrict__ x, int64_t n, uint8_t* __restrict__ q,
@@ -405,6 +406,7 @@ __global__ __launch_bounds__(kSmallThreads) void quant_small_delayed_kernel(
     const int tail = (int)(n & 7);
     const v4i* xv = reinterpret_cast<const v4i*>(x);
     const float s = delayed_scale(state);
+    const DelayedView dv = delayed_view(history, L, state);
     const Quotient d(s);
     v2i* qv = reinterpret_cast<v2i*>(q);
     float m = 0.0f;
@@ -424,7 +426,7 @@ __global__ __launch_bounds__(kSmallThreads) void quant_small_delayed_kernel(
     }
     const float a = block_max<kSmallThreads>(m, lds);
     __syncthreads();                                   // lds is reused below
-    delayed_publish<kSmallThreads>(a, history, L, state, lds);
+    delayed_publish<kSmallThreads>(a, dv, history, L, state, lds);
     if (tid == 0) {
         *scale = s;
         *amax_out = a;
@@ -440,6 +442,7 @@ __global__ __launch_bounds__(kBigThreads) void quant_delayed_kernel(
     __shared__ float lds[kBigThreads / 64];
     __shared__ int last;
     const float s = delayed_scale(state);
+    const DelayedView dv = delayed_view(history, L, state);
     const Quotient d(s);
     const int64_t nvec = n >> 3;
     const v4i* xv = reinterpret_cast<const v4i*>(x);
@@ -468,16 +471,12 @@ __global__ __launch_bounds__(kBigThreads) void quant_delayed_kernel(
         q[nvec * 8 + threadIdx.x] = scalar_quantize<DT>(th, d);
     }
     m = block_max<kBigThreads>(m, lds);
-    if (threadIdx.x == 0) {
-        atomicMax(&state[1], __float_as_uint(m));
-        __threadfence();                               // the max lands before the arrival
-        last = atomicAdd(&state[3], 1u) == gridDim.x - 1;
-    }
+    if (threadIdx.x == 0) last = delayed_arrive<1>(state, m, true);
     __syncthreads();
     if (last) {
         __threadfence();
         const float a = __uint_as_float(atomicMax(&state[1], 0u));   // every workgroup's max
-        delayed_publish<kBigThreads>(a, history, L, state, lds);
+        delayed_publish<kBigThreads>(a, dv, history, L, state, lds);
         if (threadIdx.x == 0) {
             *scale = s;
             *amax_out = a;

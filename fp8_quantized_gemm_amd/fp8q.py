@@ -58,7 +58,9 @@ for _name, (_res, _args) in _SIGS.items():
     _fn.restype = _res
     _fn.argtypes = _args
 
-ABI_VERSION = 2
+ABI_VERSION = 3
+# words of the delayed-scaling state (FP8Q_DELAYED_STATE_WORDS)
+DELAYED_STATE_WORDS = 288
 if lib.fp8q_abi_version() != ABI_VERSION:
     raise ImportError(f"libfp8q ABI {lib.fp8q_abi_version()} != binding ABI {ABI_VERSION}")
 
@@ -281,11 +283,11 @@ class DelayedScaling:
         if length < 1:
             raise ValueError("the amax history needs at least one entry")
         self.history = torch.zeros(length, dtype=torch.float32, device=device)
-        self.state = torch.zeros(4, dtype=torch.int32, device=device)
+        self.state = torch.zeros(DELAYED_STATE_WORDS, dtype=torch.int32, device=device)
 
     def _args(self):
         return (_dev(self.history, "history", torch.float32), self.history.numel(),
-                _dev(self.state, "state", torch.int32, (4,)))
+                _dev(self.state, "state", torch.int32, (DELAYED_STATE_WORDS,)))
 
     @property
     def next_scale(self) -> float:

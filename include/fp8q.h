@@ -45,7 +45,10 @@
 extern "C" {
 #endif
 
-#define FP8Q_ABI_VERSION 2
+#define FP8Q_ABI_VERSION 3
+
+/* 32-bit words of the delayed-scaling state (see fp8_quantize_act_delayed). */
+#define FP8Q_DELAYED_STATE_WORDS 288
 
 typedef enum {
     FP8Q_OK = 0,
@@ -211,12 +214,17 @@ FP8Q_API fp8q_status fp8_quantize_kv(const void* x, int dtype, int64_t tokens, i
  * once and no reduction precedes the quantization:
  *
  *   history[L]  in/out: the amax of the last L calls on this tensor (ring)
- *   state[4]    in/out: [0] float bits of the scale the next call uses
- *               (0 = no history yet, meaning 1), [1] and [3] accumulators of
- *               a call in progress (0 between calls), [2] ring position
+ *   state[FP8Q_DELAYED_STATE_WORDS]
+ *               in/out: [0] float bits of the scale the next call uses
+ *               (0 = no history yet, meaning 1), [2] ring position, [4] float
+ *               bits of max(history); every other word is an accumulator of a
+ *               call in progress (0 between calls: the workgroups of a call
+ *               count their arrival in eight 128-byte lines, so that their
+ *               atomics do not all queue on one address)
  *   Both are device memory owned by the caller, zero-filled once before the
- *   first call; state is 16-byte aligned.  Calls on one (history, state)
- *   must not overlap in time (issue them on one stream).  1 <= L <= 2^24.
+ *   first call, and changed only by these calls (a saved pair is restored
+ *   whole); state is 16-byte aligned.  Calls on one (history, state) must not
+ *   overlap in time (issue them on one stream).  1 <= L <= 2^24.
  *
  *   Call t: s = scale from state[0] (1 if 0); q_i = E4M3_rne_sat(fl32(x_i / s)),
  *   so values beyond 448 s saturate to +-448; a = max_i |x_i|;

@@ -49,8 +49,15 @@ def test_no_internal_symbols_exported():
     assert exported == set(declared_functions())
 
 
+def _header_define(name):
+    m = re.search(r"^#define\s+" + name + r"\s+(\d+)", open(HEADER).read(), flags=re.M)
+    assert m, name
+    return int(m.group(1))
+
+
 def test_version_and_status_strings():
-    assert fp8q.lib.fp8q_abi_version() == 2
+    assert fp8q.lib.fp8q_abi_version() == _header_define("FP8Q_ABI_VERSION") == 3
+    assert fp8q.DELAYED_STATE_WORDS == _header_define("FP8Q_DELAYED_STATE_WORDS")
     for s in range(8):
         assert fp8q.lib.fp8q_status_str(s)
     assert fp8q.lib.fp8q_status_str(99) == b"unknown status"
@@ -222,6 +229,8 @@ A, B, C, D, E, F, G, H = (_at(i) for i in range(8))
     # history over q, state == scale
     ("fp8_quantize_act_delayed", [A, 0, 64, B, C, D, _at(1, 32), 4, E, NULL]),
     ("fp8_quantize_act_delayed", [A, 0, 64, B, E, D, F, 4, E, NULL]),
+    # the state's last words (FP8Q_DELAYED_STATE_WORDS of them) reach amax
+    ("fp8_quantize_act_delayed", [A, 0, 64, B, C, E, F, 4, _at(3, 0x10000 - 512), NULL]),
     # fp8_linear_delayed(x, dtype, qw, sw, y, q, scale, amax, history, L, state, M, N, K):
     # history over y, state over x
     ("fp8_linear_delayed", [A, 0, C, D, B, E, F, G, B, 4, H, 1, 1, 16, NULL]),

@@ -35,7 +35,10 @@ def _check_state(ds: fp8q.DelayedScaling, od: oracle.DelayedScaling, what):
     assert np.array_equal(host(ds.history), od.history), f"{what}: history"
     st = host(ds.state).view(np.uint32)
     assert st[0] == od.state[0] and st[2] == od.state[2], f"{what}: next scale / position"
-    assert st[1] == 0 and st[3] == 0, f"{what}: accumulators not cleared"
+    assert st[4] == np.max(od.history).astype(np.float32).view(np.uint32), f"{what}: max(history)"
+    acc = st.copy()
+    acc[[0, 2, 4]] = 0
+    assert np.all(acc == 0), f"{what}: accumulators not cleared at {np.nonzero(acc)[0]}"
 
 
 @pytest.mark.parametrize("dtype", ["bf16", "fp16"])

@@ -110,6 +110,23 @@ def test_small_integers_bit_exact(M, N, K):
     assert np.array_equal(y, want)
 
 
+@pytest.mark.parametrize("M,N,K", [(16, 48, 4096), (16, 33, 4112), (9, 40, 16384),
+                                   (9, 40, 16400), (8, 5000, 11008), (13, 2100, 10000),
+                                   (3, 700, 16), (16, 16401, 9232)])
+def test_gemv_shapes_small_integers(M, N, K):
+    """The decode GEMV on shapes around its launch choices: activations of
+    64 Ki and 144 Ki codes and just past them, a K of one 16-byte unit,
+    313 tiles (8 x 5000 x 11008) and 16 x 16401 x 9232 (two 16-row tiles
+    per workgroup, the last one a one-row tile and an empty one).  Exact
+    small-integer sums."""
+    rng = np.random.Generator(np.random.PCG64(M * 11 + N * 5 + K))
+    qa, qw = _small_int(rng, M, N, K)
+    say("gemv shapes", M, N, K)
+    y = _run_gemm(qa, 1.0, qw, 1.0)
+    want = oracle.gemm_fp8_f32(qa, 1.0, qw, 1.0)
+    assert np.array_equal(y, want)
+
+
 # ------------------------------------------------------------------ tolerance
 def _quantized_operands(M, N, K, seed, outliers=False, sigma=0.02):
     x = synth.activation(M, K, seed=seed, outliers=outliers)

@@ -76,7 +76,7 @@ def _quant_case(x: torch.Tensor, what: str, guard: int = 64):
 
 
 SIZES = [1, 7, 8, 9, 1000, 4096, 4103, 32767, 32768, 32769, 8 * 11008, 98303, 98304, 98305,
-         1_000_003]
+         131071, 131072, 131073, 1_000_003]
 
 
 @pytest.mark.parametrize("n", SIZES)

@@ -78,7 +78,8 @@ def _run(qa, sa, qw, sw, guard=32):
 # 64x64 .. 256x256
 SHAPES = [(1, 37, 160), (1, 4096, 11008), (2, 300, 4096), (2, 16, 16384), (1, 5, 65536),
           (3, 100, 1040), (16, 4100, 4096), (7, 16417, 272), (17, 64, 272), (129, 257, 4096),
-          (512, 1000, 4096), (300, 4100, 1040), (2048, 1536, 512)]
+          (512, 1000, 4096), (300, 4100, 1040), (2048, 1536, 512), (8, 520, 11008),
+          (16, 16417, 9232)]
 
 
 @pytest.mark.parametrize("M,N,K", SHAPES)
