@@ -405,39 +405,37 @@ __device__ __forceinline__ float delayed_scale(const uint32_t* state)
 // the workgroup's last read of state[0]; with fold, m (the workgroup's
 // maximum) is folded into the call's running max state[1] first.  Returns
 // true in the workgroup that arrives last, which then ends the call
-// (delayed_publish); fences keep every fold ahead of its count, so the last
-// arrival sees all of them.  Same-address device-scope atomics serialize on
-// MI355X (about 8 ns each).  With GROUPS = 8 a workgroup counts in the
-// 128-byte line of its group (blockIdx.x % 8) and only the last of each group
-// counts in state[3], so the longest queue is ceil(G / 8) + 8 atomics instead
-// of G, at the price of a second round of dependent atomics: measured on the
-// 512 workgroups of the fused decode kernel the two levels pay, on the 64-256
-// of the grid-stride quantizer one level is faster.
+// (delayed_publish).  Only device-scope atomics pass information here, so
+// their order suffices and no fence is needed (a fence would also write back
+// the XCD's L2, behind the codes just stored): each atomic's returned value
+// is consumed before the next one is issued, so a fold is performed before
+// its count, and the last arrival sees every fold.  Same-address device-scope
+// atomics serialize on MI355X (about 8 ns each).  With GROUPS = 8 a workgroup
+// counts in the 128-byte line of its group (blockIdx.x % 8) and only the
+// last of each group counts in state[3], so the longest queue is ceil(G / 8)
+// + 8 atomics instead of G, at the price of a second round of dependent
+// atomics: measured on the 512 workgroups of the fused decode kernel the two
+// levels pay, on the 64-256 of the grid-stride quantizer one level is faster.
+__device__ __forceinline__ void atomic_done(uint32_t v)
+{
+    asm volatile("" ::"v"(v));        // waits for the returned value, i.e. the atomic
+}
+
 template <int GROUPS>
 __device__ __forceinline__ bool delayed_arrive(uint32_t* state, float m, bool fold)
 {
     static_assert(GROUPS == 1 || GROUPS == kDsGroups, "one level or one line per group");
     const uint32_t G = gridDim.x;
     if constexpr (GROUPS == 1) {
-        if (fold) {
-            atomicMax(&state[1], __float_as_uint(m));
-            __threadfence();
-        }
+        if (fold) atomic_done(atomicMax(&state[1], __float_as_uint(m)));
         return atomicAdd(&state[3], 1u) == G - 1;
     } else {
         const uint32_t j = blockIdx.x & (kDsGroups - 1);
         uint32_t* const line = state + kDsLine * (1 + j);
-        if (fold) {
-            atomicMax(&line[1], __float_as_uint(m));
-            __threadfence();
-        }
+        if (fold) atomic_done(atomicMax(&line[1], __float_as_uint(m)));
         const uint32_t members = (G - j + kDsGroups - 1) / kDsGroups;
         if (atomicAdd(&line[0], 1u) != members - 1) return false;
-        __threadfence();
-        if (fold) {
-            atomicMax(&state[1], atomicMax(&line[1], 0u));
-            __threadfence();
-        }
+        if (fold) atomic_done(atomicMax(&state[1], atomicMax(&line[1], 0u)));
         const uint32_t groups = G < (uint32_t)kDsGroups ? G : (uint32_t)kDsGroups;
         return atomicAdd(&state[3], 1u) == groups - 1;
     }
