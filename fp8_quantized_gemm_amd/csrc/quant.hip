@@ -16,6 +16,7 @@
 // common.hpp), so codes are a function of (x, s) alone and independent of the
 // launch shape.
 #include <algorithm>
+#include <type_traits>
 
 #include "common.hpp"
 
@@ -140,62 +141,67 @@ __global__ __launch_bounds__(kBigThreads) void quant_kernel(const uint16_t* __re
 // flight per thread and step, and the quantize pass requests its first two
 // vectors before it reads the partial maxima.  Against 256-thread workgroups
 // with four vectors and up to 2048 workgroups: 2% faster at 512 x 4096, 17%
-// at 2048 x 11008 and 1024 x 25600.
+// at 2048 x 11008 and 1024 x 25600.  Decode-sized activations (up to 65536
+// vectors) instead take one vector per thread of 256-thread workgroups: the
+// 44032 elements of the Llama-7B down projection at M = 4 then spread over 22
+// workgroups instead of 3, since one CU streams only a few tens of GB/s
+// (decode steps at M = 4 / 8 and Qwen-32B M = 16 1.5-5% faster).
 constexpr int kPartThreads = 1024;
 constexpr int kPartUnroll = 2;
 constexpr int kPartMaxGrid = 512;
+constexpr int kPartSmallThreads = 256;
 
-template <int DT>
-__global__ __launch_bounds__(kPartThreads) void amax_partial_kernel(const uint16_t* __restrict__ x,
+template <int DT, int NT, int U>
+__global__ __launch_bounds__(NT) void amax_partial_kernel(const uint16_t* __restrict__ x,
                                                                     int64_t n, float* __restrict__ part)
 {
-    __shared__ float lds[kPartThreads / 64];
+    __shared__ float lds[NT / 64];
     const int64_t nvec = n >> 3;
     const v4i* xv = reinterpret_cast<const v4i*>(x);
-    const int64_t stride = (int64_t)gridDim.x * kPartThreads;
+    const int64_t stride = (int64_t)gridDim.x * NT;
     float m = 0.0f;
-    for (int64_t i = (int64_t)blockIdx.x * kPartThreads + threadIdx.x; i < nvec; i += kPartUnroll * stride) {
-        v4i v[kPartUnroll];
+    for (int64_t i = (int64_t)blockIdx.x * NT + threadIdx.x; i < nvec; i += U * stride) {
+        v4i v[U];
 #pragma unroll
-        for (int u = 0; u < kPartUnroll; ++u)
+        for (int u = 0; u < U; ++u)
             v[u] = i + u * stride < nvec ? xv[i + u * stride] : v4i{0, 0, 0, 0};
 #pragma unroll
-        for (int u = 0; u < kPartUnroll; ++u) m = fmaxf(m, vec_absmax<DT>(v[u]));
+        for (int u = 0; u < U; ++u) m = fmaxf(m, vec_absmax<DT>(v[u]));
     }
     if (blockIdx.x == 0 && threadIdx.x < (int)(n & 7))
         m = fmaxf(m, fabsf(half_bits_to_f32<DT>(x[nvec * 8 + threadIdx.x])));
-    m = block_max<kPartThreads>(m, lds);
+    m = block_max<NT>(m, lds);
     if (threadIdx.x == 0) part[blockIdx.x] = m;
 }
 
-template <int DT>
-__global__ __launch_bounds__(kPartThreads) void quant_partial_kernel(
+template <int DT, int NT, int U>
+__global__ __launch_bounds__(NT) void quant_partial_kernel(
     const uint16_t* __restrict__ x, int64_t n, uint8_t* __restrict__ q, float* __restrict__ scale,
     float* __restrict__ amax_out, const float* __restrict__ part)
 {
-    __shared__ float lds[kPartThreads / 64];
+    __shared__ float lds[NT / 64];
     const int64_t nvec = n >> 3;
     const v4i* xv = reinterpret_cast<const v4i*>(x);
     v2i* qv = reinterpret_cast<v2i*>(q);
-    const int64_t stride = (int64_t)gridDim.x * kPartThreads;
-    int64_t i = (int64_t)blockIdx.x * kPartThreads + threadIdx.x;
-    v4i v[kPartUnroll];
+    const int64_t stride = (int64_t)gridDim.x * NT;
+    int64_t i = (int64_t)blockIdx.x * NT + threadIdx.x;
+    v4i v[U];
     auto load = [&]() {
 #pragma unroll
-        for (int u = 0; u < kPartUnroll; ++u)
+        for (int u = 0; u < U; ++u)
             v[u] = i + u * stride < nvec ? xv[i + u * stride] : v4i{0, 0, 0, 0};
     };
     load();
     float m = 0.0f;
-    for (int j = threadIdx.x; j < (int)gridDim.x; j += kPartThreads) m = fmaxf(m, part[j]);
-    const float a = block_max<kPartThreads>(m, lds);
+    for (int j = threadIdx.x; j < (int)gridDim.x; j += NT) m = fmaxf(m, part[j]);
+    const float a = block_max<NT>(m, lds);
     const float s = scale_from_amax(a);
     const Quotient d(s);
     while (i < nvec) {
 #pragma unroll
-        for (int u = 0; u < kPartUnroll; ++u)
+        for (int u = 0; u < U; ++u)
             if (i + u * stride < nvec) qv[i + u * stride] = vec_quantize<DT>(v[u], d);
-        i += kPartUnroll * stride;
+        i += U * stride;
         if (i < nvec) load();
     }
     if (blockIdx.x == 0) {
@@ -578,19 +584,28 @@ hipError_t launch_quantize_scratch(const void* x, int dtype, int64_t n, uint8_t*
                                    float* amax, float* scratch, int64_t scratch_floats,
                                    hipStream_t stream)
 {
-    const int g = (int)std::min<int64_t>(
-        kPartMaxGrid, std::max<int64_t>(1, ((n >> 3) + kPartThreads * kPartUnroll - 1) /
-                                               (kPartThreads * kPartUnroll)));
+    const int64_t nvec = n >> 3;
+    // decode-sized activations: one vector per thread of 256-thread
+    // workgroups, so that the tensor spreads over many CUs
+    const bool small = nvec <= (int64_t)kPartSmallThreads * kPartMaxGrid / 2;
+    const int64_t per = small ? kPartSmallThreads : (int64_t)kPartThreads * kPartUnroll;
+    const int g = (int)std::min<int64_t>(kPartMaxGrid, std::max<int64_t>(1, (nvec + per - 1) / per));
     if (n <= kSmallN || scratch == nullptr || scratch_floats < g)
         return launch_quantize(x, dtype, n, q, scale, amax, stream);
     const uint16_t* xs = static_cast<const uint16_t*>(x);
-    if (dtype == DT_BF16) {
-        amax_partial_kernel<DT_BF16><<<g, kPartThreads, 0, stream>>>(xs, n, scratch);
-        quant_partial_kernel<DT_BF16><<<g, kPartThreads, 0, stream>>>(xs, n, q, scale, amax, scratch);
-    } else {
-        amax_partial_kernel<DT_FP16><<<g, kPartThreads, 0, stream>>>(xs, n, scratch);
-        quant_partial_kernel<DT_FP16><<<g, kPartThreads, 0, stream>>>(xs, n, q, scale, amax, scratch);
-    }
+    auto go = [&](auto dt, auto nt, auto u) {
+        constexpr int DT = decltype(dt)::value, NT = decltype(nt)::value, U = decltype(u)::value;
+        amax_partial_kernel<DT, NT, U><<<g, NT, 0, stream>>>(xs, n, scratch);
+        quant_partial_kernel<DT, NT, U><<<g, NT, 0, stream>>>(xs, n, q, scale, amax, scratch);
+    };
+    using BF = std::integral_constant<int, DT_BF16>;
+    using FP = std::integral_constant<int, DT_FP16>;
+    using NS = std::integral_constant<int, kPartSmallThreads>;
+    using NB = std::integral_constant<int, kPartThreads>;
+    using U1 = std::integral_constant<int, 1>;
+    using UB = std::integral_constant<int, kPartUnroll>;
+    if (dtype == DT_BF16) small ? go(BF{}, NS{}, U1{}) : go(BF{}, NB{}, UB{});
+    else small ? go(FP{}, NS{}, U1{}) : go(FP{}, NB{}, UB{});
     return hipGetLastError();
 }
 
