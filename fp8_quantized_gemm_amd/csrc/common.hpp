@@ -387,7 +387,7 @@ __device__ __forceinline__ int block_sum_int(int v, int* lds)
 //   state[4]    float bits of max(history)
 //   state[32 (1 + j)], state[32 (1 + j) + 1], j = 0..7: arrivals and running
 //               max of group j (the workgroups blockIdx.x = j, j + 8, ...)
-// Every word but [0] and [2] is back at 0 when a call ends, so the caller
+// Every word but [0], [2] and [4] is back at 0 when a call ends, so the caller
 // only zero-fills state and history once.  Calls on one state must not
 // overlap.
 constexpr int kDsLine = 32;                         // words per 128-byte line
