@@ -17,9 +17,11 @@
 // Operand layout of v_mfma_f32_16x16x128_f8f6f4 (and 16x16x32_f16): lane l
 // supplies row (l % 16) of A and column (l % 16) of B, and the same slice of K
 // for both; lane group g = l / 16 takes bytes [16g, 16g+16) and
-// [64+16g, 64+16g+16) of each 128-byte K block, so every load instruction of
-// a wave reads 64 contiguous bytes of each of 16 rows.  The result lane l
-// holds D[4g + i][l % 16], i = 0..3.
+// [64+16g, 64+16g+16) of each 128-byte K block.  Loaded in that layout, an
+// instruction would read 64 bytes of each of 16 rows, half of every line;
+// the FP8 weights are instead loaded as whole lines and exchanged across
+// lanes into it (wline, w_to_mfma), the activations directly.  The result
+// lane l holds D[4g + i][l % 16], i = 0..3.
 #include <algorithm>
 
 #include "common.hpp"
@@ -38,6 +40,46 @@ __device__ __forceinline__ v4f mfma_f8(const v8i& a, const v8i& b, const v4f& c)
 __device__ __forceinline__ v8i cat(const v4i& lo, const v4i& hi)
 {
     return v8i{lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
+}
+
+// Weight loads of whole 128-byte lines.  For one 128-byte K block of a
+// 16-row tile, load A takes rows 0..7 and load B rows 8..15: lane l reads the
+// 16-byte unit l & 7 of row l >> 3 (A) and the unit ((l & 7) + 4) & 7 of row
+// 8 + (l >> 3) (B), so that each instruction reads eight whole lines and the
+// loads can be non-temporal (the operand layout's 64-byte halves needed the
+// line kept in L2 between the two loads of each line).  WLine holds a lane's
+// byte offsets within the tile and the K offsets of its units.
+struct WLine {
+    uint32_t oa, ob;   // byte offset in the tile of the lane's unit of A / B in block 0
+    int ka, kb;        // K offset of that unit within a block
+};
+__device__ __forceinline__ WLine wline(int lane, int K)
+{
+    const int ua = lane & 7, ub = ((lane & 7) + 4) & 7;
+    return WLine{(uint32_t)((lane >> 3) * K + ua * 16), (uint32_t)(((lane >> 3) + 8) * K + ub * 16),
+                 ua * 16, ub * 16};
+}
+
+// The loaded units into the MFMA operand layout: lane L = r + 16 g gets
+// units g (lo) and 4 + g (hi) of row r.  Rows r < 8 read from A and rows
+// r >= 8 from B; with B's units rotated by four, the lanes that a lo (hi)
+// exchange reads are all distinct, so a per-lane select of A or B on the
+// source side (lanes with l & 4 give B to lo, A to hi) and one ds_bpermute
+// per dword do it: 8 selects and 8 permutes per 2 KiB block.  The result is
+// bit for bit the operand the 64-byte-half loads gave.
+__device__ __forceinline__ v8i w_to_mfma(const v4i& a, const v4i& b, int lane)
+{
+    const int r = lane & 15, g = lane >> 4, up = r >> 3;
+    const int base = (r & 7) * 8 + g;
+    const int alo = (base + 4 * up) << 2, ahi = (base + 4 - 4 * up) << 2;
+    const bool sel = (lane & 4) != 0;
+    v8i w;
+#pragma unroll
+    for (int d = 0; d < 4; ++d) {
+        w[d] = __builtin_amdgcn_ds_bpermute(alo, sel ? b[d] : a[d]);
+        w[4 + d] = __builtin_amdgcn_ds_bpermute(ahi, sel ? a[d] : b[d]);
+    }
+    return w;
 }
 
 // ---------------------------------------------------------------- FP8 GEMV
@@ -75,6 +117,7 @@ __global__ __launch_bounds__(WAVES * 64) void gemv_f8_kernel(
     }
     const rsrc_t ra = make_rsrc(qa, (uint32_t)(M * K));
     const uint32_t row_off = (uint32_t)(r * K);   // past the resource for padded rows
+    const WLine wl = wline(lane, K);
 
     const int nblk = (K + 127) >> 7;
     v4f acc[TPW];
@@ -85,14 +128,17 @@ __global__ __launch_bounds__(WAVES * 64) void gemv_f8_kernel(
         v4i w0[TPW][U], w1[TPW][U], a0[U], a1[U];
 #pragma unroll
         for (int u = 0; u < U; ++u) {
-            const int k0 = (kb0 + u * WAVES) * 128 + g * 16;
+            const int kb = (kb0 + u * WAVES) * 128;
+            const int k0 = kb + g * 16;
             const int k1 = k0 + 64;
             const uint32_t o0 = k0 < K ? row_off + k0 : kOOB;
             const uint32_t o1 = k1 < K ? row_off + k1 : kOOB;
+            const uint32_t pa = kb + wl.ka < K ? wl.oa + kb : kOOB;
+            const uint32_t pb = kb + wl.kb < K ? wl.ob + kb : kOOB;
 #pragma unroll
             for (int t = 0; t < TPW; ++t) {
-                w0[t][u] = buf_load16<CP>(rw[t], o0);
-                w1[t][u] = buf_load16<CP>(rw[t], o1);
+                w0[t][u] = buf_load16<CP>(rw[t], pa);
+                w1[t][u] = buf_load16<CP>(rw[t], pb);
             }
             a0[u] = buf_load16(ra, o0);
             a1[u] = buf_load16(ra, o1);
@@ -103,7 +149,7 @@ __global__ __launch_bounds__(WAVES * 64) void gemv_f8_kernel(
         for (int u = 0; u < U; ++u)
 #pragma unroll
             for (int t = 0; t < TPW; ++t)
-                acc[t] = mfma_f8<WFMT>(cat(a0[u], a1[u]), cat(w0[t][u], w1[t][u]), acc[t]);
+                acc[t] = mfma_f8<WFMT>(cat(a0[u], a1[u]), w_to_mfma(w0[t][u], w1[t][u], lane), acc[t]);
     }
 
     const float s_w = (sw != nullptr) ? *sw : implied_wscale(WFMT);
@@ -190,16 +236,20 @@ void gemv_f8_fused_kernel(
     };
 
     // weight loads: batch of blocks kb0, kb0 + WAVES, ... of the current tile
-    const uint32_t row_off = (uint32_t)(r * K);   // past the resource for padded rows
+    // (whole lines, non-temporal; see wline)
     const int nblk = (K + 127) >> 7;
     v4i w0[U], w1[U];
     auto load_w = [&](const rsrc_t& rw, int kb0) {
+        // the lane's offsets are recomputed for each batch rather than held
+        // across the prologue and the tile loop (which spilled at 64 VGPRs)
+        int l = lane;
+        asm volatile("" : "+v"(l));
+        const WLine wl = wline(l, K);
 #pragma unroll
         for (int u = 0; u < U; ++u) {
-            const int k0 = (kb0 + u * WAVES) * 128 + g * 16;
-            const int k1 = k0 + 64;
-            w0[u] = buf_load16(rw, k0 < K ? row_off + k0 : kOOB);
-            w1[u] = buf_load16(rw, k1 < K ? row_off + k1 : kOOB);
+            const int kb = (kb0 + u * WAVES) * 128;
+            w0[u] = buf_load16<CP_NT>(rw, kb + wl.ka < K ? wl.oa + kb : kOOB);
+            w1[u] = buf_load16<CP_NT>(rw, kb + wl.kb < K ? wl.ob + kb : kOOB);
         }
     };
     auto tile_rsrc = [&](int t) {
@@ -268,7 +318,9 @@ void gemv_f8_fused_kernel(
 #pragma unroll
             for (int u = 0; u < U; ++u) {
                 const int k0 = (kb0 + u * WAVES) * 128 + g * 16;
-                acc = mfma_f8<WFMT>(cat(afrag(k0), afrag(k0 + 64)), cat(w0[u], w1[u]), acc);
+                acc = mfma_f8<WFMT>(cat(afrag(k0), afrag(k0 + 64)), w_to_mfma(w0[u], w1[u], lane), acc);
+                // one block's exchange at a time (64 VGPRs)
+                __builtin_amdgcn_sched_barrier(0);
             }
             kb0 += WAVES * U;
             if (kb0 >= nblk) break;
@@ -372,10 +424,13 @@ __global__ __launch_bounds__(WAVES * 64) void gemv_nested16_kernel(
 
 // Launch shapes measured on MI355X over the Llama-7B decode linears at M = 4
 // and 8 (weights cold in HBM): the FP8 GEMV runs 16 waves of 2 blocks each
-// per 16-row tile with the default cache policy (each 128-byte weight line is
-// read by two load instructions, one per 64-byte half, and a non-temporal
-// first half does not stay in L2 for the second: 18-22% slower on the large
-// projections); the NestedFP FP16 GEMV keeps 4 waves of 4 blocks.
+// per 16-row tile; the NestedFP FP16 GEMV keeps 4 waves of 4 blocks.  The FP8
+// weights are read as whole lines with non-temporal loads and exchanged into
+// the operand layout (wline, w_to_mfma): decode steps at M = 4 / 8 3.55 ->
+// 3.75 / 3.34 -> 3.53-3.67 TB/s, Qwen-32B M = 16 2.94 -> 3.51-3.64 TB/s,
+// against loads of 64-byte halves in the operand layout, which needed the
+// default cache policy to keep each line in L2 for its second half (with
+// non-temporal halves 18-22% slower on the large projections).
 constexpr int kGemvWaves = 16;
 constexpr int kGemvUnroll = 2;
 // workgroups of the one-launch linear: two per CU of an MI355X at most, the
@@ -421,16 +476,16 @@ hipError_t launch_gemv_fp8(const uint8_t* qa, const float* sa, const uint8_t* qw
     const int64_t tiles = ((int64_t)N + 15) / 16;
     const dim3 block(kGemvWaves * 64), grid((unsigned)tiles);
     if (wfmt == WF_E4M3 && outf == OUT_BF16 && tiles >= kGemvPairedTiles)
-        gemv_f8_kernel<WF_E4M3, OUT_BF16, kGemvWaves, 1, CP_DEFAULT, 2>
+        gemv_f8_kernel<WF_E4M3, OUT_BF16, kGemvWaves, 1, CP_NT, 2>
             <<<dim3((unsigned)((tiles + 1) / 2)), block, 0, stream>>>(qa, sa, qw, sw, y, M, N, K, rowscale);
     else if (wfmt == WF_E4M3 && outf == OUT_BF16)
-        gemv_f8_kernel<WF_E4M3, OUT_BF16, kGemvWaves, kGemvUnroll, CP_DEFAULT>
+        gemv_f8_kernel<WF_E4M3, OUT_BF16, kGemvWaves, kGemvUnroll, CP_NT>
             <<<grid, block, 0, stream>>>(qa, sa, qw, sw, y, M, N, K, rowscale);
     else if (wfmt == WF_E5M2 && outf == OUT_FP16 && !rowscale)
-        gemv_f8_kernel<WF_E5M2, OUT_FP16, kGemvWaves, kGemvUnroll, CP_DEFAULT>
+        gemv_f8_kernel<WF_E5M2, OUT_FP16, kGemvWaves, kGemvUnroll, CP_NT>
             <<<grid, block, 0, stream>>>(qa, sa, qw, sw, y, M, N, K, 0);
     else if (wfmt == WF_E4M3_SC8 && outf == OUT_FP16 && !rowscale)
-        gemv_f8_kernel<WF_E4M3_SC8, OUT_FP16, kGemvWaves, kGemvUnroll, CP_DEFAULT>
+        gemv_f8_kernel<WF_E4M3_SC8, OUT_FP16, kGemvWaves, kGemvUnroll, CP_NT>
             <<<grid, block, 0, stream>>>(qa, sa, qw, sw, y, M, N, K, 0);
     else
         return hipErrorInvalidValue;
