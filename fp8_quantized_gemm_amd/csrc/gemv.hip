@@ -51,7 +51,7 @@ __device__ __forceinline__ v8i cat(const v4i& lo, const v4i& hi)
 // byte offsets within the tile and the K offsets of its units.
 struct WLine {
     uint32_t oa, ob;   // byte offset in the tile of the lane's unit of A / B in block 0
-    int ka, kb;        // K offset of that unit within a block
+    int ua, ub;        // K offset of that unit within a block
 };
 __device__ __forceinline__ WLine wline(int lane, int K)
 {
@@ -133,8 +133,8 @@ __global__ __launch_bounds__(WAVES * 64) void gemv_f8_kernel(
             const int k1 = k0 + 64;
             const uint32_t o0 = k0 < K ? row_off + k0 : kOOB;
             const uint32_t o1 = k1 < K ? row_off + k1 : kOOB;
-            const uint32_t pa = kb + wl.ka < K ? wl.oa + kb : kOOB;
-            const uint32_t pb = kb + wl.kb < K ? wl.ob + kb : kOOB;
+            const uint32_t pa = kb + wl.ua < K ? wl.oa + kb : kOOB;
+            const uint32_t pb = kb + wl.ub < K ? wl.ob + kb : kOOB;
 #pragma unroll
             for (int t = 0; t < TPW; ++t) {
                 w0[t][u] = buf_load16<CP>(rw[t], pa);
@@ -248,8 +248,8 @@ void gemv_f8_fused_kernel(
 #pragma unroll
         for (int u = 0; u < U; ++u) {
             const int kb = (kb0 + u * WAVES) * 128;
-            w0[u] = buf_load16<CP_NT>(rw, kb + wl.ka < K ? wl.oa + kb : kOOB);
-            w1[u] = buf_load16<CP_NT>(rw, kb + wl.kb < K ? wl.ob + kb : kOOB);
+            w0[u] = buf_load16<CP_NT>(rw, kb + wl.ua < K ? wl.oa + kb : kOOB);
+            w1[u] = buf_load16<CP_NT>(rw, kb + wl.ub < K ? wl.ob + kb : kOOB);
         }
     };
     auto tile_rsrc = [&](int t) {
