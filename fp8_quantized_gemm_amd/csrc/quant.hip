@@ -142,19 +142,20 @@ __global__ __launch_bounds__(kBigThreads) void quant_kernel(const uint16_t* __re
 // vectors before it reads the partial maxima.  Against 256-thread workgroups
 // with four vectors and up to 2048 workgroups: 2% faster at 512 x 4096, 17%
 // at 2048 x 11008 and 1024 x 25600.  The quantize pass reads x for the last
-// time, with non-temporal loads (prefill steps +0.5%).  Decode-sized activations (up to 65536
-// vectors) instead take one vector per thread of 256-thread workgroups: the
-// 44032 elements of the Llama-7B down projection at M = 4 then spread over 22
-// workgroups instead of 3, since one CU streams only a few tens of GB/s
-// (decode steps at M = 4 / 8 and Qwen-32B M = 16 1.5-5% faster).
+// time, with non-temporal loads (prefill steps +0.5%).  Decode-sized
+// activations (up to 65536 vectors) instead take one vector per thread of
+// 256-thread workgroups: the 44032 elements of the Llama-7B down projection
+// at M = 4 then spread over 22 workgroups instead of 3, since one CU streams
+// only a few tens of GB/s (decode steps at M = 4 / 8 and Qwen-32B M = 16
+// 1.5-5% faster).
 constexpr int kPartThreads = 1024;
 constexpr int kPartUnroll = 2;
 constexpr int kPartMaxGrid = 512;
 constexpr int kPartSmallThreads = 256;
 
 template <int DT, int NT, int U>
-__global__ __launch_bounds__(NT) void amax_partial_kernel(const uint16_t* __restrict__ x,
-                                                                    int64_t n, float* __restrict__ part)
+__global__ __launch_bounds__(NT) void amax_partial_kernel(const uint16_t* __restrict__ x, int64_t n,
+                                                          float* __restrict__ part)
 {
     __shared__ float lds[NT / 64];
     const int64_t nvec = n >> 3;
