@@ -401,7 +401,8 @@ def secondary(torch, fp8q, synth, model1, dev, parts=PARTS, graph=True):
     if "nested" not in parts:
         return out
     # NestedFP at M = 1 and 256 on all 32 layers of fp16 weights (hi/lo planes:
-    # 12.95 GB, and as much again for the E4M3 upper-byte split)
+    # 12.95 GB, and as much again for the E4M3 upper-byte split), and at the
+    # decode sizes M = 4, 8 of the GEMV path
     nested = []
     nested4 = []                       # planes of the E4M3 upper-byte split
     for layer in range(LAYERS):
@@ -412,7 +413,7 @@ def secondary(torch, fp8q, synth, model1, dev, parts=PARTS, graph=True):
             del w
             nested.append((K, N, hi, lo))
             nested4.append((hi4, lo4))
-    for M in (1, 256):
+    for M in (1, 4, 8, 256):
         bufs = []
         for K, N, hi, lo in nested:
             a = synth.activation(M, K, seed=synth.seed_for("a16", M, K, N), dtype="fp16", device=dev)

@@ -354,9 +354,60 @@ void gemv_f8_fused_kernel(
 
 // ---------------------------------------------------------------- NestedFP FP16 GEMV
 // y[m, n] = fp16( sum_k a[m,k] * fp16((hi[n,k] << 8) | lo[n,k]) ).
-// A K block is 64 elements: lane group g takes elements [16g, 16g+16) (16
-// bytes of hi, 16 of lo, 32 of a) and feeds two 16x16x32 MFMAs.  Same
-// buffer-load scheme as the FP8 GEMV.
+// A K block is 128 elements, one 128-byte line of each plane row.  Each plane
+// is read as whole lines with non-temporal loads: load A takes rows 0..7 of
+// the tile, lane l the 16-byte unit l & 7 of row l >> 3, and load B rows
+// 8..15 with the units of each pair swapped (unit (l & 7) ^ 1), and
+// plane_to_mfma gives lane L = r + 16 g the units 2g and 2g + 1 of row r
+// (elements [32g, 32g + 32) of the block); the activation elements of the
+// same positions are loaded directly (four 16-byte pieces).  Each unit is
+// rebuilt into 16 fp16 words and feeds two 16x16x32 MFMAs.
+struct PLine {
+    uint32_t oa, ob;   // byte offset in the tile of the lane's unit of A / B in block 0
+    int ua, ub;        // K offset of that unit within a block
+};
+__device__ __forceinline__ PLine pline(int lane, int K)
+{
+    const int ua = lane & 7, ub = (lane & 7) ^ 1;
+    return PLine{(uint32_t)((lane >> 3) * K + ua * 16), (uint32_t)(((lane >> 3) + 8) * K + ub * 16),
+                 ua * 16, ub * 16};
+}
+
+// Lane L = r + 16 g gets units 2g (u0) and 2g + 1 (u1) of row r from the two
+// whole-line loads: with B's pairs swapped the lanes each exchange reads are
+// all distinct, so a per-lane select on the source side (odd lanes give B to
+// u0, A to u1) and one ds_bpermute per dword do it.
+__device__ __forceinline__ void plane_to_mfma(const v4i& a, const v4i& b, int lane, v4i& u0, v4i& u1)
+{
+    const int r = lane & 15, g = lane >> 4, up = r >> 3;
+    const int base = (r & 7) * 8 + 2 * g;
+    const int s0 = (base + up) << 2, s1 = (base + 1 - up) << 2;
+    const bool odd = (lane & 1) != 0;
+#pragma unroll
+    for (int d = 0; d < 4; ++d) {
+        u0[d] = __builtin_amdgcn_ds_bpermute(s0, odd ? b[d] : a[d]);
+        u1[d] = __builtin_amdgcn_ds_bpermute(s1, odd ? a[d] : b[d]);
+    }
+}
+
+// 16 bytes of each plane (16 elements) -> two MFMAs on activation pieces x0, x1
+template <int SP>
+__device__ __forceinline__ v4f nested_unit_mfma(const v4i& hv, const v4i& lv, const v4i& x0,
+                                                const v4i& x1, v4f acc)
+{
+    uint32_t w[8];
+    nested_rebuild4<SP>((uint32_t)hv[0], (uint32_t)lv[0], w[0], w[1]);
+    nested_rebuild4<SP>((uint32_t)hv[1], (uint32_t)lv[1], w[2], w[3]);
+    nested_rebuild4<SP>((uint32_t)hv[2], (uint32_t)lv[2], w[4], w[5]);
+    nested_rebuild4<SP>((uint32_t)hv[3], (uint32_t)lv[3], w[6], w[7]);
+    const v4i wlo = {(int)w[0], (int)w[1], (int)w[2], (int)w[3]};
+    const v4i whi = {(int)w[4], (int)w[5], (int)w[6], (int)w[7]};
+    acc = __builtin_amdgcn_mfma_f32_16x16x32_f16(__builtin_bit_cast(v8h, x0),
+                                                 __builtin_bit_cast(v8h, wlo), acc, 0, 0, 0);
+    return __builtin_amdgcn_mfma_f32_16x16x32_f16(__builtin_bit_cast(v8h, x1),
+                                                  __builtin_bit_cast(v8h, whi), acc, 0, 0, 0);
+}
+
 template <int WAVES, int U, int CP, int SP>
 __global__ __launch_bounds__(WAVES * 64) void gemv_nested16_kernel(
     const uint16_t* __restrict__ a, const uint8_t* __restrict__ hi,
@@ -373,38 +424,37 @@ __global__ __launch_bounds__(WAVES * 64) void gemv_nested16_kernel(
     const rsrc_t rh = make_rsrc(hi + (size_t)n0 * K, (uint32_t)(rows * K));
     const rsrc_t rl = make_rsrc(lo + (size_t)n0 * K, (uint32_t)(rows * K));
     const rsrc_t ra = make_rsrc(a, (uint32_t)(M * K * 2));
-    const uint32_t row_off = (uint32_t)(r * K);
+    const uint32_t row_off = (uint32_t)(r * K);   // past the resource for padded rows
+    const PLine pl = pline(lane, K);
 
-    const int nblk = (K + 63) >> 6;
+    const int nblk = (K + 127) >> 7;
     v4f acc = {0.f, 0.f, 0.f, 0.f};
 
     for (int kb0 = wave; kb0 < nblk; kb0 += WAVES * U) {
-        v4i hv[U], lv[U], a0[U], a1[U];
+        v4i ha[U], hb[U], la[U], lb[U], x[U][4];
 #pragma unroll
         for (int u = 0; u < U; ++u) {
-            const int k0 = (kb0 + u * WAVES) * 64 + g * 16;
-            const bool in = k0 < K;
-            const uint32_t ow = in ? row_off + k0 : kOOB;
-            const uint32_t oa = in ? 2 * (row_off + k0) : kOOB;
-            hv[u] = buf_load16<CP>(rh, ow);
-            lv[u] = buf_load16<CP>(rl, ow);
-            a0[u] = buf_load16(ra, oa);
-            a1[u] = buf_load16(ra, in ? oa + 16 : kOOB);
+            const int kb = (kb0 + u * WAVES) * 128;
+            const uint32_t pa = kb + pl.ua < K ? pl.oa + kb : kOOB;
+            const uint32_t pb = kb + pl.ub < K ? pl.ob + kb : kOOB;
+            ha[u] = buf_load16<CP>(rh, pa);
+            hb[u] = buf_load16<CP>(rh, pb);
+            la[u] = buf_load16<CP>(rl, pa);
+            lb[u] = buf_load16<CP>(rl, pb);
+#pragma unroll
+            for (int j = 0; j < 4; ++j) {
+                const int k = kb + 32 * g + 8 * j;   // K % 16 == 0: a piece is all in or all out
+                x[u][j] = buf_load16(ra, k < K ? 2 * (row_off + k) : kOOB);
+            }
         }
         __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
         for (int u = 0; u < U; ++u) {
-            uint32_t w[8];
-            nested_rebuild4<SP>((uint32_t)hv[u][0], (uint32_t)lv[u][0], w[0], w[1]);
-            nested_rebuild4<SP>((uint32_t)hv[u][1], (uint32_t)lv[u][1], w[2], w[3]);
-            nested_rebuild4<SP>((uint32_t)hv[u][2], (uint32_t)lv[u][2], w[4], w[5]);
-            nested_rebuild4<SP>((uint32_t)hv[u][3], (uint32_t)lv[u][3], w[6], w[7]);
-            const v4i wlo = {(int)w[0], (int)w[1], (int)w[2], (int)w[3]};
-            const v4i whi = {(int)w[4], (int)w[5], (int)w[6], (int)w[7]};
-            acc = __builtin_amdgcn_mfma_f32_16x16x32_f16(__builtin_bit_cast(v8h, a0[u]),
-                                                         __builtin_bit_cast(v8h, wlo), acc, 0, 0, 0);
-            acc = __builtin_amdgcn_mfma_f32_16x16x32_f16(__builtin_bit_cast(v8h, a1[u]),
-                                                         __builtin_bit_cast(v8h, whi), acc, 0, 0, 0);
+            v4i h0, h1, l0, l1;
+            plane_to_mfma(ha[u], hb[u], lane, h0, h1);
+            plane_to_mfma(la[u], lb[u], lane, l0, l1);
+            acc = nested_unit_mfma<SP>(h0, l0, x[u][0], x[u][1], acc);
+            acc = nested_unit_mfma<SP>(h1, l1, x[u][2], x[u][3], acc);
         }
     }
 
@@ -465,7 +515,7 @@ inline int64_t gemv_grid(int64_t N)
 // 2.70 -> 2.86-2.95 TB/s.
 constexpr int64_t kGemvPairedTiles = 2 * kGemvSlots;
 constexpr int kNestedWaves = 4;
-constexpr int kNestedUnroll = 4;
+constexpr int kNestedUnroll = 2;   // 128-element blocks: the bytes in flight of 4 blocks of 64
 
 }  // namespace
 

@@ -55,9 +55,11 @@ def _one_hot_f16(M, K, cols):
 
 
 @pytest.mark.parametrize("M,N,K", [(1, 24, 32), (2, 40, 48), (16, 40, 64), (256, 130, 256),
-                                   (48, 33, 48)])
+                                   (48, 33, 48), (16, 40, 272), (7, 17, 400)])
 def test_fp16_mode_identity_bit_exact(M, N, K):
-    """a = one-hot rows: y = rebuilt weight bit-exactly (subnormals included)."""
+    """a = one-hot rows: y = rebuilt weight bit-exactly (subnormals included);
+    16 x 40 x 272 and 7 x 17 x 400 run the decode GEMV over several whole-line
+    128-element blocks and a one-unit last block."""
     rng = np.random.Generator(np.random.PCG64(M * N * K))
     w = _finite_weights(rng, N, K)
     hi, lo = oracle.nested_split(w)
@@ -122,13 +124,13 @@ def test_fp8_mode_random(M, N, K):
     assert_within(oracle.f16_decode(y).ravel(), ref, ab, f"fp8 mode {M}x{N}x{K}", "fp16")
 
 
-@pytest.mark.parametrize("M", [1, 256, 512, 2048])
+@pytest.mark.parametrize("M", [1, 4, 16, 256, 512, 2048])
 @pytest.mark.parametrize("K,N", [(K, N) for _, K, N in synth.LLAMA7B_LINEARS])
 def test_full_size_llama_shapes_dense(M, K, N):
     """NestedFP on the Llama-7B linear shapes (GPU split, GPU fp16-activation
     quantization for FP8 mode): both planes of every weight row and the
     activation codes bit-exact; outputs of both modes within tolerance of the
-    oracle on every element at M = 1, on 32 seeded rows x all N plus 32
+    oracle on every element at M <= 16, on 32 seeded rows x all N plus 32
     seeded columns x all M otherwise."""
     seed = synth.seed_for("nested", M, K, N)
     a = synth.activation(M, K, seed=seed, dtype="fp16", device=DEV)
